@@ -1,0 +1,450 @@
+/*
+ * msa_oracle.c -- plain CPU oracle of the MSA decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the product path.  It shares no
+ * code with the HIP library.  See msa_oracle.h for the layouts.
+ *
+ * Each function below is the definition written out, one element at a time,
+ * in double precision.  Threads only split independent (row, group) units;
+ * the result does not depend on the thread count.
+ */
+#include "msa_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------ */
+/* Element formats                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* OCP FP8 e4m3fn: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; exponent field 0 is subnormal m/8 * 2^-6.
+ * The KV caches and index keys are e4m3 (vLLM blog, "MSA primer": 128 B per
+ * token of FP8 index key; PR #45744 report: e4m3 allowed, e5m2 excluded). */
+double msa_oracle_e4m3(uint8_t code) {
+  int s = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* E2M1 (FP4): 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is
+ * subnormal m * 0.5.  Magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.  NVFP4 = E2M1
+ * values with one e4m3 scale per 16 elements and a per-tensor scale (vLLM
+ * blog, "AMD NVFP4 MSA kernels": 256 possible e4m3 scales x 8 E2M1
+ * magnitudes). */
+double msa_oracle_e2m1(uint8_t nibble) {
+  int s = (nibble >> 3) & 1;
+  int e = (nibble >> 1) & 3;
+  int m = nibble & 1;
+  double v;
+  if (e == 0)
+    v = 0.5 * (double)m;
+  else
+    v = ldexp(1.0 + 0.5 * (double)m, e - 1);
+  return s ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+double msa_oracle_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double read_plain(int dtype, const void* base, size_t idx) {
+  switch (dtype) {
+    case MSA_OR_F32: return (double)((const float*)base)[idx];
+    case MSA_OR_BF16: return msa_oracle_bf16(((const uint16_t*)base)[idx]);
+    case MSA_OR_FP8: return msa_oracle_e4m3(((const uint8_t*)base)[idx]);
+    default: return NAN;
+  }
+}
+
+/* NVFP4 element: data byte idx/2 (even index in the low nibble) times the
+ * e4m3 scale that covers it. */
+static double read_nvfp4(const void* data, size_t elem, const void* scales,
+                         size_t scale_idx) {
+  uint8_t byte = ((const uint8_t*)data)[elem / 2];
+  uint8_t nib = (elem & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  return msa_oracle_e4m3(((const uint8_t*)scales)[scale_idx]) *
+         msa_oracle_e2m1(nib);
+}
+
+/* Index key element (physical block p, slot t, dim d), without the tensor
+ * scale. */
+static double index_key(const msa_oracle_problem* p, const void* data,
+                        const void* scales, int64_t pb, int t, int d) {
+  size_t row = (size_t)pb * (size_t)p->block_size + (size_t)t;
+  if (p->index_k_dtype == MSA_OR_NVFP4)
+    return read_nvfp4(data, row * (size_t)p->index_dim + (size_t)d, scales,
+                      row * (size_t)(p->index_dim / 16) + (size_t)(d / 16));
+  return read_plain(p->index_k_dtype, data, row * (size_t)p->index_dim + (size_t)d);
+}
+
+/* K or V element (physical block pb, group g, slot t, dim d), without the
+ * tensor scale.  kv = 0 reads K ([t][d]); kv = 1 reads V, stored [d][t]. */
+static double kv_elem(const msa_oracle_problem* p, const void* data,
+                      const void* scales, int64_t pb, int kv, int g, int t, int d) {
+  size_t plane = ((size_t)pb * 2 + (size_t)kv) * (size_t)p->num_groups + (size_t)g;
+  size_t per = (size_t)p->block_size * (size_t)p->head_dim;
+  size_t inner = kv == 0 ? (size_t)t * (size_t)p->head_dim + (size_t)d
+                         : (size_t)d * (size_t)p->block_size + (size_t)t;
+  if (p->kv_dtype == MSA_OR_NVFP4) {
+    size_t sidx = kv == 0 ? (size_t)t * (size_t)(p->head_dim / 16) + (size_t)(d / 16)
+                          : (size_t)(d / 16) * (size_t)p->block_size + (size_t)t;
+    return read_nvfp4(data, plane * per + inner, scales, plane * (per / 16) + sidx);
+  }
+  return read_plain(p->kv_dtype, data, plane * per + inner);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rows, positions, validity                                                */
+/* ------------------------------------------------------------------------ */
+
+static int check_problem(const msa_oracle_problem* p) {
+  if (!p) return -1;
+  if (p->num_seqs < 0 || p->rows_per_seq < 1 || p->num_groups < 1 ||
+      p->num_q_heads < p->num_groups || p->num_q_heads % p->num_groups ||
+      p->head_dim < 16 || p->head_dim % 16 || p->index_dim < 16 ||
+      p->index_dim % 16 || p->block_size < 2 || p->block_size % 2 ||
+      p->top_k < 1 || p->max_blocks < 1 || p->num_phys_blocks < 1)
+    return -1;
+  return 0;
+}
+
+/* Position of the query row: keys t <= pos are visible.  Decode rows see the
+ * whole cache, including the token just inserted. */
+static int64_t row_pos(const msa_oracle_problem* p, const int32_t* seq_lens,
+                       const int32_t* q_pos, int64_t row) {
+  int64_t b = row / p->rows_per_seq;
+  if (q_pos) return q_pos[row];
+  return (int64_t)seq_lens[b] - 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Thread fan-out over independent (row, group) units                       */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*unit_fn)(void* ctx, int64_t unit);
+typedef struct {
+  unit_fn fn;
+  void* ctx;
+  int64_t n_units;
+  int nthreads;
+  int tid;
+} fan_arg;
+
+static int g_threads_used = 1;
+
+static void* fan_worker(void* a_) {
+  fan_arg* a = (fan_arg*)a_;
+  for (int64_t u = a->tid; u < a->n_units; u += a->nthreads) a->fn(a->ctx, u);
+  return NULL;
+}
+
+static void fan_out(int requested, int64_t n_units, unit_fn fn, void* ctx) {
+  int nt = requested > 0 ? requested : (int)sysconf(_SC_NPROCESSORS_ONLN);
+  if (nt < 1) nt = 1;
+  if (nt > 256) nt = 256;
+  if ((int64_t)nt > n_units) nt = n_units > 0 ? (int)n_units : 1;
+  g_threads_used = nt;
+  pthread_t th[256];
+  fan_arg args[256];
+  for (int i = 0; i < nt; ++i) {
+    args[i].fn = fn;
+    args[i].ctx = ctx;
+    args[i].n_units = n_units;
+    args[i].nthreads = nt;
+    args[i].tid = i;
+  }
+  if (nt == 1) {
+    fan_worker(&args[0]);
+    return;
+  }
+  for (int i = 0; i < nt; ++i) pthread_create(&th[i], NULL, fan_worker, &args[i]);
+  for (int i = 0; i < nt; ++i) pthread_join(th[i], NULL);
+}
+
+int msa_oracle_threads_used(void) { return g_threads_used; }
+
+/* ------------------------------------------------------------------------ */
+/* Step 1+2: index scores and block max-pool                                */
+/* ------------------------------------------------------------------------ */
+
+/* Score of token t for (row, group): the dot product of the group's index
+ * query with the shared index key, times the score scale, in double, then
+ * rounded once to binary32.  One index query per GQA group, one index-key
+ * head shared by all groups (vLLM blog, "MSA primer"; API reference of
+ * MiniMaxM3SparseAttention: the indexer is built with scale = head_dim^-0.5
+ * and num_index_heads = num_kv_heads). */
+static float token_score(const msa_oracle_problem* p, const void* index_q,
+                         const void* ik_data, const void* ik_scales,
+                         const int32_t* block_table, int64_t row, int g, int64_t t) {
+  int64_t b = row / p->rows_per_seq;
+  int64_t j = t / p->block_size;
+  int slot = (int)(t % p->block_size);
+  int64_t pb = block_table[b * (int64_t)p->max_blocks + j];
+  size_t qoff = ((size_t)row * (size_t)p->num_groups + (size_t)g) * (size_t)p->index_dim;
+  double dot = 0.0;
+  for (int d = 0; d < p->index_dim; ++d) {
+    double qd = read_plain(p->index_q_dtype, index_q, qoff + (size_t)d);
+    double kd = index_key(p, ik_data, ik_scales, pb, slot, d);
+    dot += qd * kd;
+  }
+  return (float)(p->index_scale * p->index_k_scale * dot);
+}
+
+typedef struct {
+  const msa_oracle_problem* p;
+  const void *index_q, *ik_data, *ik_scales;
+  const int32_t *block_table, *seq_lens, *q_pos;
+  float* scores;
+} score_ctx;
+
+/* Max-pool: the score of logical block j is the largest token score over
+ * the block's visible tokens (sparse_score_type "max" in the API reference
+ * of MiniMaxM3SparseAttention.__init__).  Blocks past the row's last visible
+ * block get -inf. */
+static void score_unit(void* c_, int64_t unit) {
+  score_ctx* c = (score_ctx*)c_;
+  const msa_oracle_problem* p = c->p;
+  int64_t row = unit / p->num_groups;
+  int g = (int)(unit % p->num_groups);
+  int64_t pos = row_pos(p, c->seq_lens, c->q_pos, row);
+  float* out = c->scores + (size_t)unit * (size_t)p->max_blocks;
+  for (int64_t j = 0; j < p->max_blocks; ++j) {
+    int64_t t0 = j * p->block_size;
+    if (t0 > pos) {
+      out[j] = -INFINITY;
+      continue;
+    }
+    int64_t t1 = t0 + p->block_size - 1;
+    if (t1 > pos) t1 = pos;
+    float best = -INFINITY;
+    for (int64_t t = t0; t <= t1; ++t) {
+      float s = token_score(p, c->index_q, c->ik_data, c->ik_scales,
+                            c->block_table, row, g, t);
+      if (s > best) best = s;
+    }
+    out[j] = best;
+  }
+}
+
+int msa_oracle_index_scores(const msa_oracle_problem* p, const void* index_q,
+                            const void* ik_data, const void* ik_scales,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* q_pos, float* scores) {
+  if (check_problem(p) || !index_q || !ik_data || !block_table || !seq_lens || !scores)
+    return -1;
+  if (p->index_k_dtype == MSA_OR_NVFP4 && !ik_scales) return -1;
+  score_ctx c = {p, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores};
+  int64_t units = (int64_t)p->num_seqs * p->rows_per_seq * p->num_groups;
+  fan_out(p->num_threads, units, score_unit, &c);
+  return 0;
+}
+
+int msa_oracle_token_scores(const msa_oracle_problem* p, const void* index_q,
+                            const void* ik_data, const void* ik_scales,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* q_pos, int32_t row, int32_t group,
+                            float* out) {
+  if (check_problem(p) || !index_q || !ik_data || !block_table || !seq_lens || !out)
+    return -1;
+  int64_t pos = row_pos(p, seq_lens, q_pos, row);
+  for (int64_t t = 0; t <= pos; ++t)
+    out[t] = token_score(p, index_q, ik_data, ik_scales, block_table, row, group, t);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 3: block top-k, most recent block forced                            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  float s;
+  int32_t j;
+} cand;
+
+/* Order: higher pooled score first; equal scores go to the lower logical
+ * block index. */
+static int cand_cmp(const void* a_, const void* b_) {
+  const cand* a = (const cand*)a_;
+  const cand* b = (const cand*)b_;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->j > b->j) - (a->j < b->j);
+}
+
+static int int_cmp(const void* a_, const void* b_) {
+  int32_t a = *(const int32_t*)a_, b = *(const int32_t*)b_;
+  return (a > b) - (a < b);
+}
+
+typedef struct {
+  const msa_oracle_problem* p;
+  const float* scores;
+  const int32_t *seq_lens, *q_pos;
+  int32_t* topk;
+} topk_ctx;
+
+/* The top-k blocks with the most recent block always kept, so at most
+ * top_k * block_size keys per query (vLLM blog, "MSA primer": top 16 blocks,
+ * most recent block always kept, at most 2,048 keys).  The recent block is
+ * the one holding the row's own position; it counts inside the k.  Output:
+ * ascending logical ids, then -1. */
+static void topk_unit(void* c_, int64_t unit) {
+  topk_ctx* c = (topk_ctx*)c_;
+  const msa_oracle_problem* p = c->p;
+  int64_t row = unit / p->num_groups;
+  int64_t pos = row_pos(p, c->seq_lens, c->q_pos, row);
+  int32_t recent = (int32_t)(pos / p->block_size);
+  const float* s = c->scores + (size_t)unit * (size_t)p->max_blocks;
+  int32_t* out = c->topk + (size_t)unit * (size_t)p->top_k;
+  int32_t n_sel = 0;
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)p->top_k);
+  if (recent + 1 <= p->top_k) {
+    for (int32_t j = 0; j <= recent; ++j) sel[n_sel++] = j;
+  } else {
+    cand* cs = (cand*)malloc(sizeof(cand) * (size_t)recent);
+    for (int32_t j = 0; j < recent; ++j) {
+      cs[j].s = s[j];
+      cs[j].j = j;
+    }
+    qsort(cs, (size_t)recent, sizeof(cand), cand_cmp);
+    for (int32_t i = 0; i < p->top_k - 1; ++i) sel[n_sel++] = cs[i].j;
+    sel[n_sel++] = recent;
+    free(cs);
+    qsort(sel, (size_t)n_sel, sizeof(int32_t), int_cmp);
+  }
+  for (int32_t i = 0; i < p->top_k; ++i) out[i] = i < n_sel ? sel[i] : -1;
+  free(sel);
+}
+
+int msa_oracle_block_topk(const msa_oracle_problem* p, const float* scores,
+                          const int32_t* seq_lens, const int32_t* q_pos,
+                          int32_t* topk) {
+  if (check_problem(p) || !scores || !seq_lens || !topk) return -1;
+  topk_ctx c = {p, scores, seq_lens, q_pos, topk};
+  int64_t units = (int64_t)p->num_seqs * p->rows_per_seq * p->num_groups;
+  fan_out(p->num_threads, units, topk_unit, &c);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 4: exact GQA softmax attention over the selected blocks             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const msa_oracle_problem* p;
+  const void *q, *kv_data, *kv_scales;
+  const int32_t *block_table, *seq_lens, *q_pos, *topk;
+  double *out, *lse;
+} attend_ctx;
+
+/* Every query head of group g attends exactly the group's selected blocks
+ * (vLLM blog, "MSA primer", Figure 1 caption); within them the attention is
+ * the ordinary softmax(sm_scale * q.k) weighted sum of v over the visible
+ * tokens (t <= pos).  sm_scale is head_dim^-0.5 in the API reference of
+ * MiniMaxM3SparseAttention. */
+static void attend_unit(void* c_, int64_t unit) {
+  attend_ctx* c = (attend_ctx*)c_;
+  const msa_oracle_problem* p = c->p;
+  int64_t row = unit / p->num_groups;
+  int g = (int)(unit % p->num_groups);
+  int64_t b = row / p->rows_per_seq;
+  int64_t pos = row_pos(p, c->seq_lens, c->q_pos, row);
+  const int32_t* sel = c->topk + (size_t)unit * (size_t)p->top_k;
+  int hpg = p->num_q_heads / p->num_groups;
+  int D = p->head_dim;
+
+  /* gather the visible tokens of the selected blocks */
+  int64_t max_tok = (int64_t)p->top_k * p->block_size;
+  int64_t* tok_pb = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_tok);
+  int* tok_slot = (int*)malloc(sizeof(int) * (size_t)max_tok);
+  int64_t n = 0;
+  for (int i = 0; i < p->top_k; ++i) {
+    int32_t j = sel[i];
+    if (j < 0) continue;
+    int64_t pb = c->block_table[b * (int64_t)p->max_blocks + j];
+    for (int t = 0; t < p->block_size; ++t) {
+      int64_t tok = (int64_t)j * p->block_size + t;
+      if (tok > pos) break;
+      tok_pb[n] = pb;
+      tok_slot[n] = t;
+      ++n;
+    }
+  }
+  double* logit = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int hh = 0; hh < hpg; ++hh) {
+    int h = g * hpg + hh;
+    size_t qoff = ((size_t)row * (size_t)p->num_q_heads + (size_t)h) * (size_t)D;
+    double* o = c->out + qoff;
+    double mx = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += read_plain(p->q_dtype, c->q, qoff + (size_t)d) *
+               (p->k_scale * kv_elem(p, c->kv_data, c->kv_scales, tok_pb[i], 0, g,
+                                     tok_slot[i], d));
+      logit[i] = p->sm_scale * dot;
+      if (logit[i] > mx) mx = logit[i];
+    }
+    double den = 0.0;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+      double w = exp(logit[i] - mx);
+      den += w;
+      for (int d = 0; d < D; ++d)
+        o[d] += w * (p->v_scale * kv_elem(p, c->kv_data, c->kv_scales, tok_pb[i], 1,
+                                          g, tok_slot[i], d));
+    }
+    for (int d = 0; d < D; ++d) o[d] = n > 0 ? o[d] / den : 0.0;
+    if (c->lse)
+      c->lse[(size_t)row * (size_t)p->num_q_heads + (size_t)h] =
+          n > 0 ? mx + log(den) : -INFINITY;
+  }
+  free(logit);
+  free(tok_pb);
+  free(tok_slot);
+}
+
+int msa_oracle_sparse_attend(const msa_oracle_problem* p, const void* q,
+                             const void* kv_data, const void* kv_scales,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* q_pos, const int32_t* topk,
+                             double* out, double* lse) {
+  if (check_problem(p) || !q || !kv_data || !block_table || !seq_lens || !topk || !out)
+    return -1;
+  if (p->kv_dtype == MSA_OR_NVFP4 && !kv_scales) return -1;
+  attend_ctx c = {p, q, kv_data, kv_scales, block_table, seq_lens, q_pos, topk, out, lse};
+  int64_t units = (int64_t)p->num_seqs * p->rows_per_seq * p->num_groups;
+  fan_out(p->num_threads, units, attend_unit, &c);
+  return 0;
+}
+
+int msa_oracle_decode(const msa_oracle_problem* p, const void* index_q,
+                      const void* ik_data, const void* ik_scales, const void* q,
+                      const void* kv_data, const void* kv_scales,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* q_pos, float* scores, int32_t* topk,
+                      double* out, double* lse) {
+  int rc = msa_oracle_index_scores(p, index_q, ik_data, ik_scales, block_table,
+                                   seq_lens, q_pos, scores);
+  if (rc) return rc;
+  rc = msa_oracle_block_topk(p, scores, seq_lens, q_pos, topk);
+  if (rc) return rc;
+  return msa_oracle_sparse_attend(p, q, kv_data, kv_scales, block_table, seq_lens,
+                                  q_pos, topk, out, lse);
+}

@@ -1,0 +1,381 @@
+"""Seeded synthetic workloads for the MSA decode path.
+
+Both the CPU oracle and the HIP library consume the bytes made here.  This
+module holds none of the method's arithmetic: it draws counter-based normals
+(``synth.c``), encodes them into the stored formats (bf16, OCP e4m3fn,
+NVFP4), and lays out the paged caches, block tables and lengths.
+
+Workload recipes (shapes of the pages' workloads; all values seeded):
+
+* ``tiny``    1 sequence of 4,096 tokens (32 blocks), 4 groups x 4 heads,
+              fp32 everything, identity block table, +2.0 added to every
+              index-key element of 3 random blocks.
+* ``fp8_b32`` 32 sequences x 32,768 tokens, 64 query heads in 4 groups,
+              bf16 queries, e4m3 K/V/index keys (tensor scales 1.0), random
+              permutation block table.
+* ``fp8_long`` 8 sequences, lengths uniform in [131,072, 262,144] (a partial
+              last block allowed), as ``fp8_b32`` plus 8 planted high-score
+              blocks per sequence.
+* ``nvfp4_512k`` 4 sequences x 524,288 tokens, NVFP4 K/V/index keys.
+* ``custom``  any of the above knobs, for edge cases.
+
+Layouts are documented in ``include/msa.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libmsa_synth.so")
+_SRC = os.path.join(_HERE, "synth.c")
+
+F32, BF16, FP8, NVFP4 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", NVFP4: "nvfp4"}
+
+# NVFP4 per-tensor scale used by the quantiser: values of magnitude up to 8
+# map onto the largest e4m3 scale (448) times the largest E2M1 value (6).
+NVFP4_TENSOR_SCALE = 8.0 / (6.0 * 448.0)
+
+STREAM_INDEX_Q, STREAM_Q, STREAM_IK, STREAM_KV = 1, 2, 3, 4
+STREAM_TABLE, STREAM_LENS, STREAM_PLANT = 5, 6, 7
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build(force=False)
+        L = ctypes.CDLL(_SO)
+        u64, vp = ctypes.c_uint64, ctypes.c_void_p
+        L.synth_key.restype = u64
+        L.synth_key.argtypes = [u64, u64]
+        L.synth_u64.argtypes = [u64, u64, u64, vp]
+        L.synth_normal_f32.argtypes = [u64, u64, u64, vp]
+        L.synth_normal_e4m3.argtypes = [u64, u64, u64, vp]
+        L.synth_encode_e4m3.argtypes = [vp, u64, vp]
+        L.synth_encode_bf16.argtypes = [vp, u64, vp]
+        L.synth_nvfp4_rows.argtypes = [vp, u64, ctypes.c_int, ctypes.c_float, vp, vp]
+        _lib = L
+    return _lib
+
+
+def key(seed: int, stream: int) -> int:
+    return lib().synth_key(seed, stream)
+
+
+def normal(seed: int, stream: int, first: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    lib().synth_normal_f32(key(seed, stream), first, n, out.ctypes.data)
+    return out
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().synth_encode_e4m3(x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def encode_bf16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().synth_encode_bf16(x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def encode_nvfp4_rows(x: np.ndarray, g: float = NVFP4_TENSOR_SCALE):
+    """x[..., dim] -> (data[..., dim/2], scales[..., dim/16])."""
+    x = np.ascontiguousarray(x, np.float32)
+    dim = x.shape[-1]
+    rows = x.size // dim
+    data = np.empty(x.shape[:-1] + (dim // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (dim // 16,), np.uint8)
+    lib().synth_nvfp4_rows(x.ctypes.data, rows, dim, g, data.ctypes.data,
+                           scales.ctypes.data)
+    return data, scales
+
+
+def _nibbles_T(data: np.ndarray) -> np.ndarray:
+    """[..., t, d/2] packed along d -> [..., d, t/2] packed along t."""
+    lo = data & 15
+    hi = data >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(data.shape[:-1] + (data.shape[-1] * 2,))
+    codes = np.swapaxes(codes, -1, -2)  # [..., d, t]
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+@dataclass
+class Workload:
+    name: str
+    num_seqs: int
+    rows_per_seq: int
+    num_q_heads: int
+    num_groups: int
+    head_dim: int
+    index_dim: int
+    block_size: int
+    top_k: int
+    max_blocks: int
+    num_phys_blocks: int
+    q_dtype: int
+    index_q_dtype: int
+    kv_dtype: int
+    index_k_dtype: int
+    sm_scale: float
+    index_scale: float
+    k_scale: float
+    v_scale: float
+    index_k_scale: float
+    index_q: np.ndarray
+    q: np.ndarray
+    ik_data: np.ndarray
+    ik_scales: np.ndarray | None
+    kv_data: np.ndarray
+    kv_scales: np.ndarray | None
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    q_pos: np.ndarray | None
+    planted: dict = field(default_factory=dict)
+    recipe: str = ""
+
+    @property
+    def rows(self) -> int:
+        return self.num_seqs * self.rows_per_seq
+
+    def problem_fields(self) -> dict:
+        keys = ["num_seqs", "rows_per_seq", "num_q_heads", "num_groups", "head_dim",
+                "index_dim", "block_size", "top_k", "max_blocks", "num_phys_blocks",
+                "q_dtype", "index_q_dtype", "kv_dtype", "index_k_dtype", "sm_scale",
+                "index_scale", "k_scale", "v_scale", "index_k_scale"]
+        return {k: getattr(self, k) for k in keys}
+
+    def index_tokens(self) -> int:
+        if self.q_pos is not None:
+            return int(np.sum(self.q_pos.astype(np.int64) + 1))
+        return int(np.sum(self.seq_lens.astype(np.int64)))
+
+
+def _encode_plain(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == F32:
+        return np.ascontiguousarray(x, np.float32)
+    if dtype == BF16:
+        return encode_bf16(x)
+    if dtype == FP8:
+        return encode_e4m3(x)
+    raise ValueError(dtype)
+
+
+def _bytes_per(dtype: int) -> int:
+    return {F32: 4, BF16: 2, FP8: 1}[dtype]
+
+
+def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs: int = 1,
+         rows_per_seq: int = 1, q_pos=None, num_q_heads: int = 64, num_groups: int = 4,
+         head_dim: int = 128, index_dim: int = 128, block_size: int = 128, top_k: int = 16,
+         q_dtype: int = BF16, index_q_dtype: int | None = None, kv_dtype: int = FP8,
+         index_k_dtype: int | None = None, table: str = "permute", extra_phys: int = 0,
+         plant_per_seq: int = 0, plant_add: float = 1.0, bump_blocks: int = 0,
+         bump_add: float = 2.0, max_blocks: int | None = None, k_scale: float = 1.0,
+         v_scale: float = 1.0, ik_scale: float | None = None,
+         kv_fill: bool = True) -> Workload:
+    """Build one seeded workload.
+
+    table: "identity" (seq b's block j is physical b*max_blocks+j) or
+    "permute" (a seeded random permutation of the physical pool).
+    plant_per_seq: add ``plant_add * sign(sum_g index_q[b, g, :])`` to every
+    index-key element of that many random non-recent blocks per sequence.
+    bump_blocks: add ``bump_add`` to every index-key element of that many
+    random blocks (of sequence 0).
+    kv_fill: False leaves the K/V pool zero (timing-only callers).
+    """
+    index_q_dtype = q_dtype if index_q_dtype is None else index_q_dtype
+    index_k_dtype = kv_dtype if index_k_dtype is None else index_k_dtype
+    seq_lens = np.asarray(seq_lens if seq_lens is not None else [4096] * num_seqs,
+                          dtype=np.int64)
+    num_seqs = len(seq_lens)
+    BS = block_size
+    nb = (seq_lens + BS - 1) // BS
+    if max_blocks is None:
+        max_blocks = int(max(1, nb.max() if num_seqs else 1))
+    rows = num_seqs * rows_per_seq
+    G, H, D, Di = num_groups, num_q_heads, head_dim, index_dim
+
+    # ---- block table ----
+    P = int(nb.sum()) + extra_phys
+    P = max(P, 1)
+    bt = np.zeros((num_seqs, max_blocks), np.int32)
+    if table == "identity":
+        P = max(P, num_seqs * max_blocks)
+        for b in range(num_seqs):
+            bt[b, : nb[b]] = np.arange(b * max_blocks, b * max_blocks + nb[b])
+    else:
+        perm = np.random.default_rng([seed, STREAM_TABLE]).permutation(P).astype(np.int32)
+        off = 0
+        for b in range(num_seqs):
+            bt[b, : nb[b]] = perm[off: off + nb[b]]
+            off += nb[b]
+
+    # ---- queries ----
+    iq_f = normal(seed, STREAM_INDEX_Q, 0, rows * G * Di).reshape(rows, G, Di)
+    q_f = normal(seed, STREAM_Q, 0, rows * H * D).reshape(rows, H, D)
+    index_q = _encode_plain(iq_f, index_q_dtype)
+    q = _encode_plain(q_f, q_dtype)
+
+    # ---- planted / bumped index-key blocks (added before encoding) ----
+    add_vec = {}  # physical block -> vector added to every token of the block
+    planted = {}
+    rng_p = np.random.default_rng([seed, STREAM_PLANT])
+    if plant_per_seq:
+        iq_vals = (index_q.astype(np.uint32) << 16).view(np.float32) \
+            if index_q_dtype == BF16 else index_q.astype(np.float32)
+        for b in range(num_seqs):
+            recent = int(nb[b]) - 1
+            choices = rng_p.choice(recent, size=min(plant_per_seq, recent), replace=False)
+            planted[b] = sorted(int(c) for c in choices)
+            r0 = b * rows_per_seq
+            u = np.sign(iq_vals[r0].astype(np.float64).sum(axis=0)).astype(np.float32)
+            u[u == 0] = 1.0
+            for j in planted[b]:
+                add_vec[int(bt[b, j])] = plant_add * u
+    if bump_blocks:
+        choices = rng_p.choice(int(nb[0]), size=min(bump_blocks, int(nb[0])), replace=False)
+        planted[0] = sorted(int(c) for c in choices)
+        for j in planted[0]:
+            add_vec[int(bt[0, j])] = np.full(Di, bump_add, np.float32)
+
+    # ---- index-key pool ----
+    ik_scales = None
+    if index_k_dtype == NVFP4:
+        ik_data = np.empty((P, BS, Di // 2), np.uint8)
+        ik_scales = np.empty((P, BS, Di // 16), np.uint8)
+    else:
+        ik_data = np.empty((P, BS, Di), np.float32 if index_k_dtype == F32 else np.uint8)
+    per_blk = BS * Di
+    chunk = max(1, (1 << 22) // per_blk)
+
+    def gen_ik(p0):
+        p1 = min(P, p0 + chunk)
+        x = normal(seed, STREAM_IK, p0 * per_blk, (p1 - p0) * per_blk).reshape(p1 - p0, BS, Di)
+        for pb in range(p0, p1):
+            v = add_vec.get(pb)
+            if v is not None:
+                x[pb - p0] += v[None, :]
+        if index_k_dtype == NVFP4:
+            d, s = encode_nvfp4_rows(x)
+            ik_data[p0:p1] = d
+            ik_scales[p0:p1] = s
+        else:
+            ik_data[p0:p1] = _encode_plain(x, index_k_dtype)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(gen_ik, range(0, P, chunk)))
+
+    # ---- K/V pool: plane 0 = K [t][d], plane 1 = V^T [d][t] ----
+    kv_scales = None
+    per_kv = 2 * G * BS * D
+    if kv_dtype == NVFP4:
+        kv_data = np.zeros((P, 2, G, BS * D // 2), np.uint8)
+        kv_scales = np.zeros((P, 2, G, BS * D // 16), np.uint8)
+    elif kv_dtype == F32:
+        kv_data = np.zeros((P, 2, G, BS, D), np.float32)
+    else:
+        kv_data = np.zeros((P, 2, G, BS, D), np.uint8)
+    chunk_kv = max(1, (1 << 22) // per_kv)
+
+    def gen_kv(p0):
+        p1 = min(P, p0 + chunk_kv)
+        x = normal(seed, STREAM_KV, p0 * per_kv, (p1 - p0) * per_kv).reshape(
+            p1 - p0, 2, G, BS, D)
+        if kv_dtype == NVFP4:
+            d, s = encode_nvfp4_rows(x)  # groups of 16 along d for every token
+            kv_data[p0:p1, 0] = d[:, 0].reshape(p1 - p0, G, -1)
+            kv_scales[p0:p1, 0] = s[:, 0].reshape(p1 - p0, G, -1)
+            kv_data[p0:p1, 1] = _nibbles_T(d[:, 1]).reshape(p1 - p0, G, -1)
+            kv_scales[p0:p1, 1] = np.swapaxes(s[:, 1], -1, -2).reshape(p1 - p0, G, -1)
+        else:
+            x[:, 1] = np.swapaxes(x[:, 1], -1, -2)
+            kv_data[p0:p1] = _encode_plain(x, kv_dtype)
+
+    if kv_fill:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(gen_kv, range(0, P, chunk_kv)))
+
+    if ik_scale is None:
+        ik_scale = NVFP4_TENSOR_SCALE if index_k_dtype == NVFP4 else 1.0
+    if kv_dtype == NVFP4:
+        k_scale = k_scale * NVFP4_TENSOR_SCALE
+        v_scale = v_scale * NVFP4_TENSOR_SCALE
+    qp = None if q_pos is None else np.ascontiguousarray(q_pos, np.int32)
+    return Workload(
+        name=name, num_seqs=num_seqs, rows_per_seq=rows_per_seq, num_q_heads=H,
+        num_groups=G, head_dim=D, index_dim=Di, block_size=BS, top_k=top_k,
+        max_blocks=max_blocks, num_phys_blocks=P, q_dtype=q_dtype,
+        index_q_dtype=index_q_dtype, kv_dtype=kv_dtype, index_k_dtype=index_k_dtype,
+        sm_scale=D ** -0.5, index_scale=Di ** -0.5, k_scale=k_scale, v_scale=v_scale,
+        index_k_scale=ik_scale, index_q=index_q, q=q, ik_data=ik_data,
+        ik_scales=ik_scales, kv_data=kv_data, kv_scales=kv_scales, block_table=bt,
+        seq_lens=seq_lens.astype(np.int32), q_pos=qp, planted=planted)
+
+
+# ---------------------------------------------------------------------------
+# The named workloads
+# ---------------------------------------------------------------------------
+
+def tiny(seed: int = 0x4D5341 + 1) -> Workload:
+    w = make("tiny", seed=seed, seq_lens=[4096], num_q_heads=16, num_groups=4,
+             q_dtype=F32, kv_dtype=F32, table="identity", bump_blocks=3, bump_add=2.0)
+    w.recipe = ("1 seq x 4096 tokens, 4 groups x 4 heads, D=Di=128, fp32, N(0,1), "
+                "+2.0 on all index-key elements of 3 random blocks, identity table")
+    return w
+
+
+def fp8_b32(seed: int = 0x4D5341 + 2, **kw) -> Workload:
+    w = make("fp8_b32", seed=seed, seq_lens=[32768] * 32, q_dtype=BF16, kv_dtype=FP8, **kw)
+    w.recipe = ("32 seqs x 32768 tokens, 64 q heads / 4 groups, D=Di=128, bf16 q, "
+                "e4m3 K/V/index keys (scale 1.0), N(0,1), random permutation table")
+    return w
+
+
+def long_lens(seed: int, n: int = 8, lo: int = 131072, hi: int = 262144) -> np.ndarray:
+    rng = np.random.default_rng([seed, STREAM_LENS])
+    return rng.integers(lo, hi + 1, size=n).astype(np.int64)
+
+
+def fp8_long(seed: int = 0x4D5341 + 3, **kw) -> Workload:
+    w = make("fp8_long", seed=seed, seq_lens=long_lens(seed), q_dtype=BF16,
+             kv_dtype=FP8, plant_per_seq=8, plant_add=1.0, **kw)
+    w.recipe = ("8 seqs, lengths U[131072, 262144], 64 q heads / 4 groups, D=Di=128, "
+                "bf16 q, e4m3 K/V/index keys, N(0,1), 8 planted blocks per seq "
+                "(+1.0*sign(sum_g qI) before rounding), random permutation table")
+    return w
+
+
+def nvfp4_512k(seed: int = 0x4D5341 + 4, **kw) -> Workload:
+    w = make("nvfp4_512k", seed=seed, seq_lens=[524288] * 4, q_dtype=BF16,
+             kv_dtype=NVFP4, **kw)
+    w.recipe = ("4 seqs x 524288 tokens, 64 q heads / 4 groups, D=Di=128, bf16 q, "
+                "NVFP4 K/V/index keys quantised from N(0,1), random permutation table")
+    return w

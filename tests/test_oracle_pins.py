@@ -1,0 +1,493 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Every test here runs on the CPU.  The pins are: library decoders of the same
+formats (torch's float8_e4m3fn / bfloat16), the OCP tables, exact integer
+arithmetic, brute-force sorting, an independent dense-attention
+implementation in torch float64, closed-form special cases, and the byte
+arithmetic the pages print (tests/golden/page_numbers.txt).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.txt")
+
+
+def golden():
+    vals = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split("|")[0].split()
+            vals[k] = float(v)
+    return vals
+
+
+# ---------------------------------------------------------------------------
+# element formats
+# ---------------------------------------------------------------------------
+
+def test_e4m3_all_codes_match_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_spec_points():
+    assert oracle.e4m3(0x7E) == 448.0
+    assert oracle.e4m3(0xFE) == -448.0
+    assert oracle.e4m3(0x08) == 2.0 ** -6
+    assert oracle.e4m3(0x01) == 2.0 ** -9
+    assert oracle.e4m3(0x38) == 1.0
+    assert oracle.e4m3(0xC0) == -2.0
+    assert len({oracle.e4m3(c) for c in range(256) if c != 0x7F and c != 0xFF}) == 253
+    assert golden()["e4m3_scales"] == 256
+
+
+def test_e2m1_table():
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # OCP MX spec, FP4 E2M1
+    got = [oracle.e2m1(c) for c in range(16)]
+    assert got[:8] == mags
+    assert got[8:] == [-m for m in mags]
+    assert len(set(abs(v) for v in got)) == golden()["e2m1_magnitudes"]
+
+
+def test_bf16_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = np.concatenate([rng.integers(0, 1 << 16, 20000),
+                           [0, 0x8000, 0x3F80, 0x7F7F, 0x0001, 0x8001]]).astype(np.int64)
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------------------
+# tiny problems built by hand
+# ---------------------------------------------------------------------------
+
+def _tiny_problem(B=2, G=2, hpg=2, D=16, Di=16, BS=4, K=3, lens=(9, 14), table=None,
+                  q_dtype=oracle.F32, kv_dtype=oracle.F32, max_blocks=None):
+    nb = [(L + BS - 1) // BS for L in lens]
+    mb = max_blocks or max(nb)
+    P = sum(nb) + 3
+    bt = np.zeros((B, mb), np.int32)
+    if table is None:
+        perm = np.random.default_rng(7).permutation(P).astype(np.int32)
+        off = 0
+        for b in range(B):
+            bt[b, : nb[b]] = perm[off: off + nb[b]]
+            off += nb[b]
+    else:
+        bt[:] = table
+    p = oracle.Problem(num_seqs=B, num_q_heads=G * hpg, num_groups=G, head_dim=D,
+                       index_dim=Di, block_size=BS, top_k=K, max_blocks=mb,
+                       num_phys_blocks=P, q_dtype=q_dtype, index_q_dtype=q_dtype,
+                       kv_dtype=kv_dtype, index_k_dtype=kv_dtype, num_threads=3)
+    return p, bt, np.asarray(lens, np.int32)
+
+
+def test_index_scores_exact_integers():
+    """Small-integer queries and keys: every score is an exact integer."""
+    p, bt, lens = _tiny_problem()
+    p.index_scale = 1.0
+    p.index_k_scale = 1.0
+    rng = np.random.default_rng(3)
+    iq = rng.integers(-3, 4, (p.num_seqs, p.num_groups, p.index_dim)).astype(np.float32)
+    ik = rng.integers(-3, 4, (p.num_phys_blocks, p.block_size, p.index_dim)).astype(np.float32)
+    got = oracle.index_scores(p, iq, ik, None, bt, lens)
+    for b in range(p.num_seqs):
+        L = int(lens[b])
+        for g in range(p.num_groups):
+            for j in range(p.max_blocks):
+                toks = range(j * p.block_size, min((j + 1) * p.block_size, L))
+                if len(toks) == 0:
+                    assert got[b, g, j] == -np.inf
+                    continue
+                best = None
+                for t in toks:
+                    pb, slot = bt[b, t // p.block_size], t % p.block_size
+                    s = sum(int(iq[b, g, d]) * int(ik[pb, slot, d]) for d in range(p.index_dim))
+                    best = s if best is None else max(best, s)
+                assert got[b, g, j] == best
+
+
+def test_index_scores_scale_is_applied():
+    p, bt, lens = _tiny_problem(lens=(8, 8))
+    rng = np.random.default_rng(4)
+    iq = rng.integers(-3, 4, (2, 2, 16)).astype(np.float32)
+    ik = rng.integers(-3, 4, (p.num_phys_blocks, 4, 16)).astype(np.float32)
+    p.index_scale, p.index_k_scale = 1.0, 1.0
+    base = oracle.index_scores(p, iq, ik, None, bt, lens)
+    p.index_scale, p.index_k_scale = 0.25, 0.5
+    scaled = oracle.index_scores(p, iq, ik, None, bt, lens)
+    assert np.array_equal(scaled, (base.astype(np.float64) * 0.125).astype(np.float32))
+
+
+def test_one_hot_query_reads_fp8_key_elements():
+    """q = e_d gives the key element itself: pins the index-key layout and the
+    e4m3 decode inside scoring."""
+    p, bt, lens = _tiny_problem(lens=(8, 12), kv_dtype=oracle.FP8)
+    p.index_scale = p.index_k_scale = 1.0
+    rng = np.random.default_rng(5)
+    ik = rng.integers(0, 256, (p.num_phys_blocks, 4, 16)).astype(np.uint8)
+    ik[ik == 0x7F] = 0x10
+    ik[ik == 0xFF] = 0x90
+    keys = torch.from_numpy(ik).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for d in (0, 5, 15):
+        iq = np.zeros((2, 2, 16), np.float32)
+        iq[:, :, d] = 1.0
+        got = oracle.index_scores(p, iq, ik, None, bt, lens)
+        for b in range(2):
+            L = int(lens[b])
+            for j in range((L + 3) // 4):
+                vals = [keys[bt[b, j], t % 4, d] for t in range(j * 4, min(j * 4 + 4, L))]
+                assert got[b, 0, j] == np.float32(max(vals))
+
+
+def _decode_plain(arr, dtype):
+    if dtype == oracle.F32:
+        return arr.astype(np.float64)
+    if dtype == oracle.BF16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    if dtype == oracle.FP8:
+        return torch.from_numpy(arr).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    raise ValueError(dtype)
+
+
+def _decode_nvfp4(data, scales):
+    """data[..., n/2], scales[..., n/16] -> values[..., n] (no tensor scale)."""
+    table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
+    codes = np.stack([data & 15, data >> 4], axis=-1).reshape(data.shape[:-1] + (-1,))
+    vals = table[codes]
+    sc = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+    return vals * np.repeat(sc, 16, axis=-1)
+
+
+def _small_workload(kv_dtype, lens=(300, 517, 129), G=2, H=4, top_k=3, q_pos=None,
+                    rows_per_seq=1, seed=11, plant=0):
+    q_dtype = synth.F32 if kv_dtype == synth.F32 else synth.BF16
+    return synth.make("t", seed=seed, seq_lens=list(lens), num_q_heads=H, num_groups=G,
+                      top_k=top_k, q_dtype=q_dtype, kv_dtype=kv_dtype, q_pos=q_pos,
+                      rows_per_seq=rows_per_seq, plant_per_seq=plant)
+
+
+def _oracle_problem(w, threads=4):
+    return oracle.Problem(**w.problem_fields(), num_threads=threads)
+
+
+def _index_keys_f64(w):
+    if w.index_k_dtype == synth.NVFP4:
+        return _decode_nvfp4(w.ik_data, w.ik_scales)
+    return _decode_plain(w.ik_data, w.index_k_dtype)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.FP8, synth.NVFP4])
+def test_pooled_scores_brute_force(dtype):
+    """Token scores by a float64 matrix product on independently decoded keys,
+    rounded to fp32 and max-pooled per block (at most 1 fp32 ulp apart: only
+    the double summation order differs)."""
+    w = _small_workload(dtype)
+    p = _oracle_problem(w)
+    got = oracle.index_scores(p, w.index_q, w.ik_data, w.ik_scales, w.block_table, w.seq_lens)
+    keys = _index_keys_f64(w) * w.index_k_scale  # [P, BS, Di]
+    iq = _decode_plain(w.index_q, w.index_q_dtype)
+    BS = w.block_size
+    for b in range(w.num_seqs):
+        L = int(w.seq_lens[b])
+        nb = (L + BS - 1) // BS
+        seq_keys = keys[w.block_table[b, :nb]].reshape(nb * BS, -1)[:L]
+        s = (seq_keys @ iq[b].T * w.index_scale).astype(np.float32)  # [L, G]
+        for j in range(w.max_blocks):
+            if j >= nb:
+                assert np.all(got[b, :, j] == -np.inf)
+                continue
+            ref = s[j * BS: min(L, (j + 1) * BS)].max(axis=0)
+            np.testing.assert_array_max_ulp(got[b, :, j], ref, maxulp=1)
+
+
+def test_partial_block_ignores_tokens_past_the_end():
+    p, bt, lens = _tiny_problem(lens=(9, 14))
+    p.index_scale = p.index_k_scale = 1.0
+    iq = np.ones((2, 2, 16), np.float32)
+    ik = np.zeros((p.num_phys_blocks, 4, 16), np.float32)
+    # garbage in the unused slots of each sequence's last block
+    for b, L in enumerate(lens):
+        last = (L - 1) // 4
+        ik[bt[b, last], L % 4 or 4:] = 1000.0
+    got = oracle.index_scores(p, iq, ik, None, bt, lens)
+    assert np.all(got[:, :, :4][np.isfinite(got[:, :, :4])] == 0.0)
+
+
+def test_q_pos_limits_visible_tokens():
+    """With explicit positions a row sees keys t <= pos only."""
+    p, bt, lens = _tiny_problem(lens=(16, 16), K=2)
+    p.rows_per_seq = 2
+    p.index_scale = p.index_k_scale = 1.0
+    iq = np.ones((4, 2, 16), np.float32)
+    ik = np.zeros((p.num_phys_blocks, 4, 16), np.float32)
+    ik[bt[0, 3], 3] = 5.0  # token 15 of seq 0
+    qp = np.array([14, 15, 6, 15], np.int32)
+    got = oracle.index_scores(p, iq, ik, None, bt, lens, q_pos=qp)
+    assert got[0, 0, 3] == 0.0 and got[1, 0, 3] == 80.0
+    assert np.all(got[2, :, 2:] == -np.inf) and np.isfinite(got[2, 0, 1])
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _brute_select(scores, recent, K):
+    if recent + 1 <= K:
+        sel = list(range(recent + 1))
+    else:
+        order = sorted(range(recent), key=lambda j: (-float(scores[j]), j))
+        sel = sorted(order[: K - 1] + [recent])
+    return sel + [-1] * (K - len(sel))
+
+
+@pytest.mark.parametrize("K", [1, 4, 16, 32])
+def test_topk_matches_brute_force_sort_with_ties(K):
+    rng = np.random.default_rng(K)
+    B, G, mb, BS = 6, 3, 70, 4
+    lens = rng.integers(1, mb * BS + 1, B).astype(np.int32)
+    lens[0] = mb * BS
+    lens[1] = 1
+    p = oracle.Problem(num_seqs=B, num_q_heads=G, num_groups=G, head_dim=16, index_dim=16,
+                       block_size=BS, top_k=K, max_blocks=mb, num_phys_blocks=1)
+    # coarse values so that many scores tie exactly
+    scores = rng.integers(-4, 5, (B, G, mb)).astype(np.float32) * 0.5
+    got = oracle.block_topk(p, scores, lens)
+    for b in range(B):
+        recent = (int(lens[b]) - 1) // BS
+        for g in range(G):
+            assert list(got[b, g]) == _brute_select(scores[b, g], recent, K)
+
+
+def test_topk_invariants_and_recent_forced():
+    rng = np.random.default_rng(2)
+    B, G, mb, BS, K = 5, 4, 300, 128, 16
+    lens = rng.integers(1, mb * BS + 1, B).astype(np.int32)
+    p = oracle.Problem(num_seqs=B, num_q_heads=64, num_groups=G, block_size=BS, top_k=K,
+                       max_blocks=mb, num_phys_blocks=1)
+    scores = rng.standard_normal((B, G, mb)).astype(np.float32)
+    # the recent block gets the worst score on purpose
+    for b in range(B):
+        scores[b, :, (lens[b] - 1) // BS] = -1e30
+    got = oracle.block_topk(p, scores, lens)
+    for b in range(B):
+        r = (int(lens[b]) - 1) // BS
+        for g in range(G):
+            sel = [j for j in got[b, g] if j >= 0]
+            assert len(sel) == min(K, r + 1)
+            assert r in sel
+            assert sel == sorted(sel) and len(set(sel)) == len(sel)
+            assert all(x == -1 for x in got[b, g][len(sel):])
+            assert len(sel) * BS <= golden()["max_keys_per_query"]
+            others = [j for j in sel if j != r]
+            if others:
+                weakest = min(scores[b, g, j] for j in others)
+                unsel = [j for j in range(r) if j not in sel]
+                assert all(scores[b, g, j] <= weakest for j in unsel)
+
+
+def test_topk_shard_merge_is_exact():
+    """Context sharding of the indexer: each shard's local top-(k-1)
+    candidates, merged, give exactly the single-device selection (vLLM blog,
+    "NVFP4 indexer DCP": the owner merges the local top-16 lists and the
+    selection stays exact)."""
+    rng = np.random.default_rng(9)
+    B, G, mb, BS, K = 3, 4, 257, 128, 16
+    lens = np.array([mb * BS, 200 * BS + 5, 17 * BS], np.int32)
+    p = oracle.Problem(num_seqs=B, num_q_heads=64, num_groups=G, block_size=BS, top_k=K,
+                       max_blocks=mb, num_phys_blocks=1)
+    scores = rng.integers(-50, 50, (B, G, mb)).astype(np.float32)  # ties across shards
+    full = oracle.block_topk(p, scores, lens)
+    for nshard in (2, 3, 4):
+        for b in range(B):
+            r = (int(lens[b]) - 1) // BS
+            for g in range(G):
+                cands = []
+                bounds = np.linspace(0, r, nshard + 1).astype(int)
+                for s in range(nshard):
+                    lo, hi = bounds[s], bounds[s + 1]
+                    sub = np.full((1, 1, mb), -np.inf, np.float32)
+                    sub[0, 0, lo:hi] = scores[b, g, lo:hi]
+                    sub[0, 0, r] = 0.0
+                    p1 = oracle.Problem(num_seqs=1, num_q_heads=1, num_groups=1,
+                                        block_size=BS, top_k=K, max_blocks=mb,
+                                        num_phys_blocks=1)
+                    loc = oracle.block_topk(p1, sub, np.array([lens[b]], np.int32))
+                    cands += [j for j in loc[0, 0] if j >= 0 and lo <= j < hi]
+                merged = sorted(cands, key=lambda j: (-float(scores[b, g, j]), j))
+                want = sorted(merged[: K - 1] + [r]) if r + 1 > K else list(range(r + 1))
+                assert [j for j in full[b, g] if j >= 0] == want
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _kv_f64(w):
+    """Independent decode of the K/V pool -> K[P, G, BS, D], V[P, G, BS, D]."""
+    P, G, BS, D = w.num_phys_blocks, w.num_groups, w.block_size, w.head_dim
+    if w.kv_dtype == synth.NVFP4:
+        kd = w.kv_data[:, 0].reshape(P, G, BS, D // 2)
+        ks = w.kv_scales[:, 0].reshape(P, G, BS, D // 16)
+        K = _decode_nvfp4(kd, ks)
+        vd = w.kv_data[:, 1].reshape(P, G, D, BS // 2)
+        vs = w.kv_scales[:, 1].reshape(P, G, D // 16, BS)
+        codes = np.stack([vd & 15, vd >> 4], axis=-1).reshape(P, G, D, BS)
+        table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
+        sc = torch.from_numpy(np.ascontiguousarray(vs)).view(torch.float8_e4m3fn).to(
+            torch.float64).numpy()
+        V = np.swapaxes(table[codes] * np.repeat(sc, 16, axis=2), -1, -2)
+    else:
+        x = _decode_plain(w.kv_data, w.kv_dtype)
+        K = x[:, 0]
+        V = np.swapaxes(x[:, 1], -1, -2)
+    return K * w.k_scale, V * w.v_scale
+
+
+def _dense_attention(w, row, blocks):
+    """softmax attention in torch float64 over the given logical blocks."""
+    K, V = _kv_f64(w)
+    b = row // w.rows_per_seq
+    L = int(w.seq_lens[b])
+    pos = int(w.q_pos[row]) if w.q_pos is not None else L - 1
+    q = torch.from_numpy(_decode_plain(w.q, w.q_dtype)[row])  # [H, D]
+    hpg = w.num_q_heads // w.num_groups
+    out = torch.empty(w.num_q_heads, w.head_dim, dtype=torch.float64)
+    for g in range(w.num_groups):
+        toks = [(j, t) for j in blocks[g] for t in range(w.block_size)
+                if j * w.block_size + t <= pos]
+        Kg = torch.from_numpy(np.stack([K[w.block_table[b, j], g, t] for j, t in toks]))
+        Vg = torch.from_numpy(np.stack([V[w.block_table[b, j], g, t] for j, t in toks]))
+        qg = q[g * hpg:(g + 1) * hpg]
+        att = torch.softmax(qg @ Kg.T * w.sm_scale, dim=-1)
+        out[g * hpg:(g + 1) * hpg] = att @ Vg
+    return out.numpy()
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.FP8, synth.NVFP4])
+def test_attend_equals_dense_when_topk_covers_everything(dtype):
+    w = _small_workload(dtype, lens=(300, 517, 129), top_k=8)
+    p = _oracle_problem(w)
+    _, topk, out, _ = oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data,
+                                    w.kv_scales, w.block_table, w.seq_lens)
+    for row in range(w.rows):
+        nb = (int(w.seq_lens[row]) + 127) // 128
+        assert all(list(topk[row, g][:nb]) == list(range(nb)) for g in range(w.num_groups))
+        ref = _dense_attention(w, row, [list(range(nb))] * w.num_groups)
+        np.testing.assert_allclose(out[row], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_matches_dense_on_the_selected_blocks():
+    w = _small_workload(synth.FP8, lens=(2000, 1500), top_k=4, plant=2)
+    p = _oracle_problem(w)
+    _, topk, out, lse = oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data,
+                                      w.kv_scales, w.block_table, w.seq_lens)
+    for row in range(w.rows):
+        blocks = [[j for j in topk[row, g] if j >= 0] for g in range(w.num_groups)]
+        ref = _dense_attention(w, row, blocks)
+        np.testing.assert_allclose(out[row], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_special_cases():
+    p, bt, lens = _tiny_problem(lens=(1, 14), K=2)
+    rng = np.random.default_rng(12)
+    H, D, P = p.num_q_heads, p.head_dim, p.num_phys_blocks
+    kv = rng.standard_normal((P, 2, p.num_groups, 4, D)).astype(np.float32)
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    topk = np.array([[[0, -1], [0, -1]], [[1, 3], [0, 3]]], np.int32)
+    # single visible token: output is that token's v
+    out, lse = oracle.sparse_attend(p, q, kv, None, bt, lens, topk)
+    for g in range(2):
+        v0 = kv[bt[0, 0], 1, g].reshape(D, 4)[:, 0]  # V stored [d][t]: column t=0
+        for h in range(g * 2, g * 2 + 2):
+            np.testing.assert_array_equal(out[0, h], v0.astype(np.float64))
+    # V constant: output is that constant
+    kv_c = kv.copy()
+    kv_c[:, 1] = 0.375
+    out_c, _ = oracle.sparse_attend(p, q, kv_c, None, bt, lens, topk)
+    np.testing.assert_allclose(out_c, 0.375, rtol=0, atol=1e-15)
+    # q = 0: uniform weights, mean of V over the selected visible tokens
+    out0, lse0 = oracle.sparse_attend(p, np.zeros_like(q), kv, None, bt, lens, topk)
+    for g in range(2):
+        toks = [(j, t) for j in topk[1, g] for t in range(4) if j * 4 + t < 14]
+        mean = np.mean([kv[bt[1, j], 1, g].reshape(D, 4)[:, t].astype(np.float64)
+                        for j, t in toks], axis=0)
+        np.testing.assert_allclose(out0[1, 2 * g], mean, rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(lse0[1, 2 * g], math.log(len(toks)), rtol=1e-14)
+
+
+def test_planted_blocks_are_selected():
+    """The long-context recipe plants 8 blocks per sequence; their pooled
+    score lift is large enough that every group keeps them."""
+    w = _small_workload(synth.FP8, lens=(40 * 128, 33 * 128 + 7), G=4, H=8, top_k=16,
+                        plant=8)
+    p = _oracle_problem(w)
+    scores = oracle.index_scores(p, w.index_q, w.ik_data, w.ik_scales, w.block_table,
+                                 w.seq_lens)
+    topk = oracle.block_topk(p, scores, w.seq_lens)
+    for b, blocks in w.planted.items():
+        for g in range(w.num_groups):
+            assert set(blocks) <= set(topk[b, g].tolist())
+
+
+# ---------------------------------------------------------------------------
+# the pages' byte arithmetic
+# ---------------------------------------------------------------------------
+
+def test_page_byte_arithmetic():
+    gv = golden()
+    assert gv["topk_blocks"] * gv["block_size_tokens"] == gv["max_keys_per_query"]
+    assert gv["fp8_kv_heads"] * gv["head_dim"] * 2 * 1 == gv["fp8_kv_bytes_per_token"]
+    assert gv["index_key_bytes_per_token"] / gv["fp8_kv_bytes_per_token"] == \
+        gv["index_over_dense_fraction"]
+    # NVFP4 = 4-bit values + one 8-bit scale per 16 elements = 4.5 bits vs 8
+    nv_bits = 4 + 8 / gv["nvfp4_group"]
+    assert nv_bits / 8 == gv["nvfp4_kv_bytes_per_token_model"] / gv["fp8_kv_bytes_per_token_model"]
+    assert 1 - nv_bits / 8 == gv["nvfp4_saving_fraction"]
+
+
+@pytest.mark.parametrize("dtype,ik_bytes,kv_bytes", [(synth.FP8, 128, 1024),
+                                                     (synth.NVFP4, 72, 576)])
+def test_generated_caches_have_the_pages_bytes_per_token(dtype, ik_bytes, kv_bytes):
+    w = _small_workload(dtype, lens=(256,), G=4, H=8)
+    tok = w.num_phys_blocks * w.block_size
+    ikb = w.ik_data.nbytes + (w.ik_scales.nbytes if w.ik_scales is not None else 0)
+    kvb = w.kv_data.nbytes + (w.kv_scales.nbytes if w.kv_scales is not None else 0)
+    assert ikb / tok == ik_bytes and kvb / tok == kv_bytes
+    if dtype == synth.FP8:
+        assert ik_bytes == golden()["index_key_bytes_per_token"]
+        assert kv_bytes == golden()["fp8_kv_bytes_per_token"]
+    else:
+        assert kv_bytes / 1024 == golden()["nvfp4_kv_bytes_per_token_model"] / \
+            golden()["fp8_kv_bytes_per_token_model"]
+
+
+def test_threads_do_not_change_results():
+    w = _small_workload(synth.FP8, lens=(700, 900, 1100), top_k=4)
+    res = []
+    for th in (1, 5):
+        p = _oracle_problem(w, threads=th)
+        res.append(oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data,
+                                 w.kv_scales, w.block_table, w.seq_lens))
+        assert oracle.threads_used() == min(th, w.rows * w.num_groups)
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
