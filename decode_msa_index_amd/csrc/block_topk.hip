@@ -1,0 +1,130 @@
+// block_topk.hip -- top-k KV-block selection with the most recent block kept.
+//
+// Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
+// primer"): attention covers the top 16 blocks by pooled index score and
+// always keeps the most recent block.  The recent block counts inside the k,
+// so the rest is the best k-1 of blocks 0..rb-1; ties go to the lower block
+// index, which makes the selection unique and deterministic.
+//
+// One 256-thread workgroup per (row, group).  The k-1 best candidates are
+// found as a threshold by radix select on order-preserving 32-bit keys of the
+// fp32 scores (4 passes of 8 bits, per-wave LDS histograms), then the blocks
+// above the threshold and the lowest-indexed ties at the threshold are
+// written in ascending order through two block-wide prefix sums.  The work is
+// latency-bound (at most a few thousand candidates), not bandwidth-bound.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace msa {
+
+// Monotone map float -> uint32 (larger float -> larger key); -0 folds to +0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over 256 threads; returns the total via *total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sm,
+                                                         uint32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sm[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t t = sm[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(256) void block_topk_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
+    int K) {
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t scan_sm[4];
+  __shared__ uint32_t pick[2];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int u = blockIdx.x;
+  const int row = u / G, b = row / R;
+  const int pos = qpos ? qpos[row] : lens[b] - 1;
+  const int rb = pos / kBlock;
+  int32_t* out = topk + (size_t)u * K;
+  const float* s = scores + (size_t)u * MB;
+  if (rb + 1 <= K) {
+    for (int i = tid; i < K; i += 256) out[i] = i <= rb ? i : -1;
+    return;
+  }
+  const int ncand = rb;  // blocks 0..rb-1 compete for k-1 places
+  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)(K - 1);
+  for (int pass = 3; pass >= 0; --pass) {
+    const int shift = pass * 8;
+    for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    for (int jj = tid; jj < ncand; jj += 256) {
+      const uint32_t key = order_key(s[jj]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // count of keys whose digit is >= this thread's digit value: scan over
+    // digits in descending order (thread t handles digit 255 - t).
+    const int dig = 255 - tid;
+    const uint32_t cnt = hist[0][dig] + hist[1][dig] + hist[2][dig] + hist[3][dig];
+    uint32_t tot;
+    const uint32_t above = block_exclusive_scan(cnt, scan_sm, &tot);  // digits > dig
+    if (above < rem && above + cnt >= rem) {
+      pick[0] = (uint32_t)dig;
+      pick[1] = rem - above;
+    }
+    __syncthreads();
+    prefix |= pick[0] << shift;
+    pmask |= 0xFFu << shift;
+    rem = pick[1];
+    __syncthreads();
+  }
+  // prefix is now the key of the (k-1)-th best candidate; `rem` of the
+  // candidates equal to it are taken, lowest block index first.
+  const int chunk = (ncand + 255) / 256;
+  const int j0 = min(tid * chunk, ncand), j1 = min(j0 + chunk, ncand);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int jj = j0; jj < j1; ++jj) {
+    const uint32_t key = order_key(s[jj]);
+    n_gt += key > prefix;
+    n_eq += key == prefix;
+  }
+  uint32_t tot;
+  const uint32_t eq_before = block_exclusive_scan(n_eq, scan_sm, &tot);
+  const uint32_t eq_take =
+      eq_before >= rem ? 0u : (rem - eq_before < n_eq ? rem - eq_before : n_eq);
+  const uint32_t sel_before = block_exclusive_scan(n_gt + eq_take, scan_sm, &tot);
+  uint32_t w = sel_before, eq_seen = 0;
+  for (int jj = j0; jj < j1; ++jj) {
+    const uint32_t key = order_key(s[jj]);
+    bool take = key > prefix;
+    if (key == prefix) {
+      take = eq_seen < eq_take;
+      ++eq_seen;
+    }
+    if (take) out[w++] = jj;
+  }
+  if (tid == 0) out[K - 1] = rb;
+}
+
+hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
+                             const int32_t* q_pos, int32_t* topk, hipStream_t st) {
+  hipLaunchKernelGGL(block_topk_kernel, dim3(s.rows * s.G), dim3(256), 0, st, scores,
+                     seq_lens, q_pos, topk, s.R, s.G, s.MB, s.K);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,199 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MiniMax Sparse Attention decode path.
+ *
+ * The method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
+ * primer"): the KV cache is split into 128-token blocks; a lightning indexer
+ * scores every cached key with one index query per GQA group against a single
+ * shared index-key head; the token scores are max-pooled to one score per
+ * block; exact attention then runs over the top-k (16) blocks only, with the
+ * most recent block always kept, so a query sees at most k*128 keys.
+ *
+ * Four calls follow those steps:
+ *   msa_index_scores   scores + per-block max-pool          (indexer)
+ *   msa_block_topk     top-k blocks, recent block forced     (selection)
+ *   msa_sparse_attend  exact GQA attention over the blocks   (main attention)
+ *   msa_decode         the three in one call
+ * msa_decode's outputs are identical to the three-call chain on the same
+ * stream: bitwise for the selection, and for the attention output too.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ * All data pointers are DEVICE pointers owned by the caller; the library
+ * allocates and frees nothing and keeps no state between calls.  Every call
+ * validates its arguments on the host, synchronously, before anything is
+ * launched, then enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns without waiting.  Device-side data (block-table
+ * entries, sequence lengths, positions) are preconditions the library does
+ * not read on the host:
+ *   - 1 <= seq_lens[b] <= max_blocks * block_size;
+ *   - block_table[b][j] in [0, num_phys_blocks) for j < ceil(seq_lens[b]/bs);
+ *     entries past that are never read;
+ *   - q_pos[r] in [0, seq_lens[r / rows_per_seq]) when q_pos is given.
+ * A kernel never reads outside the blocks these preconditions name.
+ *
+ * Shapes (B = num_seqs, R = rows_per_seq, G = num_kv_groups, H = num_q_heads,
+ * D = head_dim, Di = index_dim, BS = block_size, P = num_phys_blocks,
+ * MB = max_blocks_per_seq, K = top_k):
+ *   index_q      [B*R][G][Di]        bf16 or f32          16-byte aligned
+ *   q            [B*R][H][D]         bf16 or f32; head h uses group h/(H/G)
+ *   index keys   fp8/f32: [P][BS][Di]
+ *                nvfp4:   data [P][BS][Di/2] (even element in the low nibble)
+ *                         scales [P][BS][Di/16] e4m3
+ *   K/V cache    fp8/f32: [P][2][G][BS*D]; plane 0 = K stored [t][d],
+ *                         plane 1 = V stored transposed [d][t]
+ *                nvfp4:   data [P][2][G][BS*D/2]: K [t][d/2] (even d low),
+ *                         V [d][t/2] (even t low);
+ *                         scales [P][2][G][BS*D/16]: K [t][d/16], V [d/16][t]
+ *   block_table  int32 [B][MB]       logical block -> physical block; one table
+ *                                    serves the K/V and the index-key pools
+ *   seq_lens     int32 [B]           cached tokens incl. the new one
+ *   q_pos        int32 [B*R] or NULL position of each query row; keys t <= pos
+ *                                    are visible.  NULL: R must be 1 and
+ *                                    pos = seq_len - 1 (plain decode)
+ *   block_scores f32 [B*R][G][MB]    pooled scores, -inf past the row's block
+ *   topk_idx     int32 [B*R][G][K]   ascending logical block ids, -1 padded
+ *   out          [B*R][H][D]         bf16 or f32
+ *   lse          f32 [B*R][H] or NULL natural-log softmax denominator
+ *
+ * Number formats: bf16; OCP FP8 e4m3fn; NVFP4 = E2M1 values, one e4m3 scale
+ * per 16 elements and a per-tensor fp32 scale passed as the *_scale field
+ * (a dequantisation multiplier).  FP8 caches carry a per-tensor descale the
+ * same way (k_scale, v_scale, index_k_scale).
+ *
+ * Status: every call returns an msa_status.  On failure nothing has been
+ * enqueued (INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL) or a launch
+ * failed (HIP); msa_last_error() then gives a thread-local message.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, inconsistent sizes */
+  MSA_ERR_UNSUPPORTED = 2,      /* a shape or dtype combination not built */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4               /* a HIP launch or runtime call failed */
+} msa_status;
+
+typedef enum {
+  MSA_DTYPE_F32 = 0,
+  MSA_DTYPE_BF16 = 1,
+  MSA_DTYPE_FP8_E4M3 = 2,
+  MSA_DTYPE_NVFP4 = 3
+} msa_dtype;
+
+/* Problem description, read on the host during the call only. */
+typedef struct msa_problem {
+  int32_t num_seqs;           /* B >= 0 (0: nothing to do) */
+  int32_t rows_per_seq;       /* R >= 1 query rows per sequence */
+  int32_t num_q_heads;        /* H; H/G must be in [1, 16] */
+  int32_t num_kv_groups;      /* G: KV heads = index heads; 1..8 */
+  int32_t head_dim;           /* D: 128 */
+  int32_t index_dim;          /* Di: 128 */
+  int32_t block_size;         /* BS: 128 */
+  int32_t top_k;              /* K: 1..32 blocks kept, recent included */
+  int32_t max_blocks_per_seq; /* MB >= 1: block-table row stride */
+  int32_t num_phys_blocks;    /* P >= 1 */
+  int32_t q_dtype;            /* msa_dtype of q: BF16 or F32 */
+  int32_t index_q_dtype;      /* msa_dtype of index_q: BF16 or F32 */
+  int32_t kv_dtype;           /* msa_dtype of the K/V cache: FP8_E4M3, NVFP4, F32 */
+  int32_t index_k_dtype;      /* msa_dtype of the index keys: FP8_E4M3, NVFP4, F32 */
+  int32_t out_dtype;          /* msa_dtype of out: BF16 or F32 */
+  float sm_scale;             /* attention logit multiplier (> 0), usually D^-0.5 */
+  float index_scale;          /* index score multiplier (> 0), usually Di^-0.5 */
+  float k_scale;              /* K dequant multiplier (> 0) */
+  float v_scale;              /* V dequant multiplier */
+  float index_k_scale;        /* index-key dequant multiplier (> 0) */
+} msa_problem;
+
+/*
+ * Host-side validation of a problem for one of the calls (op: 0 index
+ * scores, 1 top-k, 2 sparse attend, 3 decode).  Pure host code; performs no
+ * HIP call.  Every entry point runs it first.
+ */
+msa_status msa_check_problem(const msa_problem* p, int32_t op);
+
+/*
+ * Workspace bytes msa_sparse_attend (op 2) or msa_decode (op 3) needs for
+ * problem p; 0 for the other ops.  The workspace is caller-owned device
+ * memory, 256-byte aligned, that must be ZERO-FILLED before its first use;
+ * every call leaves its counter region zero again, so it can be reused
+ * without clearing.  Calls that share one workspace must not overlap.
+ */
+msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
+
+/*
+ * Indexer scores + block max-pool (blog, "MSA primer"; API reference of
+ * MiniMaxM3SparseAttention: one index head per KV head, scale Di^-0.5,
+ * sparse_score_type "max").  For every row r, group g and logical block j:
+ *   score(t) = index_scale * index_k_scale * sum_d index_q[r][g][d] * key(t, d)
+ *   block_scores[r][g][j] = max over visible t in block j of score(t)
+ * and -inf for blocks past the row's last visible block.  fp32 arithmetic on
+ * exactly dequantised operands.  ik_scales is required for NVFP4 index keys
+ * and ignored otherwise.
+ */
+msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* ik_data,
+                            const void* ik_scales, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* q_pos,
+                            float* block_scores, void* stream);
+
+/*
+ * Block selection (blog, "MSA primer": top 16 blocks, most recent block
+ * always kept).  For row r with last visible block rb = pos / BS: if
+ * rb + 1 <= K all blocks 0..rb are kept; otherwise rb plus the K-1 best of
+ * 0..rb-1 by (block_scores descending, block index ascending).  Output
+ * ascending, -1 padded.  Deterministic: ties go to the lower block index.
+ * block_scores entries must not be NaN.
+ */
+msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
+                          const int32_t* seq_lens, const int32_t* q_pos, int32_t* topk_idx,
+                          void* stream);
+
+/*
+ * Exact sparse GQA attention over the selected blocks (blog, "MSA primer",
+ * Figure 1: every query head of a group attends exactly the group's
+ * blocks).  For head h of group g and visible tokens t of the selected
+ * blocks: out = sum_t softmax_t(sm_scale * k_scale * q.k_t) * v_scale * v_t,
+ * with fp32 softmax state, split over the selected blocks and merged in the
+ * same launch.  topk_idx entries must be ascending with -1 padding (the
+ * msa_block_topk format) and must include the row's last visible block.
+ * kv_scales is required for NVFP4 and ignored otherwise.  lse may be NULL.
+ * workspace: msa_workspace_bytes(p, 2) bytes, zero-filled before first use.
+ */
+msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv_data,
+                             const void* kv_scales, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* q_pos,
+                             const int32_t* topk_idx, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole decode step: msa_index_scores -> msa_block_topk ->
+ * msa_sparse_attend on `stream`.  topk_idx receives the selection;
+ * block_scores (nullable) receives the pooled scores when given, otherwise
+ * they live in the workspace.  workspace: msa_workspace_bytes(p, 3).
+ */
+msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
+                      const void* ik_scales, const void* q, const void* kv_data,
+                      const void* kv_scales, const int32_t* block_table,
+                      const int32_t* seq_lens, const int32_t* q_pos, float* block_scores,
+                      int32_t* topk_idx, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status s);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* msa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

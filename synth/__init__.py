@@ -50,7 +50,7 @@ STREAM_TABLE, STREAM_LENS, STREAM_PLANT = 5, 6, 7
 def build(force: bool = True) -> str:
     if force or not os.path.exists(_SO):
         tmp = _SO + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O3", "-std=gnu11", "-fPIC", "-shared",
                                "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _SO)
     return _SO
@@ -74,6 +74,10 @@ def lib():
         L.synth_encode_e4m3.argtypes = [vp, u64, vp]
         L.synth_encode_bf16.argtypes = [vp, u64, vp]
         L.synth_nvfp4_rows.argtypes = [vp, u64, ctypes.c_int, ctypes.c_float, vp, vp]
+        i32, f32 = ctypes.c_int, ctypes.c_float
+        L.synth_kv_fp8.argtypes = [u64, u64, u64, i32, i32, i32, vp]
+        L.synth_kv_nvfp4.argtypes = [u64, u64, u64, i32, i32, i32, f32, vp, vp]
+        L.synth_ik.argtypes = [u64, u64, u64, i32, i32, i32, f32, vp, vp]
         _lib = L
     return _lib
 
@@ -278,20 +282,27 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
 
     def gen_ik(p0):
         p1 = min(P, p0 + chunk)
+        if index_k_dtype in (FP8, NVFP4):
+            sc_ptr = ik_scales[p0:p1].ctypes.data if ik_scales is not None else None
+            lib().synth_ik(key(seed, STREAM_IK), p0, p1 - p0, BS, Di, index_k_dtype,
+                           NVFP4_TENSOR_SCALE, ik_data[p0:p1].ctypes.data, sc_ptr)
+            return
         x = normal(seed, STREAM_IK, p0 * per_blk, (p1 - p0) * per_blk).reshape(p1 - p0, BS, Di)
-        for pb in range(p0, p1):
-            v = add_vec.get(pb)
-            if v is not None:
-                x[pb - p0] += v[None, :]
+        ik_data[p0:p1] = _encode_plain(x, index_k_dtype)
+
+    def plant_ik(pb):
+        x = normal(seed, STREAM_IK, pb * per_blk, per_blk).reshape(BS, Di)
+        x += add_vec[pb][None, :]
         if index_k_dtype == NVFP4:
-            d, s = encode_nvfp4_rows(x)
-            ik_data[p0:p1] = d
-            ik_scales[p0:p1] = s
+            d, s_ = encode_nvfp4_rows(x)
+            ik_data[pb] = d
+            ik_scales[pb] = s_
         else:
-            ik_data[p0:p1] = _encode_plain(x, index_k_dtype)
+            ik_data[pb] = _encode_plain(x, index_k_dtype)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(gen_ik, range(0, P, chunk)))
+        list(ex.map(plant_ik, sorted(add_vec)))
 
     # ---- K/V pool: plane 0 = K [t][d], plane 1 = V^T [d][t] ----
     kv_scales = None
@@ -307,17 +318,18 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
 
     def gen_kv(p0):
         p1 = min(P, p0 + chunk_kv)
-        x = normal(seed, STREAM_KV, p0 * per_kv, (p1 - p0) * per_kv).reshape(
-            p1 - p0, 2, G, BS, D)
         if kv_dtype == NVFP4:
-            d, s = encode_nvfp4_rows(x)  # groups of 16 along d for every token
-            kv_data[p0:p1, 0] = d[:, 0].reshape(p1 - p0, G, -1)
-            kv_scales[p0:p1, 0] = s[:, 0].reshape(p1 - p0, G, -1)
-            kv_data[p0:p1, 1] = _nibbles_T(d[:, 1]).reshape(p1 - p0, G, -1)
-            kv_scales[p0:p1, 1] = np.swapaxes(s[:, 1], -1, -2).reshape(p1 - p0, G, -1)
+            lib().synth_kv_nvfp4(key(seed, STREAM_KV), p0, p1 - p0, G, BS, D,
+                                 NVFP4_TENSOR_SCALE, kv_data[p0:p1].ctypes.data,
+                                 kv_scales[p0:p1].ctypes.data)
+        elif kv_dtype == FP8:
+            lib().synth_kv_fp8(key(seed, STREAM_KV), p0, p1 - p0, G, BS, D,
+                               kv_data[p0:p1].ctypes.data)
         else:
+            x = normal(seed, STREAM_KV, p0 * per_kv, (p1 - p0) * per_kv).reshape(
+                p1 - p0, 2, G, BS, D)
             x[:, 1] = np.swapaxes(x[:, 1], -1, -2)
-            kv_data[p0:p1] = _encode_plain(x, kv_dtype)
+            kv_data[p0:p1] = x
 
     if kv_fill:
         with ThreadPoolExecutor(_threads()) as ex:

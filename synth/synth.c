@@ -10,9 +10,10 @@
  * pure function of (seed, stream, i), so any slice can be produced on its own
  * and in parallel.  Mixer: the splitmix64 finaliser (Steele, Lea, Flood,
  * "Fast splittable pseudorandom number generators", OOPSLA 2014).  Normals:
- * Box-Muller on two 53-bit uniforms, pair k giving elements 2k (cos) and
- * 2k+1 (sin).
+ * Box-Muller in binary32 on two 24-bit uniforms cut from one 64-bit draw,
+ * pair k giving elements 2k (cos) and 2k+1 (sin).
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -36,21 +37,22 @@ void synth_u64(uint64_t key, uint64_t first, uint64_t n, uint64_t* out) {
   for (uint64_t i = 0; i < n; ++i) out[i] = draw(key, first + i);
 }
 
-static inline void normal_pair(uint64_t key, uint64_t k, double* c, double* s) {
-  uint64_t a = draw(key, 2 * k), b = draw(key, 2 * k + 1);
-  double u1 = (double)((a >> 11) + 1) * 0x1.0p-53; /* (0, 1] */
-  double u2 = (double)(b >> 11) * 0x1.0p-53;       /* [0, 1) */
-  double r = sqrt(-2.0 * log(u1));
-  double ang = 6.283185307179586476925 * u2;
-  *c = r * cos(ang);
-  *s = r * sin(ang);
+static inline void normal_pair(uint64_t key, uint64_t k, float* c, float* s) {
+  uint64_t a = draw(key, k);
+  float u1 = (float)((a >> 40) + 1) * 0x1.0p-24f;          /* (0, 1] */
+  float u2 = (float)((a >> 8) & 0xFFFFFFu) * 0x1.0p-24f;   /* [0, 1) */
+  float r = sqrtf(-2.0f * logf(u1));
+  float sn, cs;
+  sincosf(6.28318530717958647692f * u2, &sn, &cs);
+  *c = r * cs;
+  *s = r * sn;
 }
 
 void synth_normal_f32(uint64_t key, uint64_t first, uint64_t n, float* out) {
   uint64_t i = 0;
   while (i < n) {
     uint64_t e = first + i;
-    double c, s;
+    float c, s;
     normal_pair(key, e >> 1, &c, &s);
     if ((e & 1) == 0) {
       out[i++] = (float)c;
@@ -64,26 +66,24 @@ void synth_normal_f32(uint64_t key, uint64_t first, uint64_t n, float* out) {
 /* fp32 -> OCP e4m3fn, round to nearest even, saturating to +-448 (the
  * largest finite e4m3 value); NaN maps to 0x7F. */
 static inline uint8_t enc_e4m3(float xf) {
-  double x = (double)xf;
-  if (isnan(x)) return 0x7F;
-  uint8_t s = signbit(x) ? 0x80 : 0;
-  double a = fabs(x);
-  if (a >= 448.0) return s | 0x7E;
-  if (a < 0x1.0p-6) { /* subnormal range, quantum 2^-9; 8 quanta = 2^-6 = code 8 */
-    double q = nearbyint(a * 512.0);
-    return s | (uint8_t)q;
+  uint32_t u;
+  memcpy(&u, &xf, 4);
+  uint8_t s = (uint8_t)((u >> 24) & 0x80u);
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7F;
+  if (a >= 0x43E00000u) return s | 0x7E; /* |x| >= 448 */
+  if (a < 0x3C800000u) {                  /* |x| < 2^-6: quantum 2^-9 */
+    float f;
+    memcpy(&f, &a, 4);
+    float q = f * 512.0f; /* exact: scaling by a power of two */
+    uint32_t i = (uint32_t)q;
+    float frac = q - (float)i;
+    if (frac > 0.5f || (frac == 0.5f && (i & 1u))) ++i;
+    return s | (uint8_t)i; /* i == 8 is code 8 = 2^-6 */
   }
-  int e;
-  frexp(a, &e); /* a in [2^(e-1), 2^e) */
-  int E = e - 1;
-  double q = nearbyint(ldexp(a, -(E - 3))); /* 8..16 */
-  if (q >= 16.0) {
-    q = 8.0;
-    E += 1;
-  }
-  int be = E + 7;
-  if (be > 15 || (be == 15 && q > 14.0)) return s | 0x7E;
-  return s | (uint8_t)(be << 3) | (uint8_t)((int)q - 8);
+  uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20; /* keep 3 mantissa bits, RNE */
+  int e = (int)(r >> 3) - 127 + 7;
+  return s | (uint8_t)((e << 3) | (int)(r & 7u));
 }
 
 void synth_encode_e4m3(const float* x, uint64_t n, uint8_t* out) {
@@ -116,21 +116,22 @@ void synth_normal_e4m3(uint64_t key, uint64_t first, uint64_t n, uint8_t* out) {
   }
 }
 
-/* nearest E2M1 code of a magnitude in [0, 6], ties to the even code */
+/* nearest E2M1 code of a magnitude, ties to the even code:
+ * magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 -> midpoints .25 .75 1.25 1.75 2.5 3.5 5 */
 static inline uint8_t enc_e2m1_mag(double a) {
-  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-  if (a >= 6.0) return 7;
-  int best = 0;
-  for (int c = 1; c < 8; ++c) {
-    double dc = fabs(a - mag[c]), db = fabs(a - mag[best]);
-    if (dc < db || (dc == db && (c & 1) == 0)) best = c;
-  }
-  return (uint8_t)best;
+  if (a <= 0.25) return 0;
+  if (a < 0.75) return 1;
+  if (a <= 1.25) return 2;
+  if (a < 1.75) return 3;
+  if (a <= 2.5) return 4;
+  if (a < 3.5) return 5;
+  if (a <= 5.0) return 6;
+  return 7;
 }
 
 static inline double dec_e4m3_local(uint8_t c) {
   int e = (c >> 3) & 15, m = c & 7;
-  double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  double v = e == 0 ? (double)m * 0x1.0p-9 : (double)(8 + m) * (double)(1u << e) * 0x1.0p-10;
   return (c & 0x80) ? -v : v;
 }
 
@@ -163,5 +164,83 @@ void synth_nvfp4_rows(const float* x, uint64_t rows, int dim, float g,
         dr[el / 2] |= (uint8_t)((el & 1) ? (code << 4) : code);
       }
     }
+  }
+}
+
+/* ---- whole cache blocks, generated and encoded in one pass -------------- */
+
+/* K/V pool blocks [p0, p0+np) in e4m3: out[np][2][G][BS*D].  Element values
+ * follow the logical order [p][kv][g][t][d] of the stream; plane kv = 1 (V)
+ * is stored transposed, [d][t]. */
+void synth_kv_fp8(uint64_t key, uint64_t p0, uint64_t np, int G, int BS, int D, uint8_t* out) {
+  const uint64_t per = (uint64_t)BS * (uint64_t)D;
+  float* buf = (float*)__builtin_alloca(sizeof(float) * per);
+  for (uint64_t p = 0; p < np; ++p) {
+    for (int kv = 0; kv < 2; ++kv) {
+      for (int g = 0; g < G; ++g) {
+        uint64_t plane = ((p0 + p) * 2 + (uint64_t)kv) * (uint64_t)G + (uint64_t)g;
+        uint8_t* o = out + ((p * 2 + (uint64_t)kv) * (uint64_t)G + (uint64_t)g) * per;
+        synth_normal_f32(key, plane * per, per, buf);
+        if (kv == 0) {
+          for (uint64_t i = 0; i < per; ++i) o[i] = enc_e4m3(buf[i]);
+        } else {
+          for (int t = 0; t < BS; ++t)
+            for (int d = 0; d < D; ++d) o[(uint64_t)d * BS + t] = enc_e4m3(buf[(uint64_t)t * D + d]);
+        }
+      }
+    }
+  }
+}
+
+/* K/V pool blocks in NVFP4: data[np][2][G][BS*D/2], scales[np][2][G][BS*D/16].
+ * Both K and V are quantised per token in groups of 16 along d; K is stored
+ * [t][d/2] + [t][d/16], V transposed as [d][t/2] (even t in the low nibble)
+ * + [d/16][t]. */
+void synth_kv_nvfp4(uint64_t key, uint64_t p0, uint64_t np, int G, int BS, int D, float gs,
+                    uint8_t* data, uint8_t* scales) {
+  const uint64_t per = (uint64_t)BS * (uint64_t)D;
+  float* buf = (float*)__builtin_alloca(sizeof(float) * per);
+  uint8_t* td = (uint8_t*)__builtin_alloca(per / 2);
+  uint8_t* ts = (uint8_t*)__builtin_alloca(per / 16);
+  for (uint64_t p = 0; p < np; ++p) {
+    for (int kv = 0; kv < 2; ++kv) {
+      for (int g = 0; g < G; ++g) {
+        uint64_t plane = ((p0 + p) * 2 + (uint64_t)kv) * (uint64_t)G + (uint64_t)g;
+        uint64_t lp = (p * 2 + (uint64_t)kv) * (uint64_t)G + (uint64_t)g;
+        uint8_t* od = data + lp * (per / 2);
+        uint8_t* os = scales + lp * (per / 16);
+        synth_normal_f32(key, plane * per, per, buf);
+        if (kv == 0) {
+          synth_nvfp4_rows(buf, (uint64_t)BS, D, gs, od, os);
+        } else {
+          synth_nvfp4_rows(buf, (uint64_t)BS, D, gs, td, ts);
+          memset(od, 0, per / 2);
+          for (int t = 0; t < BS; ++t) {
+            for (int d = 0; d < D; ++d) {
+              uint8_t b = td[(uint64_t)t * (D / 2) + d / 2];
+              uint8_t c = (d & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+              od[(uint64_t)d * (BS / 2) + t / 2] |= (uint8_t)((t & 1) ? (c << 4) : c);
+            }
+            for (int gi = 0; gi < D / 16; ++gi)
+              os[(uint64_t)gi * BS + t] = ts[(uint64_t)t * (D / 16) + gi];
+          }
+        }
+      }
+    }
+  }
+}
+
+/* index-key pool blocks [p0, p0+np), rows [t][d]: dtype 2 = e4m3 (data
+ * [np][BS][Di]), 3 = NVFP4 (data [np][BS][Di/2], scales [np][BS][Di/16]). */
+void synth_ik(uint64_t key, uint64_t p0, uint64_t np, int BS, int Di, int dtype, float gs,
+              uint8_t* data, uint8_t* scales) {
+  const uint64_t per = (uint64_t)BS * (uint64_t)Di;
+  float* buf = (float*)__builtin_alloca(sizeof(float) * per);
+  for (uint64_t p = 0; p < np; ++p) {
+    synth_normal_f32(key, (p0 + p) * per, per, buf);
+    if (dtype == 2)
+      synth_encode_e4m3(buf, per, data + p * per);
+    else
+      synth_nvfp4_rows(buf, (uint64_t)BS, Di, gs, data + p * (per / 2), scales + p * (per / 16));
   }
 }

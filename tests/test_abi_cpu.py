@@ -1,0 +1,99 @@
+"""The C ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad problems on the host before any launch.  No call
+here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_msa_index_amd as msa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "msa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("msa_index_scores", "msa_block_topk", "msa_sparse_attend", "msa_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msa.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(msa.EXPORTS) == declared_functions()
+
+
+def test_struct_layout_matches_header():
+    # 15 int32 fields then 5 floats, no padding
+    assert ctypes.sizeof(msa.MsaProblem) == 20 * 4
+
+
+def good(**kw):
+    base = dict(num_seqs=2, max_blocks_per_seq=8, num_phys_blocks=16)
+    base.update(kw)
+    return msa.Problem(**base)
+
+
+@pytest.mark.parametrize("op", [0, 1, 2, 3])
+def test_valid_problem_passes(op):
+    assert msa.check_problem(good(), op) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_seqs=-1), 1), (dict(rows_per_seq=0), 1), (dict(num_q_heads=63), 1),
+    (dict(max_blocks_per_seq=0), 1), (dict(num_phys_blocks=0), 1), (dict(top_k=0), 1),
+    (dict(head_dim=64), 2), (dict(index_dim=256), 2), (dict(block_size=64), 2),
+    (dict(top_k=33), 2), (dict(num_kv_groups=3, num_q_heads=48), 2),
+    (dict(num_kv_groups=2, num_q_heads=64), 2),  # 32 heads per group
+    (dict(index_k_dtype=1), 2), (dict(kv_dtype=1), 2), (dict(out_dtype=2), 2),
+    (dict(index_q_dtype=0), 2), (dict(q_dtype=0), 2),
+    (dict(sm_scale=0.0), 1), (dict(index_scale=-1.0), 1), (dict(k_scale=float("nan")), 1),
+    (dict(num_seqs=20000), 2),
+])
+def test_bad_problems_rejected(kw, code):
+    p = good(**kw)
+    assert msa.check_problem(p, 3) == code
+    assert msa.lib().msa_last_error() != b""
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    p = good()
+    with pytest.raises(msa.MsaError) as e:
+        msa.index_scores(p, None, None, None, None, None, None, None, stream=0)
+    assert e.value.status == 1 and "index_q" in e.value.detail
+    with pytest.raises(msa.MsaError) as e:
+        msa.index_scores(p, 0x1001, 0x2000, None, 0x3000, 0x4000, None, 0x5000, stream=0)
+    assert e.value.status == 1 and "aligned" in e.value.detail
+    with pytest.raises(msa.MsaError) as e:  # rows_per_seq > 1 needs positions
+        msa.block_topk(good(rows_per_seq=2), 0x1000, 0x2000, None, 0x3000, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(msa.MsaError) as e:  # nvfp4 needs scales
+        msa.sparse_attend(good(kv_dtype=3), 0x1000, 0x2000, None, 0x3000, 0x4000, None,
+                          0x5000, 0x6000, None, None, stream=0)
+    assert e.value.status == 1 and "kv_scales" in e.value.detail
+
+
+def test_workspace_sizes():
+    p = good(num_seqs=8, max_blocks_per_seq=2048)
+    a = msa.workspace_bytes(p, msa.OP_ATTEND)
+    d = msa.workspace_bytes(p, msa.OP_DECODE)
+    rows_g = 8 * 4
+    assert a >= rows_g * 4 + rows_g * 16 * 16 * 130 * 4
+    assert d >= a + rows_g * 2048 * 4
+    assert msa.workspace_bytes(p, msa.OP_INDEX) == 0
+    assert a % 256 == 0 and d % 256 == 0
+
+
+def test_status_strings():
+    L = msa.lib()
+    assert L.msa_status_string(0) == b"ok"
+    assert L.msa_status_string(3) == b"workspace too small"

@@ -1,0 +1,192 @@
+"""GPU parity of every call of the C ABI against the CPU oracle.
+
+Inputs are seeded synthetic workloads (synth); expected values come from the
+oracle only.  Small cases span several blocks, ragged tails and the
+degenerate cases; the full-size cases are the benchmark's workloads in the
+benchmark's launch configuration, with the oracle computed on every output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import decode_msa_index_amd as msa
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    msa.lib()
+
+
+def _oracle_all(w, threads=0):
+    p = parity.oracle_problem(w, threads)
+    return oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data, w.kv_scales,
+                         w.block_table, w.seq_lens, w.q_pos)
+
+
+def _run_and_check(w, fused, name):
+    say(f"[parity] {name}: oracle on {w.rows} rows")
+    s_ref, k_ref, o_ref, l_ref = _oracle_all(w)
+    dw = parity.DeviceWorkload(w)
+    say(f"[parity] {name}: GPU {'msa_decode' if fused else 'three-call chain'}")
+    if fused:
+        dw.decode()
+    else:
+        dw.chain()
+    torch.cuda.synchronize()
+    s = dw.scores.cpu().numpy()
+    k = dw.topk.cpu().numpy()
+    o = dw.out.float().cpu().numpy()
+    serr = parity.check_scores(w, s, s_ref)
+    same = parity.check_selection(w, s_ref, k_ref, k)
+    aerr = parity.check_attention(w, o, o_ref, mask=same)
+    say(f"[parity] {name}: score err {serr:.3f} of bound, {int(same.sum())}/{same.size} "
+        f"selections identical, attention max-abs {aerr:.2e}")
+    return dw, same
+
+
+# ---------------------------------------------------------------------------
+# small, several tiles, ragged tails, edge cases
+# ---------------------------------------------------------------------------
+
+EDGE_LENS = [1, 127, 128, 129, 2047, 2048, 2049, 16 * 128 + 1, 5000, 130 * 128 - 3]
+
+
+@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
+@pytest.mark.parametrize("fused", [False, True])
+def test_small_ragged(kv, fused):
+    w = synth.make("edge", seed=101 + kv, seq_lens=EDGE_LENS, q_dtype=synth.BF16,
+                   kv_dtype=kv, plant_per_seq=0)
+    _run_and_check(w, fused, f"edge-{synth.DTYPE_NAMES[kv]}")
+
+
+def test_tiny_fp32_workload():
+    w = synth.tiny()
+    dw, same = _run_and_check(w, fused=False, name="tiny-f32")
+    assert same.all()
+
+
+def test_tiny_fp32_output():
+    w = synth.tiny()
+    s_ref, k_ref, o_ref, l_ref = _oracle_all(w)
+    dw = parity.DeviceWorkload(w, out_dtype=msa.F32)
+    say("[parity] tiny f32 out")
+    dw.chain()
+    torch.cuda.synchronize()
+    o = dw.out.cpu().numpy()
+    assert np.array_equal(dw.topk.cpu().numpy(), k_ref)
+    assert np.max(np.abs(o - o_ref)) < 1e-4
+    np.testing.assert_allclose(dw.lse.cpu().numpy(), l_ref, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("G,H", [(1, 16), (2, 8), (8, 8), (4, 12)])
+def test_group_shapes(G, H):
+    w = synth.make("groups", seed=7 + G + H, seq_lens=[3000, 700, 129], num_q_heads=H,
+                   num_groups=G, q_dtype=synth.BF16, kv_dtype=synth.FP8, top_k=8)
+    _run_and_check(w, fused=True, name=f"G{G}H{H}")
+
+
+@pytest.mark.parametrize("K", [1, 4, 8, 32])
+def test_topk_sizes(K):
+    w = synth.make("topk", seed=50 + K, seq_lens=[6000, 128 * 40, 300], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, top_k=K)
+    _run_and_check(w, fused=True, name=f"K{K}")
+
+
+def test_query_positions_multi_row():
+    lens = [4000, 2600]
+    qp = np.array([3999, 3000, 1, 128, 2599, 2047], np.int32)
+    w = synth.make("rows", seed=77, seq_lens=lens, rows_per_seq=3, q_pos=qp,
+                   q_dtype=synth.BF16, kv_dtype=synth.FP8, top_k=4)
+    _run_and_check(w, fused=True, name="multi-row")
+
+
+def test_block_topk_bit_exact_with_ties():
+    """Selection kernel alone, on oracle-independent scores with many exact
+    ties: identical to the oracle's selection."""
+    rng = np.random.default_rng(5)
+    B, G, MB = 9, 4, 700
+    lens = rng.integers(1, MB * 128 + 1, B).astype(np.int32)
+    lens[0], lens[1], lens[2] = MB * 128, 1, 17 * 128
+    scores = rng.integers(-6, 7, (B, G, MB)).astype(np.float32) * 0.25
+    scores[3] = -0.0  # signed zeros tie with +0
+    scores[3, :, ::3] = 0.0
+    for K in (1, 5, 16, 32):
+        op = oracle.Problem(num_seqs=B, num_q_heads=G, num_groups=G, block_size=128, top_k=K,
+                            max_blocks=MB, num_phys_blocks=1)
+        ref = oracle.block_topk(op, scores, lens)
+        p = msa.Problem(num_seqs=B, num_q_heads=G, num_kv_groups=G, top_k=K,
+                        max_blocks_per_seq=MB, num_phys_blocks=1)
+        out = torch.empty(B, G, K, dtype=torch.int32, device="cuda")
+        say(f"[parity] block_topk K={K}")
+        msa.block_topk(p, parity.dev(scores), parity.dev(lens), None, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_sparse_attend_on_oracle_selection():
+    """Attention kernel alone, fed the oracle's selection."""
+    w = synth.make("attend", seed=31, seq_lens=[9000, 2100, 128], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8)
+    s_ref, k_ref, o_ref, l_ref = _oracle_all(w)
+    dw = parity.DeviceWorkload(w)
+    say("[parity] sparse_attend on oracle selection")
+    dw.sparse_attend(topk=parity.dev(k_ref))
+    torch.cuda.synchronize()
+    parity.check_attention(w, dw.out.float().cpu().numpy(), o_ref)
+    np.testing.assert_allclose(dw.lse.cpu().numpy(), l_ref, rtol=0, atol=2e-3)
+
+
+def test_decode_equals_chain_and_is_deterministic():
+    w = synth.make("det", seed=44, seq_lens=[20000, 7000, 300], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, plant_per_seq=4)
+    dw = parity.DeviceWorkload(w)
+    say("[parity] chain vs decode vs decode")
+    dw.chain()
+    torch.cuda.synchronize()
+    a = (dw.scores.clone(), dw.topk.clone(), dw.out.clone(), dw.lse.clone())
+    for _ in range(2):
+        dw.decode(with_scores=True)
+        torch.cuda.synchronize()
+        for x, y in zip(a, (dw.scores, dw.topk, dw.out, dw.lse)):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+
+
+def test_empty_batch_and_errors():
+    p = msa.Problem(num_seqs=0, max_blocks_per_seq=4, num_phys_blocks=4)
+    z = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    i32 = torch.zeros(64, dtype=torch.int32, device="cuda")
+    f32 = torch.zeros(64, dtype=torch.float32, device="cuda")
+    msa.index_scores(p, z, z, None, i32, i32, None, f32)  # nothing to do
+    p1 = msa.Problem(num_seqs=1, max_blocks_per_seq=4, num_phys_blocks=4)
+    small = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(msa.MsaError) as e:
+        msa.sparse_attend(p1, z, z, None, i32, i32, None, i32, f32, None, small)
+    assert e.value.status == 3
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the benchmark's shapes and launch configuration)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["fp8_b32", "fp8_long", "nvfp4_512k"])
+def test_full_size(name):
+    say(f"[parity] generating {name}")
+    w = getattr(synth, name)()
+    dw, same = _run_and_check(w, fused=True, name=name)
+    assert same.mean() > 0.9
