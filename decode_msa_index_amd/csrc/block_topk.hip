@@ -65,6 +65,10 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
     for (int i = tid; i < K; i += 256) out[i] = i <= rb ? i : -1;
     return;
   }
+  if (K == 1) {  // only the forced recent block
+    if (tid == 0) out[0] = rb;
+    return;
+  }
   const int ncand = rb;  // blocks 0..rb-1 compete for k-1 places
   uint32_t prefix = 0, pmask = 0, rem = (uint32_t)(K - 1);
   for (int pass = 3; pass >= 0; --pass) {
