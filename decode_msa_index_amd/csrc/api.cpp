@@ -55,22 +55,23 @@ msa::Shape shape_of(const msa_problem* p) {
 }
 
 struct WsLayout {
-  size_t counters, part_o, part_ml, scores, total;
+  size_t scores, attend, total;
 };
 
+// Device scratch: msa_sparse_attend needs room for the split-K partial
+// states when it splits a (row, group) over several workgroups; msa_decode
+// needs that plus the pooled scores when the caller does not take them.
 WsLayout ws_layout(const msa_problem* p, int op) {
   WsLayout w{};
   if (op != kOpAttend && op != kOpDecode) return w;
   const msa::Shape s = shape_of(p);
   size_t off = 0;
-  w.counters = off;
-  off += round_up(sizeof(int32_t) * (size_t)s.rows * s.G);
-  w.part_o = off;
-  off += round_up(sizeof(float) * msa::partial_o_floats(s));
-  w.part_ml = off;
-  off += round_up(sizeof(float) * msa::partial_ml_floats(s));
-  w.scores = off;
-  if (op == kOpDecode) off += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
+  if (op == kOpDecode) {
+    w.scores = off;
+    off += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
+  }
+  w.attend = off;
+  off += round_up(msa::attend_workspace_bytes(s, msa::attend_config(s)));
   w.total = off;
   return w;
 }
@@ -245,19 +246,21 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
   if (st != MSA_OK) return st;
   REQUIRE(topk_idx, 4);
   const WsLayout w = ws_layout(p, kOpAttend);
-  REQUIRE(workspace, kAlign);
-  if (workspace_bytes < w.total)
-    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
-                workspace_bytes, w.total);
+  if (w.total) {
+    REQUIRE(workspace, kAlign);
+    if (workspace_bytes < w.total)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                  workspace_bytes, w.total);
+  } else {
+    OPTIONAL(workspace, kAlign);
+  }
   if (p->num_seqs == 0) return MSA_OK;
   const msa::Shape s = shape_of(p);
-  char* ws = static_cast<char*>(workspace);
-  return hip_status(
-      msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table, seq_lens, q_pos,
-                                topk_idx, out, lse, reinterpret_cast<int32_t*>(ws + w.counters),
-                                reinterpret_cast<float*>(ws + w.part_o),
-                                reinterpret_cast<float*>(ws + w.part_ml), (hipStream_t)stream),
-      "sparse attend launch");
+  return hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table,
+                                              seq_lens, q_pos, topk_idx, out, lse,
+                                              static_cast<char*>(workspace) + w.attend,
+                                              (hipStream_t)stream),
+                    "sparse attend launch");
 }
 
 msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
@@ -275,15 +278,36 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
   OPTIONAL(block_scores, 4);
   REQUIRE(topk_idx, 4);
   const WsLayout w = ws_layout(p, kOpDecode);
-  REQUIRE(workspace, kAlign);
-  if (workspace_bytes < w.total)
-    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
-                workspace_bytes, w.total);
+  if (w.total) {
+    REQUIRE(workspace, kAlign);
+    if (workspace_bytes < w.total)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                  workspace_bytes, w.total);
+  } else {
+    OPTIONAL(workspace, kAlign);
+  }
   if (p->num_seqs == 0) return MSA_OK;
   const msa::Shape s = shape_of(p);
   char* ws = static_cast<char*>(workspace);
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
   hipStream_t hs = (hipStream_t)stream;
+  void* aws = ws ? ws + w.attend : nullptr;
+  if (msa::select_fusable(s)) {
+    // two launches: the index scan (which also clears the attention kernel's
+    // arrival counters), then selection + attention in one kernel
+    const msa::AttendConfig c = msa::attend_config(s);
+    int32_t* counters = c.splits > 1 ? reinterpret_cast<int32_t*>(
+                                           static_cast<char*>(aws) + msa::attend_counter_offset(s, c))
+                                     : nullptr;
+    st = hip_status(msa::launch_index_scores(s, index_q, ik_data, ik_scales, block_table,
+                                             seq_lens, q_pos, scores, hs, counters,
+                                             counters ? s.rows * s.G : 0),
+                    "index scores launch");
+    if (st != MSA_OK) return st;
+    return hip_status(msa::launch_select_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
+                                                q_pos, scores, topk_idx, out, lse, aws, true, hs),
+                      "select + attend launch");
+  }
   st = hip_status(msa::launch_index_scores(s, index_q, ik_data, ik_scales, block_table,
                                            seq_lens, q_pos, scores, hs),
                   "index scores launch");
@@ -291,12 +315,9 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
   st = hip_status(msa::launch_block_topk(s, scores, seq_lens, q_pos, topk_idx, hs),
                   "block top-k launch");
   if (st != MSA_OK) return st;
-  return hip_status(
-      msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table, seq_lens, q_pos,
-                                topk_idx, out, lse, reinterpret_cast<int32_t*>(ws + w.counters),
-                                reinterpret_cast<float*>(ws + w.part_o),
-                                reinterpret_cast<float*>(ws + w.part_ml), hs),
-      "sparse attend launch");
+  return hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table,
+                                              seq_lens, q_pos, topk_idx, out, lse, aws, hs),
+                    "sparse attend launch");
 }
 
 const char* msa_status_string(msa_status s) {

@@ -6,22 +6,18 @@
 // so the rest is the best k-1 of blocks 0..rb-1; ties go to the lower block
 // index, which makes the selection unique and deterministic.
 //
-// One 256-thread workgroup per (row, group).  The k-1 best candidates are
-// found as a threshold by radix select on order-preserving 32-bit keys of the
-// fp32 scores (4 passes of 8 bits, per-wave LDS histograms), then the blocks
+// One 256-thread workgroup per (row, group).  The row's scores are read once
+// into LDS as order-preserving 32-bit keys; the k-1 best candidates are found
+// as a threshold by radix select on them (4 passes of 8 bits, per-wave LDS
+// histograms), then the blocks
 // above the threshold and the lowest-indexed ties at the threshold are
 // written in ascending order through two block-wide prefix sums.  The work is
 // latency-bound (at most a few thousand candidates), not bandwidth-bound.
 #include "device.hpp"
 #include "launch.hpp"
+#include "select_wave.hpp"
 
 namespace msa {
-
-// Monotone map float -> uint32 (larger float -> larger key); -0 folds to +0.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Exclusive prefix sum over 256 threads; returns the total via *total.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sm,
@@ -47,20 +43,30 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + x - v;
 }
 
+// Candidate keys live in LDS (kLds) when the row's block count fits, else
+// they are re-read from global memory in every pass.
+constexpr int kLdsKeys = 16384;
+
+template <bool kLds>
 __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
     int K) {
+  extern __shared__ uint32_t keys[];  // kLds: one order key per candidate block
   __shared__ uint32_t hist[4][256];
   __shared__ uint32_t scan_sm[4];
   __shared__ uint32_t pick[2];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int u = blockIdx.x;
   const int row = u / G, b = row / R;
-  const int pos = qpos ? qpos[row] : lens[b] - 1;
-  const int rb = pos / kBlock;
+  const int pos = row_last_key(lens, qpos, row, b, MB);
   int32_t* out = topk + (size_t)u * K;
   const float* s = scores + (size_t)u * MB;
+  if (pos < 0) {  // the row sees no key: nothing to select
+    for (int i = tid; i < K; i += 256) out[i] = -1;
+    return;
+  }
+  const int rb = pos / kBlock;
   if (rb + 1 <= K) {
     for (int i = tid; i < K; i += 256) out[i] = i <= rb ? i : -1;
     return;
@@ -70,14 +76,36 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
     return;
   }
   const int ncand = rb;  // blocks 0..rb-1 compete for k-1 places
+  auto key_at = [&](int jj) -> uint32_t {
+    if constexpr (kLds) return keys[jj];
+    else return order_key(s[jj]);
+  };
+  if constexpr (kLds) {
+    // read the row once, 4 loads in flight per thread per round
+    for (int base = 0; base < ncand; base += 4 * 256) {
+      float v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int jj = base + k * 256 + tid;
+        v[k] = jj < ncand ? s[jj] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int jj = base + k * 256 + tid;
+        if (jj < ncand) keys[jj] = order_key(v[k]);
+      }
+    }
+  }
   uint32_t prefix = 0, pmask = 0, rem = (uint32_t)(K - 1);
   for (int pass = 3; pass >= 0; --pass) {
     const int shift = pass * 8;
     for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int jj = tid; jj < ncand; jj += 256) {
-      const uint32_t key = order_key(s[jj]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+    for (int base = 0; base < ncand; base += 256) {
+      const int jj = base + tid;
+      const uint32_t key = jj < ncand ? key_at(jj) : 0u;
+      const uint32_t dig = (key >> shift) & 255u;
+      if (jj < ncand && (key & pmask) == prefix) atomicAdd(&hist[wave][dig], 1u);
     }
     __syncthreads();
     // count of keys whose digit is >= this thread's digit value: scan over
@@ -102,7 +130,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   const int j0 = min(tid * chunk, ncand), j1 = min(j0 + chunk, ncand);
   uint32_t n_gt = 0, n_eq = 0;
   for (int jj = j0; jj < j1; ++jj) {
-    const uint32_t key = order_key(s[jj]);
+    const uint32_t key = key_at(jj);
     n_gt += key > prefix;
     n_eq += key == prefix;
   }
@@ -113,7 +141,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   const uint32_t sel_before = block_exclusive_scan(n_gt + eq_take, scan_sm, &tot);
   uint32_t w = sel_before, eq_seen = 0;
   for (int jj = j0; jj < j1; ++jj) {
-    const uint32_t key = order_key(s[jj]);
+    const uint32_t key = key_at(jj);
     bool take = key > prefix;
     if (key == prefix) {
       take = eq_seen < eq_take;
@@ -124,10 +152,29 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   if (tid == 0) out[K - 1] = rb;
 }
 
+constexpr int kWaveSelectMax = 16000;  // keys + histogram stay under 64 KB of LDS
+
+__global__ __launch_bounds__(64) void block_topk_wave_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
+    int K) {
+  extern __shared__ uint32_t lds[];  // [256] histogram, then [MB] keys
+  const int u = blockIdx.x, row = u / G, b = row / R;
+  const int pos = row_last_key(lens, qpos, row, b, MB);
+  const int rb = pos < 0 ? -1 : pos / kBlock;
+  wave_select<64>(scores + (size_t)u * MB, rb, K, lds + 256, lds, topk + (size_t)u * K);
+}
+
 hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
                              const int32_t* q_pos, int32_t* topk, hipStream_t st) {
-  hipLaunchKernelGGL(block_topk_kernel, dim3(s.rows * s.G), dim3(256), 0, st, scores,
-                     seq_lens, q_pos, topk, s.R, s.G, s.MB, s.K);
+  if (s.MB <= kWaveSelectMax) {
+    hipLaunchKernelGGL(block_topk_wave_kernel, dim3(s.rows * s.G), dim3(64),
+                       sizeof(uint32_t) * (256 + s.MB), st, scores, seq_lens, q_pos, topk, s.R,
+                       s.G, s.MB, s.K);
+  } else {
+    hipLaunchKernelGGL(block_topk_kernel<false>, dim3(s.rows * s.G), dim3(256), 0, st, scores,
+                       seq_lens, q_pos, topk, s.R, s.G, s.MB, s.K);
+  }
   return hipGetLastError();
 }
 

@@ -65,6 +65,22 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
 }
 
+// Streaming 16-byte load with the nontemporal hint (data read exactly once).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Row bookkeeping shared by the kernels: the last key a query row may see
+// (keys t <= pos and t < seq_len, clamped to the block table's reach of
+// MB blocks); negative when the row sees none.
+__device__ __forceinline__ int row_last_key(const int32_t* lens, const int32_t* qpos, int row,
+                                            int b, int MB) {
+  const int last = min(lens[b], MB * kBlock) - 1;
+  return qpos ? min(qpos[row], last) : last;
+}
+
 // ---- lane exchanges -------------------------------------------------------
 
 template <int CTRL>
@@ -74,6 +90,7 @@ __device__ __forceinline__ float dpp(float v) {
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
 constexpr int kRowRor4 = 0x124;  // rotate right by 4 within 16 lanes
 constexpr int kRowRor8 = 0x128;
 

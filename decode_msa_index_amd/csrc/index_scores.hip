@@ -9,11 +9,10 @@
 //
 // Work decomposition: one wavefront per (query row, logical block); four
 // wavefronts per workgroup take four consecutive blocks of the same row.
-// Inside a wave four lanes share one token: lane l owns dims
-// [32*(l%4), 32*(l%4)+32) of token l/4, so a load instruction covers 16
-// tokens (2 KB FP8) contiguously and the dot product needs only a 2-step
-// quad reduction.  The block's 16 KB are loaded up front (16 x 16 B per
-// lane) to keep many bytes in flight per wave.
+// Every load instruction of a wave reads 1 KB of consecutive bytes, and a
+// block's loads are all issued before any arithmetic, to keep many bytes in
+// flight per wave.  Blocks past a row's last visible key, and block-table
+// entries outside the pool, produce -inf without touching the cache.
 //
 // Arithmetic: keys are converted exactly to bf16 (e4m3 and e2m1 values are
 // bf16-representable) and multiplied with the bf16 index query by
@@ -24,43 +23,57 @@
 
 namespace msa {
 
+// Optional side job of the first workgroup: zero n ints (the attention
+// kernel's arrival counters, cleared here so msa_decode needs no extra launch).
+struct ZeroArgs {
+  int32_t* p;
+  int n;
+  __device__ __forceinline__ void run() const {
+    if (p && blockIdx.x == 0 && blockIdx.y == 0)
+      for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+  }
+};
+
 // -------------------------------------------------------------------------
-// FP8 e4m3 index keys, bf16 index queries
+// FP8 e4m3 index keys, bf16 index queries.
+// Eight lanes share a token: lane l owns dims [16*(l%8), 16*(l%8)+16) of
+// token l/8, so each 16-byte load instruction of the wave covers 8 tokens =
+// 1 KB contiguously; the 16 KB block takes 16 such loads, all issued up front
+// with the nontemporal hint (each byte is read exactly once).  A token's dot
+// product is reduced over its 8 lanes in 3 DPP steps.
 // -------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void index_fp8_kernel(
     const uint16_t* __restrict__ iq, const uint8_t* __restrict__ ik,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ qpos, float* __restrict__ scores, int R, int MB,
-    float out_scale) {
+    const int32_t* __restrict__ qpos, float* __restrict__ scores, int R, int MB, int P,
+    float out_scale, ZeroArgs za) {
+  za.run();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y, b = row / R;
   const int j = blockIdx.x * 4 + wave;
   if (j >= MB) return;
-  const int pos = qpos ? qpos[row] : lens[b] - 1;
+  const int entry = bt[(size_t)b * MB + j];  // issued alongside the length loads
+  const int pos = row_last_key(lens, qpos, row, b, MB);
   float* out = scores + (size_t)row * G * MB + j;
-  if (j * kBlock > pos) {
+  const int pb = j * kBlock > pos ? -1 : entry;
+  if (pb < 0 || pb >= P) {  // past the row's last key (or an invalid table entry)
     if (lane < G) out[(size_t)lane * MB] = -INFINITY;
     return;
   }
-  const int pb = bt[(size_t)b * MB + j];
-  const uint4* src =
-      reinterpret_cast<const uint4*>(ik + (size_t)pb * (kBlock * kDim)) + lane * 2;
+  const uint4* src = reinterpret_cast<const uint4*>(ik + (size_t)pb * (kBlock * kDim)) + lane;
   uint4 raw[16];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    raw[2 * s] = src[s * 128];
-    raw[2 * s + 1] = src[s * 128 + 1];
-  }
-  // index query: dims [32c, 32c+32) of every group as bf16 pairs
-  const int c = lane & 3;
-  const uint4* qsrc = reinterpret_cast<const uint4*>(iq + (size_t)row * G * kDim) + c * 4;
-  uint32_t qw[G][16];
+  for (int i = 0; i < 16; ++i) raw[i] = load_stream(src + i * 64);
+  // index query: dims [16c, 16c+16) of every group as bf16 pairs
+  const int c = lane & 7;
+  const uint4* qsrc = reinterpret_cast<const uint4*>(iq + (size_t)row * G * kDim) + c * 2;
+  uint32_t qw[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 v = qsrc[g * 16 + i];
+    for (int i = 0; i < 2; ++i) {
+      const uint4 v = qsrc[g * 16 + i];
       qw[g][4 * i] = v.x;
       qw[g][4 * i + 1] = v.y;
       qw[g][4 * i + 2] = v.z;
@@ -70,17 +83,15 @@ __global__ __launch_bounds__(256) void index_fp8_kernel(
   float m[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = -INFINITY;
-  const int tok0 = j * kBlock + (lane >> 2);
+  const int tok0 = j * kBlock + (lane >> 3);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const uint32_t kw[8] = {raw[2 * s].x,     raw[2 * s].y,     raw[2 * s].z,
-                            raw[2 * s].w,     raw[2 * s + 1].x, raw[2 * s + 1].y,
-                            raw[2 * s + 1].z, raw[2 * s + 1].w};
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t kw[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
     float acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int w = 0; w < 4; ++w) {
       const bf16x2 lo = fp8x2_to_bf16x2<false>(kw[w]);
       const bf16x2 hi = fp8x2_to_bf16x2<true>(kw[w]);
 #pragma unroll
@@ -93,16 +104,17 @@ __global__ __launch_bounds__(256) void index_fp8_kernel(
     for (int g = 0; g < G; ++g) {
       acc[g] += dpp<kQuadXor1>(acc[g]);
       acc[g] += dpp<kQuadXor2>(acc[g]);
+      acc[g] += dpp<kHalfMirror>(acc[g]);
     }
-    const bool valid = tok0 + s * 16 <= pos;
+    const bool valid = tok0 + i * 8 <= pos;
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = valid ? fmaxf(m[g], acc[g]) : m[g];
   }
+  // max over the 8 token slots of the wave: lanes 8 apart hold other tokens
   float v = -INFINITY;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float x = fmaxf(m[g], dpp<kRowRor4>(m[g]));
-    x = fmaxf(x, dpp<kRowRor8>(x));
+    float x = fmaxf(m[g], dpp<kRowRor8>(m[g]));
     x = fmaxf(x, shfl_xor(x, 16));
     x = fmaxf(x, shfl_xor(x, 32));
     if (lane == g) v = x;
@@ -120,18 +132,20 @@ __global__ __launch_bounds__(256) void index_nvfp4_kernel(
     const uint16_t* __restrict__ iq, const uint8_t* __restrict__ ikd,
     const uint8_t* __restrict__ iks, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ qpos,
-    float* __restrict__ scores, int R, int MB, float out_scale) {
+    float* __restrict__ scores, int R, int MB, int P, float out_scale, ZeroArgs za) {
+  za.run();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y, b = row / R;
   const int j = blockIdx.x * 4 + wave;
   if (j >= MB) return;
-  const int pos = qpos ? qpos[row] : lens[b] - 1;
+  const int entry = bt[(size_t)b * MB + j];  // issued alongside the length loads
+  const int pos = row_last_key(lens, qpos, row, b, MB);
   float* out = scores + (size_t)row * G * MB + j;
-  if (j * kBlock > pos) {
+  const int pb = j * kBlock > pos ? -1 : entry;
+  if (pb < 0 || pb >= P) {  // past the row's last key (or an invalid table entry)
     if (lane < G) out[(size_t)lane * MB] = -INFINITY;
     return;
   }
-  const int pb = bt[(size_t)b * MB + j];
   const int c = lane & 3;
   // data: 16 tokens x 64 B = 1 KB per step; lane reads 16 B = dims [32c, 32c+32)
   const uint4* dsrc =
@@ -144,8 +158,8 @@ __global__ __launch_bounds__(256) void index_nvfp4_kernel(
   uint32_t sc[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    raw[s] = dsrc[s * 64];
-    sc[s] = ssrc[s * 64];
+    raw[s] = load_stream(dsrc + s * 64);
+    sc[s] = __builtin_nontemporal_load(ssrc + s * 64);
   }
   const uint4* qsrc = reinterpret_cast<const uint4*>(iq + (size_t)row * G * kDim) + c * 4;
   uint32_t qw[G][16];
@@ -223,8 +237,9 @@ template <int G>
 __global__ __launch_bounds__(256) void index_f32_kernel(
     const float* __restrict__ iq, const float* __restrict__ ik,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ qpos, float* __restrict__ scores, int R, int MB,
-    float out_scale) {
+    const int32_t* __restrict__ qpos, float* __restrict__ scores, int R, int MB, int P,
+    float out_scale, ZeroArgs za) {
+  za.run();
   __shared__ float qs[G * kDim];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y, b = row / R;
@@ -232,13 +247,14 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
   __syncthreads();
   const int j = blockIdx.x * 4 + wave;
   if (j >= MB) return;
-  const int pos = qpos ? qpos[row] : lens[b] - 1;
+  const int entry = bt[(size_t)b * MB + j];  // issued alongside the length loads
+  const int pos = row_last_key(lens, qpos, row, b, MB);
   float* out = scores + (size_t)row * G * MB + j;
-  if (j * kBlock > pos) {
+  const int pb = j * kBlock > pos ? -1 : entry;
+  if (pb < 0 || pb >= P) {  // past the row's last key (or an invalid table entry)
     if (lane < G) out[(size_t)lane * MB] = -INFINITY;
     return;
   }
-  const int pb = bt[(size_t)b * MB + j];
   float m[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = -INFINITY;
@@ -278,19 +294,20 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 template <int G>
 static hipError_t launch_g(const Shape& s, const void* iq, const void* ikd, const void* iks,
                            const int32_t* bt, const int32_t* lens, const int32_t* qpos,
-                           float* scores, hipStream_t st) {
+                           float* scores, hipStream_t st, int32_t* zero, int n_zero) {
   dim3 grid((s.MB + 3) / 4, s.rows), block(256);
   float out_scale = s.index_scale * s.ik_scale;
+  const ZeroArgs za{zero, n_zero};
   if (s.ik_dtype == kFP8) {
     hipLaunchKernelGGL(index_fp8_kernel<G>, grid, block, 0, st, (const uint16_t*)iq,
-                       (const uint8_t*)ikd, bt, lens, qpos, scores, s.R, s.MB, out_scale);
+                       (const uint8_t*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale, za);
   } else if (s.ik_dtype == kNVFP4) {
     hipLaunchKernelGGL(index_nvfp4_kernel<G>, grid, block, 0, st, (const uint16_t*)iq,
                        (const uint8_t*)ikd, (const uint8_t*)iks, bt, lens, qpos, scores, s.R,
-                       s.MB, out_scale);
+                       s.MB, s.P, out_scale, za);
   } else {
     hipLaunchKernelGGL(index_f32_kernel<G>, grid, block, 0, st, (const float*)iq,
-                       (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, out_scale);
+                       (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale, za);
   }
   return hipGetLastError();
 }
@@ -298,12 +315,12 @@ static hipError_t launch_g(const Shape& s, const void* iq, const void* ikd, cons
 hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* ik_data,
                                const void* ik_scales, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* q_pos,
-                               float* scores, hipStream_t st) {
+                               float* scores, hipStream_t st, int32_t* zero, int n_zero) {
   switch (s.G) {
-    case 1: return launch_g<1>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    case 2: return launch_g<2>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    case 4: return launch_g<4>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    case 8: return launch_g<8>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
+    case 1: return launch_g<1>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
+    case 2: return launch_g<2>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
+    case 4: return launch_g<4>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
+    case 8: return launch_g<8>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
     default: return hipErrorInvalidValue;
   }
 }

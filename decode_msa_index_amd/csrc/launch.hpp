@@ -19,29 +19,48 @@ struct Shape {
 // dtype codes (same values as msa_dtype)
 constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2, kNVFP4 = 3;
 
-// Split-K partials: per (row, group, split) 16 heads x (m, l) and 16 x 128
-// unnormalised outputs, fp32.
+// Query heads per group are padded to 16 (one MFMA tile).
 constexpr int kHeadsPad = 16;
-inline size_t partial_o_floats(const Shape& s) {
-  return (size_t)s.rows * s.G * s.K * kHeadsPad * 128;
-}
-inline size_t partial_ml_floats(const Shape& s) {
-  return (size_t)s.rows * s.G * s.K * kHeadsPad * 2;
-}
 
+// zero: optional int array of n_zero entries the index kernel clears in
+// passing (the attention kernel's arrival counters).
 hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* ik_data,
                                const void* ik_scales, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* q_pos,
-                               float* scores, hipStream_t st);
+                               float* scores, hipStream_t st, int32_t* zero = nullptr,
+                               int n_zero = 0);
 
 hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
                              const int32_t* q_pos, int32_t* topk, hipStream_t st);
 
+// Attention launch shape: waves per workgroup and workgroups (splits) per
+// (row, group).  splits > 1 needs attend_workspace_bytes of scratch.
+struct AttendConfig {
+  int nw, splits;
+};
+AttendConfig attend_config(const Shape& s);
+size_t attend_workspace_bytes(const Shape& s, const AttendConfig& c);
+
 hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_data,
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
-                                const int32_t* topk, void* out, float* lse,
-                                int32_t* counters, float* part_o, float* part_ml,
+                                const int32_t* topk, void* out, float* lse, void* workspace,
                                 hipStream_t st);
+// Selection fused into the attention kernel (msa_decode): needs the row's
+// block keys in LDS, so only for block tables short enough.
+bool select_fusable(const Shape& s);
+hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_data,
+                                const void* kv_scales, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* q_pos,
+                                const float* scores, int32_t* topk_out, void* out, float* lse,
+                                void* workspace, bool counters_zeroed, hipStream_t st);
+// Offset (bytes) of the arrival counters inside the attention workspace.
+size_t attend_counter_offset(const Shape& s, const AttendConfig& c);
+
+hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const void* q,
+                                    const void* kv_data, const void* kv_scales,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* q_pos, const int32_t* topk, void* out,
+                                    float* lse, void* workspace, hipStream_t st);
 
 }  // namespace msa

@@ -7,14 +7,15 @@
 // reference of MiniMaxM3SparseAttention._run_attention describes split-K
 // attend kernels that read per-request metadata).
 //
-// Grid: one single-wave workgroup per (row, group, selected block).  Each
-// computes, for the group's (up to 16) heads and the block's 128 keys,
+// Grid: one workgroup per (row, group); its 8 waves split the selected blocks
+// (split-K inside the workgroup).  For a block of 128 keys and the group's
+// (up to 16) heads a wave computes
 //   S^T = K Q^T            v_mfma_f32_16x16x32_bf16  (K e4m3/e2m1 -> bf16 exact)
 //   P   = exp2(S*scale - m) in fp32, rounded to f16 for the next product
-//   O   = P V              v_mfma_f32_16x16x32_f16   (V e4m3/e2m1 -> f16 exact)
-// and stores (m, l, O) as a partial.  The last workgroup of a (row, group) to
-// finish -- found with a device-scope counter -- merges the partials, scales
-// by v_scale / l and writes the output, then zeroes the counter.
+//   O  += P V              v_mfma_f32_16x16x32_f16   (V e4m3/e2m1 -> f16 exact)
+// with an online-softmax running state; the waves' states merge through LDS.
+// Nothing crosses workgroups, so there are no atomics, fences or partials in
+// global memory.
 //
 // Operand layout.  The contraction order inside an MFMA is free as long as
 // both operands agree, so the key order of the S^T tiles is chosen to make
@@ -25,6 +26,7 @@
 // B operand needs (V is stored transposed, [d][t], for this).
 #include "device.hpp"
 #include "launch.hpp"
+#include "select_wave.hpp"
 
 namespace msa {
 
@@ -95,168 +97,101 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Split bookkeeping shared by the kernels: publish this split's partial, and
-// if it is the last one of its (row, group), merge all of them.
+// Arguments shared by the kernels.
 // ---------------------------------------------------------------------------
 struct AttendArgs {
   const int32_t* bt;
   const int32_t* lens;
   const int32_t* qpos;
-  const int32_t* topk;
+  const int32_t* topk;    // selection input (attend only)
+  const float* scores;    // pooled scores (select + attend)
+  int32_t* topk_out;      // selection output (select + attend), may be null
   void* out;
   float* lse;
-  int32_t* counters;
-  float* part_o;
-  float* part_ml;
-  int R, H, G, hpg, MB, K;
+  int R, H, G, hpg, MB, K, P;
   float scale_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
   int out_f32;
 };
 
-__device__ __forceinline__ void finish_split(const AttendArgs& a, int u, int count) {
-  const int lane = threadIdx.x;
-  __threadfence();
-  int prev = 0;
-  if (lane == 0) prev = atomicAdd(&a.counters[u], 1);
-  prev = __shfl(prev, 0, 64);
-  if (prev != count - 1) return;
-  __threadfence();
-  const int row = u / a.G, g = u % a.G;
-  const float* po = a.part_o + (size_t)u * a.K * (kHeadsPad * 128);
-  const float* pml = a.part_ml + (size_t)u * a.K * (kHeadsPad * 2);
-  for (int h = 0; h < a.hpg; ++h) {
-    float ms = -INFINITY, ls = 0.0f;
-    if (lane < count) {
-      ms = __builtin_nontemporal_load(pml + (size_t)lane * (kHeadsPad * 2) + 2 * h);
-      ls = __builtin_nontemporal_load(pml + (size_t)lane * (kHeadsPad * 2) + 2 * h + 1);
-    }
-    const float M = wave_max(ms);
-    const float w = lane < count ? exp2f(ms - M) : 0.0f;
-    const float L = wave_sum(w * ls);
-    float o0 = 0.0f, o1 = 0.0f;
-    for (int s = 0; s < count; ++s) {
-      const float ws = __shfl(w, s, 64);
-      const float* src = po + (size_t)s * (kHeadsPad * 128) + h * 128;
-      o0 = fmaf(ws, __builtin_nontemporal_load(src + lane), o0);
-      o1 = fmaf(ws, __builtin_nontemporal_load(src + lane + 64), o1);
-    }
-    const float f = a.v_scale / L;
-    const size_t orow = ((size_t)row * a.H + (size_t)g * a.hpg + h) * 128;
-    if (a.out_f32) {
-      float* o = reinterpret_cast<float*>(a.out) + orow;
-      o[lane] = o0 * f;
-      o[lane + 64] = o1 * f;
-    } else {
-      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + orow;
-      o[lane] = f32_to_bf16(o0 * f);
-      o[lane + 64] = f32_to_bf16(o1 * f);
-    }
-    if (a.lse && lane == 0)
-      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] = (M + log2f(L)) * 0.69314718055994531f;
-  }
-  if (lane == 0) a.counters[u] = 0;
+__device__ __forceinline__ void store_out(const AttendArgs& a, int row, int h, int d, float v) {
+  const size_t idx = ((size_t)row * a.H + h) * kDim + d;
+  if (a.out_f32)
+    reinterpret_cast<float*>(a.out)[idx] = v;
+  else
+    reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
 }
 
-// Common prologue: which block this workgroup takes, or -1 if none.
-struct SplitInfo {
-  int u, row, g, b, count, j, pb, nvalid;
-};
-__device__ __forceinline__ bool split_info(const AttendArgs& a, SplitInfo& si) {
-  si.u = blockIdx.y;
-  si.row = si.u / a.G;
-  si.g = si.u % a.G;
-  si.b = si.row / a.R;
-  const int pos = a.qpos ? a.qpos[si.row] : a.lens[si.b] - 1;
-  const int rb = pos / kBlock;
-  si.count = min(a.K, rb + 1);
-  if ((int)blockIdx.x >= si.count) return false;
-  si.j = a.topk[(size_t)si.u * a.K + blockIdx.x];
-  if (si.j < 0 || si.j > rb) {  // malformed selection: contribute nothing
-    si.pb = -1;
-    si.nvalid = 0;
-    return true;
-  }
-  si.pb = a.bt[(size_t)si.b * a.MB + si.j];
-  si.nvalid = min(kBlock, pos - si.j * kBlock + 1);
-  return true;
-}
-
-__device__ __forceinline__ void store_empty_partial(const AttendArgs& a, const SplitInfo& si) {
-  const int lane = threadIdx.x;
-  float* pml = a.part_ml + ((size_t)si.u * a.K + blockIdx.x) * (kHeadsPad * 2);
-  if (lane < kHeadsPad) {
-    pml[2 * lane] = -INFINITY;
-    pml[2 * lane + 1] = 0.0f;
-  }
-  float* po = a.part_o + ((size_t)si.u * a.K + blockIdx.x) * (kHeadsPad * 128);
-  for (int i = lane; i < kHeadsPad * 128; i += 64) po[i] = 0.0f;
+// exp2(x - m) that is 0 when both are -inf (an empty partial)
+__device__ __forceinline__ float rescale(float x, float m) {
+  return x == -INFINITY ? 0.0f : exp2f(x - m);
 }
 
 // ---------------------------------------------------------------------------
 // FP8 / NVFP4 cache, bf16 queries: MFMA tiles.
+//
+// Grid: (row, group) x S splits; a workgroup of NW waves takes a contiguous
+// share of the row's selection entries and wave w of it takes every NW-th
+// entry of that share.  With SELECT the workgroup first makes the group's
+// selection itself from the pooled scores (wave 0, select_wave.hpp; every
+// split recomputes it, which costs no extra latency) and split 0 also
+// stores it.  For each block a wave computes S^T = K Q^T on MFMA, updates
+// its running max / denominator (online softmax, fp32) and accumulates P V
+// on MFMA into the rescaled running output.  The NW states of a workgroup
+// merge pairwise through LDS.  With S = 1 the workgroup writes the
+// normalised output; otherwise it publishes its state with coherent
+// (device-scope) stores, and the last of the S workgroups to arrive -- a
+// device-scope counter per (row, group) -- merges the S states and writes the
+// output.  No cache write-back fence is needed: every value another
+// workgroup reads is written and read with device-scope atomic accesses.
+// Running state layout per lane l: max and denominator of head l%16; output
+// rows (heads) 4*(l/16)+i, columns (dims) 16*dt + l%16.
 // ---------------------------------------------------------------------------
-template <int KV>
-__global__ __launch_bounds__(64) void attend_mfma_kernel(const uint16_t* __restrict__ q,
-                                                         const uint8_t* __restrict__ kvd,
-                                                         const uint8_t* __restrict__ kvs,
-                                                         AttendArgs a) {
-  SplitInfo si;
-  if (!split_info(a, si)) return;
-  const int lane = threadIdx.x;
-  if (si.pb < 0) {
-    store_empty_partial(a, si);
-    finish_split(a, si.u, si.count);
-    return;
-  }
-  const int n = lane & 15, qd = lane >> 4;
-  const size_t kplane = ((size_t)si.pb * 2 + 0) * a.G + si.g;
-  const size_t vplane = ((size_t)si.pb * 2 + 1) * a.G + si.g;
+struct Partials {
+  float* o;          // [rows*G][S][16][128] unnormalised outputs
+  float* ml;         // [rows*G][S][16][2]   running max (log2 domain) and denominator
+  int32_t* counters; // [rows*G] arrivals, zero before the launch; reset by the merger
+  int S;
+};
 
-  // ---- loads: K rows kappa(u, n), V^T rows dt*16+n; 32 dims / tokens each ----
-  uint4 kraw[16], vraw[16];
-  uint32_t ksc[8];
-  uint4 vsc[16];
-  if constexpr (KV == kFP8) {
-    const uint8_t* kb = kvd + kplane * (kBlock * kDim);
-    const uint8_t* vb = kvd + vplane * (kBlock * kDim);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kappa = 32 * (n >> 2) + 8 * (u >> 1) + 4 * (u & 1) + (n & 3);
-      const uint4* p = reinterpret_cast<const uint4*>(kb + kappa * kDim + qd * 32);
-      kraw[2 * u] = p[0];
-      kraw[2 * u + 1] = p[1];
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint4* p = reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * kBlock + qd * 32);
-      vraw[2 * dt] = p[0];
-      vraw[2 * dt + 1] = p[1];
-    }
-  } else {
-    const uint8_t* kb = kvd + kplane * (kBlock * kDim / 2);
-    const uint8_t* vb = kvd + vplane * (kBlock * kDim / 2);
-    const uint8_t* ks = kvs + kplane * (kBlock * kDim / 16);
-    const uint8_t* vs = kvs + vplane * (kBlock * kDim / 16);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kappa = 32 * (n >> 2) + 8 * (u >> 1) + 4 * (u & 1) + (n & 3);
-      kraw[u] = *reinterpret_cast<const uint4*>(kb + kappa * (kDim / 2) + qd * 16);
-      ksc[u] = *reinterpret_cast<const uint16_t*>(ks + kappa * (kDim / 16) + qd * 2);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      vraw[dt] = *reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * (kBlock / 2) + qd * 16);
-      const uint4* sp = reinterpret_cast<const uint4*>(vs + dt * kBlock + qd * 32);
-      vsc[2 * dt] = sp[0];
-      vsc[2 * dt + 1] = sp[1];
-    }
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int KV, int NW, bool SELECT>
+__global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvd,
+    const uint8_t* __restrict__ kvs, AttendArgs a, Partials part) {
+  __shared__ float red_o[NW > 1 ? NW / 2 : 1][32][64];
+  __shared__ float red_ml[NW > 1 ? NW / 2 : 1][2][16];
+  __shared__ int32_t sel[32];
+  __shared__ int is_last;
+  extern __shared__ uint32_t sel_lds[];  // SELECT: [256] histogram, then [MB] keys
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x / part.S, split = blockIdx.x % part.S;
+  const int row = u / a.G, g = u % a.G, b = row / a.R;
+  const int pos = row_last_key(a.lens, a.qpos, row, b, a.MB);
+  const int rb = pos < 0 ? -1 : pos / kBlock;
+  const int count = min(a.K, rb + 1);  // 0 when the row sees no key
+  const int per_wg = (count + part.S - 1) / part.S;
+  const int e0 = split * per_wg, e1 = min(count, e0 + per_wg);
+  const int n = lane & 15, qd = lane >> 4;
+
+  if constexpr (SELECT) {
+    if (wave == 0) wave_select<64>(a.scores + (size_t)u * a.MB, rb, a.K, sel_lds + 256, sel_lds, sel);
+    __syncthreads();
+    if (split == 0 && a.topk_out && (int)threadIdx.x < a.K)
+      a.topk_out[(size_t)u * a.K + threadIdx.x] = sel[threadIdx.x];
   }
-  // ---- Q^T operand: head n of the group, dims qd*32 + 8c + e ----
+
+  // Q^T operand: head n of the group, dims qd*32 + 8c + e (zero past hpg)
   bf16x8 qop[4];
   if (n < a.hpg) {
     const uint4* qp = reinterpret_cast<const uint4*>(
-        q + ((size_t)si.row * a.H + (size_t)si.g * a.hpg + n) * kDim + qd * 32);
+        q + ((size_t)row * a.H + (size_t)g * a.hpg + n) * kDim + qd * 32);
 #pragma unroll
     for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
   } else {
@@ -264,204 +199,492 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(const uint16_t* __restr
     for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
   }
 
-  // ---- S^T = K Q^T ----
-  f32x4 sacc[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    sacc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bf16x8 kop;
-      if constexpr (KV == kFP8) {
-        const uint4 r = kraw[2 * u + (c >> 1)];
-        kop = (c & 1) ? fp8x8_bf16(r.z, r.w) : fp8x8_bf16(r.x, r.y);
-      } else {
-        const uint32_t w = c == 0 ? kraw[u].x : c == 1 ? kraw[u].y : c == 2 ? kraw[u].z : kraw[u].w;
-        const f32x2 sc = fp8x2_to_f32x2<false>(ksc[u]);
-        kop = nvfp4x8_bf16(w, sc[c >> 1]);
-      }
-      sacc[u] = mfma_bf16(kop, qop[c], sacc[u]);
-    }
-  }
-
-  // ---- softmax over the block's keys (head n lives in lanes n, n+16, n+32, n+48) ----
-  float mx = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 32 * qd + 8 * (u >> 1) + 4 * (u & 1) + i;
-      const float t = key < si.nvalid ? sacc[u][i] * a.scale_log2 : -INFINITY;
-      sacc[u][i] = t;
-      mx = fmaxf(mx, t);
-    }
-  }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  float lsum = 0.0f;
-  f16x8 pop[4];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(sacc[u][i] - mx);
-      lsum += p;
-      pop[u >> 1][4 * (u & 1) + i] = (_Float16)p;
-    }
-  }
-  lsum += shfl_xor(lsum, 16);
-  lsum += shfl_xor(lsum, 32);
-
-  // ---- O = P V ----
+  float M = -INFINITY, Lr = 0.0f;
   f32x4 oacc[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The wave's selection entries e0+wave, e0+wave+NW, ... and their physical
+  // blocks, fetched by parallel lanes up front: lane i holds the i-th one.
+  int my_j = -1, my_pb = -1;
+  {
+    const int sidx = e0 + wave + NW * lane;
+    if (lane < 32 && sidx < e1) my_j = SELECT ? sel[sidx] : a.topk[(size_t)u * a.K + sidx];
+    if (my_j >= 0 && my_j <= rb) my_pb = a.bt[(size_t)b * a.MB + my_j];
+  }
+  for (int it = 0; e0 + wave + NW * it < e1; ++it) {
+    const int j = __shfl(my_j, it, 64);
+    const int pb = __shfl(my_pb, it, 64);
+    if (j < 0 || j > rb) continue;      // malformed selection entry: contributes nothing
+    if (pb < 0 || pb >= a.P) continue;  // invalid table entry: contributes nothing
+    const int nvalid = min(kBlock, pos - j * kBlock + 1);
+    const size_t kplane = ((size_t)pb * 2 + 0) * a.G + g;
+    const size_t vplane = ((size_t)pb * 2 + 1) * a.G + g;
+
+    // ---- loads: K rows kappa(u, n), V^T rows dt*16+n; 32 dims / tokens each ----
+    uint4 kraw[16], vraw[16];
+    uint32_t ksc[8];
+    uint4 vsc[16];
+    if constexpr (KV == kFP8) {
+      const uint8_t* kb = kvd + kplane * (kBlock * kDim);
+      const uint8_t* vb = kvd + vplane * (kBlock * kDim);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f16x8 vop;
-      if constexpr (KV == kFP8) {
-        const uint4 r = vraw[2 * dt + (c >> 1)];
-        vop = (c & 1) ? fp8x8_f16(r.z, r.w) : fp8x8_f16(r.x, r.y);
-      } else {
-        const uint32_t w = c == 0 ? vraw[dt].x : c == 1 ? vraw[dt].y : c == 2 ? vraw[dt].z : vraw[dt].w;
-        const uint4 s = vsc[2 * dt + (c >> 1)];
-        vop = (c & 1) ? nvfp4x8_f16(w, s.z, s.w) : nvfp4x8_f16(w, s.x, s.y);
+      for (int t = 0; t < 8; ++t) {
+        const int kappa = 32 * (n >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (n & 3);
+        const uint4* p = reinterpret_cast<const uint4*>(kb + kappa * kDim + qd * 32);
+        kraw[2 * t] = p[0];
+        kraw[2 * t + 1] = p[1];
       }
-      oacc[dt] = mfma_f16(pop[c], vop, oacc[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint4* p = reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * kBlock + qd * 32);
+        vraw[2 * dt] = p[0];
+        vraw[2 * dt + 1] = p[1];
+      }
+    } else {
+      const uint8_t* kb = kvd + kplane * (kBlock * kDim / 2);
+      const uint8_t* vb = kvd + vplane * (kBlock * kDim / 2);
+      const uint8_t* ks = kvs + kplane * (kBlock * kDim / 16);
+      const uint8_t* vs = kvs + vplane * (kBlock * kDim / 16);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int kappa = 32 * (n >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (n & 3);
+        kraw[t] = *reinterpret_cast<const uint4*>(kb + kappa * (kDim / 2) + qd * 16);
+        ksc[t] = *reinterpret_cast<const uint16_t*>(ks + kappa * (kDim / 16) + qd * 2);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        vraw[dt] = *reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * (kBlock / 2) + qd * 16);
+        const uint4* sp = reinterpret_cast<const uint4*>(vs + dt * kBlock + qd * 32);
+        vsc[2 * dt] = sp[0];
+        vsc[2 * dt + 1] = sp[1];
+      }
+    }
+
+    // ---- S^T = K Q^T ----
+    f32x4 sacc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      sacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x8 kop;
+        if constexpr (KV == kFP8) {
+          const uint4 r = kraw[2 * t + (c >> 1)];
+          kop = (c & 1) ? fp8x8_bf16(r.z, r.w) : fp8x8_bf16(r.x, r.y);
+        } else {
+          const uint32_t w = c == 0 ? kraw[t].x : c == 1 ? kraw[t].y : c == 2 ? kraw[t].z : kraw[t].w;
+          const f32x2 sc = fp8x2_to_f32x2<false>(ksc[t]);
+          kop = nvfp4x8_bf16(w, sc[c >> 1]);
+        }
+        sacc[t] = mfma_bf16(kop, qop[c], sacc[t]);
+      }
+    }
+
+    // ---- online softmax update (head n lives in lanes n, n+16, n+32, n+48) ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 32 * qd + 8 * (t >> 1) + 4 * (t & 1) + i;
+        const float v = key < nvalid ? sacc[t][i] * a.scale_log2 : -INFINITY;
+        sacc[t][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float Mn = fmaxf(M, mx);
+    const float alpha = rescale(M, Mn);
+    float lsum = 0.0f;
+    f16x8 pop[4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sacc[t][i] - Mn);
+        lsum += p;
+        pop[t >> 1][4 * (t & 1) + i] = (_Float16)p;
+      }
+    }
+    lsum += shfl_xor(lsum, 16);
+    lsum += shfl_xor(lsum, 32);
+    Lr = Lr * alpha + lsum;
+    M = Mn;
+    float alpha_o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * qd + i, 64);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha_o[i];
+    }
+
+    // ---- O += P V ----
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f16x8 vop;
+        if constexpr (KV == kFP8) {
+          const uint4 r = vraw[2 * dt + (c >> 1)];
+          vop = (c & 1) ? fp8x8_f16(r.z, r.w) : fp8x8_f16(r.x, r.y);
+        } else {
+          const uint32_t w = c == 0 ? vraw[dt].x : c == 1 ? vraw[dt].y : c == 2 ? vraw[dt].z : vraw[dt].w;
+          const uint4 sv = vsc[2 * dt + (c >> 1)];
+          vop = (c & 1) ? nvfp4x8_f16(w, sv.z, sv.w) : nvfp4x8_f16(w, sv.x, sv.y);
+        }
+        oacc[dt] = mfma_f16(pop[c], vop, oacc[dt]);
+      }
     }
   }
 
-  // ---- publish the partial ----
-  const size_t pidx = (size_t)si.u * a.K + blockIdx.x;
-  float* po = a.part_o + pidx * (kHeadsPad * 128);
+  // ---- merge the waves' states pairwise through LDS ----
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
+  for (int half = NW / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
+      const int slot = wave - half;
+      if (qd == 0) {
+        red_ml[slot][0][n] = M;
+        red_ml[slot][1][n] = Lr;
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) po[(4 * qd + i) * 128 + dt * 16 + n] = oacc[dt][i];
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_o[slot][dt * 4 + i][lane] = oacc[dt][i];
+      }
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float Mb = red_ml[wave][0][n], Lb = red_ml[wave][1][n];
+      const float Mn = fmaxf(M, Mb);
+      const float fa = rescale(M, Mn), fb = rescale(Mb, Mn);
+      Lr = Lr * fa + Lb * fb;
+      M = Mn;
+      float fa_o[4], fb_o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa_o[i] = __shfl(fa, 4 * qd + i, 64);
+        fb_o[i] = __shfl(fb, 4 * qd + i, 64);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[dt][i] = oacc[dt][i] * fa_o[i] + red_o[wave][dt * 4 + i][lane] * fb_o[i];
+      }
+    }
+    __syncthreads();
   }
-  if (qd == 0) {
-    float* pml = a.part_ml + pidx * (kHeadsPad * 2);
-    pml[2 * n] = mx;
-    pml[2 * n + 1] = lsum;
+
+  if (part.S == 1) {
+    if (wave != 0) return;
+    float inv_o[4];
+    const float inv = Lr > 0.0f ? a.v_scale / Lr : 0.0f;  // no visible key: zeros
+#pragma unroll
+    for (int i = 0; i < 4; ++i) inv_o[i] = __shfl(inv, 4 * qd + i, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * qd + i;
+      if (h < a.hpg) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          store_out(a, row, g * a.hpg + h, dt * 16 + n, oacc[dt][i] * inv_o[i]);
+      }
+    }
+    if (a.lse && qd == 0 && n < a.hpg)
+      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + n] =
+          Lr > 0.0f ? (M + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
+    return;
   }
-  finish_split(a, si.u, si.count);
+
+  // ---- split-K across workgroups: publish, count arrivals, last one merges ----
+  if (wave == 0) {
+    const size_t pidx = (size_t)u * part.S + split;
+    float* po = part.o + pidx * (kHeadsPad * kDim);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) coherent_store(po + (4 * qd + i) * kDim + dt * 16 + n, oacc[dt][i]);
+    }
+    if (qd == 0) {
+      coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n, M);
+      coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n + 1, Lr);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    int prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(part.counters + u, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0, 64);
+    if (lane == 0) is_last = prev == part.S - 1;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  // merge: thread t takes head t/16 and dims 8*(t%16) .. +8 (looping when NW < 4)
+  for (int t = threadIdx.x; t < kHeadsPad * 16; t += 64 * NW) {
+    const int h = t >> 4, d0 = (t & 15) * 8;
+    if (h >= a.hpg) continue;
+    const float* ml = part.ml + (size_t)u * part.S * (kHeadsPad * 2) + 2 * h;
+    const float* po = part.o + (size_t)u * part.S * (kHeadsPad * kDim) + h * kDim + d0;
+    float Mx = -INFINITY;
+    for (int sp = 0; sp < part.S; ++sp) Mx = fmaxf(Mx, coherent_load(ml + (size_t)sp * (kHeadsPad * 2)));
+    float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sp = 0; sp < part.S; ++sp) {
+      const float f = rescale(coherent_load(ml + (size_t)sp * (kHeadsPad * 2)), Mx);
+      L += f * coherent_load(ml + (size_t)sp * (kHeadsPad * 2) + 1);
+      const float* src = po + (size_t)sp * (kHeadsPad * kDim);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] += f * coherent_load(src + k);
+    }
+    const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) store_out(a, row, g * a.hpg + h, d0 + k, o[k] * inv);
+    if (a.lse && (t & 15) == 0)
+      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
+          L > 0.0f ? (Mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(part.counters + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void zero_fill_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
-// fp32 cache (small exactness workloads): plain fp32 FMAs, same partials.
+// fp32 cache (small exactness workloads): one wave per (row, group) walks
+// the selected blocks with plain fp32 FMAs and an online softmax.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void attend_f32_kernel(const void* __restrict__ q,
                                                         const float* __restrict__ kvd,
                                                         int q_bf16, AttendArgs a) {
   __shared__ float qs[kHeadsPad][kDim];
   __shared__ float ps[kHeadsPad][kBlock];
-  SplitInfo si;
-  if (!split_info(a, si)) return;
+  __shared__ float alpha_s[kHeadsPad];
   const int lane = threadIdx.x;
-  if (si.pb < 0) {
-    store_empty_partial(a, si);
-    finish_split(a, si.u, si.count);
-    return;
-  }
+  const int u = blockIdx.x, row = u / a.G, g = u % a.G, b = row / a.R;
+  const int pos = row_last_key(a.lens, a.qpos, row, b, a.MB);
+  const int rb = pos < 0 ? -1 : pos / kBlock;
+  const int count = min(a.K, rb + 1);  // 0 when the row sees no key
   for (int i = lane; i < a.hpg * kDim; i += 64) {
-    const size_t qi = ((size_t)si.row * a.H + (size_t)si.g * a.hpg) * kDim + i;
+    const size_t qi = ((size_t)row * a.H + (size_t)g * a.hpg) * kDim + i;
     qs[i / kDim][i % kDim] = q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(q)[qi])
                                     : reinterpret_cast<const float*>(q)[qi];
   }
-  __syncthreads();
-  const float* kb = kvd + (((size_t)si.pb * 2 + 0) * a.G + si.g) * (kBlock * kDim);
-  const float* vb = kvd + (((size_t)si.pb * 2 + 1) * a.G + si.g) * (kBlock * kDim);
-  float mh[kHeadsPad], lh[kHeadsPad];
-  for (int h = 0; h < a.hpg; ++h) {
-    float t[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int key = lane + 64 * half;
-      const float4* kr = reinterpret_cast<const float4*>(kb + key * kDim);
-      float acc = 0.0f;
-      for (int d4 = 0; d4 < kDim / 4; ++d4) {
-        const float4 k = kr[d4];
-        acc = fmaf(qs[h][4 * d4], k.x, acc);
-        acc = fmaf(qs[h][4 * d4 + 1], k.y, acc);
-        acc = fmaf(qs[h][4 * d4 + 2], k.z, acc);
-        acc = fmaf(qs[h][4 * d4 + 3], k.w, acc);
-      }
-      t[half] = key < si.nvalid ? acc * a.scale_log2 : -INFINITY;
-    }
-    const float m = wave_max(fmaxf(t[0], t[1]));
-    const float p0 = exp2f(t[0] - m), p1 = exp2f(t[1] - m);
-    ps[h][lane] = p0;
-    ps[h][lane + 64] = p1;
-    mh[h] = m;
-    lh[h] = wave_sum(p0 + p1);
+  float M[kHeadsPad], Lr[kHeadsPad], o0[kHeadsPad], o1[kHeadsPad];
+  for (int h = 0; h < kHeadsPad; ++h) {
+    M[h] = -INFINITY;
+    Lr[h] = 0.0f;
+    o0[h] = o1[h] = 0.0f;
   }
   __syncthreads();
-  const size_t pidx = (size_t)si.u * a.K + blockIdx.x;
-  float* po = a.part_o + pidx * (kHeadsPad * 128);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int d = lane + 64 * half;
-    const float4* vr = reinterpret_cast<const float4*>(vb + d * kBlock);
+  for (int sidx = 0; sidx < count; ++sidx) {
+    const int j = a.topk[(size_t)u * a.K + sidx];
+    if (j < 0 || j > rb) continue;
+    const int pb = a.bt[(size_t)b * a.MB + j];
+    if (pb < 0 || pb >= a.P) continue;  // invalid table entry: contributes nothing
+    const int nvalid = min(kBlock, pos - j * kBlock + 1);
+    const float* kb = kvd + (((size_t)pb * 2 + 0) * a.G + g) * (kBlock * kDim);
+    const float* vb = kvd + (((size_t)pb * 2 + 1) * a.G + g) * (kBlock * kDim);
     for (int h = 0; h < a.hpg; ++h) {
-      float acc = 0.0f;
+      float t[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key = lane + 64 * half;
+        const float4* kr = reinterpret_cast<const float4*>(kb + key * kDim);
+        float acc = 0.0f;
+        for (int d4 = 0; d4 < kDim / 4; ++d4) {
+          const float4 k = kr[d4];
+          acc = fmaf(qs[h][4 * d4], k.x, acc);
+          acc = fmaf(qs[h][4 * d4 + 1], k.y, acc);
+          acc = fmaf(qs[h][4 * d4 + 2], k.z, acc);
+          acc = fmaf(qs[h][4 * d4 + 3], k.w, acc);
+        }
+        t[half] = key < nvalid ? acc * a.scale_log2 : -INFINITY;
+      }
+      const float mx = wave_max(fmaxf(t[0], t[1]));
+      const float Mn = fmaxf(M[h], mx);
+      const float al = rescale(M[h], Mn);
+      const float p0 = exp2f(t[0] - Mn), p1 = exp2f(t[1] - Mn);
+      ps[h][lane] = p0;
+      ps[h][lane + 64] = p1;
+      Lr[h] = Lr[h] * al + wave_sum(p0 + p1);
+      M[h] = Mn;
+      if (lane == 0) alpha_s[h] = al;
+    }
+    __syncthreads();
+    for (int h = 0; h < a.hpg; ++h) {
+      const float al = alpha_s[h];
+      float acc0 = 0.0f, acc1 = 0.0f;
+      const float4* v0 = reinterpret_cast<const float4*>(vb + lane * kBlock);
+      const float4* v1 = reinterpret_cast<const float4*>(vb + (lane + 64) * kBlock);
       for (int k4 = 0; k4 < kBlock / 4; ++k4) {
-        const float4 v = vr[k4];
-        acc = fmaf(ps[h][4 * k4], v.x, acc);
-        acc = fmaf(ps[h][4 * k4 + 1], v.y, acc);
-        acc = fmaf(ps[h][4 * k4 + 2], v.z, acc);
-        acc = fmaf(ps[h][4 * k4 + 3], v.w, acc);
+        const float4 x = v0[k4], y = v1[k4];
+        acc0 = fmaf(ps[h][4 * k4], x.x, acc0);
+        acc0 = fmaf(ps[h][4 * k4 + 1], x.y, acc0);
+        acc0 = fmaf(ps[h][4 * k4 + 2], x.z, acc0);
+        acc0 = fmaf(ps[h][4 * k4 + 3], x.w, acc0);
+        acc1 = fmaf(ps[h][4 * k4], y.x, acc1);
+        acc1 = fmaf(ps[h][4 * k4 + 1], y.y, acc1);
+        acc1 = fmaf(ps[h][4 * k4 + 2], y.z, acc1);
+        acc1 = fmaf(ps[h][4 * k4 + 3], y.w, acc1);
       }
-      po[h * 128 + d] = acc;
+      o0[h] = o0[h] * al + acc0;
+      o1[h] = o1[h] * al + acc1;
     }
+    __syncthreads();
   }
-  if (lane == 0) {
-    float* pml = a.part_ml + pidx * (kHeadsPad * 2);
-    for (int h = 0; h < a.hpg; ++h) {
-      pml[2 * h] = mh[h];
-      pml[2 * h + 1] = lh[h];
-    }
+  for (int h = 0; h < a.hpg; ++h) {
+    const float inv = Lr[h] > 0.0f ? a.v_scale / Lr[h] : 0.0f;  // no visible key: zeros
+    store_out(a, row, g * a.hpg + h, lane, o0[h] * inv);
+    store_out(a, row, g * a.hpg + h, lane + 64, o1[h] * inv);
+    if (a.lse && lane == 0)
+      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
+          Lr[h] > 0.0f ? (M[h] + log2f(Lr[h])) * 0.69314718055994531f : -INFINITY;
   }
-  finish_split(a, si.u, si.count);
 }
 
-hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_data,
-                                const void* kv_scales, const int32_t* block_table,
-                                const int32_t* seq_lens, const int32_t* q_pos,
-                                const int32_t* topk, void* out, float* lse,
-                                int32_t* counters, float* part_o, float* part_ml,
-                                hipStream_t st) {
+// Launch shape of the MFMA path: waves per workgroup and splits per
+// (row, group), chosen so that the grid covers the chip while each wave still
+// takes whole blocks.
+AttendConfig attend_config(const Shape& s) {
+  AttendConfig c;
+  const int units = s.rows * s.G;
+  c.nw = 8;
+  c.splits = 1;
+  if (s.kv_dtype == kF32) return c;
+  const int target_wgs = 256;
+  int sp = (target_wgs + units - 1) / units;
+  sp = max(1, min(sp, (s.K + 3) / 4));
+  c.splits = sp;
+  const int per_wg = (s.K + sp - 1) / sp;
+  c.nw = per_wg >= 8 ? 8 : per_wg >= 4 ? 4 : per_wg >= 2 ? 2 : 1;
+  return c;
+}
+
+// [ml: units*S*16*2][o: units*S*16*128][counters: units], floats then ints
+size_t attend_workspace_bytes(const Shape& s, const AttendConfig& c) {
+  if (c.splits <= 1) return 0;
+  const size_t units = (size_t)s.rows * s.G;
+  return sizeof(float) * units * c.splits * kHeadsPad * (kDim + 2) + sizeof(int32_t) * units;
+}
+
+size_t attend_counter_offset(const Shape& s, const AttendConfig& c) {
+  return sizeof(float) * (size_t)s.rows * s.G * c.splits * kHeadsPad * (kDim + 2);
+}
+
+// The fused kernel holds the row's keys (and a 256-bin histogram) in LDS
+// next to its static merge buffers; it is used when all of it fits in 64 KB.
+bool select_fusable(const Shape& s) {
+  if (s.kv_dtype == kF32) return false;
+  const int nw = attend_config(s).nw;
+  const size_t stat = (size_t)(nw > 1 ? nw / 2 : 1) * (32 * 64 + 2 * 16) * sizeof(float) +
+                      32 * sizeof(int32_t) + 64;
+  const size_t dyn = sizeof(uint32_t) * (256 + (size_t)s.MB);
+  return stat + dyn <= 65536;
+}
+
+static AttendArgs make_args(const Shape& s, const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* q_pos, const int32_t* topk, const float* scores,
+                            int32_t* topk_out, void* out, float* lse) {
   AttendArgs a;
   a.bt = block_table;
   a.lens = seq_lens;
   a.qpos = q_pos;
   a.topk = topk;
+  a.scores = scores;
+  a.topk_out = topk_out;
   a.out = out;
   a.lse = lse;
-  a.counters = counters;
-  a.part_o = part_o;
-  a.part_ml = part_ml;
   a.R = s.R;
   a.H = s.H;
   a.G = s.G;
   a.hpg = s.hpg;
   a.MB = s.MB;
   a.K = s.K;
+  a.P = s.P;
   a.scale_log2 = s.sm_scale * s.k_scale * 1.4426950408889634f;
   a.v_scale = s.v_scale;
   a.out_f32 = s.out_dtype == kF32;
-  dim3 grid(s.K, s.rows * s.G), block(64);
-  if (s.kv_dtype == kFP8) {
-    hipLaunchKernelGGL(attend_mfma_kernel<kFP8>, grid, block, 0, st, (const uint16_t*)q,
-                       (const uint8_t*)kv_data, (const uint8_t*)nullptr, a);
-  } else if (s.kv_dtype == kNVFP4) {
-    hipLaunchKernelGGL(attend_mfma_kernel<kNVFP4>, grid, block, 0, st, (const uint16_t*)q,
-                       (const uint8_t*)kv_data, (const uint8_t*)kv_scales, a);
-  } else {
-    hipLaunchKernelGGL(attend_f32_kernel, grid, block, 0, st, q, (const float*)kv_data,
-                       (int)(s.q_dtype == kBF16), a);
+  return a;
+}
+
+template <bool SELECT>
+static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const AttendArgs& a,
+                              const void* q, const void* kv_data, const void* kv_scales,
+                              void* workspace, bool zero_counters, hipStream_t st) {
+  const int units = s.rows * s.G;
+  Partials part;
+  part.S = c.splits;
+  part.ml = static_cast<float*>(workspace);
+  part.o = part.ml + (size_t)units * c.splits * kHeadsPad * 2;
+  part.counters = reinterpret_cast<int32_t*>(part.o + (size_t)units * c.splits * kHeadsPad * kDim);
+  if (c.splits > 1 && zero_counters) {
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((units + 255) / 256), dim3(256), 0, st,
+                       part.counters, units);
   }
+  const dim3 grid(units * c.splits);
+  const size_t lds = SELECT ? sizeof(uint32_t) * (256 + s.MB) : 0;
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint8_t* kd = static_cast<const uint8_t*>(kv_data);
+  const uint8_t* ks = static_cast<const uint8_t*>(kv_scales);
+#define MSA_ATTEND_LAUNCH(KVT, NWV)                                                      \
+  hipLaunchKernelGGL((attend_mfma_kernel<KVT, NWV, SELECT>), grid, dim3(64 * NWV), lds, st, \
+                     qb, kd, ks, a, part)
+  if (s.kv_dtype == kFP8) {
+    switch (c.nw) {
+      case 1: MSA_ATTEND_LAUNCH(kFP8, 1); break;
+      case 2: MSA_ATTEND_LAUNCH(kFP8, 2); break;
+      case 4: MSA_ATTEND_LAUNCH(kFP8, 4); break;
+      default: MSA_ATTEND_LAUNCH(kFP8, 8); break;
+    }
+  } else {
+    switch (c.nw) {
+      case 1: MSA_ATTEND_LAUNCH(kNVFP4, 1); break;
+      case 2: MSA_ATTEND_LAUNCH(kNVFP4, 2); break;
+      case 4: MSA_ATTEND_LAUNCH(kNVFP4, 4); break;
+      default: MSA_ATTEND_LAUNCH(kNVFP4, 8); break;
+    }
+  }
+#undef MSA_ATTEND_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const void* q,
+                                    const void* kv_data, const void* kv_scales,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* q_pos, const int32_t* topk, void* out,
+                                    float* lse, void* workspace, hipStream_t st) {
+  const AttendArgs a = make_args(s, block_table, seq_lens, q_pos, topk, nullptr, nullptr, out, lse);
+  if (s.kv_dtype == kF32) {
+    hipLaunchKernelGGL(attend_f32_kernel, dim3(s.rows * s.G), dim3(64), 0, st, q,
+                       (const float*)kv_data, (int)(s.q_dtype == kBF16), a);
+    return hipGetLastError();
+  }
+  return launch_mfma<false>(s, c, a, q, kv_data, kv_scales, workspace, true, st);
+}
+
+hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_data,
+                                const void* kv_scales, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* q_pos,
+                                const int32_t* topk, void* out, float* lse, void* workspace,
+                                hipStream_t st) {
+  return launch_sparse_attend_cfg(s, attend_config(s), q, kv_data, kv_scales, block_table,
+                                  seq_lens, q_pos, topk, out, lse, workspace, st);
+}
+
+hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_data,
+                                const void* kv_scales, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* q_pos,
+                                const float* scores, int32_t* topk_out, void* out, float* lse,
+                                void* workspace, bool counters_zeroed, hipStream_t st) {
+  const AttendArgs a =
+      make_args(s, block_table, seq_lens, q_pos, nullptr, scores, topk_out, out, lse);
+  return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace,
+                           !counters_zeroed, st);
 }
 
 }  // namespace msa

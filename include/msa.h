@@ -24,13 +24,17 @@
  * validates its arguments on the host, synchronously, before anything is
  * launched, then enqueues its kernels on `stream` (a hipStream_t; NULL is the
  * default stream) and returns without waiting.  Device-side data (block-table
- * entries, sequence lengths, positions) are preconditions the library does
- * not read on the host:
- *   - 1 <= seq_lens[b] <= max_blocks * block_size;
- *   - block_table[b][j] in [0, num_phys_blocks) for j < ceil(seq_lens[b]/bs);
- *     entries past that are never read;
- *   - q_pos[r] in [0, seq_lens[r / rows_per_seq]) when q_pos is given.
- * A kernel never reads outside the blocks these preconditions name.
+ * entries, sequence lengths, positions) are not read on the host; the kernels
+ * bound every access by them instead:
+ *   - a row sees keys t <= min(q_pos[r], seq_lens[b] - 1, MB*BS - 1) (without
+ *     q_pos: t <= seq_lens[b] - 1 within the same reach);
+ *   - a row that sees no key (seq_len 0, or q_pos < 0) gets -inf scores, an
+ *     all -1 selection, a zero output and lse -inf;
+ *   - block_table[b][j] is read only for the blocks a row sees; an entry
+ *     outside [0, num_phys_blocks) is treated as an empty block (score -inf,
+ *     no attention contribution), never dereferenced.
+ * Sizes of the device buffers themselves are the caller's responsibility:
+ * every array must have the extent given below.
  *
  * Shapes (B = num_seqs, R = rows_per_seq, G = num_kv_groups, H = num_q_heads,
  * D = head_dim, Di = index_dim, BS = block_size, P = num_phys_blocks,
@@ -122,11 +126,15 @@ typedef struct msa_problem {
 msa_status msa_check_problem(const msa_problem* p, int32_t op);
 
 /*
- * Workspace bytes msa_sparse_attend (op 2) or msa_decode (op 3) needs for
- * problem p; 0 for the other ops.  The workspace is caller-owned device
- * memory, 256-byte aligned, that must be ZERO-FILLED before its first use;
- * every call leaves its counter region zero again, so it can be reused
- * without clearing.  Calls that share one workspace must not overlap.
+ * Workspace bytes a call needs for problem p (op as for msa_check_problem):
+ *   - msa_sparse_attend: room for the split-K partial states when a (row,
+ *     group) is split over several workgroups (0 when it is not);
+ *   - msa_decode: that plus B*R*G*MB floats for the pooled scores;
+ *   - the other calls: 0.
+ * Every region is rounded up to 256 bytes.  The workspace is caller-owned
+ * device memory, 256-byte aligned; no contents are carried between calls, so
+ * it needs no initialisation, but calls that share one must not overlap.  A
+ * call whose size is 0 accepts a NULL workspace.
  */
 msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
 
@@ -162,11 +170,14 @@ msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
  * Figure 1: every query head of a group attends exactly the group's
  * blocks).  For head h of group g and visible tokens t of the selected
  * blocks: out = sum_t softmax_t(sm_scale * k_scale * q.k_t) * v_scale * v_t,
- * with fp32 softmax state, split over the selected blocks and merged in the
- * same launch.  topk_idx entries must be ascending with -1 padding (the
- * msa_block_topk format) and must include the row's last visible block.
- * kv_scales is required for NVFP4 and ignored otherwise.  lse may be NULL.
- * workspace: msa_workspace_bytes(p, 2) bytes, zero-filled before first use.
+ * with fp32 softmax state, split over the selected blocks (across the waves
+ * of a workgroup and, for small batches, across workgroups whose partial
+ * states a second kernel merges).  topk_idx: the first
+ * min(top_k, last visible block + 1) entries of a row are read; an entry
+ * outside [0, last visible block] contributes nothing (msa_block_topk never
+ * writes one).  kv_scales is required for NVFP4 and ignored otherwise.  lse
+ * may be NULL.  workspace: msa_workspace_bytes(p, 2) bytes (may be NULL when
+ * that is 0).
  */
 msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv_data,
                              const void* kv_scales, const int32_t* block_table,
@@ -178,7 +189,7 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
  * The whole decode step: msa_index_scores -> msa_block_topk ->
  * msa_sparse_attend on `stream`.  topk_idx receives the selection;
  * block_scores (nullable) receives the pooled scores when given, otherwise
- * they live in the workspace.  workspace: msa_workspace_bytes(p, 3).
+ * they live in the workspace.  workspace: msa_workspace_bytes(p, 3) bytes.
  */
 msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
                       const void* ik_scales, const void* q, const void* kv_data,

@@ -144,8 +144,10 @@ def index_scores(p: Problem, index_q, ik_data, ik_scales, block_table, seq_lens,
 def token_scores(p: Problem, index_q, ik_data, ik_scales, block_table, seq_lens,
                  row: int, group: int, q_pos=None) -> np.ndarray:
     b = row // p.rows_per_seq
-    pos = int(q_pos[row]) if q_pos is not None else int(seq_lens[b]) - 1
-    out = np.empty(pos + 1, np.float32)
+    pos = int(seq_lens[b]) - 1
+    if q_pos is not None:
+        pos = min(pos, int(q_pos[row]))
+    out = np.empty(max(pos + 1, 0), np.float32)
     pc = p.c()
     rc = lib().msa_oracle_token_scores(ctypes.byref(pc), _ptr(index_q), _ptr(ik_data),
                                        _ptr(ik_scales), _ptr(block_table), _ptr(seq_lens),

@@ -124,13 +124,15 @@ static int check_problem(const msa_oracle_problem* p) {
   return 0;
 }
 
-/* Position of the query row: keys t <= pos are visible.  Decode rows see the
- * whole cache, including the token just inserted. */
+/* Last visible key of the query row: keys t <= pos and t < seq_len are
+ * visible.  Decode rows see the whole cache, including the token just
+ * inserted.  A negative result means the row sees no key at all. */
 static int64_t row_pos(const msa_oracle_problem* p, const int32_t* seq_lens,
                        const int32_t* q_pos, int64_t row) {
   int64_t b = row / p->rows_per_seq;
-  if (q_pos) return q_pos[row];
-  return (int64_t)seq_lens[b] - 1;
+  int64_t last = (int64_t)seq_lens[b] - 1;
+  if (q_pos && (int64_t)q_pos[row] < last) return q_pos[row];
+  return last;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -309,9 +311,13 @@ static void topk_unit(void* c_, int64_t unit) {
   const msa_oracle_problem* p = c->p;
   int64_t row = unit / p->num_groups;
   int64_t pos = row_pos(p, c->seq_lens, c->q_pos, row);
-  int32_t recent = (int32_t)(pos / p->block_size);
   const float* s = c->scores + (size_t)unit * (size_t)p->max_blocks;
   int32_t* out = c->topk + (size_t)unit * (size_t)p->top_k;
+  if (pos < 0) { /* no visible key: nothing to select */
+    for (int32_t i = 0; i < p->top_k; ++i) out[i] = -1;
+    return;
+  }
+  int32_t recent = (int32_t)(pos / p->block_size);
   int32_t n_sel = 0;
   int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)p->top_k);
   if (recent + 1 <= p->top_k) {

@@ -83,14 +83,21 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
 
 
 def test_workspace_sizes():
-    p = good(num_seqs=8, max_blocks_per_seq=2048)
+    p = good(num_seqs=8, max_blocks_per_seq=2049)
+    assert msa.workspace_bytes(p, msa.OP_INDEX) == 0
+    assert msa.workspace_bytes(p, msa.OP_TOPK) == 0
     a = msa.workspace_bytes(p, msa.OP_ATTEND)
     d = msa.workspace_bytes(p, msa.OP_DECODE)
-    rows_g = 8 * 4
-    assert a >= rows_g * 4 + rows_g * 16 * 16 * 130 * 4
-    assert d >= a + rows_g * 2048 * 4
-    assert msa.workspace_bytes(p, msa.OP_INDEX) == 0
-    assert a % 256 == 0 and d % 256 == 0
+    scores = 8 * 4 * 2049 * 4
+    assert d % 256 == 0 and a % 256 == 0
+    assert d - a >= scores and d - a - scores < 256
+    # split partials: 16 heads x (128 outputs + max + denominator) per split,
+    # then one arrival counter per (row, group)
+    units = 8 * 4
+    S = a // (units * 16 * 130 * 4)
+    assert S >= 2 and a == -(-(units * S * 16 * 130 * 4 + units * 4) // 256) * 256
+    big = good(num_seqs=512, max_blocks_per_seq=16)
+    assert msa.workspace_bytes(big, msa.OP_ATTEND) == 0  # enough (row, group)s: no split
 
 
 def test_status_strings():

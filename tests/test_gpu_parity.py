@@ -115,16 +115,24 @@ def test_query_positions_multi_row():
     _run_and_check(w, fused=True, name="multi-row")
 
 
-def test_block_topk_bit_exact_with_ties():
+@pytest.mark.parametrize("MB", [700, 17000])
+def test_block_topk_bit_exact_with_ties(MB):
     """Selection kernel alone, on oracle-independent scores with many exact
-    ties: identical to the oracle's selection."""
+    ties: identical to the oracle's selection.  MB = 17000 takes the
+    workgroup-wide path used for rows too long for LDS."""
     rng = np.random.default_rng(5)
-    B, G, MB = 9, 4, 700
-    lens = rng.integers(1, MB * 128 + 1, B).astype(np.int32)
-    lens[0], lens[1], lens[2] = MB * 128, 1, 17 * 128
+    B, G = 9, 4
+    lens = rng.integers(1, min(MB, 3000) * 128 + 1, B).astype(np.int32)
+    lens[0], lens[1], lens[2] = min(MB, 3000) * 128, 1, 17 * 128
     scores = rng.integers(-6, 7, (B, G, MB)).astype(np.float32) * 0.25
     scores[3] = -0.0  # signed zeros tie with +0
     scores[3, :, ::3] = 0.0
+    # every 8th block high: the high blocks sit in few lanes of the wave-level
+    # selection, more than 64 candidates clear its first threshold, and it
+    # takes its radix path
+    scores[4] = rng.standard_normal((G, MB)).astype(np.float32) * 1e-3
+    scores[4, :, ::8] += 1.0 + rng.random((G, (MB + 7) // 8)).astype(np.float32)
+    lens[4] = min(MB, 3000) * 128
     for K in (1, 5, 16, 32):
         op = oracle.Problem(num_seqs=B, num_q_heads=G, num_groups=G, block_size=128, top_k=K,
                             max_blocks=MB, num_phys_blocks=1)
@@ -173,11 +181,47 @@ def test_empty_batch_and_errors():
     i32 = torch.zeros(64, dtype=torch.int32, device="cuda")
     f32 = torch.zeros(64, dtype=torch.float32, device="cuda")
     msa.index_scores(p, z, z, None, i32, i32, None, f32)  # nothing to do
-    p1 = msa.Problem(num_seqs=1, max_blocks_per_seq=4, num_phys_blocks=4)
-    small = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    # no block_scores and a workspace one float short: rejected before launch
+    p1 = msa.Problem(num_seqs=4, max_blocks_per_seq=64, num_phys_blocks=4)
+    need = msa.workspace_bytes(p1, msa.OP_DECODE)
+    small = torch.zeros(need, dtype=torch.uint8, device="cuda")
     with pytest.raises(msa.MsaError) as e:
-        msa.sparse_attend(p1, z, z, None, i32, i32, None, i32, f32, None, small)
+        msa.decode(p1, z, z, None, z, z, None, i32, i32, None, None, i32, f32, None,
+                   small[: need - 4])
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("kv", [synth.FP8, synth.F32])
+def test_rows_that_see_no_key(kv):
+    """seq_len 0 and negative positions: -inf scores, empty selection, zero
+    output, lse -inf -- the oracle's reading of an empty row."""
+    lens = [0, 700, 300]
+    qp = np.array([5, 0, -1, 699, 299, -7], np.int32)
+    w = synth.make("empty", seed=3, seq_lens=lens, rows_per_seq=2, q_pos=qp, num_q_heads=8,
+                   num_groups=4, q_dtype=synth.F32 if kv == synth.F32 else synth.BF16,
+                   kv_dtype=kv, top_k=4)
+    s_ref, k_ref, o_ref, l_ref = _oracle_all(w)
+    dw = parity.DeviceWorkload(w)
+    say(f"[parity] empty rows {synth.DTYPE_NAMES[kv]}")
+    dw.decode()
+    torch.cuda.synchronize()
+    k = dw.topk.cpu().numpy()
+    assert np.array_equal(k, k_ref)
+    assert np.all(k_ref[[0, 1, 5]] == -1)
+    s = dw.scores.cpu().numpy()
+    assert np.all(s[[0, 1, 5]] == -np.inf)
+    o = dw.out.float().cpu().numpy()
+    assert np.all(o[[0, 1, 5]] == 0.0) and np.all(o_ref[[0, 1, 5]] == 0.0)
+    assert np.all(dw.lse.cpu().numpy()[[0, 1, 5]] == -np.inf)
+    parity.check_attention(w, o, o_ref)
+
+
+def test_decode_long_block_table_unfused_path():
+    """A block-table stride past the fused selection's LDS limit makes
+    msa_decode take the three-kernel path; results follow the same rules."""
+    w = synth.make("wide", seed=91, seq_lens=[5000, 20000, 130], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, max_blocks=9000, plant_per_seq=3)
+    _run_and_check(w, fused=True, name="wide-table")
 
 
 # ---------------------------------------------------------------------------
