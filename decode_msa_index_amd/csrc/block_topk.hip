@@ -158,11 +158,16 @@ __global__ __launch_bounds__(64) void block_topk_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
     int K) {
-  extern __shared__ uint32_t lds[];  // [256] histogram, then [MB] keys
+  extern __shared__ uint32_t lds[];  // [256] scratch, then [MB] keys
   const int u = blockIdx.x, row = u / G, b = row / R;
+  const float* s = scores + (size_t)u * MB;
+  // the first round of score loads does not wait for the row length
+  load_keys(s, min(MB, 32 * 64), lds + 256, 64);
   const int pos = row_last_key(lens, qpos, row, b, MB);
   const int rb = pos < 0 ? -1 : pos / kBlock;
-  wave_select<64>(scores + (size_t)u * MB, rb, K, lds + 256, lds, topk + (size_t)u * K);
+  if (rb > 32 * 64) load_keys(s + 32 * 64, rb - 32 * 64, lds + 256 + 32 * 64, 64);
+  wave_lds_sync();
+  wave_select_keys(lds + 256, rb, K, lds, topk + (size_t)u * K);
 }
 
 hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,

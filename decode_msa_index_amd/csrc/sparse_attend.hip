@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
   __shared__ float red_ml[NW > 1 ? NW / 2 : 1][2][16];
   __shared__ int32_t sel[32];
   __shared__ int is_last;
-  extern __shared__ uint32_t sel_lds[];  // SELECT: [256] histogram, then [MB] keys
+  extern __shared__ uint32_t sel_lds[];  // SELECT: [256] scratch, [MB] keys, [MB] table row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int u = blockIdx.x / part.S, split = blockIdx.x % part.S;
   const int row = u / a.G, g = u % a.G, b = row / a.R;
@@ -181,7 +181,33 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
   const int n = lane & 15, qd = lane >> 4;
 
   if constexpr (SELECT) {
-    if (wave == 0) wave_select<64>(a.scores + (size_t)u * a.MB, rb, a.K, sel_lds + 256, sel_lds, sel);
+    // every thread loads a share of the row's scores (as order keys) and of
+    // its block-table entries, in one round that does not wait for the row
+    // length; wave 0 then selects from LDS
+    uint32_t* keys = sel_lds + 256;
+    int32_t* btl = reinterpret_cast<int32_t*>(keys + a.MB);
+    const float* srow = a.scores + (size_t)u * a.MB;
+    const int32_t* brow = a.bt + (size_t)b * a.MB;
+    for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
+      float v[8];
+      int32_t e[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int jj = min(base + r * 64 * NW + (int)threadIdx.x, a.MB - 1);
+        v[r] = srow[jj];
+        e[r] = brow[jj];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int jj = base + r * 64 * NW + (int)threadIdx.x;
+        if (jj < a.MB) {
+          keys[jj] = order_key(v[r]);
+          btl[jj] = e[r];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) wave_select_keys(keys, rb, a.K, sel_lds, sel);
     __syncthreads();
     if (split == 0 && a.topk_out && (int)threadIdx.x < a.K)
       a.topk_out[(size_t)u * a.K + threadIdx.x] = sel[threadIdx.x];
@@ -210,7 +236,9 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
   {
     const int sidx = e0 + wave + NW * lane;
     if (lane < 32 && sidx < e1) my_j = SELECT ? sel[sidx] : a.topk[(size_t)u * a.K + sidx];
-    if (my_j >= 0 && my_j <= rb) my_pb = a.bt[(size_t)b * a.MB + my_j];
+    if (my_j >= 0 && my_j <= rb)
+      my_pb = SELECT ? reinterpret_cast<const int32_t*>(sel_lds + 256 + a.MB)[my_j]
+                     : a.bt[(size_t)b * a.MB + my_j];
   }
   for (int it = 0; e0 + wave + NW * it < e1; ++it) {
     const int j = __shfl(my_j, it, 64);
@@ -583,7 +611,7 @@ bool select_fusable(const Shape& s) {
   const int nw = attend_config(s).nw;
   const size_t stat = (size_t)(nw > 1 ? nw / 2 : 1) * (32 * 64 + 2 * 16) * sizeof(float) +
                       32 * sizeof(int32_t) + 64;
-  const size_t dyn = sizeof(uint32_t) * (256 + (size_t)s.MB);
+  const size_t dyn = sizeof(uint32_t) * (256 + 2 * (size_t)s.MB);
   return stat + dyn <= 65536;
 }
 
@@ -627,7 +655,7 @@ static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const Atten
                        part.counters, units);
   }
   const dim3 grid(units * c.splits);
-  const size_t lds = SELECT ? sizeof(uint32_t) * (256 + s.MB) : 0;
+  const size_t lds = SELECT ? sizeof(uint32_t) * (256 + 2 * (size_t)s.MB) : 0;
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   const uint8_t* kd = static_cast<const uint8_t*>(kv_data);
   const uint8_t* ks = static_cast<const uint8_t*>(kv_scales);
