@@ -21,6 +21,7 @@ constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2, kNVFP4 = 3;
 
 // Query heads per group are padded to 16 (one MFMA tile).
 constexpr int kHeadsPad = 16;
+constexpr int kMaxSplits = 8;  // split-K workgroups per (row, group): at most ceil(32 / 4)
 
 // zero: optional int array of n_zero entries the index kernel clears in
 // passing (the attention kernel's arrival counters).

@@ -40,8 +40,11 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Set bits of mask in the lanes below the calling lane (lane = its lane id).
 __device__ __forceinline__ int popc_below(uint64_t mask, int lane) {
-  return __popcll(mask & ((1ull << lane) - 1ull));
+  (void)lane;
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // (key, index) pair order: larger key first, then lower index.
@@ -264,6 +267,160 @@ __device__ void wave_select_keys(const uint32_t* keys, int rb, int K, uint32_t* 
     }
   }
   if (lane == 0) out[K - 1] = rb;
+  wave_lds_sync();
+}
+
+// Composite candidate: order key in the high word, complemented block index
+// in the low word, so that a larger composite is a better candidate (higher
+// score, then lower block).  Every candidate's composite is distinct.
+__device__ __forceinline__ uint64_t pack_cand(uint32_t key, int idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)idx);
+}
+__device__ __forceinline__ int cand_index(uint64_t c) { return (int)~(uint32_t)c; }
+constexpr uint64_t kNoCand = 0x80000000ull;  // pack_cand(0, INT_MAX): below any real candidate
+
+// Number of entries of v[0..n) (LDS, read by all lanes at the same address)
+// greater than c.  n is rounded up to a multiple of 8: entries past n must
+// hold values that are not greater than any c asked about.
+__device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t c) {
+  int acc[4] = {0, 0, 0, 0};
+  for (int m0 = 0; m0 < n; m0 += 8) {
+    uint64_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = v[m0 + i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i & 3] += x[i] > c ? 1 : 0;
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Selection by a whole workgroup of NW waves, for a kernel whose threads
+// have just loaded the row's keys.  keys[0..rb) in LDS hold the order keys
+// of blocks 0..rb-1; each thread passes its best candidate among the blocks
+// (< rb) it loaded, as a composite (kNoCand if none).
+//
+// The candidates fall into 64 groups: group l holds the blocks loaded by the
+// threads at lane position l of every wave.  T0 is the (k-1)-th best group
+// maximum, found by ranking the 64 maxima by counting.  At least k-1
+// candidates are >= T0, so the k-1 best all are: each wave re-reads its
+// threads' keys and compacts its survivors (ballot + mbcnt) into a region of
+// its own.  The survivors, usually about k, are gathered into lanes, ranked
+// by counting (survivor i is chosen when fewer than k-1 survivors beat it)
+// and placed by counting smaller block ids, so nothing is sorted.  Every
+// wave computes T0 and the result itself, which saves barriers and
+// broadcasts.  More than 64 survivors (strongly structured scores) fall back
+// to the radix select run by wave 0 over the LDS keys.
+//
+// On return out_w (this wave's own 32-entry row) holds the K selected block
+// ids, ascending, -1 padded, and all LDS writes the threads made before the
+// call are visible to the whole workgroup.  Called by every thread with
+// workgroup-uniform rb and K <= 32.
+template <int NW>
+struct GroupSelectLds {
+  uint64_t best[64 * NW];    // each thread's best candidate
+  uint64_t scratch[NW][64];  // per wave: group maxima, then the gathered survivors
+  uint64_t surv[NW][64];     // per wave: the survivors it found
+  uint32_t surv_n[NW];
+  int32_t radix_out[32];
+};
+
+template <int NW>
+__device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
+                             GroupSelectLds<NW>& g, uint32_t* hist, int32_t* out_w) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int need = K - 1;
+  if (rb < 0 || rb + 1 <= K || need == 0) {  // nothing to choose
+    __syncthreads();
+    if (lane < K) out_w[lane] = rb < 0 ? -1 : (rb + 1 <= K ? (lane <= rb ? lane : -1) : rb);
+    wave_lds_sync();
+    return;
+  }
+  const int ncand = rb;
+  g.best[threadIdx.x] = mine;
+  __syncthreads();
+  // ---- T0: the need-th best of the 64 group maxima ----
+  uint64_t gm = g.best[lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) gm = max(gm, g.best[w * 64 + lane]);
+  uint64_t* buf = g.scratch[wave];
+  buf[lane] = gm;
+  wave_lds_sync();
+  // groups l < min(64, ncand) hold block l, so ranks 0..need-1 belong to
+  // exactly one real group each (empty groups tie at kNoCand below them)
+  const uint64_t at = __ballot(count_greater(buf, 64, gm) == need - 1);
+  const int src = (int)__builtin_ctzll(at);
+  const uint32_t t_lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gm, src);
+  const uint32_t t_hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(gm >> 32), src);
+  const uint64_t t0 = ((uint64_t)t_hi << 32) | t_lo;
+
+  // ---- survivors (>= T0): each wave compacts its own into surv[wave] ----
+  constexpr int NT = 64 * NW;
+  uint32_t n_w = 0;
+  for (int base = 0; base < ncand; base += 8 * NT) {
+    uint32_t kk[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) kk[r] = keys[min(base + r * NT + (int)threadIdx.x, ncand - 1)];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int jj = base + r * NT + (int)threadIdx.x;
+      const uint64_t cc = pack_cand(kk[r], jj);
+      const bool s = jj < ncand && cc >= t0;
+      const uint64_t m = __ballot(s);
+      if (s) {
+        const uint32_t slot = n_w + (uint32_t)popc_below(m, lane);
+        if (slot < 64) g.surv[wave][slot] = cc;
+      }
+      n_w += (uint32_t)__popcll(m);
+    }
+  }
+  if (lane == 0) g.surv_n[wave] = n_w;
+  __syncthreads();
+  uint32_t pre[NW], total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    pre[w] = total;
+    total += g.surv_n[w];
+  }
+  if (total > 64) {
+    if (wave == 0) select_radix(keys, ncand, need, hist, g.radix_out);
+    __syncthreads();
+    if (lane < need) out_w[lane] = g.radix_out[lane];
+  } else {
+    // gather: lane l takes survivor l of the concatenated regions
+    uint64_t ci = kNoCand;
+    if ((uint32_t)lane < total) {
+      int w = 0;
+      uint32_t off = (uint32_t)lane;
+#pragma unroll
+      for (int v = 1; v < NW; ++v) {
+        if ((uint32_t)lane >= pre[v]) {
+          w = v;
+          off = (uint32_t)lane - pre[v];
+        }
+      }
+      ci = g.surv[w][off];
+    }
+    buf[lane] = ci;
+    wave_lds_sync();
+    const int rank = count_greater(buf, (int)total, ci);
+    const bool chosen = (uint32_t)lane < total && rank < need;
+    const uint64_t cm = __ballot(chosen);
+    const int j = cand_index(ci);
+    // the chosen ids, unordered, then each one's place = smaller chosen ids
+    if (chosen) out_w[popc_below(cm, lane)] = j;
+    wave_lds_sync();
+    int acc[4] = {0, 0, 0, 0};
+    for (int m0 = 0; m0 < need; m0 += 8) {
+      int x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = out_w[m0 + i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i & 3] += (m0 + i < need && x[i] < j) ? 1 : 0;
+    }
+    wave_lds_sync();
+    if (chosen) out_w[(acc[0] + acc[1]) + (acc[2] + acc[3])] = j;
+  }
+  if (lane == 0) out_w[K - 1] = rb;
   wave_lds_sync();
 }
 

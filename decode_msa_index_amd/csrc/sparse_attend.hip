@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
     const uint8_t* __restrict__ kvs, AttendArgs a, Partials part) {
   __shared__ float red_o[NW > 1 ? NW / 2 : 1][32][64];
   __shared__ float red_ml[NW > 1 ? NW / 2 : 1][2][16];
-  __shared__ int32_t sel[32];
+  __shared__ int32_t sel_w[SELECT ? NW : 1][32];  // SELECT: each wave's copy of the selection
   __shared__ int is_last;
   extern __shared__ uint32_t sel_lds[];  // SELECT: [256] scratch, [MB] keys, [MB] table row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,14 +180,29 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
   const int e0 = split * per_wg, e1 = min(count, e0 + per_wg);
   const int n = lane & 15, qd = lane >> 4;
 
+  // Q^T operand: head n of the group, dims qd*32 + 8c + e (zero past hpg);
+  // loaded first so that its latency overlaps the selection
+  bf16x8 qop[4];
+  if (n < a.hpg) {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        q + ((size_t)row * a.H + (size_t)g * a.hpg + n) * kDim + qd * 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+
   if constexpr (SELECT) {
     // every thread loads a share of the row's scores (as order keys) and of
     // its block-table entries, in one round that does not wait for the row
-    // length; wave 0 then selects from LDS
+    // length, and keeps its best candidate; the workgroup then selects
+    __shared__ GroupSelectLds<NW> gsl;
     uint32_t* keys = sel_lds + 256;
     int32_t* btl = reinterpret_cast<int32_t*>(keys + a.MB);
     const float* srow = a.scores + (size_t)u * a.MB;
     const int32_t* brow = a.bt + (size_t)b * a.MB;
+    uint64_t best = kNoCand;
     for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
       float v[8];
       int32_t e[8];
@@ -201,28 +216,16 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
       for (int r = 0; r < 8; ++r) {
         const int jj = base + r * 64 * NW + (int)threadIdx.x;
         if (jj < a.MB) {
-          keys[jj] = order_key(v[r]);
+          const uint32_t k = order_key(v[r]);
+          keys[jj] = k;
           btl[jj] = e[r];
+          if (jj < rb) best = max(best, pack_cand(k, jj));
         }
       }
     }
-    __syncthreads();
-    if (wave == 0) wave_select_keys(keys, rb, a.K, sel_lds, sel);
-    __syncthreads();
-    if (split == 0 && a.topk_out && (int)threadIdx.x < a.K)
-      a.topk_out[(size_t)u * a.K + threadIdx.x] = sel[threadIdx.x];
-  }
-
-  // Q^T operand: head n of the group, dims qd*32 + 8c + e (zero past hpg)
-  bf16x8 qop[4];
-  if (n < a.hpg) {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        q + ((size_t)row * a.H + (size_t)g * a.hpg + n) * kDim + qd * 32);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    group_select<NW>(keys, rb, a.K, best, gsl, sel_lds, sel_w[wave]);
+    if (split == 0 && wave == 0 && a.topk_out && lane < a.K)
+      a.topk_out[(size_t)u * a.K + lane] = sel_w[0][lane];
   }
 
   float M = -INFINITY, Lr = 0.0f;
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
   int my_j = -1, my_pb = -1;
   {
     const int sidx = e0 + wave + NW * lane;
-    if (lane < 32 && sidx < e1) my_j = SELECT ? sel[sidx] : a.topk[(size_t)u * a.K + sidx];
+    if (lane < 32 && sidx < e1) my_j = SELECT ? sel_w[wave][sidx] : a.topk[(size_t)u * a.K + sidx];
     if (my_j >= 0 && my_j <= rb)
       my_pb = SELECT ? reinterpret_cast<const int32_t*>(sel_lds + 256 + a.MB)[my_j]
                      : a.bt[(size_t)b * a.MB + my_j];
@@ -450,21 +453,37 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
   }
   __syncthreads();
   if (!is_last) return;
-  // merge: thread t takes head t/16 and dims 8*(t%16) .. +8 (looping when NW < 4)
+  // merge: thread t takes head t/16 and dims 8*(t%16) .. +8 (looping when
+  // NW < 4); every partial is loaded before any is used, so the coherent
+  // loads overlap
   for (int t = threadIdx.x; t < kHeadsPad * 16; t += 64 * NW) {
     const int h = t >> 4, d0 = (t & 15) * 8;
     if (h >= a.hpg) continue;
     const float* ml = part.ml + (size_t)u * part.S * (kHeadsPad * 2) + 2 * h;
     const float* po = part.o + (size_t)u * part.S * (kHeadsPad * kDim) + h * kDim + d0;
-    float Mx = -INFINITY;
-    for (int sp = 0; sp < part.S; ++sp) Mx = fmaxf(Mx, coherent_load(ml + (size_t)sp * (kHeadsPad * 2)));
-    float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int sp = 0; sp < part.S; ++sp) {
-      const float f = rescale(coherent_load(ml + (size_t)sp * (kHeadsPad * 2)), Mx);
-      L += f * coherent_load(ml + (size_t)sp * (kHeadsPad * 2) + 1);
-      const float* src = po + (size_t)sp * (kHeadsPad * kDim);
+    float pm[kMaxSplits], pl[kMaxSplits], pv[kMaxSplits][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] += f * coherent_load(src + k);
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      if (sp < part.S) {
+        pm[sp] = coherent_load(ml + (size_t)sp * (kHeadsPad * 2));
+        pl[sp] = coherent_load(ml + (size_t)sp * (kHeadsPad * 2) + 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pv[sp][k] = coherent_load(po + (size_t)sp * (kHeadsPad * kDim) + k);
+      }
+    }
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      if (sp < part.S) Mx = fmaxf(Mx, pm[sp]);
+    float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      if (sp < part.S) {
+        const float f = rescale(pm[sp], Mx);
+        L += f * pl[sp];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] += f * pv[sp][k];
+      }
     }
     const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
 #pragma unroll
@@ -610,7 +629,7 @@ bool select_fusable(const Shape& s) {
   if (s.kv_dtype == kF32) return false;
   const int nw = attend_config(s).nw;
   const size_t stat = (size_t)(nw > 1 ? nw / 2 : 1) * (32 * 64 + 2 * 16) * sizeof(float) +
-                      32 * sizeof(int32_t) + 64;
+                      (size_t)nw * 32 * sizeof(int32_t) + sizeof(GroupSelectLds<8>) + 64;
   const size_t dyn = sizeof(uint32_t) * (256 + 2 * (size_t)s.MB);
   return stat + dyn <= 65536;
 }
@@ -645,6 +664,7 @@ static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const Atten
                               const void* q, const void* kv_data, const void* kv_scales,
                               void* workspace, bool zero_counters, hipStream_t st) {
   const int units = s.rows * s.G;
+  if (c.splits < 1 || c.splits > kMaxSplits) return hipErrorInvalidValue;
   Partials part;
   part.S = c.splits;
   part.ml = static_cast<float*>(workspace);
