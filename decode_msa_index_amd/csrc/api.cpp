@@ -55,18 +55,21 @@ msa::Shape shape_of(const msa_problem* p) {
 }
 
 struct WsLayout {
-  size_t scores, attend, total;
+  size_t header, scores, attend, total;
 };
 
 // Device scratch: msa_sparse_attend needs room for the split-K partial
 // states when it splits a (row, group) over several workgroups; msa_decode
-// needs that plus the pooled scores when the caller does not take them.
+// needs a 256-byte header (the fused kernel's task ticket and error flag),
+// the pooled scores (as order keys for the fused kernel) and that.
 WsLayout ws_layout(const msa_problem* p, int op) {
   WsLayout w{};
   if (op != kOpAttend && op != kOpDecode) return w;
   const msa::Shape s = shape_of(p);
   size_t off = 0;
   if (op == kOpDecode) {
+    w.header = off;
+    off += kAlign;
     w.scores = off;
     off += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
   }
@@ -289,9 +292,10 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
   if (p->num_seqs == 0) return MSA_OK;
   const msa::Shape s = shape_of(p);
   char* ws = static_cast<char*>(workspace);
-  float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
   hipStream_t hs = (hipStream_t)stream;
-  void* aws = ws ? ws + w.attend : nullptr;
+  void* aws = ws + w.attend;
+  float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
+  float* ws_scores = block_scores ? nullptr : scores;  // cleared again after use
   if (msa::select_fusable(s)) {
     // two launches: the index scan (which also clears the attention kernel's
     // arrival counters), then selection + attention in one kernel
@@ -305,9 +309,11 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
                     "index scores launch");
     if (st != MSA_OK) return st;
     return hip_status(msa::launch_select_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
-                                                q_pos, scores, topk_idx, out, lse, aws, true, hs),
+                                                q_pos, scores, topk_idx, out, lse, aws, true,
+                                                ws_scores, hs),
                       "select + attend launch");
   }
+  // three kernels; pooled scores kept in the workspace are cleared again
   st = hip_status(msa::launch_index_scores(s, index_q, ik_data, ik_scales, block_table,
                                            seq_lens, q_pos, scores, hs),
                   "index scores launch");
@@ -315,9 +321,12 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
   st = hip_status(msa::launch_block_topk(s, scores, seq_lens, q_pos, topk_idx, hs),
                   "block top-k launch");
   if (st != MSA_OK) return st;
-  return hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table,
-                                              seq_lens, q_pos, topk_idx, out, lse, aws, hs),
-                    "sparse attend launch");
+  st = hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
+                                            q_pos, topk_idx, out, lse, aws, hs),
+                  "sparse attend launch");
+  if (st != MSA_OK || block_scores) return st;
+  return hip_status(msa::launch_zero_fill(ws + w.scores, w.attend - w.scores, hs),
+                    "workspace clear launch");
 }
 
 const char* msa_status_string(msa_status s) {

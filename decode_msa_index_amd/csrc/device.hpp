@@ -8,6 +8,12 @@
 
 namespace msa {
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: loops and addresses derived from it stay scalar.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
@@ -81,7 +87,75 @@ __device__ __forceinline__ int row_last_key(const int32_t* lens, const int32_t* 
   return qpos ? min(qpos[row], last) : last;
 }
 
+// ---- 8-element conversions for MFMA operands -------------------------------
+
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+
+__device__ __forceinline__ bf16x8 cat(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x8 cat(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 8 e4m3 bytes (w0: elements 0..3, w1: 4..7) -> bf16x8 / f16x8, exact.
+__device__ __forceinline__ bf16x8 fp8x8_bf16(uint32_t w0, uint32_t w1) {
+  return cat(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+             fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+}
+__device__ __forceinline__ f16x8 fp8x8_f16(uint32_t w0, uint32_t w1) {
+  return cat(fp8x2_to_f16x2<false>(w0), fp8x2_to_f16x2<true>(w0),
+             fp8x2_to_f16x2<false>(w1), fp8x2_to_f16x2<true>(w1));
+}
+
+// upper halves of two f32 -> one bf16x2 word (exact when the low halves are 0)
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// 8 E2M1 values (nibbles of w, element 2b in the low nibble of byte b) times
+// one e4m3 block scale -> bf16x8.  The product of an e4m3 and an E2M1 value
+// has at most 6 significant bits and lies in [2^-10, 2688]: exact in fp32 and
+// in bf16.
+__device__ __forceinline__ bf16x8 nvfp4x8_bf16(uint32_t w, float scale) {
+  const f32x2 a = fp4x2_to_f32x2<0>(w), b = fp4x2_to_f32x2<1>(w);
+  const f32x2 c = fp4x2_to_f32x2<2>(w), d = fp4x2_to_f32x2<3>(w);
+  uint4 r;
+  r.x = pack_hi16(a[0] * scale, a[1] * scale);
+  r.y = pack_hi16(b[0] * scale, b[1] * scale);
+  r.z = pack_hi16(c[0] * scale, c[1] * scale);
+  r.w = pack_hi16(d[0] * scale, d[1] * scale);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 8 E2M1 values, element e scaled by e4m3 byte e of (s0, s1) -> f16x8 (exact:
+// same bound as above, inside f16's normal range).
+__device__ __forceinline__ f16x8 nvfp4x8_f16(uint32_t w, uint32_t s0, uint32_t s1) {
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return cat(v0 * fp8x2_to_f16x2<false>(s0), v1 * fp8x2_to_f16x2<true>(s0),
+             v2 * fp8x2_to_f16x2<false>(s1), v3 * fp8x2_to_f16x2<true>(s1));
+}
+
 // ---- lane exchanges -------------------------------------------------------
+
+// Keeps the compiler from moving LDS accesses across this point; the
+// hardware already executes a wave's LDS operations in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Set bits of mask in the lanes below the calling lane (lane = its lane id).
+
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -95,6 +169,40 @@ constexpr int kRowRor4 = 0x124;  // rotate right by 4 within 16 lanes
 constexpr int kRowRor8 = 0x128;
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Value of lane (lane ^ J).  J = 1, 2, 8 are single DPP moves (quad
+// permutes, rotate a 16-lane row by 8); J = 4 takes the lane 4 up or down
+// with two DPP row shifts; 16 and 32 use the CDNA4 row-swap instructions
+// (v_permlane16_swap / v_permlane32_swap with both operands = v: the first
+// result holds the even rows / lower half, the second the odd rows / upper
+// half).
+template <int J>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+}
+
+template <int J>
+__device__ __forceinline__ float lane_xor_f(float v) {
+  return __builtin_bit_cast(float, lane_xor<J>(__builtin_bit_cast(int, v)));
+}
+
 
 // ---- MFMA -----------------------------------------------------------------
 // 16x16x32: A lane l holds A[l%16][8*(l/16)+e], B lane l holds B[8*(l/16)+e][l%16],

@@ -19,6 +19,7 @@
 // v_dot2c_f32_bf16: exact products, fp32 accumulation.  The positive score
 // scale commutes with the max, so it is applied once per block.
 #include "device.hpp"
+#include "index_block.hpp"
 #include "launch.hpp"
 
 namespace msa {
@@ -35,198 +36,34 @@ struct ZeroArgs {
 };
 
 // -------------------------------------------------------------------------
-// FP8 e4m3 index keys, bf16 index queries.
-// Eight lanes share a token: lane l owns dims [16*(l%8), 16*(l%8)+16) of
-// token l/8, so each 16-byte load instruction of the wave covers 8 tokens =
-// 1 KB contiguously; the 16 KB block takes 16 such loads, all issued up front
-// with the nontemporal hint (each byte is read exactly once).  A token's dot
-// product is reduced over its 8 lanes in 3 DPP steps.
+// FP8 e4m3 / NVFP4 index keys, bf16 index queries: one wave per block, on
+// MFMA (the layouts and arithmetic are those of index_block.hpp).
 // -------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256) void index_fp8_kernel(
-    const uint16_t* __restrict__ iq, const uint8_t* __restrict__ ik,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ qpos, float* __restrict__ scores, int R, int MB, int P,
-    float out_scale, ZeroArgs za) {
+template <int G, int IK>
+__global__ __launch_bounds__(256) void index_mfma_kernel(IndexArgs x, ZeroArgs za) {
+  __shared__ uint4 stage[4][kStageBytes / 16];  // one staging area per wave
   za.run();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.y, b = row / R;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int row = blockIdx.y, b = row / x.R;
   const int j = blockIdx.x * 4 + wave;
-  if (j >= MB) return;
-  const int entry = bt[(size_t)b * MB + j];  // issued alongside the length loads
-  const int pos = row_last_key(lens, qpos, row, b, MB);
-  float* out = scores + (size_t)row * G * MB + j;
+  if (j >= x.MB) return;
+  const int entry = x.bt[(size_t)b * x.MB + j];  // issued alongside the length loads
+  const int pos = row_last_key(x.lens, x.qpos, row, b, x.MB);
   const int pb = j * kBlock > pos ? -1 : entry;
-  if (pb < 0 || pb >= P) {  // past the row's last key (or an invalid table entry)
-    if (lane < G) out[(size_t)lane * MB] = -INFINITY;
+  if (pb < 0 || pb >= x.P) {  // past the row's last key (or an invalid table entry)
+    put_block_scores<G, false>(x, row, j, lane, -INFINITY);
     return;
   }
-  const uint4* src = reinterpret_cast<const uint4*>(ik + (size_t)pb * (kBlock * kDim)) + lane;
-  uint4 raw[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) raw[i] = load_stream(src + i * 64);
-  // index query: dims [16c, 16c+16) of every group as bf16 pairs
-  const int c = lane & 7;
-  const uint4* qsrc = reinterpret_cast<const uint4*>(iq + (size_t)row * G * kDim) + c * 2;
-  uint32_t qw[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 v = qsrc[g * 16 + i];
-      qw[g][4 * i] = v.x;
-      qw[g][4 * i + 1] = v.y;
-      qw[g][4 * i + 2] = v.z;
-      qw[g][4 * i + 3] = v.w;
-    }
-  }
-  float m[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) m[g] = -INFINITY;
-  const int tok0 = j * kBlock + (lane >> 3);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t kw[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const bf16x2 lo = fp8x2_to_bf16x2<false>(kw[w]);
-      const bf16x2 hi = fp8x2_to_bf16x2<true>(kw[w]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        acc[g] = dot2_bf16(lo, as_bf16x2(qw[g][2 * w]), acc[g]);
-        acc[g] = dot2_bf16(hi, as_bf16x2(qw[g][2 * w + 1]), acc[g]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc[g] += dpp<kQuadXor1>(acc[g]);
-      acc[g] += dpp<kQuadXor2>(acc[g]);
-      acc[g] += dpp<kHalfMirror>(acc[g]);
-    }
-    const bool valid = tok0 + i * 8 <= pos;
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = valid ? fmaxf(m[g], acc[g]) : m[g];
-  }
-  // max over the 8 token slots of the wave: lanes 8 apart hold other tokens
-  float v = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float x = fmaxf(m[g], dpp<kRowRor8>(m[g]));
-    x = fmaxf(x, shfl_xor(x, 16));
-    x = fmaxf(x, shfl_xor(x, 32));
-    if (lane == g) v = x;
-  }
-  if (lane < G) out[(size_t)lane * MB] = v * out_scale;
-}
-
-// -------------------------------------------------------------------------
-// NVFP4 index keys (E2M1 data [BS][Di/2] + e4m3 scales [BS][Di/16]), bf16
-// index queries.  The per-16 block scale is applied once per 16-element
-// partial dot product; the tensor scale is folded into out_scale.
-// -------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256) void index_nvfp4_kernel(
-    const uint16_t* __restrict__ iq, const uint8_t* __restrict__ ikd,
-    const uint8_t* __restrict__ iks, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ lens, const int32_t* __restrict__ qpos,
-    float* __restrict__ scores, int R, int MB, int P, float out_scale, ZeroArgs za) {
-  za.run();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.y, b = row / R;
-  const int j = blockIdx.x * 4 + wave;
-  if (j >= MB) return;
-  const int entry = bt[(size_t)b * MB + j];  // issued alongside the length loads
-  const int pos = row_last_key(lens, qpos, row, b, MB);
-  float* out = scores + (size_t)row * G * MB + j;
-  const int pb = j * kBlock > pos ? -1 : entry;
-  if (pb < 0 || pb >= P) {  // past the row's last key (or an invalid table entry)
-    if (lane < G) out[(size_t)lane * MB] = -INFINITY;
-    return;
-  }
-  const int c = lane & 3;
-  // data: 16 tokens x 64 B = 1 KB per step; lane reads 16 B = dims [32c, 32c+32)
-  const uint4* dsrc =
-      reinterpret_cast<const uint4*>(ikd + (size_t)pb * (kBlock * kDim / 2)) + lane;
-  // scales: 16 tokens x 8 B per step; lane reads the 2 scales of its 32 dims
-  const uint16_t* ssrc = reinterpret_cast<const uint16_t*>(
-                             iks + (size_t)pb * (kBlock * kDim / 16)) +
-                         (lane >> 2) * 4 + c;
-  uint4 raw[8];
-  uint32_t sc[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    raw[s] = load_stream(dsrc + s * 64);
-    sc[s] = __builtin_nontemporal_load(ssrc + s * 64);
-  }
-  const uint4* qsrc = reinterpret_cast<const uint4*>(iq + (size_t)row * G * kDim) + c * 4;
-  uint32_t qw[G][16];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 v = qsrc[g * 16 + i];
-      qw[g][4 * i] = v.x;
-      qw[g][4 * i + 1] = v.y;
-      qw[g][4 * i + 2] = v.z;
-      qw[g][4 * i + 3] = v.w;
-    }
-  }
-  float m[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) m[g] = -INFINITY;
-  const int tok0 = j * kBlock + (lane >> 2);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const uint32_t dw[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-    const f32x2 scl = fp8x2_to_f32x2<false>(sc[s]);  // scales of dims [32c,+16), [32c+16,+16)
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float part[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) part[g] = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < 2; ++ww) {
-        const int w = half * 2 + ww;  // dword w holds dims 32c + 8w .. 8w+7
-        const bf16x2 k0 = fp4x2_to_bf16x2<0>(dw[w]);
-        const bf16x2 k1 = fp4x2_to_bf16x2<1>(dw[w]);
-        const bf16x2 k2 = fp4x2_to_bf16x2<2>(dw[w]);
-        const bf16x2 k3 = fp4x2_to_bf16x2<3>(dw[w]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          part[g] = dot2_bf16(k0, as_bf16x2(qw[g][4 * w]), part[g]);
-          part[g] = dot2_bf16(k1, as_bf16x2(qw[g][4 * w + 1]), part[g]);
-          part[g] = dot2_bf16(k2, as_bf16x2(qw[g][4 * w + 2]), part[g]);
-          part[g] = dot2_bf16(k3, as_bf16x2(qw[g][4 * w + 3]), part[g]);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = fmaf(scl[half], part[g], acc[g]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc[g] += dpp<kQuadXor1>(acc[g]);
-      acc[g] += dpp<kQuadXor2>(acc[g]);
-    }
-    const bool valid = tok0 + s * 16 <= pos;
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = valid ? fmaxf(m[g], acc[g]) : m[g];
-  }
-  float v = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float x = fmaxf(m[g], dpp<kRowRor4>(m[g]));
-    x = fmaxf(x, dpp<kRowRor8>(x));
-    x = fmaxf(x, shfl_xor(x, 16));
-    x = fmaxf(x, shfl_xor(x, 32));
-    if (lane == g) v = x;
-  }
-  if (lane < G) out[(size_t)lane * MB] = v * out_scale;
+  HalfRaw<IK> h0, h1;
+  h0.issue(x, pb, 0, lane);
+  h1.issue(x, pb, 1, lane);
+  QueryB q;
+  load_query_b<G, IK>(x, row, lane, q);
+  TileMax tm;
+  tm.init();
+  h0.pool(j, 0, pos, lane, q, tm, stage[wave]);
+  h1.pool(j, 1, pos, lane, q, tm, stage[wave]);
+  put_block_scores<G, false>(x, row, j, lane, finish_block(x, tm));
 }
 
 // -------------------------------------------------------------------------
@@ -241,7 +78,7 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
     float out_scale, ZeroArgs za) {
   za.run();
   __shared__ float qs[G * kDim];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int row = blockIdx.y, b = row / R;
   for (int i = threadIdx.x; i < G * kDim; i += 256) qs[i] = iq[(size_t)row * G * kDim + i];
   __syncthreads();
@@ -298,13 +135,12 @@ static hipError_t launch_g(const Shape& s, const void* iq, const void* ikd, cons
   dim3 grid((s.MB + 3) / 4, s.rows), block(256);
   float out_scale = s.index_scale * s.ik_scale;
   const ZeroArgs za{zero, n_zero};
+  const IndexArgs x{(const uint16_t*)iq, (const uint8_t*)ikd, (const uint8_t*)iks, bt, lens,
+                    qpos, scores, s.R, s.MB, s.P, out_scale};
   if (s.ik_dtype == kFP8) {
-    hipLaunchKernelGGL(index_fp8_kernel<G>, grid, block, 0, st, (const uint16_t*)iq,
-                       (const uint8_t*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale, za);
+    hipLaunchKernelGGL((index_mfma_kernel<G, kFP8>), grid, block, 0, st, x, za);
   } else if (s.ik_dtype == kNVFP4) {
-    hipLaunchKernelGGL(index_nvfp4_kernel<G>, grid, block, 0, st, (const uint16_t*)iq,
-                       (const uint8_t*)ikd, (const uint8_t*)iks, bt, lens, qpos, scores, s.R,
-                       s.MB, s.P, out_scale, za);
+    hipLaunchKernelGGL((index_mfma_kernel<G, kNVFP4>), grid, block, 0, st, x, za);
   } else {
     hipLaunchKernelGGL(index_f32_kernel<G>, grid, block, 0, st, (const float*)iq,
                        (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale, za);

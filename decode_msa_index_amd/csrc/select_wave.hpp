@@ -32,15 +32,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Keeps the compiler from moving LDS accesses across this point; the
-// hardware already executes a wave's LDS operations in order.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Set bits of mask in the lanes below the calling lane (lane = its lane id).
 __device__ __forceinline__ int popc_below(uint64_t mask, int lane) {
   (void)lane;
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -50,34 +41,6 @@ __device__ __forceinline__ int popc_below(uint64_t mask, int lane) {
 // (key, index) pair order: larger key first, then lower index.
 __device__ __forceinline__ bool better(uint32_t ka, int ia, uint32_t kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
-}
-
-// Value of lane (lane ^ J).  J = 1, 2, 8 are single DPP moves (quad
-// permutes, rotate a 16-lane row by 8); J = 4 takes the lane 4 up or down
-// with two DPP row shifts; 16 and 32 use the CDNA4 row-swap instructions
-// (v_permlane16_swap / v_permlane32_swap with both operands = v: the first
-// result holds the even rows / lower half, the second the odd rows / upper
-// half).
-template <int J>
-__device__ __forceinline__ int lane_xor(int v) {
-  if constexpr (J == 1) {
-    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4) {
-    const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4
-    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    return (threadIdx.x & 4) ? dn : up;
-  } else if constexpr (J == 8) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
-  } else if constexpr (J == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-    return (int)((threadIdx.x & 16) ? r[0] : r[1]);
-  } else {
-    static_assert(J == 32, "lane distance");
-    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-    return (int)((threadIdx.x & 32) ? r[0] : r[1]);
-  }
 }
 
 __device__ __forceinline__ uint32_t wave_reduce_max_u32(uint32_t v) {
@@ -327,7 +290,7 @@ struct GroupSelectLds {
 template <int NW>
 __device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
                              GroupSelectLds<NW>& g, uint32_t* hist, int32_t* out_w) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int need = K - 1;
   if (rb < 0 || rb + 1 <= K || need == 0) {  // nothing to choose
     __syncthreads();

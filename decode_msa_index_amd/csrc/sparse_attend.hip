@@ -1,504 +1,45 @@
-// sparse_attend.hip -- exact GQA attention over the selected KV blocks.
+// sparse_attend.hip -- the attention kernels and their launch shapes.
 //
 // Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
 // primer" and Figure 1): every query head of a GQA group attends exactly the
-// group's selected blocks, at most k*128 keys.  The attention itself is
-// ordinary softmax attention, run split-K over the selected blocks (the API
+// group's selected blocks, at most k*128 keys; the attention itself is
+// ordinary softmax attention, here split-K over the selected blocks (the API
 // reference of MiniMaxM3SparseAttention._run_attention describes split-K
 // attend kernels that read per-request metadata).
 //
-// Grid: one workgroup per (row, group); its 8 waves split the selected blocks
-// (split-K inside the workgroup).  For a block of 128 keys and the group's
-// (up to 16) heads a wave computes
-//   S^T = K Q^T            v_mfma_f32_16x16x32_bf16  (K e4m3/e2m1 -> bf16 exact)
-//   P   = exp2(S*scale - m) in fp32, rounded to f16 for the next product
-//   O  += P V              v_mfma_f32_16x16x32_f16   (V e4m3/e2m1 -> f16 exact)
-// with an online-softmax running state; the waves' states merge through LDS.
-// Nothing crosses workgroups, so there are no atomics, fences or partials in
-// global memory.
-//
-// Operand layout.  The contraction order inside an MFMA is free as long as
-// both operands agree, so the key order of the S^T tiles is chosen to make
-// every global load contiguous: tile u (0..7) row m holds key
-//   kappa(u, m) = 32*(m/4) + 8*(u/2) + 4*(u%2) + m%4,
-// which puts, for PV chunk c, keys 32*(l/16) + 8*c + 0..7 into lane l's
-// eight A elements -- exactly the 8 consecutive bytes of a V^T row that the
-// B operand needs (V is stored transposed, [d][t], for this).
+// attend_mfma_kernel runs one attend_task (attend_task.hpp) per workgroup:
+// grid = (row, group) units x S splits.  Its SELECT form first makes the
+// group's block selection from the pooled scores (msa_decode's second
+// kernel).  attend_f32_kernel is the plain fp32 path for fp32 caches.
+#include "attend_task.hpp"
 #include "device.hpp"
 #include "launch.hpp"
-#include "select_wave.hpp"
 
 namespace msa {
-
-typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
-typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
-
-__device__ __forceinline__ bf16x8 cat(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
-  const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-  const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
-  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ f16x8 cat(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
-  const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-  const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
-  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// 8 e4m3 bytes (w0: elements 0..3, w1: 4..7) -> bf16x8 / f16x8, exact.
-__device__ __forceinline__ bf16x8 fp8x8_bf16(uint32_t w0, uint32_t w1) {
-  return cat(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-             fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
-}
-__device__ __forceinline__ f16x8 fp8x8_f16(uint32_t w0, uint32_t w1) {
-  return cat(fp8x2_to_f16x2<false>(w0), fp8x2_to_f16x2<true>(w0),
-             fp8x2_to_f16x2<false>(w1), fp8x2_to_f16x2<true>(w1));
-}
-
-// upper halves of two f32 -> one bf16x2 word (exact when the low halves are 0)
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// 8 E2M1 values (nibbles of w, element 2b in the low nibble of byte b) times
-// one e4m3 block scale -> bf16x8.  The product of an e4m3 and an E2M1 value
-// has at most 6 significant bits and lies in [2^-10, 2688]: exact in fp32 and
-// in bf16.
-__device__ __forceinline__ bf16x8 nvfp4x8_bf16(uint32_t w, float scale) {
-  const f32x2 a = fp4x2_to_f32x2<0>(w), b = fp4x2_to_f32x2<1>(w);
-  const f32x2 c = fp4x2_to_f32x2<2>(w), d = fp4x2_to_f32x2<3>(w);
-  uint4 r;
-  r.x = pack_hi16(a[0] * scale, a[1] * scale);
-  r.y = pack_hi16(b[0] * scale, b[1] * scale);
-  r.z = pack_hi16(c[0] * scale, c[1] * scale);
-  r.w = pack_hi16(d[0] * scale, d[1] * scale);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 8 E2M1 values, element e scaled by e4m3 byte e of (s0, s1) -> f16x8 (exact:
-// same bound as above, inside f16's normal range).
-__device__ __forceinline__ f16x8 nvfp4x8_f16(uint32_t w, uint32_t s0, uint32_t s1) {
-  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-  return cat(v0 * fp8x2_to_f16x2<false>(s0), v1 * fp8x2_to_f16x2<true>(s0),
-             v2 * fp8x2_to_f16x2<false>(s1), v3 * fp8x2_to_f16x2<true>(s1));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += shfl_xor(v, o);
-  return v;
-}
-
-// ---------------------------------------------------------------------------
-// Arguments shared by the kernels.
-// ---------------------------------------------------------------------------
-struct AttendArgs {
-  const int32_t* bt;
-  const int32_t* lens;
-  const int32_t* qpos;
-  const int32_t* topk;    // selection input (attend only)
-  const float* scores;    // pooled scores (select + attend)
-  int32_t* topk_out;      // selection output (select + attend), may be null
-  void* out;
-  float* lse;
-  int R, H, G, hpg, MB, K, P;
-  float scale_log2;  // sm_scale * k_scale * log2(e)
-  float v_scale;
-  int out_f32;
-};
-
-__device__ __forceinline__ void store_out(const AttendArgs& a, int row, int h, int d, float v) {
-  const size_t idx = ((size_t)row * a.H + h) * kDim + d;
-  if (a.out_f32)
-    reinterpret_cast<float*>(a.out)[idx] = v;
-  else
-    reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
-}
-
-// exp2(x - m) that is 0 when both are -inf (an empty partial)
-__device__ __forceinline__ float rescale(float x, float m) {
-  return x == -INFINITY ? 0.0f : exp2f(x - m);
-}
-
-// ---------------------------------------------------------------------------
-// FP8 / NVFP4 cache, bf16 queries: MFMA tiles.
-//
-// Grid: (row, group) x S splits; a workgroup of NW waves takes a contiguous
-// share of the row's selection entries and wave w of it takes every NW-th
-// entry of that share.  With SELECT the workgroup first makes the group's
-// selection itself from the pooled scores (wave 0, select_wave.hpp; every
-// split recomputes it, which costs no extra latency) and split 0 also
-// stores it.  For each block a wave computes S^T = K Q^T on MFMA, updates
-// its running max / denominator (online softmax, fp32) and accumulates P V
-// on MFMA into the rescaled running output.  The NW states of a workgroup
-// merge pairwise through LDS.  With S = 1 the workgroup writes the
-// normalised output; otherwise it publishes its state with coherent
-// (device-scope) stores, and the last of the S workgroups to arrive -- a
-// device-scope counter per (row, group) -- merges the S states and writes the
-// output.  No cache write-back fence is needed: every value another
-// workgroup reads is written and read with device-scope atomic accesses.
-// Running state layout per lane l: max and denominator of head l%16; output
-// rows (heads) 4*(l/16)+i, columns (dims) 16*dt + l%16.
-// ---------------------------------------------------------------------------
-struct Partials {
-  float* o;          // [rows*G][S][16][128] unnormalised outputs
-  float* ml;         // [rows*G][S][16][2]   running max (log2 domain) and denominator
-  int32_t* counters; // [rows*G] arrivals, zero before the launch; reset by the merger
-  int S;
-};
-
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <int KV, int NW, bool SELECT>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvd,
     const uint8_t* __restrict__ kvs, AttendArgs a, Partials part) {
-  __shared__ float red_o[NW > 1 ? NW / 2 : 1][32][64];
-  __shared__ float red_ml[NW > 1 ? NW / 2 : 1][2][16];
-  __shared__ int32_t sel_w[SELECT ? NW : 1][32];  // SELECT: each wave's copy of the selection
-  __shared__ int is_last;
-  extern __shared__ uint32_t sel_lds[];  // SELECT: [256] scratch, [MB] keys, [MB] table row
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int u = blockIdx.x / part.S, split = blockIdx.x % part.S;
-  const int row = u / a.G, g = u % a.G, b = row / a.R;
-  const int pos = row_last_key(a.lens, a.qpos, row, b, a.MB);
-  const int rb = pos < 0 ? -1 : pos / kBlock;
-  const int count = min(a.K, rb + 1);  // 0 when the row sees no key
-  const int per_wg = (count + part.S - 1) / part.S;
-  const int e0 = split * per_wg, e1 = min(count, e0 + per_wg);
-  const int n = lane & 15, qd = lane >> 4;
-
-  // Q^T operand: head n of the group, dims qd*32 + 8c + e (zero past hpg);
-  // loaded first so that its latency overlaps the selection
-  bf16x8 qop[4];
-  if (n < a.hpg) {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        q + ((size_t)row * a.H + (size_t)g * a.hpg + n) * kDim + qd * 32);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-  }
-
-  if constexpr (SELECT) {
-    // every thread loads a share of the row's scores (as order keys) and of
-    // its block-table entries, in one round that does not wait for the row
-    // length, and keeps its best candidate; the workgroup then selects
-    __shared__ GroupSelectLds<NW> gsl;
-    uint32_t* keys = sel_lds + 256;
-    int32_t* btl = reinterpret_cast<int32_t*>(keys + a.MB);
-    const float* srow = a.scores + (size_t)u * a.MB;
-    const int32_t* brow = a.bt + (size_t)b * a.MB;
-    uint64_t best = kNoCand;
-    for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
-      float v[8];
-      int32_t e[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int jj = min(base + r * 64 * NW + (int)threadIdx.x, a.MB - 1);
-        v[r] = srow[jj];
-        e[r] = brow[jj];
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int jj = base + r * 64 * NW + (int)threadIdx.x;
-        if (jj < a.MB) {
-          const uint32_t k = order_key(v[r]);
-          keys[jj] = k;
-          btl[jj] = e[r];
-          if (jj < rb) best = max(best, pack_cand(k, jj));
-        }
-      }
-    }
-    group_select<NW>(keys, rb, a.K, best, gsl, sel_lds, sel_w[wave]);
-    if (split == 0 && wave == 0 && a.topk_out && lane < a.K)
-      a.topk_out[(size_t)u * a.K + lane] = sel_w[0][lane];
-  }
-
-  float M = -INFINITY, Lr = 0.0f;
-  f32x4 oacc[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // The wave's selection entries e0+wave, e0+wave+NW, ... and their physical
-  // blocks, fetched by parallel lanes up front: lane i holds the i-th one.
-  int my_j = -1, my_pb = -1;
-  {
-    const int sidx = e0 + wave + NW * lane;
-    if (lane < 32 && sidx < e1) my_j = SELECT ? sel_w[wave][sidx] : a.topk[(size_t)u * a.K + sidx];
-    if (my_j >= 0 && my_j <= rb)
-      my_pb = SELECT ? reinterpret_cast<const int32_t*>(sel_lds + 256 + a.MB)[my_j]
-                     : a.bt[(size_t)b * a.MB + my_j];
-  }
-  for (int it = 0; e0 + wave + NW * it < e1; ++it) {
-    const int j = __shfl(my_j, it, 64);
-    const int pb = __shfl(my_pb, it, 64);
-    if (j < 0 || j > rb) continue;      // malformed selection entry: contributes nothing
-    if (pb < 0 || pb >= a.P) continue;  // invalid table entry: contributes nothing
-    const int nvalid = min(kBlock, pos - j * kBlock + 1);
-    const size_t kplane = ((size_t)pb * 2 + 0) * a.G + g;
-    const size_t vplane = ((size_t)pb * 2 + 1) * a.G + g;
-
-    // ---- loads: K rows kappa(u, n), V^T rows dt*16+n; 32 dims / tokens each ----
-    uint4 kraw[16], vraw[16];
-    uint32_t ksc[8];
-    uint4 vsc[16];
-    if constexpr (KV == kFP8) {
-      const uint8_t* kb = kvd + kplane * (kBlock * kDim);
-      const uint8_t* vb = kvd + vplane * (kBlock * kDim);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int kappa = 32 * (n >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (n & 3);
-        const uint4* p = reinterpret_cast<const uint4*>(kb + kappa * kDim + qd * 32);
-        kraw[2 * t] = p[0];
-        kraw[2 * t + 1] = p[1];
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint4* p = reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * kBlock + qd * 32);
-        vraw[2 * dt] = p[0];
-        vraw[2 * dt + 1] = p[1];
-      }
-    } else {
-      const uint8_t* kb = kvd + kplane * (kBlock * kDim / 2);
-      const uint8_t* vb = kvd + vplane * (kBlock * kDim / 2);
-      const uint8_t* ks = kvs + kplane * (kBlock * kDim / 16);
-      const uint8_t* vs = kvs + vplane * (kBlock * kDim / 16);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int kappa = 32 * (n >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (n & 3);
-        kraw[t] = *reinterpret_cast<const uint4*>(kb + kappa * (kDim / 2) + qd * 16);
-        ksc[t] = *reinterpret_cast<const uint16_t*>(ks + kappa * (kDim / 16) + qd * 2);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        vraw[dt] = *reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * (kBlock / 2) + qd * 16);
-        const uint4* sp = reinterpret_cast<const uint4*>(vs + dt * kBlock + qd * 32);
-        vsc[2 * dt] = sp[0];
-        vsc[2 * dt + 1] = sp[1];
-      }
-    }
-
-    // ---- S^T = K Q^T ----
-    f32x4 sacc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      sacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bf16x8 kop;
-        if constexpr (KV == kFP8) {
-          const uint4 r = kraw[2 * t + (c >> 1)];
-          kop = (c & 1) ? fp8x8_bf16(r.z, r.w) : fp8x8_bf16(r.x, r.y);
-        } else {
-          const uint32_t w = c == 0 ? kraw[t].x : c == 1 ? kraw[t].y : c == 2 ? kraw[t].z : kraw[t].w;
-          const f32x2 sc = fp8x2_to_f32x2<false>(ksc[t]);
-          kop = nvfp4x8_bf16(w, sc[c >> 1]);
-        }
-        sacc[t] = mfma_bf16(kop, qop[c], sacc[t]);
-      }
-    }
-
-    // ---- online softmax update (head n lives in lanes n, n+16, n+32, n+48) ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 32 * qd + 8 * (t >> 1) + 4 * (t & 1) + i;
-        const float v = key < nvalid ? sacc[t][i] * a.scale_log2 : -INFINITY;
-        sacc[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float Mn = fmaxf(M, mx);
-    const float alpha = rescale(M, Mn);
-    float lsum = 0.0f;
-    f16x8 pop[4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sacc[t][i] - Mn);
-        lsum += p;
-        pop[t >> 1][4 * (t & 1) + i] = (_Float16)p;
-      }
-    }
-    lsum += shfl_xor(lsum, 16);
-    lsum += shfl_xor(lsum, 32);
-    Lr = Lr * alpha + lsum;
-    M = Mn;
-    float alpha_o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * qd + i, 64);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha_o[i];
-    }
-
-    // ---- O += P V ----
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        f16x8 vop;
-        if constexpr (KV == kFP8) {
-          const uint4 r = vraw[2 * dt + (c >> 1)];
-          vop = (c & 1) ? fp8x8_f16(r.z, r.w) : fp8x8_f16(r.x, r.y);
-        } else {
-          const uint32_t w = c == 0 ? vraw[dt].x : c == 1 ? vraw[dt].y : c == 2 ? vraw[dt].z : vraw[dt].w;
-          const uint4 sv = vsc[2 * dt + (c >> 1)];
-          vop = (c & 1) ? nvfp4x8_f16(w, sv.z, sv.w) : nvfp4x8_f16(w, sv.x, sv.y);
-        }
-        oacc[dt] = mfma_f16(pop[c], vop, oacc[dt]);
-      }
-    }
-  }
-
-  // ---- merge the waves' states pairwise through LDS ----
-#pragma unroll
-  for (int half = NW / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
-      const int slot = wave - half;
-      if (qd == 0) {
-        red_ml[slot][0][n] = M;
-        red_ml[slot][1][n] = Lr;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red_o[slot][dt * 4 + i][lane] = oacc[dt][i];
-      }
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float Mb = red_ml[wave][0][n], Lb = red_ml[wave][1][n];
-      const float Mn = fmaxf(M, Mb);
-      const float fa = rescale(M, Mn), fb = rescale(Mb, Mn);
-      Lr = Lr * fa + Lb * fb;
-      M = Mn;
-      float fa_o[4], fb_o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa_o[i] = __shfl(fa, 4 * qd + i, 64);
-        fb_o[i] = __shfl(fb, 4 * qd + i, 64);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          oacc[dt][i] = oacc[dt][i] * fa_o[i] + red_o[wave][dt * 4 + i][lane] * fb_o[i];
-      }
-    }
-    __syncthreads();
-  }
-
-  if (part.S == 1) {
-    if (wave != 0) return;
-    float inv_o[4];
-    const float inv = Lr > 0.0f ? a.v_scale / Lr : 0.0f;  // no visible key: zeros
-#pragma unroll
-    for (int i = 0; i < 4; ++i) inv_o[i] = __shfl(inv, 4 * qd + i, 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * qd + i;
-      if (h < a.hpg) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          store_out(a, row, g * a.hpg + h, dt * 16 + n, oacc[dt][i] * inv_o[i]);
-      }
-    }
-    if (a.lse && qd == 0 && n < a.hpg)
-      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + n] =
-          Lr > 0.0f ? (M + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
-    return;
-  }
-
-  // ---- split-K across workgroups: publish, count arrivals, last one merges ----
-  if (wave == 0) {
-    const size_t pidx = (size_t)u * part.S + split;
-    float* po = part.o + pidx * (kHeadsPad * kDim);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) coherent_store(po + (4 * qd + i) * kDim + dt * 16 + n, oacc[dt][i]);
-    }
-    if (qd == 0) {
-      coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n, M);
-      coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n + 1, Lr);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
-    int prev = 0;
-    if (lane == 0)
-      prev = __hip_atomic_fetch_add(part.counters + u, 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0, 64);
-    if (lane == 0) is_last = prev == part.S - 1;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  // merge: thread t takes head t/16 and dims 8*(t%16) .. +8 (looping when
-  // NW < 4); every partial is loaded before any is used, so the coherent
-  // loads overlap
-  for (int t = threadIdx.x; t < kHeadsPad * 16; t += 64 * NW) {
-    const int h = t >> 4, d0 = (t & 15) * 8;
-    if (h >= a.hpg) continue;
-    const float* ml = part.ml + (size_t)u * part.S * (kHeadsPad * 2) + 2 * h;
-    const float* po = part.o + (size_t)u * part.S * (kHeadsPad * kDim) + h * kDim + d0;
-    float pm[kMaxSplits], pl[kMaxSplits], pv[kMaxSplits][8];
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      if (sp < part.S) {
-        pm[sp] = coherent_load(ml + (size_t)sp * (kHeadsPad * 2));
-        pl[sp] = coherent_load(ml + (size_t)sp * (kHeadsPad * 2) + 1);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) pv[sp][k] = coherent_load(po + (size_t)sp * (kHeadsPad * kDim) + k);
-      }
-    }
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp)
-      if (sp < part.S) Mx = fmaxf(Mx, pm[sp]);
-    float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      if (sp < part.S) {
-        const float f = rescale(pm[sp], Mx);
-        L += f * pl[sp];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] += f * pv[sp][k];
-      }
-    }
-    const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) store_out(a, row, g * a.hpg + h, d0 + k, o[k] * inv);
-    if (a.lse && (t & 15) == 0)
-      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
-          L > 0.0f ? (Mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
-  }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(part.counters + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  extern __shared__ uint32_t sel_lds[];
+  attend_task<KV, NW, SELECT, false>(q, kvd, kvs, a, part, blockIdx.x / part.S,
+                                     blockIdx.x % part.S, sel_lds);
 }
 
 __global__ void zero_fill_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
+}
+
+// Clears bytes (a multiple of 4) at p with a fill kernel (no memset node, so
+// the call can sit inside a captured graph).
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     static_cast<int32_t*>(p), (int)n);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -634,42 +175,13 @@ bool select_fusable(const Shape& s) {
   return stat + dyn <= 65536;
 }
 
-static AttendArgs make_args(const Shape& s, const int32_t* block_table, const int32_t* seq_lens,
-                            const int32_t* q_pos, const int32_t* topk, const float* scores,
-                            int32_t* topk_out, void* out, float* lse) {
-  AttendArgs a;
-  a.bt = block_table;
-  a.lens = seq_lens;
-  a.qpos = q_pos;
-  a.topk = topk;
-  a.scores = scores;
-  a.topk_out = topk_out;
-  a.out = out;
-  a.lse = lse;
-  a.R = s.R;
-  a.H = s.H;
-  a.G = s.G;
-  a.hpg = s.hpg;
-  a.MB = s.MB;
-  a.K = s.K;
-  a.P = s.P;
-  a.scale_log2 = s.sm_scale * s.k_scale * 1.4426950408889634f;
-  a.v_scale = s.v_scale;
-  a.out_f32 = s.out_dtype == kF32;
-  return a;
-}
-
 template <bool SELECT>
 static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const AttendArgs& a,
                               const void* q, const void* kv_data, const void* kv_scales,
                               void* workspace, bool zero_counters, hipStream_t st) {
   const int units = s.rows * s.G;
   if (c.splits < 1 || c.splits > kMaxSplits) return hipErrorInvalidValue;
-  Partials part;
-  part.S = c.splits;
-  part.ml = static_cast<float*>(workspace);
-  part.o = part.ml + (size_t)units * c.splits * kHeadsPad * 2;
-  part.counters = reinterpret_cast<int32_t*>(part.o + (size_t)units * c.splits * kHeadsPad * kDim);
+  const Partials part = make_partials(s, c, workspace);
   if (c.splits > 1 && zero_counters) {
     hipLaunchKernelGGL(zero_fill_kernel, dim3((units + 255) / 256), dim3(256), 0, st,
                        part.counters, units);
@@ -706,7 +218,7 @@ hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const
                                     const int32_t* block_table, const int32_t* seq_lens,
                                     const int32_t* q_pos, const int32_t* topk, void* out,
                                     float* lse, void* workspace, hipStream_t st) {
-  const AttendArgs a = make_args(s, block_table, seq_lens, q_pos, topk, nullptr, nullptr, out, lse);
+  const AttendArgs a = make_attend_args(s, block_table, seq_lens, q_pos, topk, nullptr, nullptr, out, lse);
   if (s.kv_dtype == kF32) {
     hipLaunchKernelGGL(attend_f32_kernel, dim3(s.rows * s.G), dim3(64), 0, st, q,
                        (const float*)kv_data, (int)(s.q_dtype == kBF16), a);
@@ -728,9 +240,11 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, bool counters_zeroed, hipStream_t st) {
-  const AttendArgs a =
-      make_args(s, block_table, seq_lens, q_pos, nullptr, scores, topk_out, out, lse);
+                                void* workspace, bool counters_zeroed, float* clear_scores,
+                                hipStream_t st) {
+  AttendArgs a =
+      make_attend_args(s, block_table, seq_lens, q_pos, nullptr, scores, topk_out, out, lse);
+  a.clear = reinterpret_cast<uint32_t*>(clear_scores);
   return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace,
                            !counters_zeroed, st);
 }

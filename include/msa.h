@@ -129,12 +129,18 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * Workspace bytes a call needs for problem p (op as for msa_check_problem):
  *   - msa_sparse_attend: room for the split-K partial states when a (row,
  *     group) is split over several workgroups (0 when it is not);
- *   - msa_decode: that plus B*R*G*MB floats for the pooled scores;
+ *   - msa_decode: that plus a 256-byte header and B*R*G*MB words for the
+ *     pooled scores;
  *   - the other calls: 0.
  * Every region is rounded up to 256 bytes.  The workspace is caller-owned
- * device memory, 256-byte aligned; no contents are carried between calls, so
- * it needs no initialisation, but calls that share one must not overlap.  A
- * call whose size is 0 accepts a NULL workspace.
+ * device memory, 256-byte aligned.  msa_decode requires it to be zero-filled
+ * before its first use (e.g. hipMemset once after allocation): its one
+ * kernel synchronises its workgroups through counters and ready flags that
+ * start at zero.  Every msa_decode and msa_sparse_attend call leaves the
+ * workspace zero-filled again, so one zero fill serves any sequence of calls
+ * and problem shapes; msa_sparse_attend itself needs no initialisation.
+ * Calls that share a workspace must not overlap.  A call whose size is 0
+ * accepts a NULL workspace.
  */
 msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
 
@@ -186,10 +192,15 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The whole decode step: msa_index_scores -> msa_block_topk ->
- * msa_sparse_attend on `stream`.  topk_idx receives the selection;
- * block_scores (nullable) receives the pooled scores when given, otherwise
- * they live in the workspace.  workspace: msa_workspace_bytes(p, 3) bytes.
+ * The whole decode step (blog, "MSA primer"): msa_index_scores ->
+ * msa_block_topk -> msa_sparse_attend, with the same results.  For FP8 or
+ * NVFP4 caches (index keys and K/V of one format) and block tables of up to
+ * about 5000 blocks it is one persistent kernel that runs the selection and
+ * attention of each row as soon as that row's scores are complete, overlapped
+ * with the scan of later rows; otherwise the three kernels run in turn.
+ * topk_idx receives the selection; block_scores (nullable) receives the
+ * pooled scores.  workspace: msa_workspace_bytes(p, 3) bytes, zero-filled
+ * before its first use (see msa_workspace_bytes) and left zero-filled.
  */
 msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
                       const void* ik_scales, const void* q, const void* kv_data,

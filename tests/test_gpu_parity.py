@@ -167,12 +167,40 @@ def test_decode_equals_chain_and_is_deterministic():
     dw.chain()
     torch.cuda.synchronize()
     a = (dw.scores.clone(), dw.topk.clone(), dw.out.clone(), dw.lse.clone())
-    for _ in range(2):
-        dw.decode(with_scores=True)
+    for with_scores in (True, True, False):
+        dw.decode(with_scores=with_scores)
         torch.cuda.synchronize()
-        for x, y in zip(a, (dw.scores, dw.topk, dw.out, dw.lse)):
+        got = (dw.scores, dw.topk, dw.out, dw.lse) if with_scores else (dw.topk, dw.out, dw.lse)
+        for x, y in zip(a if with_scores else a[1:], got):
             assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                                y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+        assert int(torch.count_nonzero(dw.ws_decode)) == 0, "workspace not left zero-filled"
+
+
+def test_one_workspace_across_shapes():
+    """msa_decode leaves its workspace zero-filled, so one workspace (zeroed
+    once) serves calls of different shapes in any order."""
+    ws_ = [synth.make("shapeA", seed=61, seq_lens=[9000, 40000, 128, 1], q_dtype=synth.BF16,
+                      kv_dtype=synth.FP8, plant_per_seq=3),
+           synth.make("shapeB", seed=62, seq_lens=[70000, 3000], q_dtype=synth.BF16,
+                      kv_dtype=synth.FP8, num_q_heads=32, num_groups=8, top_k=8)]
+    dws = [parity.DeviceWorkload(w) for w in ws_]
+    refs = []
+    for dw in dws:
+        dw.chain()
+        torch.cuda.synchronize()
+        refs.append((dw.topk.clone(), dw.out.clone()))
+    shared = torch.zeros(max(int(dw.ws_decode.numel()) for dw in dws), dtype=torch.uint8,
+                         device="cuda")
+    for k in (0, 1, 0, 1, 1, 0):
+        dw = dws[k]
+        say(f"[parity] shared workspace, shape {'AB'[k]}")
+        dw.ws_decode = shared
+        dw.decode(with_scores=False)
+        torch.cuda.synchronize()
+        assert torch.equal(dw.topk, refs[k][0])
+        assert torch.equal(dw.out.view(torch.uint8), refs[k][1].view(torch.uint8))
+        assert int(torch.count_nonzero(shared)) == 0
 
 
 def test_empty_batch_and_errors():
