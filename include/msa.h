@@ -194,10 +194,9 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
 /*
  * The whole decode step (blog, "MSA primer"): msa_index_scores ->
  * msa_block_topk -> msa_sparse_attend, with the same results.  For FP8 or
- * NVFP4 caches (index keys and K/V of one format) and block tables of up to
- * about 5000 blocks it is one persistent kernel that runs the selection and
- * attention of each row as soon as that row's scores are complete, overlapped
- * with the scan of later rows; otherwise the three kernels run in turn.
+ * NVFP4 caches and block tables of up to about 16000 blocks it is two
+ * kernels, the scan and then selection + attention in one; otherwise the
+ * three kernels run in turn.
  * topk_idx receives the selection; block_scores (nullable) receives the
  * pooled scores.  workspace: msa_workspace_bytes(p, 3) bytes, zero-filled
  * before its first use (see msa_workspace_bytes) and left zero-filled.
