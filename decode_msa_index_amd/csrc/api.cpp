@@ -191,7 +191,7 @@ static msa_status check_attend_args(const msa_problem* p, const void* q, const v
   REQUIRE(block_table, 4);
   REQUIRE(seq_lens, 4);
   OPTIONAL(q_pos, 4);
-  REQUIRE(out, 4);
+  REQUIRE(out, 16);
   OPTIONAL(lse, 4);
   if (!q_pos && p->rows_per_seq != 1)
     return fail(MSA_ERR_INVALID_ARGUMENT, "q_pos is required when rows_per_seq > 1");

@@ -75,6 +75,25 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, int row, int h, i
     reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
 }
 
+// Dims d0 .. d0+7 of head h (d0 a multiple of 8): one 16-byte store (bf16)
+// or two (f32).
+__device__ __forceinline__ void store_out8(const AttendArgs& a, int row, int h, int d0,
+                                           const float (&o)[8]) {
+  const size_t idx = ((size_t)row * a.H + h) * kDim + d0;
+  if (a.out_f32) {
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx);
+    p[0] = make_float4(o[0], o[1], o[2], o[3]);
+    p[1] = make_float4(o[4], o[5], o[6], o[7]);
+  } else {
+    uint4 w;
+    w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+    w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + idx) = w;
+  }
+}
+
 // exp2(x - m) that is 0 when both are -inf (an empty partial)
 __device__ __forceinline__ float rescale(float x, float m) {
   return x == -INFINITY ? 0.0f : exp2f(x - m);
@@ -156,6 +175,20 @@ __device__ __forceinline__ void coherent_store(float* p, float v) {
 __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Device-scope (sc1) vector loads through a buffer resource over [base,
+// base + bytes): data another workgroup of the same kernel wrote with
+// device-scope stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+constexpr int kCoherentAux = 16;  // cache policy: sc1
+__device__ __forceinline__ f32x4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAux));
+}
+__device__ __forceinline__ f32x2 coherent_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentAux));
+}
+
 __device__ __forceinline__ uint32_t coherent_load_u32(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -479,10 +512,12 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
   if (wave == 0) {
     const size_t pidx = (size_t)u * part.S + split;
     float* po = part.o + pidx * (kHeadsPad * kDim);
+    // lane-major: value (dt, i) of lane l at (4 dt + i) * 64 + l, so each
+    // store instruction writes 256 contiguous bytes
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) coherent_store(po + (4 * qd + i) * kDim + dt * 16 + n, oacc[dt][i]);
+      for (int i = 0; i < 4; ++i) coherent_store(po + (4 * dt + i) * 64 + lane, oacc[dt][i]);
     }
     if (qd == 0) {
       coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n, M);
@@ -498,62 +533,66 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
   }
   __syncthreads();
   if (!is_last) return;
-  // merge: thread t takes head t/16 and dims 8*(t%16) .. +8 (looping when
-  // NW < 4); every partial is loaded before any is used, so the coherent
-  // loads overlap.  Each thread then zeroes what it read (and the padded
-  // heads' entries), leaving the workspace as the call found it.
+  // merge: thread t takes head h = t/16 and dims d0 = 8*(t%16) .. +8
+  // (looping when NW < 4).  Head h = 4*qd + i, dim 16*dt + n sits at
+  // (4 dt + i) * 64 + 16 qd + n in a partial, so the 8 dims are 32
+  // contiguous bytes: two 16-byte device-scope loads per partial, all issued
+  // before any is used.  Each thread then zeroes what it read (and the
+  // padded heads' entries), leaving the workspace as the call found it.
+  const size_t ubase = (size_t)u * part.S;
+  const __amdgpu_buffer_rsrc_t ro =
+      coherent_rsrc(part.o + ubase * (kHeadsPad * kDim), part.S * kHeadsPad * kDim * 4);
+  const __amdgpu_buffer_rsrc_t rm =
+      coherent_rsrc(part.ml + ubase * (kHeadsPad * 2), part.S * kHeadsPad * 2 * 4);
   for (int t = threadIdx.x; t < kHeadsPad * 16; t += 64 * NW) {
     const int h = t >> 4, d0 = (t & 15) * 8;
-    float* ml = part.ml + (size_t)u * part.S * (kHeadsPad * 2) + 2 * h;
-    float* po = part.o + (size_t)u * part.S * (kHeadsPad * kDim) + h * kDim + d0;
-    if (h >= a.hpg) {
-      for (int sp = 0; sp < part.S; ++sp) {
+    const int off = (4 * (d0 >> 4) + (h & 3)) * 64 + 16 * (h >> 2) + (d0 & 15);  // floats
+    float* po = part.o + ubase * (kHeadsPad * kDim) + off;
+    float* ml = part.ml + ubase * (kHeadsPad * 2) + 2 * h;
+    if (h < a.hpg) {
+      float pm[kMaxSplits], pl[kMaxSplits], pv[kMaxSplits][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) po[(size_t)sp * (kHeadsPad * kDim) + k] = 0.0f;
-        if ((t & 15) == 0) {
-          ml[(size_t)sp * (kHeadsPad * 2)] = 0.0f;
-          ml[(size_t)sp * (kHeadsPad * 2) + 1] = 0.0f;
+      for (int sp = 0; sp < kMaxSplits; ++sp) {
+        if (sp < part.S) {
+          const f32x2 m2 = coherent_load8(rm, (uint32_t)((sp * kHeadsPad + h) * 2 * 4));
+          pm[sp] = m2[0];
+          pl[sp] = m2[1];
+          const uint32_t ob = (uint32_t)((sp * kHeadsPad * kDim + off) * 4);
+          const f32x4 v0 = coherent_load16(ro, ob), v1 = coherent_load16(ro, ob + 16);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            pv[sp][k] = v0[k];
+            pv[sp][4 + k] = v1[k];
+          }
         }
       }
-      continue;
-    }
-    float pm[kMaxSplits], pl[kMaxSplits], pv[kMaxSplits][8];
+      float Mx = -INFINITY;
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      if (sp < part.S) {
-        pm[sp] = coherent_load(ml + (size_t)sp * (kHeadsPad * 2));
-        pl[sp] = coherent_load(ml + (size_t)sp * (kHeadsPad * 2) + 1);
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < part.S) Mx = fmaxf(Mx, pm[sp]);
+      float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pv[sp][k] = coherent_load(po + (size_t)sp * (kHeadsPad * kDim) + k);
+      for (int sp = 0; sp < kMaxSplits; ++sp) {
+        if (sp < part.S) {
+          const float f = rescale(pm[sp], Mx);
+          L += f * pl[sp];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] += f * pv[sp][k];
+        }
       }
+      const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] *= inv;
+      store_out8(a, row, g * a.hpg + h, d0, o);
+      if (a.lse && (t & 15) == 0)
+        a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
+            L > 0.0f ? (Mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
     }
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp)
-      if (sp < part.S) Mx = fmaxf(Mx, pm[sp]);
-    float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      if (sp < part.S) {
-        const float f = rescale(pm[sp], Mx);
-        L += f * pl[sp];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] += f * pv[sp][k];
-      }
-    }
-    const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) store_out(a, row, g * a.hpg + h, d0 + k, o[k] * inv);
-    if (a.lse && (t & 15) == 0)
-      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
-          L > 0.0f ? (Mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
     for (int sp = 0; sp < part.S; ++sp) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) po[(size_t)sp * (kHeadsPad * kDim) + k] = 0.0f;
-      if ((t & 15) == 0) {
-        ml[(size_t)sp * (kHeadsPad * 2)] = 0.0f;
-        ml[(size_t)sp * (kHeadsPad * 2) + 1] = 0.0f;
-      }
+      float4* z = reinterpret_cast<float4*>(po + (size_t)sp * (kHeadsPad * kDim));
+      z[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      z[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if ((t & 15) == 0) *reinterpret_cast<float2*>(ml + (size_t)sp * (kHeadsPad * 2)) = make_float2(0.0f, 0.0f);
     }
   }
   if (SELECT && a.clear) clear_row(a, u, NW);

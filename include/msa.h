@@ -57,7 +57,7 @@
  *                                    pos = seq_len - 1 (plain decode)
  *   block_scores f32 [B*R][G][MB]    pooled scores, -inf past the row's block
  *   topk_idx     int32 [B*R][G][K]   ascending logical block ids, -1 padded
- *   out          [B*R][H][D]         bf16 or f32
+ *   out          [B*R][H][D]         bf16 or f32          16-byte aligned
  *   lse          f32 [B*R][H] or NULL natural-log softmax denominator
  *
  * Number formats: bf16; OCP FP8 e4m3fn; NVFP4 = E2M1 values, one e4m3 scale

@@ -80,6 +80,10 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
         msa.sparse_attend(good(kv_dtype=3), 0x1000, 0x2000, None, 0x3000, 0x4000, None,
                           0x5000, 0x6000, None, None, stream=0)
     assert e.value.status == 1 and "kv_scales" in e.value.detail
+    with pytest.raises(msa.MsaError) as e:  # outputs are written 16 bytes at a time
+        msa.sparse_attend(good(), 0x1000, 0x2000, None, 0x3000, 0x4000, None,
+                          0x5000, 0x6008, None, None, stream=0)
+    assert e.value.status == 1 and "out" in e.value.detail and "aligned" in e.value.detail
 
 
 def test_workspace_sizes():
