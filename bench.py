@@ -2,17 +2,21 @@
 """MSA decode benchmark on one MI355X.
 
 One step = one msa_decode call: one pass of the whole decode hot path over
-one batch (index scores + block max-pool, block top-k, sparse attention).  Inputs are resident in HBM before timing starts.  To
-keep the 256 MB Infinity Cache from serving the scan, the step rotates over
-several copies of the caches at different addresses ("layers"), as a real
-model's decode would over its layers.
+one batch (index scores + block max-pool, block top-k, sparse attention).
+Inputs are resident in HBM before timing starts.  To keep the 256 MB
+Infinity Cache from serving the scan, the step rotates over several copies of
+the caches at different addresses ("layers"), as a real model's decode would
+over its layers.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
-the launch stream inside the timed region.
+the launch stream inside the timed region.  The HBM traffic of the index scan
+comes from committed rocprofv3 counter runs (profiles/index_scan_traffic.json)
+and is reported only while the scan's sources are unchanged since then.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,10 +27,36 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MSA decode queries/s + achieved HBM GB/s (% of peak) at 256K ctx, FP8 KV"
 HBM_PEAK_GBPS = 8000.0
+# sources that determine the index scan kernel's memory traffic
+SCAN_SOURCES = ["decode_msa_index_amd/csrc/index_block.hpp",
+                "decode_msa_index_amd/csrc/index_scores.hip",
+                "decode_msa_index_amd/csrc/device.hpp"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def scan_fingerprint() -> str:
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per index-scan launch from the committed counter runs, or
+    None when they were taken on another workload or older scan sources."""
+    path = os.path.join(ROOT, "profiles", "index_scan_traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("scan_sources_sha256") != scan_fingerprint():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def algorithmic_bytes(w, topk_counts):
@@ -51,11 +81,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="fp8_long",
-                    choices=["fp8_long", "fp8_b32", "nvfp4_512k", "fp8_256k"])
+    ap.add_argument("--workload", default="fp8_256k",
+                    choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device-to-device (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -65,6 +98,17 @@ def main():
     import numpy as np
     import torch
 
+    if args.calibrate_copy:
+        # a plain copy of known size: it reads and writes 2^30 bytes once, so
+        # the HBM counters of this dispatch calibrate FETCH_SIZE / WRITE_SIZE
+        a = torch.empty(2**30, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copied 1073741824 bytes")
+        return
+
     import decode_msa_index_amd as msa
     import synth
     from tests import parity
@@ -72,12 +116,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     msa.lib()
     t0 = time.time()
-    if args.workload == "fp8_256k":
-        w = synth.make("fp8_256k", seed=0x4D5341 + 5, seq_lens=[262144] * 8,
-                       q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=8)
-        w.recipe = "8 seqs x 262144 tokens, as fp8_long otherwise"
-    else:
-        w = getattr(synth, args.workload)()
+    w = getattr(synth, args.workload)()
     log(f"[bench] generated {w.name} in {time.time() - t0:.1f}s: {w.recipe}")
 
     dws = [parity.DeviceWorkload(w)]
@@ -88,13 +127,12 @@ def main():
         d.kv_data = dws[0].kv_data.clone()
         d.ik_scales = None if dws[0].ik_scales is None else dws[0].ik_scales.clone()
         d.kv_scales = None if dws[0].kv_scales is None else dws[0].kv_scales.clone()
-        d.ws_attend = dws[0].ws_attend.clone()
         dws.append(d)
     torch.cuda.synchronize()
     log(f"[bench] {args.layers} cache copies resident; "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
-    # ---- timed region 1: whole decode steps (msa_decode) ----
+    # ---- timed region 1: whole decode steps (msa_decode), eager ----
     for i in range(args.warmup):
         dws[i % len(dws)].decode(with_scores=False)
     torch.cuda.synchronize()
@@ -105,7 +143,39 @@ def main():
     t_total = time.perf_counter() - t_start
     ms_step = t_total * 1e3 / args.steps
 
-    # ---- timed region 2: the dominant kernel (index scan) per launch, HIP
+    # per-step distribution (events around each step; a separate pass)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        dws[i % len(dws)].decode(with_scores=False)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    # ---- timed region 2: the same steps replayed from a HIP graph ----
+    graph_ms = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for d in dws:  # warm the capture stream
+                d.decode(with_scores=False)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for d in dws:
+                d.decode(with_scores=False)
+        reps = max(1, args.steps // len(dws))
+        g.replay()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t_g) * 1e3 / (reps * len(dws))
+
+    # ---- timed region 3: the dominant kernel (index scan) per launch, HIP
     # events on the launch stream ----
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.warmup):
@@ -117,8 +187,6 @@ def main():
         evs[i][1].record()
     torch.cuda.synchronize()
     k_idx = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    k_topk = np.array([0.0])
-    k_att = np.array([0.0])
     dws[0].decode(with_scores=True)
     torch.cuda.synchronize()
 
@@ -126,37 +194,46 @@ def main():
     sel_tokens = 0
     for r in range(w.rows):
         L = int(w.seq_lens[r])
-        for g in range(w.num_groups):
-            for j in topk[r, g]:
+        for gi in range(w.num_groups):
+            for j in topk[r, gi]:
                 if j >= 0:
                     sel_tokens += min(128, L - 128 * int(j))
     b_idx, b_topk, b_att = algorithmic_bytes(w, sel_tokens)
     b_step = b_idx + b_topk + b_att
-    idx_us = float(np.mean(k_idx)) * 1e3
+    idx_us = float(np.median(k_idx)) * 1e3
     achieved = b_idx / (idx_us * 1e-6) / 1e9
     tokens = int(w.seq_lens.astype(np.int64).sum())
     dense_bytes = tokens * (256 if w.kv_dtype == 2 else 144) * w.num_groups
-    log(f"[bench] ms/step {ms_step:.4f}; index kernel {idx_us:.1f} us/launch "
-        f"({achieved:.0f} GB/s)")
+    log(f"[bench] ms/step {ms_step:.4f} (p10/p50/p90 {np.percentile(step_ms, 10):.4f}/"
+        f"{np.percentile(step_ms, 50):.4f}/{np.percentile(step_ms, 90):.4f}; graph "
+        f"{graph_ms if graph_ms is None else round(graph_ms, 4)}); index kernel "
+        f"{idx_us:.1f} us/launch ({achieved:.0f} GB/s)")
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
-        p = parity.oracle_problem(w, threads)
-        reps, t_c0 = 0, time.perf_counter()
-        while True:
-            oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data, w.kv_scales,
-                          w.block_table, w.seq_lens, w.q_pos)
-            reps += 1
-            if time.perf_counter() - t_c0 >= args.cpu_seconds:
-                break
-        t_c = time.perf_counter() - t_c0
-        cpu = {"value": reps * w.rows / t_c, "unit": "queries/s",
-               "cores": oracle.threads_used(), "kind": "oracle",
+
+        def time_oracle(nthreads, seconds):
+            p = parity.oracle_problem(w, nthreads)
+            reps, t_c0 = 0, time.perf_counter()
+            while True:
+                oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data,
+                              w.kv_scales, w.block_table, w.seq_lens, w.q_pos)
+                reps += 1
+                if time.perf_counter() - t_c0 >= seconds:
+                    break
+            return reps, time.perf_counter() - t_c0, oracle.threads_used()
+
+        reps, t_c, used = time_oracle(threads, args.cpu_seconds)
+        reps1, t_c1, _ = time_oracle(1, max(1.0, args.cpu_seconds / 4))
+        cpu = {"value": reps * w.rows / t_c, "unit": "queries/s", "cores": used,
+               "kind": "oracle",
                "sample": f"{reps} full decode step(s) of the same {w.rows}-query batch "
-                         f"({tokens} cached tokens) in {t_c:.1f}s, fp64"}
-        log(f"[bench] oracle: {cpu['value']:.3f} queries/s on {cpu['cores']} threads")
+                         f"({tokens} cached tokens) in {t_c:.1f}s, fp64, {used} threads",
+               "value_1_thread": reps1 * w.rows / t_c1}
+        log(f"[bench] oracle: {cpu['value']:.3f} queries/s on {used} threads, "
+            f"{cpu['value_1_thread']:.3f} on 1")
 
     out = {
         "metric": METRIC,
@@ -178,6 +255,8 @@ def main():
             "kv_groups": w.num_groups, "head_dim": w.head_dim, "block": w.block_size,
             "top_k": w.top_k, "cache_copies": args.layers,
         },
+        "ms_per_step_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "ms_per_step_graph": graph_ms,
         "hbm_gbps_step": b_step / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": b_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "tokens_scanned_per_s": tokens / (ms_step * 1e-3),
@@ -185,9 +264,9 @@ def main():
         "dense_attention_bytes_ratio": dense_bytes / b_step,
         "kernel_us": {"index_scores": idx_us,
                       "select_attend_and_gaps": ms_step * 1e3 - idx_us},
-        "roofline": {"bound": "hbm", "kernel": "index_scores", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "index_mfma_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_launch": b_idx},
+                     "traffic": measured_traffic(w.name), "bytes_per_launch": b_idx},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -385,6 +385,15 @@ def fp8_long(seed: int = 0x4D5341 + 3, **kw) -> Workload:
     return w
 
 
+def fp8_256k(seed: int = 0x4D5341 + 5, **kw) -> Workload:
+    w = make("fp8_256k", seed=seed, seq_lens=[262144] * 8, q_dtype=BF16, kv_dtype=FP8,
+             plant_per_seq=8, plant_add=1.0, **kw)
+    w.recipe = ("8 seqs x 262144 tokens (256K, batch 8), 64 q heads / 4 groups, D=Di=128, "
+                "bf16 q, e4m3 K/V/index keys, N(0,1), 8 planted blocks per seq "
+                "(+1.0*sign(sum_g qI) before rounding), random permutation table")
+    return w
+
+
 def nvfp4_512k(seed: int = 0x4D5341 + 4, **kw) -> Workload:
     w = make("nvfp4_512k", seed=seed, seq_lens=[524288] * 4, q_dtype=BF16,
              kv_dtype=NVFP4, **kw)

@@ -177,6 +177,40 @@ def test_decode_equals_chain_and_is_deterministic():
         assert int(torch.count_nonzero(dw.ws_decode)) == 0, "workspace not left zero-filled"
 
 
+def test_decode_in_graph_replays_match_eager():
+    """msa_decode captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, reproduces the eager results bit for
+    bit and leaves the workspace zero-filled."""
+    w = synth.make("graph", seed=71, seq_lens=[20000, 9000, 300, 65536], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, plant_per_seq=2)
+    dw = parity.DeviceWorkload(w)
+    dw.decode(with_scores=True)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dw.scores, dw.topk, dw.out, dw.lse)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dw.decode(with_scores=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dw.decode(with_scores=True)
+    for rep in range(4):
+        say(f"[parity] graph replay {rep}")
+        dw.scores.zero_()
+        dw.topk.fill_(-7)
+        dw.out.zero_()
+        dw.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(ref, (dw.scores, dw.topk, dw.out, dw.lse)):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+        assert int(torch.count_nonzero(dw.ws_decode)) == 0
+
+
 def test_one_workspace_across_shapes():
     """msa_decode leaves its workspace zero-filled, so one workspace (zeroed
     once) serves calls of different shapes in any order."""
@@ -256,7 +290,7 @@ def test_decode_long_block_table_unfused_path():
 # full-size workloads (the benchmark's shapes and launch configuration)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["fp8_b32", "fp8_long", "nvfp4_512k"])
+@pytest.mark.parametrize("name", ["fp8_b32", "fp8_long", "fp8_256k", "nvfp4_512k"])
 def test_full_size(name):
     say(f"[parity] generating {name}")
     w = getattr(synth, name)()
