@@ -54,7 +54,6 @@ struct AttendArgs {
   const int32_t* qpos;
   const int32_t* topk;    // selection input (attend only)
   const float* scores;    // pooled scores (select + attend, written by an earlier kernel)
-  uint32_t* keys;         // pooled scores as order keys, 0 = not yet written (COHERENT)
   uint32_t* clear;        // SELECT: [units][MB] words the last reader zeroes (nullable)
   int32_t* topk_out;      // selection output (select + attend), may be null
   void* out;
@@ -63,8 +62,6 @@ struct AttendArgs {
   float scale_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
   int out_f32;
-  int spin_limit;   // COHERENT: polls of the keys before giving up
-  int32_t* error;   // COHERENT: set to 1 when a poll gives up
 };
 
 __device__ __forceinline__ void store_out(const AttendArgs& a, int row, int h, int d, float v) {
@@ -137,7 +134,6 @@ inline AttendArgs make_attend_args(const Shape& s, const int32_t* block_table,
   a.qpos = q_pos;
   a.topk = topk;
   a.scores = scores;
-  a.keys = nullptr;
   a.clear = nullptr;
   a.topk_out = topk_out;
   a.out = out;
@@ -152,8 +148,6 @@ inline AttendArgs make_attend_args(const Shape& s, const int32_t* block_table,
   a.scale_log2 = s.sm_scale * s.k_scale * 1.4426950408889634f;
   a.v_scale = s.v_scale;
   a.out_f32 = s.out_dtype == kF32;
-  a.spin_limit = 0;
-  a.error = nullptr;
   return a;
 }
 
@@ -189,12 +183,8 @@ __device__ __forceinline__ f32x2 coherent_load8(__amdgpu_buffer_rsrc_t r, uint32
   return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentAux));
 }
 
-__device__ __forceinline__ uint32_t coherent_load_u32(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Returns the unit's row of the scores (or keys) to 0 once every reader is
-// done with it, so that the workspace is left as the call found it.
+// Returns the unit's row of the scores to 0 once every reader is done with
+// it, so that the workspace is left as the call found it.
 __device__ __forceinline__ void clear_row(const AttendArgs& a, int u, int nw) {
   uint32_t* row = a.clear + (size_t)u * a.MB;
   for (int jj = threadIdx.x; jj < a.MB; jj += 64 * nw) row[jj] = 0u;
@@ -202,10 +192,9 @@ __device__ __forceinline__ void clear_row(const AttendArgs& a, int u, int nw) {
 
 // One attention task: (row, group) unit u, split `split` of part.S, run by
 // the calling workgroup of NW waves.  sel_lds: the dynamic LDS of a SELECT
-// kernel.  COHERENT: the pooled scores were written during the same kernel
-// and are read with device-scope loads.  Returns early (all threads of the
-// workgroup together) where it has nothing more to do.
-template <int KV, int NW, bool SELECT, bool COHERENT>
+// kernel.  Returns early (all threads of the workgroup together) where it
+// has nothing more to do.
+template <int KV, int NW, bool SELECT>
 __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
                                             const uint8_t* __restrict__ kvd,
                                             const uint8_t* __restrict__ kvs, const AttendArgs& a,
@@ -247,56 +236,24 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     int32_t* btl = reinterpret_cast<int32_t*>(keys + a.MB);
     const int32_t* brow = a.bt + (size_t)b * a.MB;
     uint64_t best = kNoCand;
-    if constexpr (COHERENT) {
-      // The keys of blocks 0..rb are written by other workgroups of the same
-      // kernel, each exactly once and never as 0: poll until none is 0.
-      for (int jj = threadIdx.x; jj < a.MB; jj += 64 * NW) btl[jj] = brow[jj];
-      const uint32_t* krow = a.keys + (size_t)u * a.MB;
-      for (int spin = 0;; ++spin) {
-        best = kNoCand;
-        bool missing = false;
-        for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
-          uint32_t v[8];
+    const float* srow = a.scores + (size_t)u * a.MB;
+    for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
+      float v[8];
+      int32_t e[8];
 #pragma unroll
-          for (int r = 0; r < 8; ++r)
-            v[r] = coherent_load_u32(krow + min(base + r * 64 * NW + (int)threadIdx.x, a.MB - 1));
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int jj = base + r * 64 * NW + (int)threadIdx.x;
-            if (jj < a.MB) {
-              keys[jj] = v[r];
-              missing |= jj <= rb && v[r] == 0u;
-              if (jj < rb) best = max(best, pack_cand(v[r], jj));
-            }
-          }
-        }
-        if (!__syncthreads_or(missing)) break;
-        if (spin >= a.spin_limit) {  // never reached when the keys were zero at entry
-          if (threadIdx.x == 0) __hip_atomic_store(a.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(16);
+      for (int r = 0; r < 8; ++r) {
+        const int jj = min(base + r * 64 * NW + (int)threadIdx.x, a.MB - 1);
+        v[r] = srow[jj];
+        e[r] = brow[jj];
       }
-    } else {
-      const float* srow = a.scores + (size_t)u * a.MB;
-      for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
-        float v[8];
-        int32_t e[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int jj = min(base + r * 64 * NW + (int)threadIdx.x, a.MB - 1);
-          v[r] = srow[jj];
-          e[r] = brow[jj];
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int jj = base + r * 64 * NW + (int)threadIdx.x;
-          if (jj < a.MB) {
-            const uint32_t k = order_key(v[r]);
-            keys[jj] = k;
-            btl[jj] = e[r];
-            if (jj < rb) best = max(best, pack_cand(k, jj));
-          }
+      for (int r = 0; r < 8; ++r) {
+        const int jj = base + r * 64 * NW + (int)threadIdx.x;
+        if (jj < a.MB) {
+          const uint32_t k = order_key(v[r]);
+          keys[jj] = k;
+          btl[jj] = e[r];
+          if (jj < rb) best = max(best, pack_cand(k, jj));
         }
       }
     }

@@ -58,20 +58,7 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
                                 void* workspace, bool counters_zeroed, float* clear_scores,
                                 hipStream_t st);
-// The whole decode step in one persistent kernel (decode_fused.hip).  keys:
-// rows*G*MB words and header: 2 words (ticket, error flag) of workspace, zero
-// at entry and left zero; block_scores (nullable) receives the pooled scores.
-constexpr size_t kFusedMaxLds = 56 * 1024;  // dynamic LDS the fused kernel may use
-constexpr int kFusedSpinLimit = 1 << 20;    // polls (about 1 us each) before giving up
-bool fused_decode_supported(const Shape& s);
-size_t fused_lds_bytes(const Shape& s);
-hipError_t launch_decode_fused(const Shape& s, const void* index_q, const void* ik_data,
-                               const void* ik_scales, const void* q, const void* kv_data,
-                               const void* kv_scales, const int32_t* block_table,
-                               const int32_t* seq_lens, const int32_t* q_pos,
-                               float* block_scores, uint32_t* keys, int32_t* topk_out,
-                               void* out, float* lse, void* attend_ws, int32_t* header,
-                               hipStream_t st);
+// Clears bytes (a multiple of 4) with a fill kernel.
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 
 // Offset (bytes) of the arrival counters inside the attention workspace.
