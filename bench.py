@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_256k",
-                    choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k"])
+                    choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "prefill_64k"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,6 +118,8 @@ def main():
     t0 = time.time()
     w = getattr(synth, args.workload)()
     log(f"[bench] generated {w.name} in {time.time() - t0:.1f}s: {w.recipe}")
+    if w.rows_per_seq > 1:
+        return run_prefill(args, w)
 
     dws = [parity.DeviceWorkload(w)]
     for _ in range(1, args.layers):
@@ -267,6 +269,80 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "index_mfma_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name), "bytes_per_launch": b_idx},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_prefill(args, w):
+    """Chunked prefill (many query rows per sequence): one step = one
+    msa_decode call over all rows; the dominant kernel is the MFMA index
+    contraction, reported against the bf16 dense MFMA peak."""
+    import numpy as np
+    import torch
+
+    from tests import parity
+
+    PEAK_BF16_TFLOPS = 2500.0
+    dw = parity.DeviceWorkload(w)
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup)):
+        dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        dw.index_scores()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    idx_us = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    # algorithmic flops of the index contraction: every row against its
+    # visible keys, G groups x 128 dims, multiply + add
+    seen = np.array([parity.row_pos(w, r) + 1 for r in range(w.rows)], np.int64).clip(0)
+    flops = 2.0 * 128 * w.num_groups * float(seen.sum())
+    achieved = flops / (idx_us * 1e-6) / 1e12
+    log(f"[bench] prefill ms/step {ms_step:.4f}; index contraction {idx_us:.1f} us "
+        f"({achieved:.0f} TFLOP/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        sample = list(range(0, w.rows, max(1, w.rows // 64)))[:64]
+        ws = parity.subset_rows(w, sample)
+        p = parity.oracle_problem(ws, threads)
+        reps, t_c0 = 0, time.perf_counter()
+        while True:
+            oracle.decode(p, ws.index_q, ws.ik_data, ws.ik_scales, ws.q, ws.kv_data,
+                          ws.kv_scales, ws.block_table, ws.seq_lens, ws.q_pos)
+            reps += 1
+            if time.perf_counter() - t_c0 >= args.cpu_seconds:
+                break
+        t_c = time.perf_counter() - t_c0
+        cpu = {"value": reps * len(sample) / t_c, "unit": "rows/s",
+               "cores": oracle.threads_used(), "kind": "oracle",
+               "sample": f"{reps} pass(es) over {len(sample)} of the {w.rows} rows (every "
+                         f"{max(1, w.rows // 64)}th), fp64, in {t_c:.1f}s"}
+    out = {
+        "metric": "MSA chunked-prefill query rows/s (indexer QK^T on MFMA + per-row top-k + "
+                  "sparse attention)",
+        "value": w.rows / (ms_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "recipe": w.recipe, "rows": w.rows,
+                   "context_tokens": int(w.seq_lens.sum()), "kv_groups": w.num_groups,
+                   "q_heads": w.num_q_heads, "top_k": w.top_k},
+        "kernel_us": {"index_contraction": idx_us,
+                      "select_attend_and_gaps": ms_step * 1e3 - idx_us},
+        "roofline": {"bound": "mfma", "kernel": "prefill_index_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
-SOURCES = ["api.cpp", "index_scores.hip", "block_topk.hip", "sparse_attend.hip"]
+SOURCES = ["api.cpp", "index_scores.hip", "block_topk.hip", "sparse_attend.hip",
+           "prefill_index.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -152,6 +152,14 @@ hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* 
                                const void* ik_scales, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* q_pos,
                                float* scores, hipStream_t st, int32_t* zero, int n_zero) {
+  if (prefill_index_supported(s)) {
+    if (zero && n_zero > 0) {
+      const hipError_t e = launch_zero_fill(zero, (size_t)n_zero * sizeof(int32_t), st);
+      if (e != hipSuccess) return e;
+    }
+    return launch_prefill_index_scores(s, index_q, ik_data, block_table, seq_lens, q_pos,
+                                       scores, st);
+  }
   switch (s.G) {
     case 1: return launch_g<1>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
     case 2: return launch_g<2>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);

@@ -1,0 +1,197 @@
+// prefill_index.hip -- indexer scores + block max-pool for many query rows
+// per sequence (chunked prefill, speculative decode) as a dense MFMA
+// contraction.
+//
+// Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
+// primer", and its list of MSA kernels, which names an indexer prefill
+// kernel): every query row r of a sequence scores the keys it can see (t <=
+// pos_r) with one index query per group, and the scores are max-pooled per
+// 128-token block.  With many rows per sequence this is the dense product
+// Q [rows*G x 128] . K^T [128 x tokens] with a causal mask, followed by a
+// per-block max: MFMA-bound, not HBM-bound, because every key serves every
+// row of its sequence.
+//
+// Work decomposition: a workgroup takes a tile of 256 consecutive (row,
+// group) columns of one sequence (wave w: columns 64w .. 64w+63 as four
+// 16-column MFMA tiles, held as B operands for the whole kernel) and a range
+// of 32 logical blocks.  Per block, the 256 threads stream its 16 KB of
+// e4m3 keys contiguously into registers (the next block's while the current
+// one computes), then into LDS with the 16-byte chunks swizzled (chunk c of
+// token t at slot c ^ (t % 8), free of bank conflicts both ways); each wave
+// then runs S^T = K Q^T on v_mfma_f32_16x16x32_bf16 for its 64 columns over
+// the block's 8 tiles of 16 tokens, keeping a masked running max per column.
+// The per-block maxima gather in LDS and leave as 128-byte runs per column.
+//
+// Arithmetic: e4m3 keys convert exactly to bf16; products with the bf16
+// index queries are exact and accumulate in fp32.  Blocks past a row's last
+// visible key, and table entries outside the pool, give -inf.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace msa {
+
+constexpr int kCols = 256;   // (row, group) columns per workgroup
+constexpr int kRange = 32;   // logical blocks per workgroup
+
+struct PrefillArgs {
+  const uint16_t* iq;  // [rows][G][128] bf16
+  const uint8_t* ik;   // [P][128][128] e4m3
+  const int32_t* bt;
+  const int32_t* lens;
+  const int32_t* qpos;
+  float* scores;  // [rows][G][MB]
+  int R, G, MB, P;
+  int tiles_per_seq;  // ceil(R*G / kCols)
+  float out_scale;
+};
+
+__global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
+  __shared__ uint4 stage[2][kBlock * kDim / 16];  // two 16 KB key blocks, swizzled
+  __shared__ float smax[kCols][kRange + 1];       // per-column block maxima (+1: no bank conflicts)
+  __shared__ int s_pos_max;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int b = blockIdx.x / x.tiles_per_seq, tile = blockIdx.x % x.tiles_per_seq;
+  const int seq_cols = x.R * x.G;
+  const int col0 = tile * kCols;  // first column of the tile within the sequence
+  const int ncols = min(kCols, seq_cols - col0);
+  const int j0 = blockIdx.y * kRange, j1 = min(x.MB, j0 + kRange);
+  const int n = lane & 15, r = lane >> 4;
+
+  // ---- B operands and visibility of this lane's four columns ----
+  bf16x8 qb[4][4];
+  int cpos[4];
+  int pos_lo = 0x7FFFFFFF, pos_hi = -1;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = 64 * wave + 16 * t + n;  // column within the tile
+    const bool valid = c < ncols;
+    const int flat = b * seq_cols + col0 + c;  // (row, group) index
+    const int row = flat / x.G;
+    cpos[t] = valid ? row_last_key(x.lens, x.qpos, row, b, x.MB) : -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = 16 * r + 64 * (k >> 1) + 8 * (k & 1);
+      qb[t][k] = valid ? *reinterpret_cast<const bf16x8*>(x.iq + (size_t)flat * kDim + d)
+                       : bf16x8{};
+    }
+    if (valid) {
+      pos_lo = min(pos_lo, cpos[t]);
+      pos_hi = max(pos_hi, cpos[t]);
+    }
+  }
+  // wave-uniform bounds: every column of the wave sees keys <= wave_lo; none
+  // sees keys > wave_hi
+  int wave_lo = pos_lo, wave_hi = pos_hi;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    wave_lo = min(wave_lo, __shfl_xor(wave_lo, o, 64));
+    wave_hi = max(wave_hi, __shfl_xor(wave_hi, o, 64));
+  }
+  if (threadIdx.x == 0) s_pos_max = -1;
+  for (int i = threadIdx.x; i < kCols * (kRange + 1); i += 256) (&smax[0][0])[i] = -INFINITY;
+  __syncthreads();
+  if (lane == 0) atomicMax(&s_pos_max, wave_hi);
+  __syncthreads();
+  // blocks this workgroup computes: [j0, jend)
+  const int jend = min(j1, s_pos_max < 0 ? j0 : s_pos_max / kBlock + 1);
+
+  // ---- stream the blocks: registers -> LDS (swizzled) -> MFMA ----
+  const int32_t* brow = x.bt + (size_t)b * x.MB;
+  auto issue = [&](int j, uint4 (&raw)[4]) {
+    const int e = brow[j];
+    const int pb = e >= 0 && e < x.P ? e : 0;  // invalid entries are masked below
+    const uint4* src = reinterpret_cast<const uint4*>(x.ik + (size_t)pb * (kBlock * kDim));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = load_stream(src + i * 256 + threadIdx.x);
+  };
+  uint4 raw[4];
+  if (j0 < jend) issue(j0, raw);
+  for (int j = j0; j < jend; ++j) {
+    const int st = (j - j0) & 1;
+    // thread t holds chunk t%8 of tokens 32i + t/8; chunk c of token k at slot c ^ (k%8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 32 * i + ((int)threadIdx.x >> 3);
+      stage[st][tok * 8 + (((int)threadIdx.x & 7) ^ (tok & 7))] = raw[i];
+    }
+    __syncthreads();  // the stage is written; the other stage's readers are done
+    if (j + 1 < jend) issue(j + 1, raw);
+    const int e = brow[j];
+    if (e < 0 || e >= x.P) continue;  // invalid table entry: the block stays -inf
+    if (j * kBlock > wave_hi) continue;  // no column of this wave sees the block
+    const bool full = j * kBlock + kBlock - 1 <= wave_lo;
+    f32x4 m[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 2
+    for (int u = 0; u < 8; ++u) {
+      const int tok = 16 * u + n;
+      const uint4 v0 = stage[st][tok * 8 + (r ^ (n & 7))];
+      const uint4 v1 = stage[st][tok * 8 + ((r + 4) ^ (n & 7))];
+      const bf16x8 a0 = fp8x8_bf16(v0.x, v0.y), a1 = fp8x8_bf16(v0.z, v0.w);
+      const bf16x8 a2 = fp8x8_bf16(v1.x, v1.y), a3 = fp8x8_bf16(v1.z, v1.w);
+      const int key0 = j * kBlock + 16 * u + 4 * r;  // D rows 4r + i: keys key0 + i
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mfma_bf16(a0, qb[t][0], acc);
+        acc = mfma_bf16(a1, qb[t][1], acc);
+        acc = mfma_bf16(a2, qb[t][2], acc);
+        acc = mfma_bf16(a3, qb[t][3], acc);
+        if (full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[t][i] = fmaxf(m[t][i], acc[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            m[t][i] = key0 + i <= cpos[t] ? fmaxf(m[t][i], acc[i]) : m[t][i];
+        }
+      }
+    }
+    // max over the lane's 4 keys and the 4 lane groups: lanes 0..15 keep
+    // column 16t + n's block maximum
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float v = fmaxf(fmaxf(m[t][0], m[t][1]), fmaxf(m[t][2], m[t][3]));
+      v = fmaxf(v, lane_xor_f<16>(v));
+      v = fmaxf(v, lane_xor_f<32>(v));
+      if (r == 0) smax[64 * wave + 16 * t + n][j - j0] = v * x.out_scale;
+    }
+  }
+  __syncthreads();
+  // ---- column c's blocks [j0, j1): one contiguous run each ----
+  const int c = threadIdx.x;
+  if (c < ncols) {
+    float* dst = x.scores + (size_t)(b * seq_cols + col0 + c) * x.MB + j0;
+    for (int k = 0; k < j1 - j0; ++k) dst[k] = smax[c][k];
+  }
+}
+
+bool prefill_index_supported(const Shape& s) {
+  return s.ik_dtype == kFP8 && s.R >= 16;
+}
+
+hipError_t launch_prefill_index_scores(const Shape& s, const void* index_q, const void* ik_data,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* q_pos, float* scores, hipStream_t st) {
+  PrefillArgs x;
+  x.iq = static_cast<const uint16_t*>(index_q);
+  x.ik = static_cast<const uint8_t*>(ik_data);
+  x.bt = block_table;
+  x.lens = seq_lens;
+  x.qpos = q_pos;
+  x.scores = scores;
+  x.R = s.R;
+  x.G = s.G;
+  x.MB = s.MB;
+  x.P = s.P;
+  x.tiles_per_seq = (s.R * s.G + kCols - 1) / kCols;
+  x.out_scale = s.index_scale * s.ik_scale;
+  const int nseq = s.rows / s.R;
+  const dim3 grid((unsigned)(nseq * x.tiles_per_seq), (unsigned)((s.MB + kRange - 1) / kRange));
+  if (grid.x == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_index_kernel, grid, dim3(256), 0, st, x);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -394,6 +394,17 @@ def fp8_256k(seed: int = 0x4D5341 + 5, **kw) -> Workload:
     return w
 
 
+def prefill_64k(seed: int = 0x4D5341 + 6, **kw) -> Workload:
+    cached, chunk = 65536, 4096
+    w = make("prefill_64k", seed=seed, seq_lens=[cached + chunk], rows_per_seq=chunk,
+             q_pos=np.arange(cached, cached + chunk, dtype=np.int32), q_dtype=BF16,
+             kv_dtype=FP8, **kw)
+    w.recipe = ("chunked prefill: 1 seq, 65536 cached tokens + a 4096-query chunk at "
+                "positions 65536..69631, causal; 64 q heads / 4 groups, D=Di=128, bf16 q, "
+                "e4m3 K/V/index keys, N(0,1), random permutation table")
+    return w
+
+
 def nvfp4_512k(seed: int = 0x4D5341 + 4, **kw) -> Workload:
     w = make("nvfp4_512k", seed=seed, seq_lens=[524288] * 4, q_dtype=BF16,
              kv_dtype=NVFP4, **kw)

@@ -41,6 +41,18 @@ def oracle_problem(w: synth.Workload, threads: int = 0):
     return oracle.Problem(**w.problem_fields(), num_threads=threads)
 
 
+def subset_rows(w: synth.Workload, rows) -> synth.Workload:
+    """The same caches with only the given query rows of a one-sequence,
+    many-row workload: the oracle's share of a sampled comparison."""
+    import dataclasses
+    assert w.num_seqs == 1 and w.q_pos is not None
+    idx = np.asarray(rows, np.int64)
+    return dataclasses.replace(
+        w, name=w.name + "-sample", rows_per_seq=len(idx),
+        index_q=np.ascontiguousarray(w.index_q[idx]), q=np.ascontiguousarray(w.q[idx]),
+        q_pos=np.ascontiguousarray(w.q_pos[idx]))
+
+
 def dev(a: np.ndarray | None, device="cuda"):
     if a is None:
         return None
@@ -128,6 +140,14 @@ def index_keys_abs(w: synth.Workload, pblocks: np.ndarray) -> np.ndarray:
     return np.abs(v) * np.float32(w.index_k_scale)
 
 
+def row_pos(w: synth.Workload, r: int) -> int:
+    """The last key row r sees: its position clamped to the sequence and to
+    the block table's reach (negative: none)."""
+    b = r // w.rows_per_seq
+    last = min(int(w.seq_lens[b]), w.max_blocks * w.block_size) - 1
+    return min(int(w.q_pos[r]), last) if w.q_pos is not None else last
+
+
 def score_bound(w: synth.Workload) -> np.ndarray:
     """1e-5-relative error bound per (row, group, block)."""
     rows, G, MB, BS = w.rows, w.num_groups, w.max_blocks, w.block_size
@@ -135,8 +155,8 @@ def score_bound(w: synth.Workload) -> np.ndarray:
     iq = np.abs(_f32_of(w.index_q, w.index_q_dtype))  # [rows, G, Di]
     for r in range(rows):
         b = r // w.rows_per_seq
-        pos = int(w.q_pos[r]) if w.q_pos is not None else int(w.seq_lens[b]) - 1
-        nb = pos // BS + 1
+        pos = row_pos(w, r)
+        nb = pos // BS + 1 if pos >= 0 else 0
         for j0 in range(0, nb, 512):
             j1 = min(nb, j0 + 512)
             k = index_keys_abs(w, w.block_table[b, j0:j1])  # [n, BS, Di]
@@ -170,8 +190,7 @@ def selection_matches(w, ref_scores, ref_sel, got_sel, row, g) -> bool:
     assert bsel == sorted(bsel), "selection not ascending"
     if a == bsel:
         return True
-    b = row // w.rows_per_seq
-    pos = int(w.q_pos[row]) if w.q_pos is not None else int(w.seq_lens[b]) - 1
+    pos = row_pos(w, row)
     rb = pos // w.block_size
     assert rb in bsel and len(bsel) == len(a), f"row {row} group {g}: {bsel} vs {a}"
     s = ref_scores[row, g].astype(np.float64)

@@ -287,6 +287,58 @@ def test_decode_long_block_table_unfused_path():
 
 
 # ---------------------------------------------------------------------------
+# many query rows per sequence (chunked prefill): the MFMA form of the scan
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,H", [(4, 64), (8, 64), (1, 16)])
+def test_prefill_chunk(G, H):
+    """A causal chunk of R = 80 rows ending at each sequence's last key: more
+    columns than one tile (G >= 4), more blocks than one block range, ragged
+    lengths."""
+    R = 80
+    lens = np.array([5000, 9003])
+    qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
+    w = synth.make(f"prefill-g{G}", seed=91 + G, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                   num_q_heads=H, num_groups=G, q_dtype=synth.BF16, kv_dtype=synth.FP8,
+                   plant_per_seq=3)
+    _run_and_check(w, fused=True, name=f"prefill-g{G}")
+    _run_and_check(w, fused=False, name=f"prefill-g{G}-chain")
+
+
+def test_prefill_scattered_positions():
+    """Rows anywhere in the sequence, including ones that see no key or one
+    key, block edges and a row past the sequence's end (clamped)."""
+    qp = np.array([-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 2900,
+                   2998, 2999, 5000, 40, 300, 1700, 3, 64, 2222, 2500], np.int32)
+    w = synth.make("prefill-scatter", seed=97, seq_lens=[3000], rows_per_seq=len(qp),
+                   q_pos=qp, q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=2)
+    _run_and_check(w, fused=True, name="prefill-scatter")
+
+
+def test_prefill_64k_sampled_rows():
+    """The full chunked-prefill shape (65536 cached + 4096 queries, causal),
+    all rows on the GPU; the oracle computes a sample of rows one by one."""
+    say("[parity] generating prefill_64k")
+    w = synth.prefill_64k()
+    dw = parity.DeviceWorkload(w)
+    say("[parity] prefill_64k: GPU msa_decode over 4096 rows")
+    dw.decode()
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 1000, 2047, 2048, 3333, 4094, 4095]
+    ws = parity.subset_rows(w, rows)
+    say(f"[parity] prefill_64k: oracle on rows {rows}")
+    s_ref, k_ref, o_ref, l_ref = _oracle_all(ws)
+    s = dw.scores.cpu().numpy()[rows]
+    k = dw.topk.cpu().numpy()[rows]
+    o = dw.out.float().cpu().numpy()[rows]
+    serr = parity.check_scores(ws, s, s_ref)
+    same = parity.check_selection(ws, s_ref, k_ref, k)
+    aerr = parity.check_attention(ws, o, o_ref, mask=same)
+    say(f"[parity] prefill_64k: score err {serr:.3f} of bound, {int(same.sum())}/{same.size} "
+        f"selections identical, attention max-abs {aerr:.2e}")
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads (the benchmark's shapes and launch configuration)
 # ---------------------------------------------------------------------------
 
