@@ -55,21 +55,18 @@ msa::Shape shape_of(const msa_problem* p) {
 }
 
 struct WsLayout {
-  size_t header, scores, attend, total;
+  size_t scores, attend, total;
 };
 
 // Device scratch: msa_sparse_attend needs room for the split-K partial
 // states when it splits a (row, group) over several workgroups; msa_decode
-// needs a 256-byte header (the fused kernel's task ticket and error flag),
-// the pooled scores (as order keys for the fused kernel) and that.
+// needs the pooled scores before that.
 WsLayout ws_layout(const msa_problem* p, int op) {
   WsLayout w{};
   if (op != kOpAttend && op != kOpDecode) return w;
   const msa::Shape s = shape_of(p);
   size_t off = 0;
   if (op == kOpDecode) {
-    w.header = off;
-    off += kAlign;
     w.scores = off;
     off += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
   }
@@ -297,19 +294,13 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
   float* ws_scores = block_scores ? nullptr : scores;  // cleared again after use
   if (msa::select_fusable(s)) {
-    // two launches: the index scan (which also clears the attention kernel's
-    // arrival counters), then selection + attention in one kernel
-    const msa::AttendConfig c = msa::attend_config(s);
-    int32_t* counters = c.splits > 1 ? reinterpret_cast<int32_t*>(
-                                           static_cast<char*>(aws) + msa::attend_counter_offset(s, c))
-                                     : nullptr;
+    // two launches: the index scan, then selection + attention in one kernel
     st = hip_status(msa::launch_index_scores(s, index_q, ik_data, ik_scales, block_table,
-                                             seq_lens, q_pos, scores, hs, counters,
-                                             counters ? s.rows * s.G : 0),
+                                             seq_lens, q_pos, scores, hs),
                     "index scores launch");
     if (st != MSA_OK) return st;
     return hip_status(msa::launch_select_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
-                                                q_pos, scores, topk_idx, out, lse, aws, true,
+                                                q_pos, scores, topk_idx, out, lse, aws,
                                                 ws_scores, hs),
                       "select + attend launch");
   }

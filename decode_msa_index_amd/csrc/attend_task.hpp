@@ -102,24 +102,25 @@ __device__ __forceinline__ float rescale(float x, float m) {
 // Grid: (row, group) x S splits; a workgroup of NW waves takes a contiguous
 // share of the row's selection entries and wave w of it takes every NW-th
 // entry of that share.  With SELECT the workgroup first makes the group's
-// selection itself from the pooled scores (wave 0, select_wave.hpp; every
-// split recomputes it, which costs no extra latency) and split 0 also
-// stores it.  For each block a wave computes S^T = K Q^T on MFMA, updates
-// its running max / denominator (online softmax, fp32) and accumulates P V
-// on MFMA into the rescaled running output.  The NW states of a workgroup
-// merge pairwise through LDS.  With S = 1 the workgroup writes the
-// normalised output; otherwise it publishes its state with coherent
-// (device-scope) stores, and the last of the S workgroups to arrive -- a
-// device-scope counter per (row, group) -- merges the S states and writes the
-// output.  No cache write-back fence is needed: every value another
-// workgroup reads is written and read with device-scope atomic accesses.
+// selection itself from the pooled scores (select_wave.hpp; every split
+// recomputes it, which costs no extra latency) and split 0 also stores it.
+// For each block a wave computes S^T = K Q^T on MFMA, updates its running
+// max / denominator (online softmax, fp32) and accumulates P V on MFMA into
+// the rescaled running output.  The NW states then meet in LDS, where wave w
+// combines a 1/NW slice of the head dims for all heads.  With S = 1 each
+// wave normalises and stores its slice.  With S > 1, splits 0 .. S-2 store
+// their combined states with device-scope stores and leave; split S-1 (the
+// highest workgroup id of the unit, so the other splits are already
+// dispatched when it runs) polls for those states -- each word is encoded so
+// that zero means "not yet written" -- merges them into its own and stores
+// the output.  The launch makes sure all workgroups of the grid can be
+// resident at once.
 // Running state layout per lane l: max and denominator of head l%16; output
 // rows (heads) 4*(l/16)+i, columns (dims) 16*dt + l%16.
 // ---------------------------------------------------------------------------
 struct Partials {
-  float* o;          // [rows*G][S][16][128] unnormalised outputs
-  float* ml;         // [rows*G][S][16][2]   running max (log2 domain) and denominator
-  int32_t* counters; // [rows*G] arrivals, zero before the launch; reset by the merger
+  float* o;   // [rows*G][S][8 dim tiles][64 lanes][4]: unnormalised outputs, lane-major
+  float* ml;  // [rows*G][S][16 heads][2]: running max (log2 domain) and denominator
   int S;
 };
 
@@ -152,36 +153,54 @@ inline AttendArgs make_attend_args(const Shape& s, const int32_t* block_table,
 }
 
 // Split-K scratch inside the attention workspace (attend_workspace_bytes):
-// [ml: units*S*16*2][o: units*S*16*128] floats, then [units] arrival counters.
+// [ml: units*S*16*2][o: units*S*16*128] floats.  Zero before a launch, and
+// zero again after it (the merging workgroup clears what it read).
 inline Partials make_partials(const Shape& s, const AttendConfig& c, void* workspace) {
   const size_t units = (size_t)s.rows * s.G;
   Partials part;
   part.S = c.splits;
   part.ml = static_cast<float*>(workspace);
   part.o = part.ml + units * c.splits * kHeadsPad * 2;
-  part.counters = reinterpret_cast<int32_t*>(part.o + units * c.splits * kHeadsPad * kDim);
   return part;
 }
 
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Device-scope (sc1) vector loads through a buffer resource over [base,
-// base + bytes): data another workgroup of the same kernel wrote with
-// device-scope stores.
+// Device-scope (sc1) 16-byte accesses through a buffer resource over [base,
+// base + bytes): stores that write through to the device's coherence point
+// and loads that read from it, for data other workgroups of the same kernel
+// exchange while it runs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 constexpr int kCoherentAux = 16;  // cache policy: sc1
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAux));
 }
-__device__ __forceinline__ f32x2 coherent_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentAux));
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCoherentAux);
 }
+
+// Partial states travel with every 32-bit word stored as bits ^ kPartialXor.
+// The pattern kPartialXor itself (a NaN whose low 16 mantissa bits are set)
+// never occurs: this arithmetic makes NaNs only from bf16, fp8 or fp4
+// operands and from invalid operations, and all of those have zero low
+// bits.  So an encoded word is never 0, and a reader that polls zero-filled
+// memory knows each word it sees non-zero is complete -- no flag, fence or
+// counter is needed.
+constexpr uint32_t kPartialXor = 0x7FFFFFFFu;
+__device__ __forceinline__ f32x4 encode_partial(f32x4 v) {
+  u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+  w ^= kPartialXor;
+  return __builtin_bit_cast(f32x4, w);
+}
+__device__ __forceinline__ f32x4 decode_partial(f32x4 v) { return encode_partial(v); }
+__device__ __forceinline__ bool all_landed(f32x4 v) {
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+  return w.x != 0u && w.y != 0u && w.z != 0u && w.w != 0u;
+}
+// Polls of one batch of partials before the merger gives up (each poll is a
+// device-memory round trip, about a microsecond).
+constexpr int kSpinLimit = 1 << 20;
 
 // Returns the unit's row of the scores to 0 once every reader is done with
 // it, so that the workspace is left as the call found it.
@@ -200,10 +219,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
                                             const uint8_t* __restrict__ kvs, const AttendArgs& a,
                                             const Partials& part, int u, int split,
                                             uint32_t* sel_lds) {
-  __shared__ float red_o[NW > 1 ? NW / 2 : 1][32][64];
-  __shared__ float red_ml[NW > 1 ? NW / 2 : 1][2][16];
   __shared__ int32_t sel_w[SELECT ? NW : 1][32];  // SELECT: each wave's copy of the selection
-  __shared__ int is_last;
   // sel_lds (SELECT): [256] scratch, [MB] keys, [MB] table row
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int row = u / a.G, g = u % a.G, b = row / a.R;
@@ -230,12 +246,12 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
   if constexpr (SELECT) {
     // every thread loads a share of the row's scores (as order keys) and of
     // its block-table entries, in one round that does not wait for the row
-    // length, and keeps its best candidate; the workgroup then selects
+    // length, and keeps its largest key; the workgroup then selects
     __shared__ GroupSelectLds<NW> gsl;
     uint32_t* keys = sel_lds + 256;
     int32_t* btl = reinterpret_cast<int32_t*>(keys + a.MB);
     const int32_t* brow = a.bt + (size_t)b * a.MB;
-    uint64_t best = kNoCand;
+    uint32_t tmax = 0u;
     const float* srow = a.scores + (size_t)u * a.MB;
     for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
       float v[8];
@@ -253,14 +269,16 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
           const uint32_t k = order_key(v[r]);
           keys[jj] = k;
           btl[jj] = e[r];
-          if (jj < rb) best = max(best, pack_cand(k, jj));
+          if (jj < rb) tmax = max(tmax, k);
         }
       }
     }
-    group_select<NW>(keys, rb, a.K, best, gsl, sel_lds, sel_w[wave]);
+    group_select<NW>(keys, rb, a.K, tmax, gsl, sel_lds, sel_w[wave]);
     if (a.clear && part.S == 1) clear_row(a, u, NW);
-    if (split == 0 && wave == 0 && a.topk_out && lane < a.K)
-      a.topk_out[(size_t)u * a.K + lane] = sel_w[0][lane];
+    if (split == 0 && wave == 0 && a.topk_out) {  // the stored selection ascends
+      const int v = sort_selection(lane < a.K ? sel_w[0][lane] : -1, a.K);
+      if (lane < a.K) a.topk_out[(size_t)u * a.K + lane] = v;
+    }
   }
 
   float M = -INFINITY, Lr = 0.0f;
@@ -406,155 +424,184 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
   }
 
-  // ---- merge the waves' states pairwise through LDS ----
+  // ---- combine the NW waves' states: each wave stores its state in LDS,
+  // then wave w combines dims [16 w DTW, +16 DTW) of all heads ----
+  constexpr int DTW = 8 / NW;  // 16-dim tiles per wave after the combine
+  f32x4 co[DTW];               // combined output: heads 4qd+i, dims 16 d + n
+  float cm[4], cl[4];          // combined max (log2 domain) and denominator of heads 4qd+i
+  if constexpr (NW == 1) {
 #pragma unroll
-  for (int half = NW / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
-      const int slot = wave - half;
-      if (qd == 0) {
-        red_ml[slot][0][n] = M;
-        red_ml[slot][1][n] = Lr;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red_o[slot][dt * 4 + i][lane] = oacc[dt][i];
-      }
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float Mb = red_ml[wave][0][n], Lb = red_ml[wave][1][n];
-      const float Mn = fmaxf(M, Mb);
-      const float fa = rescale(M, Mn), fb = rescale(Mb, Mn);
-      Lr = Lr * fa + Lb * fb;
-      M = Mn;
-      float fa_o[4], fb_o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa_o[i] = __shfl(fa, 4 * qd + i, 64);
-        fb_o[i] = __shfl(fb, 4 * qd + i, 64);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          oacc[dt][i] = oacc[dt][i] * fa_o[i] + red_o[wave][dt * 4 + i][lane] * fb_o[i];
-      }
-    }
-    __syncthreads();
-  }
-
-  if (part.S == 1) {
-    if (wave != 0) return;
-    float inv_o[4];
-    const float inv = Lr > 0.0f ? a.v_scale / Lr : 0.0f;  // no visible key: zeros
-#pragma unroll
-    for (int i = 0; i < 4; ++i) inv_o[i] = __shfl(inv, 4 * qd + i, 64);
+    for (int d = 0; d < DTW; ++d) co[d] = oacc[d];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * qd + i;
-      if (h < a.hpg) {
+      cm[i] = __shfl(M, 4 * qd + i, 64);
+      cl[i] = __shfl(Lr, 4 * qd + i, 64);
+    }
+  } else {
+    __shared__ f32x4 st_o[NW][8][64];
+    __shared__ f32x2 st_ml[NW][kHeadsPad];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          store_out(a, row, g * a.hpg + h, dt * 16 + n, oacc[dt][i] * inv_o[i]);
+    for (int dt = 0; dt < 8; ++dt) st_o[wave][dt][lane] = oacc[dt];
+    if (qd == 0) st_ml[wave][n] = f32x2{M, Lr};
+    __syncthreads();
+    float f[NW][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cm[i] = -INFINITY;
+    float l[NW][4];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 ml = st_ml[v][4 * qd + i];
+        f[v][i] = ml[0];
+        l[v][i] = ml[1];
+        cm[i] = fmaxf(cm[i], ml[0]);
       }
     }
-    if (a.lse && qd == 0 && n < a.hpg)
-      a.lse[(size_t)row * a.H + (size_t)g * a.hpg + n] =
-          Lr > 0.0f ? (M + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cl[i] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[v][i] = rescale(f[v][i], cm[i]);
+        cl[i] += f[v][i] * l[v][i];
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DTW; ++d) {
+      co[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const f32x4 x = st_o[v][wave * DTW + d][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) co[d][i] += f[v][i] * x[i];
+      }
+    }
+  }
+  const int dt0 = wave * DTW;  // first 16-dim tile this wave holds
+
+  // ---- split-K across workgroups: splits 0 .. S-2 publish their states;
+  // split S-1 polls for them and merges ----
+  if (part.S > 1 && split < part.S - 1) {
+    // every word is stored as bits ^ kPartialXor, which is never 0 (see
+    // kPartialXor), so a reader sees 0 until the store has landed
+    const size_t pidx = (size_t)u * part.S + split;
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(part.o + pidx * (kHeadsPad * kDim),
+                                                    kHeadsPad * kDim * 4);
+#pragma unroll
+    for (int d = 0; d < DTW; ++d)
+      coherent_store16(ro, (uint32_t)(((dt0 + d) * 64 + lane) * 16), encode_partial(co[d]));
+    if (wave == 0 && n == 0) {  // lanes 0, 16, 32, 48: heads 4qd .. 4qd+3
+      const __amdgpu_buffer_rsrc_t rm = coherent_rsrc(part.ml + pidx * (kHeadsPad * 2),
+                                                      kHeadsPad * 2 * 4);
+      coherent_store16(rm, (uint32_t)(qd * 32),
+                       encode_partial(f32x4{cm[0], cl[0], cm[1], cl[1]}));
+      coherent_store16(rm, (uint32_t)(qd * 32 + 16),
+                       encode_partial(f32x4{cm[2], cl[2], cm[3], cl[3]}));
+    }
     return;
   }
-
-  // ---- split-K across workgroups: publish, count arrivals, last one merges ----
-  if (wave == 0) {
-    const size_t pidx = (size_t)u * part.S + split;
-    float* po = part.o + pidx * (kHeadsPad * kDim);
-    // lane-major: value (dt, i) of lane l at (4 dt + i) * 64 + l, so each
-    // store instruction writes 256 contiguous bytes
+  bool timed_out = false;
+  if (part.S > 1) {
+    // merge the other splits' partials, a batch at a time, into (co, cm, cl)
+    constexpr int CH = 128 / (4 * DTW + 8);  // partials whose words a batch holds
+    const size_t ubase = (size_t)u * part.S;
+    for (int sp0 = 0; sp0 < part.S - 1; sp0 += CH) {
+      f32x4 po[CH][DTW], pm[CH][2];
+      for (int tries = 0;; ++tries) {
+        // the loads below must be issued again on every pass: without this
+        // barrier the compiler may hoist them out of the loop
+        asm volatile("" ::: "memory");
+        bool ok = true;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+        for (int c = 0; c < CH; ++c) {
+          const int sp = sp0 + c;
+          if (sp < part.S - 1) {
+            const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(
+                part.o + (ubase + sp) * (kHeadsPad * kDim), kHeadsPad * kDim * 4);
+            const __amdgpu_buffer_rsrc_t rm = coherent_rsrc(
+                part.ml + (ubase + sp) * (kHeadsPad * 2), kHeadsPad * 2 * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) coherent_store(po + (4 * dt + i) * 64 + lane, oacc[dt][i]);
-    }
-    if (qd == 0) {
-      coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n, M);
-      coherent_store(part.ml + pidx * (kHeadsPad * 2) + 2 * n + 1, Lr);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
-    int prev = 0;
-    if (lane == 0)
-      prev = __hip_atomic_fetch_add(part.counters + u, 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0, 64);
-    if (lane == 0) is_last = prev == part.S - 1;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  // merge: thread t takes head h = t/16 and dims d0 = 8*(t%16) .. +8
-  // (looping when NW < 4).  Head h = 4*qd + i, dim 16*dt + n sits at
-  // (4 dt + i) * 64 + 16 qd + n in a partial, so the 8 dims are 32
-  // contiguous bytes: two 16-byte device-scope loads per partial, all issued
-  // before any is used.  Each thread then zeroes what it read (and the
-  // padded heads' entries), leaving the workspace as the call found it.
-  const size_t ubase = (size_t)u * part.S;
-  const __amdgpu_buffer_rsrc_t ro =
-      coherent_rsrc(part.o + ubase * (kHeadsPad * kDim), part.S * kHeadsPad * kDim * 4);
-  const __amdgpu_buffer_rsrc_t rm =
-      coherent_rsrc(part.ml + ubase * (kHeadsPad * 2), part.S * kHeadsPad * 2 * 4);
-  for (int t = threadIdx.x; t < kHeadsPad * 16; t += 64 * NW) {
-    const int h = t >> 4, d0 = (t & 15) * 8;
-    const int off = (4 * (d0 >> 4) + (h & 3)) * 64 + 16 * (h >> 2) + (d0 & 15);  // floats
-    float* po = part.o + ubase * (kHeadsPad * kDim) + off;
-    float* ml = part.ml + ubase * (kHeadsPad * 2) + 2 * h;
-    if (h < a.hpg) {
-      float pm[kMaxSplits], pl[kMaxSplits], pv[kMaxSplits][8];
+            for (int d = 0; d < DTW; ++d)
+              po[c][d] = coherent_load16(ro, (uint32_t)(((dt0 + d) * 64 + lane) * 16));
+            pm[c][0] = coherent_load16(rm, (uint32_t)(qd * 32));
+            pm[c][1] = coherent_load16(rm, (uint32_t)(qd * 32 + 16));
 #pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp) {
-        if (sp < part.S) {
-          const f32x2 m2 = coherent_load8(rm, (uint32_t)((sp * kHeadsPad + h) * 2 * 4));
-          pm[sp] = m2[0];
-          pl[sp] = m2[1];
-          const uint32_t ob = (uint32_t)((sp * kHeadsPad * kDim + off) * 4);
-          const f32x4 v0 = coherent_load16(ro, ob), v1 = coherent_load16(ro, ob + 16);
+            for (int d = 0; d < DTW; ++d) ok = ok && all_landed(po[c][d]);
+            ok = ok && all_landed(pm[c][0]) && all_landed(pm[c][1]);
+          }
+        }
+        if (__ballot(!ok) == 0) break;
+        if (tries >= kSpinLimit) {  // never expected: the output becomes NaN
+          timed_out = true;
+          break;
+        }
+      }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            pv[sp][k] = v0[k];
-            pv[sp][4 + k] = v1[k];
+      for (int c = 0; c < CH; ++c) {
+        if (sp0 + c < part.S - 1) {
+          const f32x4 m0 = decode_partial(pm[c][0]), m1 = decode_partial(pm[c][1]);
+          const float sm[4] = {m0[0], m0[2], m1[0], m1[2]};
+          const float sl[4] = {m0[1], m0[3], m1[1], m1[3]};
+          float fa[4], fb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float mx = fmaxf(cm[i], sm[i]);
+            fa[i] = rescale(cm[i], mx);
+            fb[i] = rescale(sm[i], mx);
+            cm[i] = mx;
+            cl[i] = cl[i] * fa[i] + sl[i] * fb[i];
+          }
+#pragma unroll
+          for (int d = 0; d < DTW; ++d) {
+            const f32x4 x = decode_partial(po[c][d]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) co[d][i] = co[d][i] * fa[i] + x[i] * fb[i];
           }
         }
       }
-      float Mx = -INFINITY;
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp)
-        if (sp < part.S) Mx = fmaxf(Mx, pm[sp]);
-      float L = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp) {
-        if (sp < part.S) {
-          const float f = rescale(pm[sp], Mx);
-          L += f * pl[sp];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) o[k] += f * pv[sp][k];
-        }
-      }
-      const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] *= inv;
-      store_out8(a, row, g * a.hpg + h, d0, o);
-      if (a.lse && (t & 15) == 0)
-        a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
-            L > 0.0f ? (Mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
     }
-    for (int sp = 0; sp < part.S; ++sp) {
-      float4* z = reinterpret_cast<float4*>(po + (size_t)sp * (kHeadsPad * kDim));
-      z[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      z[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if ((t & 15) == 0) *reinterpret_cast<float2*>(ml + (size_t)sp * (kHeadsPad * 2)) = make_float2(0.0f, 0.0f);
+    // return the partials read to zero: the workspace is left as found
+#pragma unroll 1
+    for (int sp = 0; sp < part.S - 1; ++sp) {
+      f32x4* zo = reinterpret_cast<f32x4*>(part.o + (ubase + sp) * (kHeadsPad * kDim));
+#pragma unroll
+      for (int d = 0; d < DTW; ++d) zo[(dt0 + d) * 64 + lane] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (wave == 0 && n == 0) {
+        f32x4* zm = reinterpret_cast<f32x4*>(part.ml + (ubase + sp) * (kHeadsPad * 2));
+        zm[2 * qd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        zm[2 * qd + 1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    // every split has finished its selection: the scores row is free
+    if (SELECT && a.clear) clear_row(a, u, NW);
+  }
+
+  // ---- normalise and store: heads 4qd+i, dims 16 (dt0 + d) + n ----
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    inv[i] = timed_out ? __builtin_nanf("") : (cl[i] > 0.0f ? a.v_scale / cl[i] : 0.0f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * qd + i;
+    if (h < a.hpg) {
+#pragma unroll
+      for (int d = 0; d < DTW; ++d)
+        store_out(a, row, g * a.hpg + h, (dt0 + d) * 16 + n, co[d][i] * inv[i]);
     }
   }
-  if (SELECT && a.clear) clear_row(a, u, NW);
-  if (threadIdx.x == 0)
-    __hip_atomic_store(part.counters + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.lse && wave == 0 && n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * qd + i;
+      if (h < a.hpg)
+        a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
+            timed_out ? __builtin_nanf("")
+                      : (cl[i] > 0.0f ? (cm[i] + log2f(cl[i])) * 0.69314718055994531f : -INFINITY);
+    }
+  }
 }
 
 }  // namespace msa

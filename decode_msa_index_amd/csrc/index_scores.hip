@@ -15,34 +15,23 @@
 // entries outside the pool, produce -inf without touching the cache.
 //
 // Arithmetic: keys are converted exactly to bf16 (e4m3 and e2m1 values are
-// bf16-representable) and multiplied with the bf16 index query by
-// v_dot2c_f32_bf16: exact products, fp32 accumulation.  The positive score
-// scale commutes with the max, so it is applied once per block.
+// bf16-representable) and multiplied with the bf16 index queries on MFMA
+// (index_block.hpp): exact products, fp32 accumulation.  The fp32 path uses
+// plain fp32 FMAs.  The positive score scale commutes with the max, so it is
+// applied once per block.
 #include "device.hpp"
 #include "index_block.hpp"
 #include "launch.hpp"
 
 namespace msa {
 
-// Optional side job of the first workgroup: zero n ints (the attention
-// kernel's arrival counters, cleared here so msa_decode needs no extra launch).
-struct ZeroArgs {
-  int32_t* p;
-  int n;
-  __device__ __forceinline__ void run() const {
-    if (p && blockIdx.x == 0 && blockIdx.y == 0)
-      for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
-  }
-};
-
 // -------------------------------------------------------------------------
 // FP8 e4m3 / NVFP4 index keys, bf16 index queries: one wave per block, on
 // MFMA (the layouts and arithmetic are those of index_block.hpp).
 // -------------------------------------------------------------------------
 template <int G, int IK>
-__global__ __launch_bounds__(256) void index_mfma_kernel(IndexArgs x, ZeroArgs za) {
+__global__ __launch_bounds__(256) void index_mfma_kernel(IndexArgs x) {
   __shared__ uint4 stage[4][kStageBytes / 16];  // one staging area per wave
-  za.run();
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int row = blockIdx.y, b = row / x.R;
   const int j = blockIdx.x * 4 + wave;
@@ -75,8 +64,7 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
     const float* __restrict__ iq, const float* __restrict__ ik,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, float* __restrict__ scores, int R, int MB, int P,
-    float out_scale, ZeroArgs za) {
-  za.run();
+    float out_scale) {
   __shared__ float qs[G * kDim];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int row = blockIdx.y, b = row / R;
@@ -131,19 +119,18 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 template <int G>
 static hipError_t launch_g(const Shape& s, const void* iq, const void* ikd, const void* iks,
                            const int32_t* bt, const int32_t* lens, const int32_t* qpos,
-                           float* scores, hipStream_t st, int32_t* zero, int n_zero) {
+                           float* scores, hipStream_t st) {
   dim3 grid((s.MB + 3) / 4, s.rows), block(256);
   float out_scale = s.index_scale * s.ik_scale;
-  const ZeroArgs za{zero, n_zero};
   const IndexArgs x{(const uint16_t*)iq, (const uint8_t*)ikd, (const uint8_t*)iks, bt, lens,
                     qpos, scores, s.R, s.MB, s.P, out_scale};
   if (s.ik_dtype == kFP8) {
-    hipLaunchKernelGGL((index_mfma_kernel<G, kFP8>), grid, block, 0, st, x, za);
+    hipLaunchKernelGGL((index_mfma_kernel<G, kFP8>), grid, block, 0, st, x);
   } else if (s.ik_dtype == kNVFP4) {
-    hipLaunchKernelGGL((index_mfma_kernel<G, kNVFP4>), grid, block, 0, st, x, za);
+    hipLaunchKernelGGL((index_mfma_kernel<G, kNVFP4>), grid, block, 0, st, x);
   } else {
     hipLaunchKernelGGL(index_f32_kernel<G>, grid, block, 0, st, (const float*)iq,
-                       (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale, za);
+                       (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale);
   }
   return hipGetLastError();
 }
@@ -151,20 +138,16 @@ static hipError_t launch_g(const Shape& s, const void* iq, const void* ikd, cons
 hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* ik_data,
                                const void* ik_scales, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* q_pos,
-                               float* scores, hipStream_t st, int32_t* zero, int n_zero) {
+                               float* scores, hipStream_t st) {
   if (prefill_index_supported(s)) {
-    if (zero && n_zero > 0) {
-      const hipError_t e = launch_zero_fill(zero, (size_t)n_zero * sizeof(int32_t), st);
-      if (e != hipSuccess) return e;
-    }
     return launch_prefill_index_scores(s, index_q, ik_data, block_table, seq_lens, q_pos,
                                        scores, st);
   }
   switch (s.G) {
-    case 1: return launch_g<1>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
-    case 2: return launch_g<2>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
-    case 4: return launch_g<4>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
-    case 8: return launch_g<8>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st, zero, n_zero);
+    case 1: return launch_g<1>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
+    case 2: return launch_g<2>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
+    case 4: return launch_g<4>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
+    case 8: return launch_g<8>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,13 +23,10 @@ constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2, kNVFP4 = 3;
 constexpr int kHeadsPad = 16;
 constexpr int kMaxSplits = 8;  // split-K workgroups per (row, group): at most ceil(32 / 4)
 
-// zero: optional int array of n_zero entries the index kernel clears in
-// passing (the attention kernel's arrival counters).
 hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* ik_data,
                                const void* ik_scales, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* q_pos,
-                               float* scores, hipStream_t st, int32_t* zero = nullptr,
-                               int n_zero = 0);
+                               float* scores, hipStream_t st);
 
 // Many rows per sequence (chunked prefill): the dense MFMA form of the
 // index scan (prefill_index.hip), used by launch_index_scores when supported.
@@ -55,7 +52,8 @@ hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_da
                                 const int32_t* topk, void* out, float* lse, void* workspace,
                                 hipStream_t st);
 // Selection fused into the attention kernel (msa_decode): needs the row's
-// block keys in LDS, so only for block tables short enough.  clear_scores
+// block keys in LDS, so only for block tables short enough.  The split-K
+// partials in workspace must be zero (they are left zero).  clear_scores
 // (nullable): the scores array (the workspace's), zeroed again by each
 // unit's last reader.
 bool select_fusable(const Shape& s);
@@ -63,13 +61,9 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, bool counters_zeroed, float* clear_scores,
-                                hipStream_t st);
+                                void* workspace, float* clear_scores, hipStream_t st);
 // Clears bytes (a multiple of 4) with a fill kernel.
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
-
-// Offset (bytes) of the arrival counters inside the attention workspace.
-size_t attend_counter_offset(const Shape& s, const AttendConfig& c);
 
 hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const void* q,
                                     const void* kv_data, const void* kv_scales,

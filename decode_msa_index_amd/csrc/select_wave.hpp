@@ -240,55 +240,78 @@ __device__ __forceinline__ uint64_t pack_cand(uint32_t key, int idx) {
   return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)idx);
 }
 __device__ __forceinline__ int cand_index(uint64_t c) { return (int)~(uint32_t)c; }
-constexpr uint64_t kNoCand = 0x80000000ull;  // pack_cand(0, INT_MAX): below any real candidate
 
-// Number of entries of v[0..n) (LDS, read by all lanes at the same address)
-// greater than c.  n is rounded up to a multiple of 8: entries past n must
-// hold values that are not greater than any c asked about.
-__device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t c) {
-  int acc[4] = {0, 0, 0, 0};
-  for (int m0 = 0; m0 < n; m0 += 8) {
-    uint64_t x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = v[m0 + i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i & 3] += x[i] > c ? 1 : 0;
-  }
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+// Descending bitonic sort over groups of N lanes (N = 32 or 64): lane i of
+// a group ends with the group's i-th largest value (for N = 32 the upper
+// group of the wave is sorted the other way round and is not used).  Lane
+// exchanges are DPP moves and CDNA4 row swaps; the lane-pattern masks are
+// compile-time constants, so a stage is an exchange, a max, a min and a
+// select.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  return (uint32_t)lane_xor<J>((int)v);
+}
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v) {
+  const uint32_t lo = lane_xor_u32<J>((uint32_t)v);
+  const uint32_t hi = lane_xor_u32<J>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One merge pass of a descending bitonic sort: stages J, J/2, .., 1 of the
+// blocks of K lanes.
+template <int K, int J, typename T>
+__device__ __forceinline__ void sort_desc_merge(T& v) {
+  const int lane = threadIdx.x & 63;
+  T p;
+  if constexpr (sizeof(T) == 8)
+    p = lane_xor_u64<J>(v);
+  else
+    p = lane_xor_u32<J>(v);
+  const bool keep_larger = ((lane & J) == 0) == ((lane & K) == 0);
+  v = (keep_larger == (p > v)) ? p : v;
+  if constexpr (J > 1) sort_desc_merge<K, J / 2>(v);
+}
+
+template <int N, int K = 2, typename T>
+__device__ __forceinline__ void sort_desc(T& v) {
+  sort_desc_merge<K, K / 2>(v);
+  if constexpr (K < N) sort_desc<N, K * 2>(v);
 }
 
 // Selection by a whole workgroup of NW waves, for a kernel whose threads
 // have just loaded the row's keys.  keys[0..rb) in LDS hold the order keys
-// of blocks 0..rb-1; each thread passes its best candidate among the blocks
-// (< rb) it loaded, as a composite (kNoCand if none).
+// of blocks 0..rb-1; each thread passes the largest key among the blocks
+// (< rb) it loaded (0 if none).
 //
-// The candidates fall into 64 groups: group l holds the blocks loaded by the
-// threads at lane position l of every wave.  T0 is the (k-1)-th best group
-// maximum, found by ranking the 64 maxima by counting.  At least k-1
+// The candidates fall into 32 groups: group l holds the blocks loaded by the
+// threads at lane positions l and l + 32 of every wave.  T0 is the (k-1)-th
+// largest group maximum (a 32-lane sort of the maxima).  At least k-1
 // candidates are >= T0, so the k-1 best all are: each wave re-reads its
-// threads' keys and compacts its survivors (ballot + mbcnt) into a region of
-// its own.  The survivors, usually about k, are gathered into lanes, ranked
-// by counting (survivor i is chosen when fewer than k-1 survivors beat it)
-// and placed by counting smaller block ids, so nothing is sorted.  Every
-// wave computes T0 and the result itself, which saves barriers and
-// broadcasts.  More than 64 survivors (strongly structured scores) fall back
-// to the radix select run by wave 0 over the LDS keys.
+// threads' keys and compacts its survivors (ballot + mbcnt) into a region
+// of its own.  The survivors, usually about k, are gathered into lanes as
+// composites (key, then lower block id) and sorted, 32 or 64 lanes wide;
+// the first k-1 lanes hold the selection.  All of it runs in registers with
+// lane exchanges; every wave computes T0 and the result itself, which saves
+// barriers and broadcasts.  More than 64 survivors (strongly structured
+// scores) fall back to the radix select run by wave 0 over the LDS keys.
 //
 // On return out_w (this wave's own 32-entry row) holds the K selected block
-// ids, ascending, -1 padded, and all LDS writes the threads made before the
-// call are visible to the whole workgroup.  Called by every thread with
-// workgroup-uniform rb and K <= 32.
+// ids, -1 padded: the recent block rb at K-1, the others before it in an
+// order that is the same in every workgroup making this selection (not
+// sorted; sort_selection orders a copy).  All LDS writes the threads made
+// before the call are visible to the whole workgroup.  Called by every
+// thread with workgroup-uniform rb and K <= 32.
 template <int NW>
 struct GroupSelectLds {
-  uint64_t best[64 * NW];    // each thread's best candidate
-  uint64_t scratch[NW][64];  // per wave: group maxima, then the gathered survivors
+  uint32_t tmax[64 * NW];    // each thread's largest key
   uint64_t surv[NW][64];     // per wave: the survivors it found
   uint32_t surv_n[NW];
   int32_t radix_out[32];
 };
 
 template <int NW>
-__device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
+__device__ __forceinline__ void group_select(const uint32_t* keys, int rb, int K, uint32_t tmax,
                              GroupSelectLds<NW>& g, uint32_t* hist, int32_t* out_w) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int need = K - 1;
@@ -299,24 +322,19 @@ __device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
     return;
   }
   const int ncand = rb;
-  g.best[threadIdx.x] = mine;
+  g.tmax[threadIdx.x] = tmax;
   __syncthreads();
-  // ---- T0: the need-th best of the 64 group maxima ----
-  uint64_t gm = g.best[lane];
+  // ---- T0: the need-th largest of the 32 group maxima.  Groups l <
+  // min(32, ncand) hold block l and ncand > need, so at least need groups
+  // are non-empty; empty groups hold 0, below every real key ----
+  uint32_t gm = g.tmax[lane];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) gm = max(gm, g.best[w * 64 + lane]);
-  uint64_t* buf = g.scratch[wave];
-  buf[lane] = gm;
-  wave_lds_sync();
-  // groups l < min(64, ncand) hold block l, so ranks 0..need-1 belong to
-  // exactly one real group each (empty groups tie at kNoCand below them)
-  const uint64_t at = __ballot(count_greater(buf, 64, gm) == need - 1);
-  const int src = (int)__builtin_ctzll(at);
-  const uint32_t t_lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gm, src);
-  const uint32_t t_hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(gm >> 32), src);
-  const uint64_t t0 = ((uint64_t)t_hi << 32) | t_lo;
+  for (int w = 1; w < NW; ++w) gm = max(gm, g.tmax[w * 64 + lane]);
+  gm = max(gm, (uint32_t)lane_xor<32>((int)gm));
+  sort_desc<32>(gm);
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)gm, need - 1);
 
-  // ---- survivors (>= T0): each wave compacts its own into surv[wave] ----
+  // ---- survivors (key >= T0): each wave compacts its own into surv[wave] ----
   constexpr int NT = 64 * NW;
   uint32_t n_w = 0;
   for (int base = 0; base < ncand; base += 8 * NT) {
@@ -326,12 +344,11 @@ __device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int jj = base + r * NT + (int)threadIdx.x;
-      const uint64_t cc = pack_cand(kk[r], jj);
-      const bool s = jj < ncand && cc >= t0;
+      const bool s = jj < ncand && kk[r] >= t0;
       const uint64_t m = __ballot(s);
       if (s) {
         const uint32_t slot = n_w + (uint32_t)popc_below(m, lane);
-        if (slot < 64) g.surv[wave][slot] = cc;
+        if (slot < 64) g.surv[wave][slot] = pack_cand(kk[r], jj);
       }
       n_w += (uint32_t)__popcll(m);
     }
@@ -350,7 +367,7 @@ __device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
     if (lane < need) out_w[lane] = g.radix_out[lane];
   } else {
     // gather: lane l takes survivor l of the concatenated regions
-    uint64_t ci = kNoCand;
+    uint64_t ci = 0;  // below every real composite
     if ((uint32_t)lane < total) {
       int w = 0;
       uint32_t off = (uint32_t)lane;
@@ -363,28 +380,26 @@ __device__ void group_select(const uint32_t* keys, int rb, int K, uint64_t mine,
       }
       ci = g.surv[w][off];
     }
-    buf[lane] = ci;
-    wave_lds_sync();
-    const int rank = count_greater(buf, (int)total, ci);
-    const bool chosen = (uint32_t)lane < total && rank < need;
-    const uint64_t cm = __ballot(chosen);
-    const int j = cand_index(ci);
-    // the chosen ids, unordered, then each one's place = smaller chosen ids
-    if (chosen) out_w[popc_below(cm, lane)] = j;
-    wave_lds_sync();
-    int acc[4] = {0, 0, 0, 0};
-    for (int m0 = 0; m0 < need; m0 += 8) {
-      int x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = out_w[m0 + i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i & 3] += (m0 + i < need && x[i] < j) ? 1 : 0;
-    }
-    wave_lds_sync();
-    if (chosen) out_w[(acc[0] + acc[1]) + (acc[2] + acc[3])] = j;
+    // the need best composites in lanes 0..need-1 (need <= 31)
+    if (total <= 32)
+      sort_desc<32>(ci);
+    else
+      sort_desc<64>(ci);
+    if (lane < need) out_w[lane] = cand_index(ci);
   }
   if (lane == 0) out_w[K - 1] = rb;
   wave_lds_sync();
+}
+
+// A selection row of K <= 32 entries (block ids and -1 padding, any order)
+// in ascending order, padding last: lane l < K returns entry l.  Called by
+// all 64 lanes of a wave; `entry` is lane l's entry (lanes >= K: anything).
+__device__ __forceinline__ int sort_selection(int entry, int K) {
+  const int lane = threadIdx.x & 63;
+  uint32_t dummy = 0;
+  int v = lane < K && entry >= 0 ? entry : 0x7FFFFFFF;
+  wave_bitonic<false, 32>(dummy, v);
+  return v == 0x7FFFFFFF ? -1 : v;
 }
 
 // Loads the row's scores s[0..n) into LDS as order keys.  All loads of a

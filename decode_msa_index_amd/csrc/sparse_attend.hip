@@ -15,6 +15,9 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+#include <mutex>
+#include <vector>
+
 namespace msa {
 
 template <int KV, int NW, bool SELECT>
@@ -153,64 +156,103 @@ AttendConfig attend_config(const Shape& s) {
   return c;
 }
 
-// [ml: units*S*16*2][o: units*S*16*128][counters: units], floats then ints
+// [ml: units*S*16*2][o: units*S*16*128] floats
 size_t attend_workspace_bytes(const Shape& s, const AttendConfig& c) {
   if (c.splits <= 1) return 0;
   const size_t units = (size_t)s.rows * s.G;
-  return sizeof(float) * units * c.splits * kHeadsPad * (kDim + 2) + sizeof(int32_t) * units;
+  return sizeof(float) * units * c.splits * kHeadsPad * (kDim + 2);
 }
 
-size_t attend_counter_offset(const Shape& s, const AttendConfig& c) {
-  return sizeof(float) * (size_t)s.rows * s.G * c.splits * kHeadsPad * (kDim + 2);
+// LDS of the fused kernel: the row's keys, its block-table row and a 256-word
+// scratch (dynamic), next to the static selection and wave-combine buffers.
+static size_t select_dyn_lds(const Shape& s) { return sizeof(uint32_t) * (256 + 2 * (size_t)s.MB); }
+static size_t select_static_lds(int nw) {
+  const size_t combine = nw > 1 ? (size_t)nw * (8 * 64 * 16 + kHeadsPad * 8) : 0;
+  return combine + (size_t)nw * 32 * sizeof(int32_t) + sizeof(GroupSelectLds<8>) + 256;
 }
 
-// The fused kernel holds the row's keys (and a 256-bin histogram) in LDS
-// next to its static merge buffers; it is used when all of it fits in 64 KB.
+// The fused kernel needs the row's keys in LDS: block tables whose rows fit
+// in 64 KB of dynamic LDS, with the whole workgroup inside gfx950's 160 KB.
 bool select_fusable(const Shape& s) {
   if (s.kv_dtype == kF32) return false;
-  const int nw = attend_config(s).nw;
-  const size_t stat = (size_t)(nw > 1 ? nw / 2 : 1) * (32 * 64 + 2 * 16) * sizeof(float) +
-                      (size_t)nw * 32 * sizeof(int32_t) + sizeof(GroupSelectLds<8>) + 64;
-  const size_t dyn = sizeof(uint32_t) * (256 + 2 * (size_t)s.MB);
-  return stat + dyn <= 65536;
+  const size_t dyn = select_dyn_lds(s);
+  return dyn <= 65536 && dyn + select_static_lds(attend_config(s).nw) <= 160 * 1024;
 }
 
+// Workgroups of `kernel` (block threads, lds dynamic bytes) the current
+// device holds at once; 0 if the runtime cannot tell.  Cached per kernel.
+static long resident_capacity(const void* kernel, int threads, size_t lds) {
+  struct Entry {
+    const void* k;
+    size_t lds;
+    int dev;
+    long cap;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.k == kernel && e.lds == lds && e.dev == dev) return e.cap;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache.push_back(Entry{kernel, lds, dev, (long)per_cu * cus});
+  return (long)per_cu * cus;
+}
+
+template <int KVT, int NWV, bool SELECT>
+static hipError_t launch_kernel(const Shape& s, int splits, const AttendArgs& a, const void* q,
+                                const void* kv_data, const void* kv_scales, void* workspace,
+                                bool zero_partials, hipStream_t st) {
+  const int units = s.rows * s.G;
+  const void* fn = reinterpret_cast<const void*>(&attend_mfma_kernel<KVT, NWV, SELECT>);
+  const size_t lds = SELECT ? select_dyn_lds(s) : 0;
+  // the merging workgroup of a split unit waits for the unit's other
+  // workgroups: split only when the whole grid can be resident at once
+  if (splits > 1 && (long)units * splits > resident_capacity(fn, 64 * NWV, lds)) splits = 1;
+  const Partials part = make_partials(s, AttendConfig{NWV, splits}, workspace);
+  if (splits > 1 && zero_partials) {
+    const hipError_t e = launch_zero_fill(part.ml, attend_workspace_bytes(s, AttendConfig{NWV, splits}), st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((attend_mfma_kernel<KVT, NWV, SELECT>), dim3(units * splits), dim3(64 * NWV),
+                     lds, st, static_cast<const uint16_t*>(q),
+                     static_cast<const uint8_t*>(kv_data), static_cast<const uint8_t*>(kv_scales),
+                     a, part);
+  return hipGetLastError();
+}
+
+// zero_partials: clear the split-K partials first (msa_sparse_attend, whose
+// workspace carries no zero-fill guarantee); msa_decode's workspace is zero.
 template <bool SELECT>
 static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const AttendArgs& a,
                               const void* q, const void* kv_data, const void* kv_scales,
-                              void* workspace, bool zero_counters, hipStream_t st) {
-  const int units = s.rows * s.G;
+                              void* workspace, bool zero_partials, hipStream_t st) {
   if (c.splits < 1 || c.splits > kMaxSplits) return hipErrorInvalidValue;
-  const Partials part = make_partials(s, c, workspace);
-  if (c.splits > 1 && zero_counters) {
-    hipLaunchKernelGGL(zero_fill_kernel, dim3((units + 255) / 256), dim3(256), 0, st,
-                       part.counters, units);
-  }
-  const dim3 grid(units * c.splits);
-  const size_t lds = SELECT ? sizeof(uint32_t) * (256 + 2 * (size_t)s.MB) : 0;
-  const uint16_t* qb = static_cast<const uint16_t*>(q);
-  const uint8_t* kd = static_cast<const uint8_t*>(kv_data);
-  const uint8_t* ks = static_cast<const uint8_t*>(kv_scales);
-#define MSA_ATTEND_LAUNCH(KVT, NWV)                                                      \
-  hipLaunchKernelGGL((attend_mfma_kernel<KVT, NWV, SELECT>), grid, dim3(64 * NWV), lds, st, \
-                     qb, kd, ks, a, part)
+#define MSA_ATTEND_LAUNCH(KVT, NWV) \
+  return launch_kernel<KVT, NWV, SELECT>(s, c.splits, a, q, kv_data, kv_scales, workspace, \
+                                         zero_partials, st)
   if (s.kv_dtype == kFP8) {
     switch (c.nw) {
-      case 1: MSA_ATTEND_LAUNCH(kFP8, 1); break;
-      case 2: MSA_ATTEND_LAUNCH(kFP8, 2); break;
-      case 4: MSA_ATTEND_LAUNCH(kFP8, 4); break;
-      default: MSA_ATTEND_LAUNCH(kFP8, 8); break;
+      case 1: MSA_ATTEND_LAUNCH(kFP8, 1);
+      case 2: MSA_ATTEND_LAUNCH(kFP8, 2);
+      case 4: MSA_ATTEND_LAUNCH(kFP8, 4);
+      default: MSA_ATTEND_LAUNCH(kFP8, 8);
     }
   } else {
     switch (c.nw) {
-      case 1: MSA_ATTEND_LAUNCH(kNVFP4, 1); break;
-      case 2: MSA_ATTEND_LAUNCH(kNVFP4, 2); break;
-      case 4: MSA_ATTEND_LAUNCH(kNVFP4, 4); break;
-      default: MSA_ATTEND_LAUNCH(kNVFP4, 8); break;
+      case 1: MSA_ATTEND_LAUNCH(kNVFP4, 1);
+      case 2: MSA_ATTEND_LAUNCH(kNVFP4, 2);
+      case 4: MSA_ATTEND_LAUNCH(kNVFP4, 4);
+      default: MSA_ATTEND_LAUNCH(kNVFP4, 8);
     }
   }
 #undef MSA_ATTEND_LAUNCH
-  return hipGetLastError();
 }
 
 hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const void* q,
@@ -240,13 +282,11 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, bool counters_zeroed, float* clear_scores,
-                                hipStream_t st) {
+                                void* workspace, float* clear_scores, hipStream_t st) {
   AttendArgs a =
       make_attend_args(s, block_table, seq_lens, q_pos, nullptr, scores, topk_out, out, lse);
   a.clear = reinterpret_cast<uint32_t*>(clear_scores);
-  return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace,
-                           !counters_zeroed, st);
+  return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace, false, st);
 }
 
 }  // namespace msa

@@ -129,16 +129,16 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * Workspace bytes a call needs for problem p (op as for msa_check_problem):
  *   - msa_sparse_attend: room for the split-K partial states when a (row,
  *     group) is split over several workgroups (0 when it is not);
- *   - msa_decode: that plus a 256-byte header and B*R*G*MB words for the
- *     pooled scores;
+ *   - msa_decode: B*R*G*MB words for the pooled scores, then that;
  *   - the other calls: 0.
  * Every region is rounded up to 256 bytes.  The workspace is caller-owned
  * device memory, 256-byte aligned.  msa_decode requires it to be zero-filled
- * before its first use (e.g. hipMemset once after allocation): its one
- * kernel synchronises its workgroups through counters and ready flags that
- * start at zero.  Every msa_decode and msa_sparse_attend call leaves the
- * workspace zero-filled again, so one zero fill serves any sequence of calls
- * and problem shapes; msa_sparse_attend itself needs no initialisation.
+ * before its first use (e.g. hipMemset once after allocation): the
+ * workgroups of its attention kernel hand partial states to each other
+ * through it, and a word still zero means "not yet written".  Every
+ * msa_decode and msa_sparse_attend call leaves the workspace zero-filled
+ * again, so one zero fill serves any sequence of calls and problem shapes;
+ * msa_sparse_attend itself needs no initialisation (it clears what it uses).
  * Calls that share a workspace must not overlap.  A call whose size is 0
  * accepts a NULL workspace.
  */
@@ -177,8 +177,8 @@ msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
  * blocks).  For head h of group g and visible tokens t of the selected
  * blocks: out = sum_t softmax_t(sm_scale * k_scale * q.k_t) * v_scale * v_t,
  * with fp32 softmax state, split over the selected blocks (across the waves
- * of a workgroup and, for small batches, across workgroups whose partial
- * states a second kernel merges).  topk_idx: the first
+ * of a workgroup and, for small batches, across workgroups, one of which
+ * merges the others' partial states).  topk_idx: the first
  * min(top_k, last visible block + 1) entries of a row are read; an entry
  * outside [0, last visible block] contributes nothing (msa_block_topk never
  * writes one).  kv_scales is required for NVFP4 and ignored otherwise.  lse
@@ -193,10 +193,12 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
 
 /*
  * The whole decode step (blog, "MSA primer"): msa_index_scores ->
- * msa_block_topk -> msa_sparse_attend, with the same results.  For FP8 or
- * NVFP4 caches and block tables of up to about 16000 blocks it is two
- * kernels, the scan and then selection + attention in one; otherwise the
- * three kernels run in turn.
+ * msa_block_topk -> msa_sparse_attend, with the same scores and selection;
+ * the attention may visit the selected blocks in another order, so out and
+ * lse agree with the three calls' to rounding.  For FP8 or NVFP4 caches
+ * and block tables of up to 8064 blocks per row (about a million tokens) it
+ * is two kernels, the scan and then selection + attention in one; otherwise
+ * the three kernels run in turn.
  * topk_idx receives the selection; block_scores (nullable) receives the
  * pooled scores.  workspace: msa_workspace_bytes(p, 3) bytes, zero-filled
  * before its first use (see msa_workspace_bytes) and left zero-filled.

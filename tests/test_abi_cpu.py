@@ -94,13 +94,12 @@ def test_workspace_sizes():
     d = msa.workspace_bytes(p, msa.OP_DECODE)
     scores = 8 * 4 * 2049 * 4
     assert d % 256 == 0 and a % 256 == 0
-    # decode: a 256-byte header, then the pooled scores rounded up to 256
-    assert d - a == 256 + -(-scores // 256) * 256
-    # split partials: 16 heads x (128 outputs + max + denominator) per split,
-    # then one arrival counter per (row, group)
+    # decode: the pooled scores rounded up to 256, then the attention's part
+    assert d - a == -(-scores // 256) * 256
+    # split partials: 16 heads x (128 outputs + max + denominator) per split
     units = 8 * 4
     S = a // (units * 16 * 130 * 4)
-    assert S >= 2 and a == -(-(units * S * 16 * 130 * 4 + units * 4) // 256) * 256
+    assert S >= 2 and a == -(-(units * S * 16 * 130 * 4) // 256) * 256
     big = good(num_seqs=512, max_blocks_per_seq=16)
     assert msa.workspace_bytes(big, msa.OP_ATTEND) == 0  # enough (row, group)s: no split
 
