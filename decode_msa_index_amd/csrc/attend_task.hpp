@@ -562,7 +562,10 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
         }
       }
     }
-    // return the partials read to zero: the workspace is left as found
+    // return the partials read to zero: the workspace is left as found.  The
+    // max / denominator words are shared by all waves: none may be cleared
+    // while another wave is still polling them.
+    __syncthreads();
 #pragma unroll 1
     for (int sp = 0; sp < part.S - 1; ++sp) {
       f32x4* zo = reinterpret_cast<f32x4*>(part.o + (ubase + sp) * (kHeadsPad * kDim));

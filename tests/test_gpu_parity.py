@@ -224,6 +224,30 @@ def test_decode_in_graph_replays_match_eager():
         assert int(torch.count_nonzero(dw.ws_decode)) == 0
 
 
+def test_repeated_decode_never_stalls():
+    """Split-K units merge by polling: many decodes in a row (every wave of
+    the merging workgroup polls the shared max / denominator words, which
+    may only be cleared once all of them are done) all finish promptly with
+    finite, identical outputs."""
+    import time
+    w = synth.make("repeat", seed=81, seq_lens=EDGE_LENS, q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, plant_per_seq=2)
+    dw = parity.DeviceWorkload(w)
+    dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    ref = dw.out.view(torch.uint8).clone()
+    say("[parity] 40 decodes in a row")
+    t0 = time.perf_counter()
+    for _ in range(40):
+        dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert elapsed < 0.5, f"40 decodes took {elapsed:.3f} s: a merge waited for its spin limit"
+    assert torch.isfinite(dw.out.float()).all()
+    assert torch.equal(dw.out.view(torch.uint8), ref)
+    assert int(torch.count_nonzero(dw.ws_decode)) == 0
+
+
 def test_one_workspace_across_shapes():
     """msa_decode leaves its workspace zero-filled, so one workspace (zeroed
     once) serves calls of different shapes in any order."""
