@@ -181,19 +181,25 @@ __device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint3
 }
 
 // Partial states travel with every 32-bit word stored as bits ^ kPartialXor.
-// The pattern kPartialXor itself (a NaN whose low 16 mantissa bits are set)
-// never occurs: this arithmetic makes NaNs only from bf16, fp8 or fp4
-// operands and from invalid operations, and all of those have zero low
-// bits.  So an encoded word is never 0, and a reader that polls zero-filled
-// memory knows each word it sees non-zero is complete -- no flag, fence or
-// counter is needed.
+// kPartialXor is itself a NaN pattern, and NaNs are stored as the canonical
+// quiet NaN first, so an encoded word is never 0: a reader polling
+// zero-filled memory knows each word it sees non-zero is complete -- no
+// flag, fence or counter is needed.
 constexpr uint32_t kPartialXor = 0x7FFFFFFFu;
+constexpr uint32_t kQuietNaN = 0x7FC00000u;
 __device__ __forceinline__ f32x4 encode_partial(f32x4 v) {
+  u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+  w.x = (v[0] != v[0] ? kQuietNaN : w.x) ^ kPartialXor;
+  w.y = (v[1] != v[1] ? kQuietNaN : w.y) ^ kPartialXor;
+  w.z = (v[2] != v[2] ? kQuietNaN : w.z) ^ kPartialXor;
+  w.w = (v[3] != v[3] ? kQuietNaN : w.w) ^ kPartialXor;
+  return __builtin_bit_cast(f32x4, w);
+}
+__device__ __forceinline__ f32x4 decode_partial(f32x4 v) {
   u32x4_t w = __builtin_bit_cast(u32x4_t, v);
   w ^= kPartialXor;
   return __builtin_bit_cast(f32x4, w);
 }
-__device__ __forceinline__ f32x4 decode_partial(f32x4 v) { return encode_partial(v); }
 __device__ __forceinline__ bool all_landed(f32x4 v) {
   const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
   return w.x != 0u && w.y != 0u && w.z != 0u && w.w != 0u;

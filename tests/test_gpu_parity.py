@@ -248,6 +248,39 @@ def test_repeated_decode_never_stalls():
     assert int(torch.count_nonzero(dw.ws_decode)) == 0
 
 
+def test_nan_in_cache_reaches_the_output_without_stalling_the_merge():
+    """A NaN in V (e4m3 0x7F) at token 0 of every block of one (sequence,
+    group), dim 5: every split's partial for that dim is NaN, the merge
+    still completes at once (partials carry NaNs in a form that is never
+    the all-zero 'not yet written' word), the NaN reaches exactly that
+    dim of that group's heads, and every other output is unchanged."""
+    import time
+    w = synth.make("nanv", seed=91, seq_lens=[20000, 9000], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, plant_per_seq=2)
+    dw = parity.DeviceWorkload(w)
+    dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    ref = dw.out.float().clone()
+    b, g, d = 0, 1, 5
+    nb = -(-int(w.seq_lens[b]) // 128)
+    pbs = torch.from_numpy(w.block_table[b, :nb].astype(np.int64)).cuda()
+    dw.kv_data[pbs, 1, g, d, 0] = 0x7F
+    torch.cuda.synchronize()
+    say("[parity] decode with a NaN in V")
+    t0 = time.perf_counter()
+    dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    assert time.perf_counter() - t0 < 0.2, "the split-K merge waited for its spin limit"
+    out = dw.out.float()
+    hpg = w.num_q_heads // w.num_groups
+    heads = slice(g * hpg, (g + 1) * hpg)
+    assert torch.isnan(out[b, heads, d]).all()
+    mask = torch.ones_like(out, dtype=torch.bool)
+    mask[b, heads, d] = False
+    assert torch.equal(out[mask], ref[mask])
+    assert int(torch.count_nonzero(dw.ws_decode)) == 0
+
+
 def test_one_workspace_across_shapes():
     """msa_decode leaves its workspace zero-filled, so one workspace (zeroed
     once) serves calls of different shapes in any order."""
