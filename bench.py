@@ -60,7 +60,9 @@ def measured_traffic(workload: str):
 
 
 def algorithmic_bytes(w, topk_counts):
-    """Bytes the method must move per step (decode rows, R = 1)."""
+    """Bytes the method must move per step: the index keys once per sequence
+    (the rows of a sequence share one scan), per-row queries, scores and
+    selections, and the selected tokens' K/V per (row, group)."""
     import numpy as np
     ik_tok = {2: 128, 3: 72, 0: 512}[w.index_k_dtype]
     kv_tok = {2: 256, 3: 144, 0: 1024}[w.kv_dtype]  # K+V per token per head
@@ -82,7 +84,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_256k",
-                    choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "prefill_64k"])
+                    choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "spec4_256k",
+                             "prefill_64k"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,7 +121,7 @@ def main():
     t0 = time.time()
     w = getattr(synth, args.workload)()
     log(f"[bench] generated {w.name} in {time.time() - t0:.1f}s: {w.recipe}")
-    if w.rows_per_seq > 1:
+    if w.rows_per_seq >= 16:  # a prefill chunk: its own line (rows/s, MFMA roofline)
         return run_prefill(args, w)
 
     dws = [parity.DeviceWorkload(w)]
@@ -196,7 +199,9 @@ def main():
     topk = dws[0].topk.cpu().numpy()
     sel_tokens = 0
     for r in range(w.rows):
-        L = int(w.seq_lens[r])
+        L = int(w.seq_lens[r // w.rows_per_seq])  # visible keys of row r: t < L, t <= pos
+        if w.q_pos is not None:
+            L = min(L, int(w.q_pos[r]) + 1)
         for gi in range(w.num_groups):
             for j in topk[r, gi]:
                 if j >= 0:

@@ -1,5 +1,5 @@
-// index_block.hpp -- one wavefront scores one logical block: the pieces the
-// standalone indexer kernels and the persistent decode kernel share.
+// index_block.hpp -- one wavefront scores one logical block for the index
+// queries of one or a few rows of a sequence.
 //
 // Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
 // primer"): every cached key is scored by one index query per GQA group
@@ -29,30 +29,25 @@ struct IndexArgs {
   const int32_t* lens;
   const int32_t* qpos;
   float* scores;  // [rows][G][MB]
-  int R, MB, P;
-  float out_scale;  // index_scale * index_k_scale (NVFP4: times the tensor scale)
+  int R, G, MB, P;
+  int rows_per_wave;  // rows of one sequence a wave scores together (rows_per_wave * G <= 16)
+  int row_groups;     // ceil(R / rows_per_wave)
+  float out_scale;    // index_scale * index_k_scale (NVFP4: times the tensor scale)
 };
 
-// Score store; the coherent form (device-scope, bypassing the non-coherent
-// per-XCD L2) is for scores another workgroup reads during the same kernel.
-template <bool COHERENT>
-__device__ __forceinline__ void put_score(float* p, float v) {
-  if constexpr (COHERENT)
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    *p = v;
-}
-
-// Lanes 0..G-1 store the G scores of block j of `row`.
-template <int G, bool COHERENT>
-__device__ __forceinline__ void put_block_scores(const IndexArgs& x, int row, int j, int lane,
-                                                 float v) {
-  if (lane < G) put_score<COHERENT>(x.scores + ((size_t)row * G + lane) * x.MB + j, v);
+// Lanes 0..cols-1 store block j's scores of the wave's columns: column c is
+// (row, group) pair col0 + c of the [rows][G] order.
+__device__ __forceinline__ void put_block_scores(const IndexArgs& x, size_t col0, int cols, int j,
+                                                 int lane, float v) {
+  if (lane < cols) x.scores[(col0 + lane) * x.MB + j] = v;
 }
 
 // The scores of a 16-token tile come from MFMA: S = K Q^T as
-// v_mfma_f32_16x16x32_bf16 with the tile's tokens as A rows, the G groups'
-// queries as B columns (padded to 16 with zeros) and 4 K-chunks of 32 dims.
+// v_mfma_f32_16x16x32_bf16 with the tile's tokens as A rows, the wave's
+// index queries as B columns -- the G groups of up to 16 / G rows of one
+// sequence (several rows per sequence: speculative decode), padded to 16
+// with zeros -- and 4 K-chunks of 32 dims.  One pass over the keys serves
+// all those rows.
 // A lane's A rows are tokens lane%16 -- 16 different rows -- while the loads
 // that stream HBM best read contiguous kilobytes, so a wave loads half a
 // block contiguously into registers, writes it to its own LDS area, and
@@ -67,25 +62,28 @@ __device__ __forceinline__ void put_block_scores(const IndexArgs& x, int row, in
 //          c = 2h + e takes dims 16r + 64h + 8e + 0..7;
 //   NVFP4: lane reads dims [32r, +32) (16 bytes) and the two scales of
 //          them; chunk e takes dims 32r + 8e + 0..7.
-// D lane l holds tokens 4r + i (i = 0..3) of the tile for group l%16; a
-// running max per lane over the tiles, then over i and over the four lane
-// groups, gives the block's score of group l%16 (lanes 0..G-1 keep them).
+// D lane l holds tokens 4r + i (i = 0..3) of the tile for column l%16; a
+// running max per lane over the tiles (keys up to that column's row's last
+// visible key), then over i and over the four lane groups, gives the block's
+// score of column l%16 (lanes 0..cols-1 keep them).
 
 constexpr int kStageBytes = 8192;  // LDS per wave: half a block (FP8) staged
 
-// B operand: the queries of the G groups (zero columns past G).
+// B operand: the wave's cols index queries, (row, group) pairs col0 ..
+// col0 + cols - 1 (zero columns past cols).
 struct QueryB {
   bf16x8 b[4];
 };
 
-template <int G, int IK>
-__device__ __forceinline__ void load_query_b(const IndexArgs& x, int row, int lane, QueryB& q) {
+template <int IK>
+__device__ __forceinline__ void load_query_b(const IndexArgs& x, size_t col0, int cols, int lane,
+                                             QueryB& q) {
   const int n = lane & 15, r = lane >> 4;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int d = IK == kFP8 ? 16 * r + 64 * (c >> 1) + 8 * (c & 1) : 32 * r + 8 * c;
-    q.b[c] = n < G ? *reinterpret_cast<const bf16x8*>(x.iq + ((size_t)row * G + n) * kDim + d)
-                   : bf16x8{};
+    q.b[c] = n < cols ? *reinterpret_cast<const bf16x8*>(x.iq + (col0 + n) * kDim + d)
+                      : bf16x8{};
   }
 }
 

@@ -7,8 +7,9 @@
 // (FP8) or 72 B (NVFP4), so these kernels stream each block once, coalesced,
 // and keep all arithmetic in registers.
 //
-// Work decomposition: one wavefront per (query row, logical block); four
-// wavefronts per workgroup take four consecutive blocks of the same row.
+// Work decomposition: one wavefront per (logical block, group of up to 16 / G
+// rows of one sequence); four wavefronts per workgroup take four consecutive
+// blocks.
 // Every load instruction of a wave reads 1 KB of consecutive bytes, and a
 // block's loads are all issued before any arithmetic, to keep many bytes in
 // flight per wave.  Blocks past a row's last visible key, and block-table
@@ -26,33 +27,45 @@
 namespace msa {
 
 // -------------------------------------------------------------------------
-// FP8 e4m3 / NVFP4 index keys, bf16 index queries: one wave per block, on
-// MFMA (the layouts and arithmetic are those of index_block.hpp).
+// FP8 e4m3 / NVFP4 index keys, bf16 index queries: one wave per (block, row
+// group), on MFMA (the layouts and arithmetic are those of index_block.hpp).
+// A row group is up to 16 / G consecutive rows of one sequence (R > 1:
+// speculative-decode rows, each with its own last visible key); its
+// rows_per_wave * G index queries are the MFMA's columns, so the block's
+// keys are read once for all of them.
 // -------------------------------------------------------------------------
-template <int G, int IK>
+template <int IK>
 __global__ __launch_bounds__(256) void index_mfma_kernel(IndexArgs x) {
   __shared__ uint4 stage[4][kStageBytes / 16];  // one staging area per wave
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int row = blockIdx.y, b = row / x.R;
+  const int b = blockIdx.y / x.row_groups, rg = blockIdx.y % x.row_groups;
+  const int r0 = rg * x.rows_per_wave, nr = min(x.rows_per_wave, x.R - r0);
+  const int cols = nr * x.G;
+  const size_t col0 = ((size_t)b * x.R + r0) * x.G;  // first (row, group) pair
   const int j = blockIdx.x * 4 + wave;
   if (j >= x.MB) return;
   const int entry = x.bt[(size_t)b * x.MB + j];  // issued alongside the length loads
-  const int pos = row_last_key(x.lens, x.qpos, row, b, x.MB);
-  const int pb = j * kBlock > pos ? -1 : entry;
-  if (pb < 0 || pb >= x.P) {  // past the row's last key (or an invalid table entry)
-    put_block_scores<G, false>(x, row, j, lane, -INFINITY);
+  // this lane's column: its row's last visible key (-1 past the columns)
+  const int n = lane & 15;
+  const int pos = n < cols ? row_last_key(x.lens, x.qpos, b * x.R + r0 + n / x.G, b, x.MB) : -1;
+  int pos_max = pos;  // the wave's furthest-seeing column
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) pos_max = max(pos_max, __shfl_xor(pos_max, o, 64));
+  const int pb = j * kBlock > pos_max ? -1 : entry;
+  if (pb < 0 || pb >= x.P) {  // past every column's last key (or an invalid table entry)
+    put_block_scores(x, col0, cols, j, lane, -INFINITY);
     return;
   }
   HalfRaw<IK> h0, h1;
   h0.issue(x, pb, 0, lane);
   h1.issue(x, pb, 1, lane);
   QueryB q;
-  load_query_b<G, IK>(x, row, lane, q);
+  load_query_b<IK>(x, col0, cols, lane, q);
   TileMax tm;
   tm.init();
   h0.pool(j, 0, pos, lane, q, tm, stage[wave]);
   h1.pool(j, 1, pos, lane, q, tm, stage[wave]);
-  put_block_scores<G, false>(x, row, j, lane, finish_block(x, tm));
+  put_block_scores(x, col0, cols, j, lane, finish_block(x, tm));
 }
 
 // -------------------------------------------------------------------------
@@ -91,6 +104,7 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
     float acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+#pragma unroll 4
     for (int d4 = 0; d4 < kDim / 4; ++d4) {
       const float4 k = krow[d4];
 #pragma unroll
@@ -117,21 +131,13 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 }
 
 template <int G>
-static hipError_t launch_g(const Shape& s, const void* iq, const void* ikd, const void* iks,
-                           const int32_t* bt, const int32_t* lens, const int32_t* qpos,
-                           float* scores, hipStream_t st) {
+static hipError_t launch_f32(const Shape& s, const void* iq, const void* ikd, const int32_t* bt,
+                             const int32_t* lens, const int32_t* qpos, float* scores,
+                             hipStream_t st) {
   dim3 grid((s.MB + 3) / 4, s.rows), block(256);
-  float out_scale = s.index_scale * s.ik_scale;
-  const IndexArgs x{(const uint16_t*)iq, (const uint8_t*)ikd, (const uint8_t*)iks, bt, lens,
-                    qpos, scores, s.R, s.MB, s.P, out_scale};
-  if (s.ik_dtype == kFP8) {
-    hipLaunchKernelGGL((index_mfma_kernel<G, kFP8>), grid, block, 0, st, x);
-  } else if (s.ik_dtype == kNVFP4) {
-    hipLaunchKernelGGL((index_mfma_kernel<G, kNVFP4>), grid, block, 0, st, x);
-  } else {
-    hipLaunchKernelGGL(index_f32_kernel<G>, grid, block, 0, st, (const float*)iq,
-                       (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P, out_scale);
-  }
+  hipLaunchKernelGGL(index_f32_kernel<G>, grid, block, 0, st, (const float*)iq,
+                     (const float*)ikd, bt, lens, qpos, scores, s.R, s.MB, s.P,
+                     s.index_scale * s.ik_scale);
   return hipGetLastError();
 }
 
@@ -143,13 +149,38 @@ hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* 
     return launch_prefill_index_scores(s, index_q, ik_data, block_table, seq_lens, q_pos,
                                        scores, st);
   }
-  switch (s.G) {
-    case 1: return launch_g<1>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    case 2: return launch_g<2>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    case 4: return launch_g<4>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    case 8: return launch_g<8>(s, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores, st);
-    default: return hipErrorInvalidValue;
+  if (s.ik_dtype == kF32) {
+    switch (s.G) {
+      case 1: return launch_f32<1>(s, index_q, ik_data, block_table, seq_lens, q_pos, scores, st);
+      case 2: return launch_f32<2>(s, index_q, ik_data, block_table, seq_lens, q_pos, scores, st);
+      case 4: return launch_f32<4>(s, index_q, ik_data, block_table, seq_lens, q_pos, scores, st);
+      case 8: return launch_f32<8>(s, index_q, ik_data, block_table, seq_lens, q_pos, scores, st);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (s.G < 1 || s.G > 16) return hipErrorInvalidValue;
+  IndexArgs x{};
+  x.iq = static_cast<const uint16_t*>(index_q);
+  x.ikd = static_cast<const uint8_t*>(ik_data);
+  x.iks = static_cast<const uint8_t*>(ik_scales);
+  x.bt = block_table;
+  x.lens = seq_lens;
+  x.qpos = q_pos;
+  x.scores = scores;
+  x.R = s.R;
+  x.G = s.G;
+  x.MB = s.MB;
+  x.P = s.P;
+  x.rows_per_wave = min(s.R, 16 / s.G);
+  x.row_groups = (s.R + x.rows_per_wave - 1) / x.rows_per_wave;
+  x.out_scale = s.index_scale * s.ik_scale;
+  const int nseq = s.rows / s.R;
+  const dim3 grid((s.MB + 3) / 4, (unsigned)(nseq * x.row_groups));
+  if (s.ik_dtype == kFP8)
+    hipLaunchKernelGGL(index_mfma_kernel<kFP8>, grid, dim3(256), 0, st, x);
+  else
+    hipLaunchKernelGGL(index_mfma_kernel<kNVFP4>, grid, dim3(256), 0, st, x);
+  return hipGetLastError();
 }
 
 }  // namespace msa

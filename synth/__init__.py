@@ -394,6 +394,20 @@ def fp8_256k(seed: int = 0x4D5341 + 5, **kw) -> Workload:
     return w
 
 
+def spec4_256k(seed: int = 0x4D5341 + 7, **kw) -> Workload:
+    """Speculative decode: the 256K batch-8 caches with 4 query rows per
+    sequence at its last 4 positions (each row its own causal end)."""
+    L, R = 262144, 4
+    qp = np.concatenate([np.arange(L - R, L)] * 8).astype(np.int32)
+    w = make("spec4_256k", seed=seed, seq_lens=[L] * 8, rows_per_seq=R, q_pos=qp,
+             q_dtype=BF16, kv_dtype=FP8, plant_per_seq=8, plant_add=1.0, **kw)
+    w.recipe = ("8 seqs x 262144 tokens, 4 speculative query rows per seq at positions "
+                "262140..262143 (each its own causal end), 64 q heads / 4 groups, D=Di=128, "
+                "bf16 q, e4m3 K/V/index keys, N(0,1), 8 planted blocks per seq, random "
+                "permutation table")
+    return w
+
+
 def prefill_64k(seed: int = 0x4D5341 + 6, **kw) -> Workload:
     cached, chunk = 65536, 4096
     w = make("prefill_64k", seed=seed, seq_lens=[cached + chunk], rows_per_seq=chunk,

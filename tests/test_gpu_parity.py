@@ -115,6 +115,23 @@ def test_query_positions_multi_row():
     _run_and_check(w, fused=True, name="multi-row")
 
 
+@pytest.mark.parametrize("kv,R,G,H", [(synth.FP8, 4, 4, 64), (synth.NVFP4, 4, 4, 64),
+                                       (synth.FP8, 6, 4, 64), (synth.FP8, 5, 2, 16),
+                                       (synth.FP8, 3, 8, 64)])
+def test_speculative_rows_share_one_scan(kv, R, G, H):
+    """Several query rows per sequence (speculative decode: the last R
+    positions, each row with its own causal end and recent block): the scan
+    scores up to 16 / G rows per pass over the keys (R = 6 with G = 4: two
+    row groups, of 4 and 2 rows), and every row matches the oracle."""
+    lens = [9000, 4100, 129, 20000]
+    qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
+    qp[R] = 5  # one row far behind the others of its sequence
+    w = synth.make(f"spec-r{R}", seed=120 + R + kv, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                   num_q_heads=H, num_groups=G, q_dtype=synth.BF16, kv_dtype=kv,
+                   plant_per_seq=2)
+    _run_and_check(w, fused=True, name=f"spec-r{R}-g{G}-{synth.DTYPE_NAMES[kv]}")
+
+
 @pytest.mark.parametrize("MB", [700, 17000])
 def test_block_topk_bit_exact_with_ties(MB):
     """Selection kernel alone, on oracle-independent scores with many exact
