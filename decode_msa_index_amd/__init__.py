@@ -16,13 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 F32, BF16, FP8_E4M3, NVFP4 = 0, 1, 2, 3
-OP_INDEX, OP_TOPK, OP_ATTEND, OP_DECODE = 0, 1, 2, 3
+OP_INDEX, OP_TOPK, OP_ATTEND, OP_DECODE, OP_CACHE_WRITE = 0, 1, 2, 3, 4
 
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
           3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
 
 EXPORTS = ["msa_check_problem", "msa_workspace_bytes", "msa_index_scores", "msa_block_topk",
-           "msa_sparse_attend", "msa_decode", "msa_status_string", "msa_last_error"]
+           "msa_sparse_attend", "msa_decode", "msa_cache_write", "msa_status_string",
+           "msa_last_error"]
 
 
 class MsaError(RuntimeError):
@@ -104,6 +105,8 @@ def lib():
         L.msa_decode.restype = ctypes.c_int
         L.msa_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+        L.msa_cache_write.restype = ctypes.c_int
+        L.msa_cache_write.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_last_error.restype = ctypes.c_char_p
@@ -179,6 +182,17 @@ def decode(p: Problem, index_q, ik_data, ik_scales, q, kv_data, kv_scales, block
                             _ptr(q), _ptr(kv_data), _ptr(kv_scales), _ptr(block_table),
                             _ptr(seq_lens), _ptr(q_pos), _ptr(block_scores), _ptr(topk_idx),
                             _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def cache_write(p: Problem, token_seq, token_pos, k_new, v_new, ik_new, block_table, kv_data,
+                kv_scales, ik_data, ik_scales, stream=None):
+    """Quantise new tokens into the caches (in place)."""
+    pc = p.c()
+    n = int(token_seq.numel()) if token_seq is not None else 0
+    _check(lib().msa_cache_write(ctypes.byref(pc), n, _ptr(token_seq), _ptr(token_pos),
+                                 _ptr(k_new), _ptr(v_new), _ptr(ik_new), _ptr(block_table),
+                                 _ptr(kv_data), _ptr(kv_scales), _ptr(ik_data),
+                                 _ptr(ik_scales), _stream(stream)))
 
 
 def new_workspace(p: Problem, op: int, device="cuda"):

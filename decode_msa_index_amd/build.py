@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.cpp", "index_scores.hip", "block_topk.hip", "sparse_attend.hip",
-           "prefill_index.hip"]
+           "prefill_index.hip", "cache_write.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

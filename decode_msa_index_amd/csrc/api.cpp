@@ -29,7 +29,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-enum Op { kOpIndex = 0, kOpTopk = 1, kOpAttend = 2, kOpDecode = 3 };
+enum Op { kOpIndex = 0, kOpTopk = 1, kOpAttend = 2, kOpDecode = 3, kOpCacheWrite = 4 };
 
 msa::Shape shape_of(const msa_problem* p) {
   msa::Shape s;
@@ -85,7 +85,7 @@ extern "C" {
 msa_status msa_check_problem(const msa_problem* p, int32_t op) {
   clear_error();
   if (!p) return fail(MSA_ERR_INVALID_ARGUMENT, "problem is NULL");
-  if (op < kOpIndex || op > kOpDecode) return fail(MSA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
+  if (op < kOpIndex || op > kOpCacheWrite) return fail(MSA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   if (p->num_seqs < 0) return fail(MSA_ERR_INVALID_ARGUMENT, "num_seqs < 0");
   if (p->rows_per_seq < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "rows_per_seq < 1");
   if (p->num_kv_groups < 1 || p->num_q_heads < 1)
@@ -108,8 +108,8 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op) {
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(MSA_ERR_UNSUPPORTED, "num_kv_groups must be 1, 2, 4 or 8");
   if (hpg > 16) return fail(MSA_ERR_UNSUPPORTED, "more than 16 query heads per group");
-  const bool need_index = op == kOpIndex || op == kOpDecode;
-  const bool need_attend = op == kOpAttend || op == kOpDecode;
+  const bool need_index = op == kOpIndex || op == kOpDecode || op == kOpCacheWrite;
+  const bool need_attend = op == kOpAttend || op == kOpDecode || op == kOpCacheWrite;
   if (need_index) {
     const int ik = p->index_k_dtype, iq = p->index_q_dtype;
     if (ik == MSA_DTYPE_FP8_E4M3 || ik == MSA_DTYPE_NVFP4) {
@@ -318,6 +318,34 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
   if (st != MSA_OK || block_scores) return st;
   return hip_status(msa::launch_zero_fill(ws + w.scores, w.attend - w.scores, hs),
                     "workspace clear launch");
+}
+
+msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32_t* token_seq,
+                           const int32_t* token_pos, const void* k_new, const void* v_new,
+                           const void* ik_new, const int32_t* block_table, void* kv_data,
+                           void* kv_scales, void* ik_data, void* ik_scales, void* stream) {
+  msa_status st = msa_check_problem(p, kOpCacheWrite);
+  if (st != MSA_OK) return st;
+  if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (num_tokens > 65535)
+    return fail(MSA_ERR_UNSUPPORTED, "more than 65535 tokens in one call");
+  if (num_tokens == 0) return MSA_OK;
+  REQUIRE(token_seq, 4);
+  REQUIRE(token_pos, 4);
+  REQUIRE(k_new, 4);
+  REQUIRE(v_new, 4);
+  REQUIRE(ik_new, 4);
+  REQUIRE(block_table, 4);
+  REQUIRE(kv_data, 16);
+  REQUIRE(ik_data, 16);
+  if (p->kv_dtype == MSA_DTYPE_NVFP4) REQUIRE(kv_scales, 16);
+  if (p->index_k_dtype == MSA_DTYPE_NVFP4) REQUIRE(ik_scales, 16);
+  if (p->num_seqs == 0) return MSA_OK;
+  const msa::Shape s = shape_of(p);
+  return hip_status(msa::launch_cache_write(s, num_tokens, token_seq, token_pos, k_new, v_new,
+                                            ik_new, block_table, kv_data, kv_scales, ik_data,
+                                            ik_scales, (hipStream_t)stream),
+                    "cache write launch");
 }
 
 const char* msa_status_string(msa_status s) {

@@ -62,6 +62,12 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
                                 void* workspace, float* clear_scores, hipStream_t st);
+// Quantises new tokens' K, V and index keys into their cache slots
+// (cache_write.hip).
+hipError_t launch_cache_write(const Shape& s, int num_tokens, const int32_t* token_seq,
+                              const int32_t* token_pos, const void* k_new, const void* v_new,
+                              const void* ik_new, const int32_t* block_table, void* kv_data,
+                              void* kv_scales, void* ik_data, void* ik_scales, hipStream_t st);
 // Clears bytes (a multiple of 4) with a fill kernel.
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 

@@ -13,8 +13,10 @@
  *   msa_block_topk     top-k blocks, recent block forced     (selection)
  *   msa_sparse_attend  exact GQA attention over the blocks   (main attention)
  *   msa_decode         the three in one call
- * msa_decode's outputs are identical to the three-call chain on the same
- * stream: bitwise for the selection, and for the attention output too.
+ * msa_decode's scores and selection are bitwise those of the three-call
+ * chain; its attention output agrees with the chain's to rounding.  A fifth
+ * call writes new tokens into the caches the others read:
+ *   msa_cache_write    quantise new K / V / index keys into their slots
  *
  * ---------------------------------------------------------------------------
  * Conventions
@@ -120,8 +122,8 @@ typedef struct msa_problem {
 
 /*
  * Host-side validation of a problem for one of the calls (op: 0 index
- * scores, 1 top-k, 2 sparse attend, 3 decode).  Pure host code; performs no
- * HIP call.  Every entry point runs it first.
+ * scores, 1 top-k, 2 sparse attend, 3 decode, 4 cache write).  Pure host
+ * code; performs no HIP call.  Every entry point runs it first.
  */
 msa_status msa_check_problem(const msa_problem* p, int32_t op);
 
@@ -210,7 +212,36 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
                       int32_t* topk_idx, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* Static description of a status code. */
+/*
+ * Cache write, the insert half of a decode step (blog, "MSA primer": FP8 index
+ * keys of 128 B per token; the NVFP4 kernels section: E2M1 values with one
+ * e4m3 scale per 16 elements and a per-tensor scale).  New token i belongs to
+ * sequence token_seq[i] at position token_pos[i]; its slot is logical block
+ * token_pos[i] / BS of that sequence (through block_table), row
+ * token_pos[i] % BS.  Its K and V for every group and its index key are
+ * quantised into kv_data / kv_scales and ik_data / ik_scales, in the layouts
+ * the other calls read, so that their dequantisation gives the values back
+ * to the format's precision.  Every step is one correctly rounded binary32
+ * operation, with scale = k_scale, v_scale or index_k_scale:
+ *   F32  : x / scale
+ *   FP8  : e4m3(x / scale), round to nearest even, saturating at +-448
+ *   NVFP4: per 16 consecutive elements of a token (K and index keys: 16
+ *          dims of the row; V: 16 dims of the token's column),
+ *          s = e4m3(amax / (6 * scale)); element e2m1(x / (e4m3(s) * scale)),
+ *          nearest even, saturating at +-6; all 0 when s is 0.
+ * Inputs: k_new, v_new [num_tokens][G][D] in q_dtype, ik_new
+ * [num_tokens][Di] in index_q_dtype, all finite.  The other tokens' slots
+ * are not touched (V's NVFP4 nibbles shared with a neighbour token are
+ * updated atomically).  Tokens whose sequence, position or table entry is
+ * out of range are skipped.  Two new tokens must not map to the same slot.
+ * num_tokens <= 65535 per call.  Format pairs as for msa_decode.
+ */
+msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32_t* token_seq,
+                           const int32_t* token_pos, const void* k_new, const void* v_new,
+                           const void* ik_new, const int32_t* block_table, void* kv_data,
+                           void* kv_scales, void* ik_data, void* ik_scales, void* stream);
+
+/* Static description of a status code. *//* Static description of a status code. */
 const char* msa_status_string(msa_status s);
 
 /* Thread-local detail of the last failure on this thread ("" if none). */

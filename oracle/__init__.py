@@ -75,6 +75,12 @@ def lib():
         L.msa_oracle_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp]
         L.msa_oracle_threads_used.restype = ctypes.c_int
+        L.msa_oracle_encode_e4m3.restype = ctypes.c_uint8
+        L.msa_oracle_encode_e4m3.argtypes = [ctypes.c_double]
+        L.msa_oracle_encode_e2m1.restype = ctypes.c_uint8
+        L.msa_oracle_encode_e2m1.argtypes = [ctypes.c_double]
+        L.msa_oracle_cache_write.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -198,3 +204,24 @@ def decode(p: Problem, index_q, ik_data, ik_scales, q, kv_data, kv_scales,
 
 def threads_used() -> int:
     return lib().msa_oracle_threads_used()
+
+
+def encode_e4m3(x: float) -> int:
+    return lib().msa_oracle_encode_e4m3(x)
+
+
+def encode_e2m1(x: float) -> int:
+    return lib().msa_oracle_encode_e2m1(x)
+
+
+def cache_write(p: Problem, token_seq, token_pos, k_new, v_new, ik_new, block_table,
+                kv_data, kv_scales, ik_data, ik_scales) -> None:
+    """Quantises the new tokens into the caches, in place (the arrays are
+    updated)."""
+    pc = p.c()
+    rc = lib().msa_oracle_cache_write(ctypes.byref(pc), len(token_seq), _ptr(token_seq),
+                                      _ptr(token_pos), _ptr(k_new), _ptr(v_new), _ptr(ik_new),
+                                      _ptr(block_table), _ptr(kv_data), _ptr(kv_scales),
+                                      _ptr(ik_data), _ptr(ik_scales))
+    if rc:
+        raise ValueError("oracle rejected the problem")

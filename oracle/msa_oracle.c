@@ -55,6 +55,45 @@ double msa_oracle_e2m1(uint8_t nibble) {
   return s ? -v : v;
 }
 
+/* Encoders, by their definition: the code whose value is nearest to x, a
+ * tie going to the code whose last bit is 0 (round to nearest, ties to
+ * even); magnitudes beyond the largest finite value take it (saturation);
+ * the sign is kept, so negative values that round to zero give -0.  x must
+ * not be NaN.  A search over the finite codes, with no bit tricks. */
+uint8_t msa_oracle_encode_e4m3(double x) {
+  int neg = signbit(x) != 0;
+  double a = fabs(x);
+  int best = 0x7E;  /* 448: the answer for +inf and every a >= 448 */
+  double best_err = INFINITY;
+  if (!isinf(a)) {
+    for (int c = 0; c <= 0x7E; ++c) {  /* 0x7F is NaN */
+      double err = fabs(msa_oracle_e4m3((uint8_t)c) - a);
+      if (err < best_err || (err == best_err && (c & 1) == 0)) {
+        best = c;
+        best_err = err;
+      }
+    }
+  }
+  return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+uint8_t msa_oracle_encode_e2m1(double x) {
+  int neg = signbit(x) != 0;
+  double a = fabs(x);
+  int best = 7;  /* 6.0 */
+  double best_err = INFINITY;
+  if (!isinf(a)) {
+    for (int c = 0; c <= 7; ++c) {
+      double err = fabs(msa_oracle_e2m1((uint8_t)c) - a);
+      if (err < best_err || (err == best_err && (c & 1) == 0)) {
+        best = c;
+        best_err = err;
+      }
+    }
+  }
+  return (uint8_t)(best | (neg ? 8 : 0));
+}
+
 /* bfloat16 is the upper half of an IEEE binary32. */
 double msa_oracle_bf16(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16;
@@ -453,4 +492,103 @@ int msa_oracle_decode(const msa_oracle_problem* p, const void* index_q,
   if (rc) return rc;
   return msa_oracle_sparse_attend(p, q, kv_data, kv_scales, block_table, seq_lens,
                                   q_pos, topk, out, lse);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cache write: quantise new tokens into the paged caches                   */
+/* ------------------------------------------------------------------------ */
+
+/* binary32 rounding of a double: every step below is one correctly rounded
+ * binary32 operation (a double result of an operation on binary32 operands,
+ * rounded once to binary32, is the correctly rounded binary32 result). */
+static double f32(double x) { return (double)(float)x; }
+
+/* Stores the `n` values x[0..n) of one cache row (or column) in format
+ * `dtype` with dequant multiplier `scale`: element i goes to code index
+ * idx(i) of data; for NVFP4 the e4m3 scale of group i/16 goes to scale index
+ * sidx(i/16).  Plain: code = round(x / scale) in the cache's format.  NVFP4
+ * (the generator's quantiser, with the given tensor scale g = scale): per
+ * group of 16, s = e4m3(amax / (6 g)); element q = e2m1(x / (e4m3value(s) g)),
+ * 0 when the scale is 0. */
+typedef size_t (*index_fn)(const void* ctx, int i);
+
+static void store_row(int dtype, double scale, const double* x, int n, void* data, void* scales,
+                      index_fn idx, index_fn sidx, const void* ctx) {
+  double sc = f32(scale);
+  if (dtype == MSA_OR_NVFP4) {
+    for (int g0 = 0; g0 < n; g0 += 16) {
+      double amax = 0.0;
+      for (int i = g0; i < g0 + 16; ++i) amax = fmax(amax, fabs(x[i]));
+      uint8_t s = msa_oracle_encode_e4m3(f32(amax / f32(6.0 * sc)));
+      ((uint8_t*)scales)[sidx(ctx, g0 / 16)] = s;
+      double sg = f32(msa_oracle_e4m3(s) * sc);
+      for (int i = g0; i < g0 + 16; ++i) {
+        uint8_t q = sg == 0.0 ? 0 : msa_oracle_encode_e2m1(f32(x[i] / sg));
+        size_t e = idx(ctx, i);
+        uint8_t* byte = (uint8_t*)data + e / 2;
+        *byte = (e & 1) ? (uint8_t)((*byte & 0x0F) | (q << 4)) : (uint8_t)((*byte & 0xF0) | q);
+      }
+    }
+    return;
+  }
+  for (int i = 0; i < n; ++i) {
+    double v = f32(x[i] / sc);
+    if (dtype == MSA_OR_FP8)
+      ((uint8_t*)data)[idx(ctx, i)] = msa_oracle_encode_e4m3(v);
+    else
+      ((float*)data)[idx(ctx, i)] = (float)v;
+  }
+}
+
+/* element index of a row: K / index keys are token-major ([t][d]), V is
+ * stored transposed ([d][t]) */
+typedef struct {
+  size_t base, row_len;  /* element index of (t = 0, d = 0) of the plane; D or BS */
+  int t, bs, transposed;
+} row_ctx;
+
+static size_t row_elem(const void* c_, int d) {
+  const row_ctx* c = (const row_ctx*)c_;
+  return c->transposed ? c->base + (size_t)d * (size_t)c->bs + (size_t)c->t
+                       : c->base + (size_t)c->t * c->row_len + (size_t)d;
+}
+static size_t row_scale(const void* c_, int grp) {
+  const row_ctx* c = (const row_ctx*)c_;
+  return c->transposed ? c->base / 16 + (size_t)grp * (size_t)c->bs + (size_t)c->t
+                       : c->base / 16 + (size_t)c->t * (c->row_len / 16) + (size_t)grp;
+}
+
+int msa_oracle_cache_write(const msa_oracle_problem* p, int32_t num_tokens,
+                           const int32_t* token_seq, const int32_t* token_pos,
+                           const void* k_new, const void* v_new, const void* ik_new,
+                           const int32_t* block_table, void* kv_data, void* kv_scales,
+                           void* ik_data, void* ik_scales) {
+  if (check_problem(p) || num_tokens < 0) return -1;
+  const int G = p->num_groups, D = p->head_dim, Di = p->index_dim, BS = p->block_size;
+  double* x = (double*)malloc(sizeof(double) * (size_t)(D > Di ? D : Di));
+  if (!x) return -1;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    int32_t b = token_seq[i], pos = token_pos[i];
+    if (b < 0 || b >= p->num_seqs || pos < 0 || pos >= p->max_blocks * BS) continue;
+    int32_t pb = block_table[(size_t)b * (size_t)p->max_blocks + (size_t)(pos / BS)];
+    if (pb < 0 || pb >= p->num_phys_blocks) continue;
+    int t = pos % BS;
+    for (int kv = 0; kv < 2; ++kv) {
+      const void* src = kv == 0 ? k_new : v_new;
+      double scale = kv == 0 ? p->k_scale : p->v_scale;
+      for (int g = 0; g < G; ++g) {
+        for (int d = 0; d < D; ++d)
+          x[d] = read_plain(p->q_dtype, src, ((size_t)i * (size_t)G + (size_t)g) * (size_t)D + (size_t)d);
+        size_t plane = ((size_t)pb * 2 + (size_t)kv) * (size_t)G + (size_t)g;
+        row_ctx c = {plane * (size_t)BS * (size_t)D, (size_t)D, t, BS, kv == 1};
+        store_row(p->kv_dtype, scale, x, D, kv_data, kv_scales, row_elem, row_scale, &c);
+      }
+    }
+    for (int d = 0; d < Di; ++d)
+      x[d] = read_plain(p->index_q_dtype, ik_new, (size_t)i * (size_t)Di + (size_t)d);
+    row_ctx c = {(size_t)pb * (size_t)BS * (size_t)Di, (size_t)Di, t, BS, 0};
+    store_row(p->index_k_dtype, p->index_k_scale, x, Di, ik_data, ik_scales, row_elem, row_scale, &c);
+  }
+  free(x);
+  return 0;
 }

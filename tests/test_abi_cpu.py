@@ -108,3 +108,27 @@ def test_status_strings():
     L = msa.lib()
     assert L.msa_status_string(0) == b"ok"
     assert L.msa_status_string(3) == b"workspace too small"
+
+
+def test_cache_write_rejects_bad_arguments_before_launch():
+    p = good(num_seqs=2, max_blocks_per_seq=4)
+    ok = dict(token_seq=0x1000, token_pos=0x2000, k_new=0x3000, v_new=0x4000, ik_new=0x5000,
+              block_table=0x6000, kv_data=0x7000, kv_scales=None, ik_data=0x8000,
+              ik_scales=None)
+    L = msa.lib()
+
+    def call(n, **kw):
+        a = dict(ok, **kw)
+        return L.msa_cache_write(ctypes.byref(p.c()), n, a["token_seq"], a["token_pos"],
+                                 a["k_new"], a["v_new"], a["ik_new"], a["block_table"],
+                                 a["kv_data"], a["kv_scales"], a["ik_data"], a["ik_scales"],
+                                 None)
+    assert call(0) == 0  # nothing to write: no launch, no pointer needed
+    assert call(-1) == 1
+    assert call(70000) == 2
+    assert call(3, k_new=None) == 1
+    assert call(3, kv_data=0x7008) == 1  # misaligned
+    p4 = good(num_seqs=2, max_blocks_per_seq=4, kv_dtype=msa.NVFP4)
+    assert L.msa_cache_write(ctypes.byref(p4.c()), 3, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000,
+                             0x6000, 0x7000, None, 0x8000, None, None) == 1  # scales missing
+    assert msa.check_problem(p, msa.OP_CACHE_WRITE) == 0

@@ -298,6 +298,85 @@ def test_nan_in_cache_reaches_the_output_without_stalling_the_merge():
     assert int(torch.count_nonzero(dw.ws_decode)) == 0
 
 
+def _cache_write_inputs(kv, ik, q_dtype, iq_dtype, seed, spikes=True):
+    lens = [900, 300, 129, 5000]
+    w = synth.make("cw", seed=seed, seq_lens=lens, q_dtype=q_dtype, index_q_dtype=iq_dtype,
+                   kv_dtype=kv, index_k_dtype=ik, k_scale=0.75, v_scale=1.25,
+                   ik_scale=0.5 if ik != synth.NVFP4 else None, plant_per_seq=1)
+    # block boundaries, both tokens of a V nibble pair, a sequence's last
+    # key, and tokens out of range (skipped)
+    seq = np.array([0, 0, 0, 1, 1, 2, 2, 3, 3, 3, -1, 4, 0], np.int32)
+    pos = np.array([0, 1, 899, 128, 129, 127, 128, 4998, 4999, 2500, 5, 5,
+                    w.max_blocks * 128], np.int32)
+    rng = np.random.default_rng(seed)
+    n, G, D = len(seq), w.num_groups, w.head_dim
+
+    def vals(*shape):
+        x = rng.normal(0, 2.0, shape) * np.where(rng.random(shape) < 0.1, 1e-3, 1.0)
+        if spikes:
+            x[rng.random(shape) < 0.01] = 3000.0  # saturating values
+        return x.astype(np.float32)
+
+    enc = lambda x, dt: x if dt == synth.F32 else synth.encode_bf16(x)
+    new = dict(k=enc(vals(n, G, D), q_dtype), v=enc(vals(n, G, D), q_dtype),
+               ik=enc(vals(n, w.index_dim), iq_dtype))
+    return w, seq, pos, new
+
+
+@pytest.mark.parametrize("kv,ik,q,iq", [(synth.FP8, synth.FP8, synth.BF16, synth.BF16),
+                                        (synth.NVFP4, synth.NVFP4, synth.BF16, synth.BF16),
+                                        (synth.F32, synth.F32, synth.F32, synth.F32),
+                                        (synth.FP8, synth.NVFP4, synth.BF16, synth.BF16)])
+def test_cache_write_is_bit_exact_with_the_oracle(kv, ik, q, iq):
+    w, seq, pos, new = _cache_write_inputs(kv, ik, q, iq, seed=31 + kv + 4 * ik)
+    ref = {k: (None if getattr(w, k) is None else getattr(w, k).copy())
+           for k in ("kv_data", "kv_scales", "ik_data", "ik_scales")}
+    oracle.cache_write(parity.oracle_problem(w), seq, pos, new["k"], new["v"], new["ik"],
+                       w.block_table, ref["kv_data"], ref["kv_scales"], ref["ik_data"],
+                       ref["ik_scales"])
+    dw = parity.DeviceWorkload(w)
+    say(f"[parity] cache write kv={kv} ik={ik}")
+    msa.cache_write(dw.p, parity.dev(seq), parity.dev(pos), parity.dev(new["k"]),
+                    parity.dev(new["v"]), parity.dev(new["ik"]), dw.block_table, dw.kv_data,
+                    dw.kv_scales, dw.ik_data, dw.ik_scales)
+    torch.cuda.synchronize()
+    for name in ("kv_data", "kv_scales", "ik_data", "ik_scales"):
+        if ref[name] is None:
+            continue
+        got = getattr(dw, name).cpu().numpy().view(np.uint8)
+        want = ref[name].view(np.uint8)
+        assert np.array_equal(got, want), f"{name}: {int((got != want).sum())} bytes differ"
+    assert not np.array_equal(ref["kv_data"], w.kv_data)  # the write changed something
+
+
+def test_cache_write_then_decode_sees_the_new_tokens():
+    """A decode step end to end: write every sequence's newest token (and a
+    few older ones) into FP8 caches, then msa_decode; the oracle decodes
+    the caches its own write produced, and the two agree.  (Values of
+    ordinary magnitude: the attention bound is absolute.)"""
+    w, seq, pos, new = _cache_write_inputs(synth.FP8, synth.FP8, synth.BF16, synth.BF16,
+                                           seed=77, spikes=False)
+    keep = (seq >= 0) & (seq < w.num_seqs) & (pos < w.max_blocks * 128)
+    seq, pos = seq[keep], pos[keep]
+    new = {k: np.ascontiguousarray(v[keep]) for k, v in new.items()}
+    import dataclasses
+    ref = {k: getattr(w, k).copy() for k in ("kv_data", "ik_data")}
+    oracle.cache_write(parity.oracle_problem(w), seq, pos, new["k"], new["v"], new["ik"],
+                       w.block_table, ref["kv_data"], None, ref["ik_data"], None)
+    dw = parity.DeviceWorkload(w)
+    msa.cache_write(dw.p, parity.dev(seq), parity.dev(pos), parity.dev(new["k"]),
+                    parity.dev(new["v"]), parity.dev(new["ik"]), dw.block_table, dw.kv_data,
+                    None, dw.ik_data, None)
+    w2 = dataclasses.replace(w, kv_data=ref["kv_data"], ik_data=ref["ik_data"])
+    say("[parity] decode after the cache write")
+    dw.decode()
+    torch.cuda.synchronize()
+    s_ref, k_ref, o_ref, _ = _oracle_all(w2)
+    parity.check_scores(w2, dw.scores.cpu().numpy(), s_ref)
+    same = parity.check_selection(w2, s_ref, k_ref, dw.topk.cpu().numpy())
+    parity.check_attention(w2, dw.out.float().cpu().numpy(), o_ref, mask=same)
+
+
 def test_one_workspace_across_shapes():
     """msa_decode leaves its workspace zero-filled, so one workspace (zeroed
     once) serves calls of different shapes in any order."""

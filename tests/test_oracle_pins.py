@@ -64,6 +64,136 @@ def test_e2m1_table():
     assert len(set(abs(v) for v in got)) == golden()["e2m1_magnitudes"]
 
 
+def _e4m3_test_values():
+    rng = np.random.default_rng(3)
+    v = np.array([oracle.e4m3(c) for c in range(0x7F)])
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)  # every tie between neighbours
+    x = np.concatenate([rng.normal(0, 50, 3000), rng.normal(0, 0.01, 2000), mid, -mid,
+                        [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10]]).astype(np.float32)
+    return x
+
+
+def test_e4m3_encoder_matches_torch_and_the_generator():
+    """Round to nearest even, every tie between neighbouring codes included:
+    torch's float8_e4m3fn cast and the input generator's own encoder agree
+    with the oracle's code-search encoder (within +-448, where torch does
+    not saturate)."""
+    x = _e4m3_test_values()
+    ours = np.array([oracle.encode_e4m3(float(t)) for t in x], np.uint8)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(ours, synth.encode_e4m3(x))
+
+
+def test_e4m3_encoder_saturates_and_keeps_the_sign():
+    assert oracle.encode_e4m3(449.0) == 0x7E
+    assert oracle.encode_e4m3(1e30) == 0x7E and oracle.encode_e4m3(-1e30) == 0xFE
+    assert oracle.encode_e4m3(math.inf) == 0x7E and oracle.encode_e4m3(-math.inf) == 0xFE
+    assert oracle.encode_e4m3(-1e-6) == 0x80 and oracle.encode_e4m3(-0.0) == 0x80
+
+
+def test_e2m1_encoder_round_trip_ties_and_saturation():
+    for c in range(16):  # every code decodes to a value that encodes back to it
+        assert oracle.encode_e2m1(oracle.e2m1(c)) == c
+    # the midpoints between neighbouring magnitudes go to the even code
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for c in range(7):
+        m = (mags[c] + mags[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.encode_e2m1(m) == even
+        assert oracle.encode_e2m1(-m) == even | 8
+        assert oracle.encode_e2m1(m * (1 - 1e-9)) == c
+        assert oracle.encode_e2m1(m * (1 + 1e-9)) == c + 1
+    assert oracle.encode_e2m1(7.0) == 7 and oracle.encode_e2m1(-1e9) == 15
+
+
+def _cache_write_case(kv, ik, q_dtype, iq_dtype, seed=5):
+    """A small problem, its generated caches, and new tokens (some out of
+    range) with their values."""
+    lens = [900, 300, 129]
+    w = synth.make("cw", seed=seed, seq_lens=lens, num_q_heads=16, num_groups=2,
+                   q_dtype=q_dtype, index_q_dtype=iq_dtype, kv_dtype=kv, index_k_dtype=ik,
+                   k_scale=0.75, v_scale=1.25, ik_scale=0.5 if ik != synth.NVFP4 else None)
+    seq = np.array([0, 0, 0, 1, 1, 2, 2, -1, 3, 0], np.int32)
+    pos = np.array([0, 1, 899, 128, 129, 127, 128, 5, 5, w.max_blocks * 128], np.int32)
+    rng = np.random.default_rng(seed)
+    n, G, D = len(seq), w.num_groups, w.head_dim
+    vals = lambda *shape: (rng.normal(0, 2.0, shape) * np.where(rng.random(shape) < 0.1, 1e-3, 1)
+                           ).astype(np.float32)
+    enc = lambda x, dt: x if dt == synth.F32 else synth.encode_bf16(x)
+    new = dict(k=enc(vals(n, G, D), q_dtype), v=enc(vals(n, G, D), q_dtype),
+               ik=enc(vals(n, w.index_dim), iq_dtype))
+    return w, seq, pos, new
+
+
+def _oracle_write(w, seq, pos, new):
+    caches = {k: (None if getattr(w, k) is None else getattr(w, k).copy())
+              for k in ("kv_data", "kv_scales", "ik_data", "ik_scales")}
+    oracle.cache_write(parity_problem(w), seq, pos, new["k"], new["v"], new["ik"],
+                       w.block_table, caches["kv_data"], caches["kv_scales"],
+                       caches["ik_data"], caches["ik_scales"])
+    return caches
+
+
+def parity_problem(w):
+    return oracle.Problem(**w.problem_fields())
+
+
+def test_cache_write_fp8_bytes_are_torch_casts_at_the_right_slots():
+    """Each new value lands, as torch's e4m3 cast of x / scale, exactly at
+    the slot the read side takes it from (K [t][d], V [d][t], index keys
+    [t][d]); out-of-range tokens and every other byte are left alone."""
+    w, seq, pos, new = _cache_write_case(synth.FP8, synth.FP8, synth.BF16, synth.BF16)
+    c = _oracle_write(w, seq, pos, new)
+    kv = w.kv_data.copy()
+    ik = w.ik_data.copy()
+    bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    cast = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for i, (b, p) in enumerate(zip(seq, pos)):
+        if b < 0 or b >= w.num_seqs or p >= w.max_blocks * 128:
+            continue
+        pb, t = w.block_table[b, p // 128], p % 128
+        for g in range(w.num_groups):
+            kv[pb, 0, g, t, :] = cast(np.float32(bf(new["k"][i, g])) / np.float32(w.k_scale))
+            kv[pb, 1, g, :, t] = cast(np.float32(bf(new["v"][i, g])) / np.float32(w.v_scale))
+        ik[pb, t, :] = cast(np.float32(bf(new["ik"][i])) / np.float32(w.index_k_scale))
+    assert np.array_equal(c["kv_data"], kv)
+    assert np.array_equal(c["ik_data"], ik)
+
+
+def test_cache_write_nvfp4_representable_values_come_back_exactly():
+    """Values built as e4m3(s) * e2m1(q) * scale, with each group holding a
+    +-6 element (so amax / (6 scale) is exactly the e4m3 value of s), are
+    stored as exactly those codes: the NVFP4 write is exact on its own grid."""
+    import dataclasses
+    w, seq, pos, new = _cache_write_case(synth.NVFP4, synth.NVFP4, synth.BF16, synth.BF16)
+    w = dataclasses.replace(w, k_scale=2.0 ** -8)  # a power of two: every product exact
+    rng = np.random.default_rng(9)
+    G, D = w.num_groups, w.head_dim
+    s_codes = rng.integers(0x20, 0x50, (len(seq), G, D // 16))
+    q_codes = rng.integers(0, 16, (len(seq), G, D))
+    q_codes[..., ::16] = 7  # one +6 per group
+    e4 = np.vectorize(oracle.e4m3)(s_codes)
+    e2 = np.vectorize(oracle.e2m1)(q_codes)
+    x = (np.repeat(e4, 16, axis=-1) * e2 * w.k_scale).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), np.repeat(e4, 16, axis=-1) * e2 * w.k_scale)
+    bfx = synth.encode_bf16(x)
+    assert np.array_equal((bfx.astype(np.uint32) << 16).view(np.float32), x)  # bf16-exact
+    new["k"] = bfx
+    c = _oracle_write(w, seq, pos, new)
+    b, p = int(seq[0]), int(pos[0])
+    pb, t = w.block_table[b, p // 128], p % 128
+    for g in range(G):
+        plane = c["kv_data"][pb, 0, g].reshape(128, D // 2)[t]
+        got_q = np.stack([plane & 15, plane >> 4], -1).reshape(D)
+        got_q = np.where(got_q == 8, 0, got_q)  # a zero element may keep its sign
+        want_q = np.where(q_codes[0, g] == 8, 0, q_codes[0, g])
+        assert np.array_equal(got_q, want_q)
+        sc = c["kv_scales"][pb, 0, g].reshape(128, D // 16)[t]
+        assert np.array_equal(sc, s_codes[0, g])
+
+
 def test_bf16_matches_torch():
     rng = np.random.default_rng(1)
     bits = np.concatenate([rng.integers(0, 1 << 16, 20000),
