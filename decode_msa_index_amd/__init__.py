@@ -46,6 +46,7 @@ class MsaProblem(ctypes.Structure):
         ("sm_scale", ctypes.c_float), ("index_scale", ctypes.c_float),
         ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("index_k_scale", ctypes.c_float),
+        ("init_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
     ]
 
 
@@ -72,6 +73,8 @@ class Problem:
     k_scale: float = 1.0
     v_scale: float = 1.0
     index_k_scale: float = 1.0
+    init_blocks: int = 0
+    local_blocks: int = 0
 
     def c(self) -> MsaProblem:
         return MsaProblem(*[getattr(self, f.name) for f in fields(self)])

@@ -41,6 +41,8 @@ msa::Shape shape_of(const msa_problem* p) {
   s.MB = p->max_blocks_per_seq;
   s.P = p->num_phys_blocks;
   s.K = p->top_k;
+  s.init = p->init_blocks;
+  s.local = p->local_blocks > 1 ? p->local_blocks : 1;
   s.q_dtype = p->q_dtype;
   s.iq_dtype = p->index_q_dtype;
   s.kv_dtype = p->kv_dtype;
@@ -104,6 +106,11 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op) {
     return fail(MSA_ERR_UNSUPPORTED, "head_dim and index_dim must be 128");
   if (p->block_size != 128) return fail(MSA_ERR_UNSUPPORTED, "block_size must be 128");
   if (p->top_k > 32) return fail(MSA_ERR_UNSUPPORTED, "top_k must be <= 32");
+  if (p->init_blocks < 0 || p->local_blocks < 0)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "init_blocks and local_blocks must be >= 0");
+  if ((long long)p->init_blocks + (p->local_blocks > 1 ? p->local_blocks : 1) > p->top_k)
+    return fail(MSA_ERR_INVALID_ARGUMENT,
+                "init_blocks + max(local_blocks, 1) > top_k: the forced blocks do not fit");
   const int G = p->num_kv_groups, hpg = p->num_q_heads / p->num_kv_groups;
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(MSA_ERR_UNSUPPORTED, "num_kv_groups must be 1, 2, 4 or 8");

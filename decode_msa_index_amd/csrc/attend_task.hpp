@@ -17,7 +17,8 @@
 //   P   = exp2(S*scale - m) in fp32, rounded to f16 for the next product
 //   O  += P V              v_mfma_f32_16x16x32_f16   (V e4m3/e2m1 -> f16 exact)
 // with an online-softmax running state; the waves' states merge through LDS,
-// and the S shares through device-scope stores and a last-arriver merge.
+// and the S shares through coherent stores that the unit's last share polls
+// for and merges.
 //
 // Operand layout.  The contraction order inside an MFMA is free as long as
 // both operands agree, so the key order of the S^T tiles is chosen to make
@@ -59,6 +60,7 @@ struct AttendArgs {
   void* out;
   float* lse;
   int R, H, G, hpg, MB, K, P;
+  int init, local;   // forced blocks (select + attend): first `init`, last `local` (>= 1)
   float scale_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
   int out_f32;
@@ -146,6 +148,8 @@ inline AttendArgs make_attend_args(const Shape& s, const int32_t* block_table,
   a.MB = s.MB;
   a.K = s.K;
   a.P = s.P;
+  a.init = s.init;
+  a.local = s.local;
   a.scale_log2 = s.sm_scale * s.k_scale * 1.4426950408889634f;
   a.v_scale = s.v_scale;
   a.out_f32 = s.out_dtype == kF32;
@@ -258,6 +262,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     int32_t* btl = reinterpret_cast<int32_t*>(keys + a.MB);
     const int32_t* brow = a.bt + (size_t)b * a.MB;
     uint32_t tmax = 0u;
+    const int c0 = a.init, c1 = rb + 1 - a.local;  // the free candidates
     const float* srow = a.scores + (size_t)u * a.MB;
     for (int base = 0; base < a.MB; base += 8 * 64 * NW) {
       float v[8];
@@ -275,11 +280,11 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
           const uint32_t k = order_key(v[r]);
           keys[jj] = k;
           btl[jj] = e[r];
-          if (jj < rb) tmax = max(tmax, k);
+          if (jj >= c0 && jj < c1) tmax = max(tmax, k);
         }
       }
     }
-    group_select<NW>(keys, rb, a.K, tmax, gsl, sel_lds, sel_w[wave]);
+    group_select<NW>(keys, rb, a.K, a.init, a.local, tmax, gsl, sel_lds, sel_w[wave]);
     if (a.clear && part.S == 1) clear_row(a, u, NW);
     if (split == 0 && wave == 0 && a.topk_out) {  // the stored selection ascends
       const int v = sort_selection(lane < a.K ? sel_w[0][lane] : -1, a.K);

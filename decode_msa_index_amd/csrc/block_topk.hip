@@ -2,12 +2,15 @@
 //
 // Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
 // primer"): attention covers the top 16 blocks by pooled index score and
-// always keeps the most recent block.  The recent block counts inside the k,
-// so the rest is the best k-1 of blocks 0..rb-1; ties go to the lower block
+// always keeps the most recent block.  The recent block counts inside the k;
+// so do the leading and trailing blocks that the indexer's init_blocks /
+// local_blocks settings force (select_wave.hpp states the reading).  The
+// rest is the best of the free blocks c0 .. c1-1; ties go to the lower block
 // index, which makes the selection unique and deterministic.
 //
-// One 256-thread workgroup per (row, group).  The row's scores are read once
-// into LDS as order-preserving 32-bit keys; the k-1 best candidates are found
+// Rows of more than 16,000 blocks: one 256-thread workgroup per (row,
+// group).  The row's scores are read as order-preserving 32-bit keys; the
+// best free candidates are found
 // as a threshold by radix select on them (4 passes of 8 bits, per-wave LDS
 // histograms), then the blocks
 // above the threshold and the lowest-indexed ties at the threshold are
@@ -51,7 +54,7 @@ template <bool kLds>
 __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
-    int K) {
+    int K, int init, int local) {
   extern __shared__ uint32_t keys[];  // kLds: one order key per candidate block
   __shared__ uint32_t hist[4][256];
   __shared__ uint32_t scan_sm[4];
@@ -71,14 +74,16 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
     for (int i = tid; i < K; i += 256) out[i] = i <= rb ? i : -1;
     return;
   }
-  if (K == 1) {  // only the forced recent block
-    if (tid == 0) out[0] = rb;
-    return;
-  }
-  const int ncand = rb;  // blocks 0..rb-1 compete for k-1 places
+  // forced blocks: 0 .. init-1 lead the row, c1 .. rb end it
+  const int c0 = init, c1 = rb + 1 - local, need = K - init - local;
+  for (int i = tid; i < init; i += 256) out[i] = i;
+  for (int i = tid; i < local; i += 256) out[init + need + i] = c1 + i;
+  if (need == 0) return;
+  const int ncand = c1 - c0;  // free blocks c0 .. c1-1 compete for `need` places
+  const float* sc = s + c0;
   auto key_at = [&](int jj) -> uint32_t {
     if constexpr (kLds) return keys[jj];
-    else return order_key(s[jj]);
+    else return order_key(sc[jj]);
   };
   if constexpr (kLds) {
     // read the row once, 4 loads in flight per thread per round
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int jj = base + k * 256 + tid;
-        v[k] = jj < ncand ? s[jj] : 0.0f;
+        v[k] = jj < ncand ? sc[jj] : 0.0f;
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
       }
     }
   }
-  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)(K - 1);
+  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)need;
   for (int pass = 3; pass >= 0; --pass) {
     const int shift = pass * 8;
     for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
     rem = pick[1];
     __syncthreads();
   }
-  // prefix is now the key of the (k-1)-th best candidate; `rem` of the
+  // prefix is now the key of the need-th best candidate; `rem` of the
   // candidates equal to it are taken, lowest block index first.
   const int chunk = (ncand + 255) / 256;
   const int j0 = min(tid * chunk, ncand), j1 = min(j0 + chunk, ncand);
@@ -147,9 +152,8 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
       take = eq_seen < eq_take;
       ++eq_seen;
     }
-    if (take) out[w++] = jj;
+    if (take) out[init + w++] = c0 + jj;
   }
-  if (tid == 0) out[K - 1] = rb;
 }
 
 constexpr int kWaveSelectMax = 16000;  // keys + histogram stay under 64 KB of LDS
@@ -157,7 +161,7 @@ constexpr int kWaveSelectMax = 16000;  // keys + histogram stay under 64 KB of L
 __global__ __launch_bounds__(64) void block_topk_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
-    int K) {
+    int K, int init, int local) {
   extern __shared__ uint32_t lds[];  // [256] scratch, then [MB] keys
   const int u = blockIdx.x, row = u / G, b = row / R;
   const float* s = scores + (size_t)u * MB;
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(64) void block_topk_wave_kernel(
   const int rb = pos < 0 ? -1 : pos / kBlock;
   if (rb > 32 * 64) load_keys(s + 32 * 64, rb - 32 * 64, lds + 256 + 32 * 64, 64);
   wave_lds_sync();
-  wave_select_keys(lds + 256, rb, K, lds, topk + (size_t)u * K);
+  wave_select_keys(lds + 256, rb, K, init, local, lds, topk + (size_t)u * K);
 }
 
 hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
@@ -175,10 +179,10 @@ hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t*
   if (s.MB <= kWaveSelectMax) {
     hipLaunchKernelGGL(block_topk_wave_kernel, dim3(s.rows * s.G), dim3(64),
                        sizeof(uint32_t) * (256 + s.MB), st, scores, seq_lens, q_pos, topk, s.R,
-                       s.G, s.MB, s.K);
+                       s.G, s.MB, s.K, s.init, s.local);
   } else {
     hipLaunchKernelGGL(block_topk_kernel<false>, dim3(s.rows * s.G), dim3(256), 0, st, scores,
-                       seq_lens, q_pos, topk, s.R, s.G, s.MB, s.K);
+                       seq_lens, q_pos, topk, s.R, s.G, s.MB, s.K, s.init, s.local);
   }
   return hipGetLastError();
 }

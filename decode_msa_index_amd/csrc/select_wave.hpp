@@ -2,22 +2,30 @@
 //
 // Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
 // primer"): keep the top-k blocks by pooled index score, the most recent
-// block always among them.  The recent block counts inside the k, so the
-// rest is the best k-1 of blocks 0..rb-1, ties to the lower block index.
+// block always among them.  The recent block counts inside the k.  The
+// indexer's init_blocks / local_blocks settings (same blog, the sparse
+// attention layer's constructor) add more always-kept blocks: read here as
+// the first `init` blocks and the last `local` (>= 1, the recent one
+// included) blocks of 0..rb, all inside the k.  When rb + 1 > k the free
+// candidates are then the contiguous blocks c0 = init .. c1 - 1 with
+// c1 = rb + 1 - local, and the k - init - local best of them are kept, ties
+// to the lower block index (the host checks init + local <= k, so there are
+// more free candidates than places).
 //
 // Candidates are ordered by the composite key (order-preserving 32-bit key of
 // the score, then lower block index), which makes every key distinct.  The
 // keys sit in LDS (the caller may have put them there with several waves).
 //
-// Fast path: each lane, holding blocks l, l+64, ..., takes its best
-// candidate; a 64-lane bitonic sort of those gives T0, the (k-1)-th best lane
-// maximum.  At least k-1 candidates are >= T0, so the k-1 best are all >= T0:
-// only those "survivors" can be selected.  They are usually about k; they
-// take slots through an LDS counter (order is irrelevant, they are sorted
-// next), a second bitonic sort puts the k-1 best in the first lanes and a
-// third orders their block ids.  With more than 64 survivors (a strongly
+// Fast path (need = the number of places left for free candidates): each
+// lane, holding candidates l, l+64, ..., takes its best; a 64-lane bitonic
+// sort of those gives T0, the need-th best lane maximum.  At least need
+// candidates are >= T0, so the need best are all >= T0: only those
+// "survivors" can be selected.  They are usually about k; they take slots
+// through an LDS counter (order is irrelevant, they are sorted next), a
+// second bitonic sort puts the need best in the first lanes and a third
+// orders their block ids.  With more than 64 survivors (a strongly
 // structured score pattern) a radix select over the bits below the keys'
-// common prefix (8-bit digits, LDS histogram, wave scan) finds the (k-1)-th
+// common prefix (8-bit digits, LDS histogram, wave scan) finds the need-th
 // key and a ballot-based compaction writes the ids.  Lane exchanges use DPP
 // and the CDNA4 row-swap instructions, not LDS permutes.
 #pragma once
@@ -92,8 +100,10 @@ __device__ __forceinline__ void wave_bitonic(uint32_t& key, int& idx) {
 }
 
 // Radix path.  keys[0..ncand) in LDS; writes out[0..need) ascending.
+// Radix select of the `need` best of keys[0..ncand): writes base + their
+// indices to out in ascending order.
 __device__ __noinline__ void select_radix(const uint32_t* keys, int ncand, int need,
-                                          uint32_t* hist, int32_t* out) {
+                                          uint32_t* hist, int32_t* out, int base) {
   const int lane = threadIdx.x & 63;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int jj = lane; jj < ncand; jj += 64) {
@@ -165,18 +175,25 @@ __device__ __noinline__ void select_radix(const uint32_t* keys, int ncand, int n
     const uint64_t eqm = __ballot(eq);
     const bool take = gt || (eq && ties_seen + (uint32_t)popc_below(eqm, lane) < rem);
     const uint64_t tm = __ballot(take);
-    if (take) out[written + (uint32_t)popc_below(tm, lane)] = jj;
+    if (take) out[written + (uint32_t)popc_below(tm, lane)] = base + jj;
     written += (uint32_t)__popcll(tm);
     ties_seen += (uint32_t)__popcll(eqm);
   }
 }
 
-// Selection from keys already in LDS: keys[0..rb) hold the order keys of
-// blocks 0..rb-1 (rb = last visible block, -1 if the row sees no key).  hist:
-// 256 words of LDS scratch.  Writes K entries to out: ascending block ids,
-// -1 padded.  Must be called by all 64 lanes of one wave.
-__device__ void wave_select_keys(const uint32_t* keys, int rb, int K, uint32_t* hist,
-                                 int32_t* out) {
+// The f-th forced block (f < init + local) of a row whose free candidates
+// end at c1: the leading blocks first, then the trailing ones.
+__device__ __forceinline__ int forced_block(int f, int init, int c1) {
+  return f < init ? f : c1 + (f - init);
+}
+
+// Selection from keys already in LDS: keys[0..rb] hold the order keys of
+// blocks 0..rb (rb = last visible block, -1 if the row sees no key; the
+// forced blocks' keys are not read).  hist: 256 words of LDS scratch.
+// Writes K entries to out: ascending block ids, -1 padded.  Must be called
+// by all 64 lanes of one wave.
+__device__ void wave_select_keys(const uint32_t* keys, int rb, int K, int init, int local,
+                                 uint32_t* hist, int32_t* out) {
   const int lane = threadIdx.x & 63;
   if (rb < 0) {  // the row sees no key: nothing to select
     for (int i = lane; i < K; i += 64) out[i] = -1;
@@ -186,13 +203,15 @@ __device__ void wave_select_keys(const uint32_t* keys, int rb, int K, uint32_t* 
     for (int i = lane; i < K; i += 64) out[i] = i <= rb ? i : -1;
     return;
   }
-  const int ncand = rb, need = K - 1;
+  const int c0 = init, c1 = rb + 1 - local;
+  const int ncand = c1 - c0, need = K - init - local;
+  const uint32_t* ck = keys + c0;  // the free candidates
   if (need > 0) {
     // ---- each lane's best, then T0 = the need-th best lane maximum ----
     uint32_t bk = 0u;
     int bi = 0x7FFFFFFF;
     for (int jj = lane; jj < ncand; jj += 64) {
-      const uint32_t k = keys[jj];
+      const uint32_t k = ck[jj];
       if (k > bk) {  // jj ascends: the first maximum has the lowest index
         bk = k;
         bi = jj;
@@ -206,7 +225,7 @@ __device__ void wave_select_keys(const uint32_t* keys, int rb, int K, uint32_t* 
     if (lane == 0) *cnt = 0u;
     wave_lds_sync();
     for (int jj = lane; jj < ncand; jj += 64) {
-      const uint32_t k = keys[jj];
+      const uint32_t k = ck[jj];
       if (!better(tk, ti, k, jj)) {
         const uint32_t slot = atomicAdd(cnt, 1u);
         if (slot < 64) {
@@ -219,17 +238,19 @@ __device__ void wave_select_keys(const uint32_t* keys, int rb, int K, uint32_t* 
     const uint32_t total = *cnt;
     wave_lds_sync();
     if (total > 64) {  // strongly structured scores: take the radix path
-      select_radix(keys, ncand, need, hist, out);
+      select_radix(ck, ncand, need, hist, out + init, c0);
     } else {
-      uint32_t ck = (uint32_t)lane < total ? hist[lane] : 0u;
-      int ci = (uint32_t)lane < total ? (int)hist[64 + lane] : 0x7FFFFFFF;
-      wave_bitonic<true, 64>(ck, ci);  // lanes 0..need-1: the selection (need <= 31)
-      if (lane >= need) ci = 0x7FFFFFFF;
-      wave_bitonic<false, 32>(ck, ci);  // ascending block ids in lanes 0..need-1
-      if (lane < need) out[lane] = ci;
+      uint32_t sk = (uint32_t)lane < total ? hist[lane] : 0u;
+      int si = (uint32_t)lane < total ? (int)hist[64 + lane] : 0x7FFFFFFF;
+      wave_bitonic<true, 64>(sk, si);  // lanes 0..need-1: the selection (need <= 31)
+      if (lane >= need) si = 0x7FFFFFFF;
+      wave_bitonic<false, 32>(sk, si);  // ascending block ids in lanes 0..need-1
+      if (lane < need) out[init + lane] = c0 + si;
     }
   }
-  if (lane == 0) out[K - 1] = rb;
+  // forced blocks around the chosen ones keep the row ascending
+  if (lane < init) out[lane] = lane;
+  if (lane < local) out[init + need + lane] = c1 + lane;
   wave_lds_sync();
 }
 
@@ -280,28 +301,31 @@ __device__ __forceinline__ void sort_desc(T& v) {
 }
 
 // Selection by a whole workgroup of NW waves, for a kernel whose threads
-// have just loaded the row's keys.  keys[0..rb) in LDS hold the order keys
-// of blocks 0..rb-1; each thread passes the largest key among the blocks
-// (< rb) it loaded (0 if none).
+// have just loaded the row's keys, thread t the blocks jj with jj % (64 NW)
+// == t.  keys[0..rb] in LDS hold the order keys of blocks 0..rb; each
+// thread passes the largest key among the free candidates c0 .. c1-1 it
+// loaded (0 if none).
 //
 // The candidates fall into 32 groups: group l holds the blocks loaded by the
-// threads at lane positions l and l + 32 of every wave.  T0 is the (k-1)-th
-// largest group maximum (a 32-lane sort of the maxima).  At least k-1
-// candidates are >= T0, so the k-1 best all are: each wave re-reads its
-// threads' keys and compacts its survivors (ballot + mbcnt) into a region
-// of its own.  The survivors, usually about k, are gathered into lanes as
-// composites (key, then lower block id) and sorted, 32 or 64 lanes wide;
-// the first k-1 lanes hold the selection.  All of it runs in registers with
-// lane exchanges; every wave computes T0 and the result itself, which saves
-// barriers and broadcasts.  More than 64 survivors (strongly structured
-// scores) fall back to the radix select run by wave 0 over the LDS keys.
+// threads at lane positions l and l + 32 of every wave, i.e. the blocks with
+// jj % 32 == l.  T0 is the need-th largest group maximum (a 32-lane sort of
+// the maxima); the candidates are contiguous and more than need, so at
+// least need groups are non-empty and at least need candidates are >= T0:
+// the need best all are.  Each wave re-reads its threads' keys and compacts
+// its survivors (ballot + mbcnt) into a region of its own.  The survivors,
+// usually about k, are gathered into lanes as composites (key, then lower
+// block id) and sorted, 32 or 64 lanes wide; the first need lanes hold the
+// selection.  All of it runs in registers with lane exchanges; every wave
+// computes T0 and the result itself, which saves barriers and broadcasts.
+// More than 64 survivors (strongly structured scores) fall back to the
+// radix select run by wave 0 over the LDS keys.
 //
 // On return out_w (this wave's own 32-entry row) holds the K selected block
-// ids, -1 padded: the recent block rb at K-1, the others before it in an
+// ids, -1 padded: the chosen free blocks first, then the forced ones, in an
 // order that is the same in every workgroup making this selection (not
 // sorted; sort_selection orders a copy).  All LDS writes the threads made
 // before the call are visible to the whole workgroup.  Called by every
-// thread with workgroup-uniform rb and K <= 32.
+// thread with workgroup-uniform rb, K <= 32, init and local.
 template <int NW>
 struct GroupSelectLds {
   uint32_t tmax[64 * NW];    // each thread's largest key
@@ -311,22 +335,26 @@ struct GroupSelectLds {
 };
 
 template <int NW>
-__device__ __forceinline__ void group_select(const uint32_t* keys, int rb, int K, uint32_t tmax,
-                             GroupSelectLds<NW>& g, uint32_t* hist, int32_t* out_w) {
+__device__ __forceinline__ void group_select(const uint32_t* keys, int rb, int K, int init,
+                                             int local, uint32_t tmax, GroupSelectLds<NW>& g,
+                                             uint32_t* hist, int32_t* out_w) {
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int need = K - 1;
+  const int c0 = init, c1 = rb + 1 - local;
+  const int need = K - init - local;
   if (rb < 0 || rb + 1 <= K || need == 0) {  // nothing to choose
     __syncthreads();
-    if (lane < K) out_w[lane] = rb < 0 ? -1 : (rb + 1 <= K ? (lane <= rb ? lane : -1) : rb);
+    if (lane < K)
+      out_w[lane] = rb < 0 ? -1
+                           : (rb + 1 <= K ? (lane <= rb ? lane : -1) : forced_block(lane, init, c1));
     wave_lds_sync();
     return;
   }
-  const int ncand = rb;
+  const int ncand = c1 - c0;
+  const uint32_t* ck = keys + c0;  // the free candidates
   g.tmax[threadIdx.x] = tmax;
   __syncthreads();
-  // ---- T0: the need-th largest of the 32 group maxima.  Groups l <
-  // min(32, ncand) hold block l and ncand > need, so at least need groups
-  // are non-empty; empty groups hold 0, below every real key ----
+  // ---- T0: the need-th largest of the 32 group maxima; empty groups hold
+  // 0, below every real key ----
   uint32_t gm = g.tmax[lane];
 #pragma unroll
   for (int w = 1; w < NW; ++w) gm = max(gm, g.tmax[w * 64 + lane]);
@@ -340,7 +368,7 @@ __device__ __forceinline__ void group_select(const uint32_t* keys, int rb, int K
   for (int base = 0; base < ncand; base += 8 * NT) {
     uint32_t kk[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) kk[r] = keys[min(base + r * NT + (int)threadIdx.x, ncand - 1)];
+    for (int r = 0; r < 8; ++r) kk[r] = ck[min(base + r * NT + (int)threadIdx.x, ncand - 1)];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int jj = base + r * NT + (int)threadIdx.x;
@@ -362,7 +390,7 @@ __device__ __forceinline__ void group_select(const uint32_t* keys, int rb, int K
     total += g.surv_n[w];
   }
   if (total > 64) {
-    if (wave == 0) select_radix(keys, ncand, need, hist, g.radix_out);
+    if (wave == 0) select_radix(ck, ncand, need, hist, g.radix_out, c0);
     __syncthreads();
     if (lane < need) out_w[lane] = g.radix_out[lane];
   } else {
@@ -385,9 +413,9 @@ __device__ __forceinline__ void group_select(const uint32_t* keys, int rb, int K
       sort_desc<32>(ci);
     else
       sort_desc<64>(ci);
-    if (lane < need) out_w[lane] = cand_index(ci);
+    if (lane < need) out_w[lane] = c0 + cand_index(ci);
   }
-  if (lane == 0) out_w[K - 1] = rb;
+  if (lane >= need && lane < K) out_w[lane] = forced_block(lane - need, init, c1);
   wave_lds_sync();
 }
 

@@ -11,6 +11,7 @@
  * Four calls follow those steps:
  *   msa_index_scores   scores + per-block max-pool          (indexer)
  *   msa_block_topk     top-k blocks, recent block forced     (selection)
+ *                      (and optional leading / trailing blocks)
  *   msa_sparse_attend  exact GQA attention over the blocks   (main attention)
  *   msa_decode         the three in one call
  * msa_decode's scores and selection are bitwise those of the three-call
@@ -118,6 +119,10 @@ typedef struct msa_problem {
   float k_scale;              /* K dequant multiplier (> 0) */
   float v_scale;              /* V dequant multiplier */
   float index_k_scale;        /* index-key dequant multiplier (> 0) */
+  int32_t init_blocks;        /* >= 0: leading blocks 0..init_blocks-1 always kept */
+  int32_t local_blocks;       /* >= 0: the last max(local_blocks, 1) visible blocks
+                                 always kept (0 and 1: the recent block alone);
+                                 init_blocks + max(local_blocks, 1) <= top_k */
 } msa_problem;
 
 /*
@@ -164,10 +169,15 @@ msa_status msa_index_scores(const msa_problem* p, const void* index_q, const voi
 /*
  * Block selection (blog, "MSA primer": top 16 blocks, most recent block
  * always kept).  For row r with last visible block rb = pos / BS: if
- * rb + 1 <= K all blocks 0..rb are kept; otherwise rb plus the K-1 best of
- * 0..rb-1 by (block_scores descending, block index ascending).  Output
- * ascending, -1 padded.  Deterministic: ties go to the lower block index.
- * block_scores entries must not be NaN.
+ * rb + 1 <= K all blocks 0..rb are kept.  Otherwise the forced blocks are
+ * kept -- 0 .. init_blocks-1 and the last L = max(local_blocks, 1) blocks
+ * rb-L+1 .. rb (the indexer's sparse_init_block / sparse_local_block
+ * settings, named in the blog's sparse attention layer; read as blocks
+ * always kept inside the k) -- plus the K - init_blocks - L best of the
+ * free blocks init_blocks .. rb-L by (block_scores descending, block index
+ * ascending).  With init_blocks = local_blocks = 0 that is rb plus the K-1
+ * best of 0..rb-1.  Output ascending, -1 padded.  Deterministic: ties go to
+ * the lower block index.  block_scores entries must not be NaN.
  */
 msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
                           const int32_t* seq_lens, const int32_t* q_pos, int32_t* topk_idx,

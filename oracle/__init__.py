@@ -47,6 +47,7 @@ class _Problem(ctypes.Structure):
         ("sm_scale", ctypes.c_double), ("index_scale", ctypes.c_double),
         ("k_scale", ctypes.c_double), ("v_scale", ctypes.c_double),
         ("index_k_scale", ctypes.c_double), ("num_threads", ctypes.c_int32),
+        ("init_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
     ]
 
 
@@ -107,6 +108,8 @@ class Problem:
     v_scale: float = 1.0
     index_k_scale: float = 1.0
     num_threads: int = 0
+    init_blocks: int = 0
+    local_blocks: int = 0
 
     def c(self) -> _Problem:
         return _Problem(*[getattr(self, f[0]) for f in _Problem._fields_])

@@ -158,7 +158,9 @@ static int check_problem(const msa_oracle_problem* p) {
       p->num_q_heads < p->num_groups || p->num_q_heads % p->num_groups ||
       p->head_dim < 16 || p->head_dim % 16 || p->index_dim < 16 ||
       p->index_dim % 16 || p->block_size < 2 || p->block_size % 2 ||
-      p->top_k < 1 || p->max_blocks < 1 || p->num_phys_blocks < 1)
+      p->top_k < 1 || p->max_blocks < 1 || p->num_phys_blocks < 1 ||
+      p->init_blocks < 0 || p->local_blocks < 0 ||
+      p->init_blocks + (p->local_blocks > 1 ? p->local_blocks : 1) > p->top_k)
     return -1;
   return 0;
 }
@@ -343,8 +345,17 @@ typedef struct {
 /* The top-k blocks with the most recent block always kept, so at most
  * top_k * block_size keys per query (vLLM blog, "MSA primer": top 16 blocks,
  * most recent block always kept, at most 2,048 keys).  The recent block is
- * the one holding the row's own position; it counts inside the k.  Output:
- * ascending logical ids, then -1. */
+ * the one holding the row's own position; it counts inside the k.
+ *
+ * The indexer also takes sparse_init_block and sparse_local_block (vLLM
+ * blog, "MiniMaxM3SparseAttention" constructor: init_blocks and
+ * local_blocks, both 0 unless configured; nothing more is said of them).
+ * Read here as blocks that are always kept besides the recent one, inside
+ * the k like it: the first init_blocks blocks 0 .. init_blocks-1 and the
+ * last max(local_blocks, 1) blocks of 0..recent (so local_blocks 0 and 1
+ * both mean the recent block alone).  The k - (number forced) best of the
+ * remaining blocks fill the rest, by score and then lower block index.
+ * Output: ascending logical ids, then -1. */
 static void topk_unit(void* c_, int64_t unit) {
   topk_ctx* c = (topk_ctx*)c_;
   const msa_oracle_problem* p = c->p;
@@ -357,19 +368,26 @@ static void topk_unit(void* c_, int64_t unit) {
     return;
   }
   int32_t recent = (int32_t)(pos / p->block_size);
+  int32_t n_local = p->local_blocks > 1 ? p->local_blocks : 1;
   int32_t n_sel = 0;
   int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)p->top_k);
   if (recent + 1 <= p->top_k) {
     for (int32_t j = 0; j <= recent; ++j) sel[n_sel++] = j;
   } else {
-    cand* cs = (cand*)malloc(sizeof(cand) * (size_t)recent);
-    for (int32_t j = 0; j < recent; ++j) {
-      cs[j].s = s[j];
-      cs[j].j = j;
+    cand* cs = (cand*)malloc(sizeof(cand) * (size_t)(recent + 1));
+    int32_t n_cand = 0;
+    for (int32_t j = 0; j <= recent; ++j) {
+      int forced = j < p->init_blocks || j > recent - n_local;
+      if (forced) {
+        sel[n_sel++] = j;
+      } else {
+        cs[n_cand].s = s[j];
+        cs[n_cand].j = j;
+        ++n_cand;
+      }
     }
-    qsort(cs, (size_t)recent, sizeof(cand), cand_cmp);
-    for (int32_t i = 0; i < p->top_k - 1; ++i) sel[n_sel++] = cs[i].j;
-    sel[n_sel++] = recent;
+    qsort(cs, (size_t)n_cand, sizeof(cand), cand_cmp);
+    for (int32_t i = 0; n_sel < p->top_k && i < n_cand; ++i) sel[n_sel++] = cs[i].j;
     free(cs);
     qsort(sel, (size_t)n_sel, sizeof(int32_t), int_cmp);
   }

@@ -163,6 +163,8 @@ class Workload:
     seq_lens: np.ndarray
     q_pos: np.ndarray | None
     planted: dict = field(default_factory=dict)
+    init_blocks: int = 0    # leading blocks always selected
+    local_blocks: int = 0   # trailing blocks always selected (0, 1: the recent one)
     recipe: str = ""
 
     @property
@@ -173,7 +175,8 @@ class Workload:
         keys = ["num_seqs", "rows_per_seq", "num_q_heads", "num_groups", "head_dim",
                 "index_dim", "block_size", "top_k", "max_blocks", "num_phys_blocks",
                 "q_dtype", "index_q_dtype", "kv_dtype", "index_k_dtype", "sm_scale",
-                "index_scale", "k_scale", "v_scale", "index_k_scale"]
+                "index_scale", "k_scale", "v_scale", "index_k_scale", "init_blocks",
+                "local_blocks"]
         return {k: getattr(self, k) for k in keys}
 
     def index_tokens(self) -> int:

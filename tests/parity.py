@@ -33,7 +33,8 @@ def problem(w: synth.Workload, out_dtype=msa.BF16) -> msa.Problem:
         num_phys_blocks=w.num_phys_blocks, q_dtype=w.q_dtype, index_q_dtype=w.index_q_dtype,
         kv_dtype=w.kv_dtype, index_k_dtype=w.index_k_dtype, out_dtype=out_dtype,
         sm_scale=w.sm_scale, index_scale=w.index_scale, k_scale=w.k_scale,
-        v_scale=w.v_scale, index_k_scale=w.index_k_scale)
+        v_scale=w.v_scale, index_k_scale=w.index_k_scale, init_blocks=w.init_blocks,
+        local_blocks=w.local_blocks)
 
 
 def oracle_problem(w: synth.Workload, threads: int = 0):
@@ -192,16 +193,20 @@ def selection_matches(w, ref_scores, ref_sel, got_sel, row, g) -> bool:
         return True
     pos = row_pos(w, row)
     rb = pos // w.block_size
-    assert rb in bsel and len(bsel) == len(a), f"row {row} group {g}: {bsel} vs {a}"
+    n_local = max(w.local_blocks, 1)
+    forced = {j for j in range(rb + 1) if j < w.init_blocks or j > rb - n_local}
+    free = [j for j in range(rb + 1) if j not in forced]
+    assert forced <= set(bsel) and len(bsel) == len(a), f"row {row} group {g}: {bsel} vs {a}"
     s = ref_scores[row, g].astype(np.float64)
-    kept = [j for j in a if j != rb]
-    dropped = [j for j in range(rb) if j not in a]
+    kept = [j for j in a if j not in forced]
+    dropped = [j for j in free if j not in a]
+    assert kept and dropped, f"row {row} group {g}: {bsel} vs {a} with nothing to choose"
     cK = min(s[j] for j in kept)
     cK1 = max(s[j] for j in dropped)
     gap = (cK - cK1) / max(abs(cK), 1e-30)
     assert gap < TIE_RTOL, (f"row {row} group {g}: selection differs without a near tie "
                             f"(gap {gap:.2e}): {bsel} vs {a}")
-    band = {j for j in range(rb) if abs(s[j] - cK) <= TIE_RTOL * abs(cK)}
+    band = {j for j in free if abs(s[j] - cK) <= TIE_RTOL * abs(cK)}
     assert set(a) - band == set(bsel) - band, f"row {row} group {g}: differs outside the tie band"
     return False
 

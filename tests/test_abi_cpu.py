@@ -33,8 +33,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # 15 int32 fields then 5 floats, no padding
-    assert ctypes.sizeof(msa.MsaProblem) == 20 * 4
+    # 15 int32 fields, 5 floats, then the 2 forced-block counts, no padding
+    assert ctypes.sizeof(msa.MsaProblem) == 22 * 4
+    assert msa.MsaProblem.init_blocks.offset == 20 * 4
+    assert msa.MsaProblem.local_blocks.offset == 21 * 4
 
 
 def good(**kw):
@@ -46,6 +48,9 @@ def good(**kw):
 @pytest.mark.parametrize("op", [0, 1, 2, 3])
 def test_valid_problem_passes(op):
     assert msa.check_problem(good(), op) == 0
+    # forced blocks that fill the k exactly are fine
+    assert msa.check_problem(good(top_k=8, init_blocks=3, local_blocks=5), op) == 0
+    assert msa.check_problem(good(top_k=4, init_blocks=3, local_blocks=0), op) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -58,6 +63,9 @@ def test_valid_problem_passes(op):
     (dict(index_q_dtype=0), 2), (dict(q_dtype=0), 2),
     (dict(sm_scale=0.0), 1), (dict(index_scale=-1.0), 1), (dict(k_scale=float("nan")), 1),
     (dict(num_seqs=20000), 2),
+    (dict(init_blocks=-1), 1), (dict(local_blocks=-2), 1),
+    (dict(top_k=16, init_blocks=16), 1),  # no place left for the recent block
+    (dict(top_k=8, init_blocks=3, local_blocks=6), 1),
 ])
 def test_bad_problems_rejected(kw, code):
     p = good(**kw)

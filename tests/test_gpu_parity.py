@@ -163,6 +163,58 @@ def test_block_topk_bit_exact_with_ties(MB):
         assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("MB", [700, 17000])
+def test_block_topk_forced_blocks_bit_exact(MB):
+    """Leading (init) and trailing (local) blocks always kept: the selection
+    kernel alone matches the oracle exactly, for every top-k the attention
+    accepts, forced sets that leave few or no free places, and the score
+    pattern that sends the wave-level selection down its radix path."""
+    rng = np.random.default_rng(6)
+    B, G = 8, 2
+    n = min(MB, 3000)
+    lens = rng.integers(1, n * 128 + 1, B).astype(np.int32)
+    lens[0], lens[1], lens[2], lens[3] = n * 128, 1, 9 * 128, 33 * 128 + 1
+    scores = rng.integers(-6, 7, (B, G, MB)).astype(np.float32) * 0.25
+    scores[4] = rng.standard_normal((G, MB)).astype(np.float32) * 1e-3
+    scores[4, :, ::8] += 1.0 + rng.random((G, (MB + 7) // 8)).astype(np.float32)
+    lens[4] = n * 128
+    for K, init, local in [(4, 1, 1), (8, 2, 4), (16, 1, 3), (16, 4, 0), (32, 8, 8),
+                           (8, 7, 1), (16, 0, 16), (32, 1, 2)]:
+        op = oracle.Problem(num_seqs=B, num_q_heads=G, num_groups=G, block_size=128, top_k=K,
+                            max_blocks=MB, num_phys_blocks=1, init_blocks=init,
+                            local_blocks=local)
+        ref = oracle.block_topk(op, scores, lens)
+        p = msa.Problem(num_seqs=B, num_q_heads=G, num_kv_groups=G, top_k=K,
+                        max_blocks_per_seq=MB, num_phys_blocks=1, init_blocks=init,
+                        local_blocks=local)
+        out = torch.full((B, G, K), 7, dtype=torch.int32, device="cuda")
+        say(f"[parity] block_topk MB={MB} K={K} init={init} local={local}")
+        msa.block_topk(p, parity.dev(scores), parity.dev(lens), None, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), (K, init, local)
+
+
+@pytest.mark.parametrize("K,init,local", [(16, 2, 4), (8, 1, 2), (32, 4, 8), (4, 3, 1)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_with_forced_blocks(K, init, local, fused):
+    """Decode with leading and trailing blocks always kept: selection (with
+    the near-tie rule for the free places) and attention match the oracle,
+    through the fused decode and through the three-call chain."""
+    import dataclasses
+    base = synth.make("forced", seed=140 + K + init, seq_lens=[20000, 9000, 3 * 128 + 5, 1100],
+                      q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3, top_k=K)
+    w = dataclasses.replace(base, init_blocks=init, local_blocks=local)
+    dw, same = _run_and_check(w, fused, f"forced-k{K}-i{init}-l{local}")
+    topk = dw.topk.cpu().numpy()
+    for r in range(w.rows):
+        rb = (int(w.seq_lens[r]) - 1) // 128
+        for g in range(w.num_groups):
+            sel = set(int(x) for x in topk[r, g] if x >= 0)
+            if rb + 1 > K:
+                assert set(range(init)) <= sel
+                assert set(range(rb + 1 - max(local, 1), rb + 1)) <= sel
+
+
 def test_sparse_attend_on_oracle_selection():
     """Attention kernel alone, fed the oracle's selection."""
     w = synth.make("attend", seed=31, seq_lens=[9000, 2100, 128], q_dtype=synth.BF16,

@@ -435,6 +435,126 @@ def test_topk_invariants_and_recent_forced():
                 assert all(scores[b, g, j] <= weakest for j in unsel)
 
 
+def _forced_set(recent, init, local):
+    n_local = max(local, 1)
+    return {j for j in range(recent + 1) if j < init or j > recent - n_local}
+
+
+def _rank_select(scores, recent, K, init, local):
+    """The selection by ranks: a free block is kept when fewer than
+    (K - forced) free blocks beat it (higher score, or equal score and lower
+    index)."""
+    if recent + 1 <= K:
+        sel = list(range(recent + 1))
+    else:
+        forced = _forced_set(recent, init, local)
+        free = [j for j in range(recent + 1) if j not in forced]
+        need = K - len(forced)
+        sel = sorted(forced)
+        for j in free:
+            beaten_by = sum(1 for i in free
+                            if scores[i] > scores[j] or (scores[i] == scores[j] and i < j))
+            if beaten_by < need:
+                sel.append(j)
+        sel.sort()
+    return sel + [-1] * (K - len(sel))
+
+
+def _subset_select(scores, recent, K, init, local):
+    """The selection as the best K-subset: among all K-subsets of 0..recent
+    that hold the forced blocks, the one whose free members, listed best
+    first as (score, -index), form the largest sequence."""
+    import itertools
+    if recent + 1 <= K:
+        return list(range(recent + 1)) + [-1] * (K - recent - 1)
+    forced = _forced_set(recent, init, local)
+    free = [j for j in range(recent + 1) if j not in forced]
+    best, best_key = None, None
+    for comb in itertools.combinations(free, K - len(forced)):
+        key = sorted(((float(scores[j]), -j) for j in comb), reverse=True)
+        if best_key is None or key > best_key:
+            best, best_key = comb, key
+    return sorted(list(forced) + list(best))
+
+
+@pytest.mark.parametrize("K,init,local", [(4, 1, 0), (4, 0, 3), (4, 2, 2), (5, 1, 2),
+                                          (3, 2, 0), (3, 0, 0), (2, 0, 2)])
+def test_topk_forced_blocks_match_best_subset_on_tiny_rows(K, init, local):
+    rng = np.random.default_rng(100 * K + 10 * init + local)
+    B, G, mb, BS = 9, 2, 11, 2
+    lens = np.arange(1, B + 1, dtype=np.int32) * 2 + 3  # 2 .. 10 visible blocks
+    p = oracle.Problem(num_seqs=B, num_q_heads=G, num_groups=G, head_dim=16, index_dim=16,
+                       block_size=BS, top_k=K, max_blocks=mb, num_phys_blocks=1,
+                       init_blocks=init, local_blocks=local)
+    scores = rng.integers(-2, 3, (B, G, mb)).astype(np.float32)  # many exact ties
+    got = oracle.block_topk(p, scores, lens)
+    for b in range(B):
+        recent = (int(lens[b]) - 1) // BS
+        for g in range(G):
+            want = _subset_select(scores[b, g], recent, K, init, local)
+            assert [j for j in got[b, g] if j >= 0] == [j for j in want if j >= 0]
+
+
+@pytest.mark.parametrize("K,init,local", [(4, 1, 1), (8, 2, 4), (16, 1, 3), (16, 8, 8),
+                                          (32, 4, 0), (32, 0, 32), (8, 7, 0)])
+def test_topk_forced_blocks_match_rank_rule(K, init, local):
+    rng = np.random.default_rng(K + 7 * init + 31 * local)
+    B, G, mb, BS = 7, 3, 90, 4
+    lens = rng.integers(1, mb * BS + 1, B).astype(np.int32)
+    lens[0], lens[1], lens[2] = mb * BS, 1, K * BS + 1  # full, one key, one block past k
+    p = oracle.Problem(num_seqs=B, num_q_heads=G, num_groups=G, head_dim=16, index_dim=16,
+                       block_size=BS, top_k=K, max_blocks=mb, num_phys_blocks=1,
+                       init_blocks=init, local_blocks=local)
+    scores = rng.integers(-3, 4, (B, G, mb)).astype(np.float32) * 0.25
+    got = oracle.block_topk(p, scores, lens)
+    for b in range(B):
+        recent = (int(lens[b]) - 1) // BS
+        for g in range(G):
+            sel = [j for j in got[b, g] if j >= 0]
+            assert list(got[b, g]) == _rank_select(scores[b, g], recent, K, init, local)
+            assert len(sel) == min(K, recent + 1)
+            if recent + 1 > K:
+                assert _forced_set(recent, init, local) <= set(sel)
+
+
+def test_topk_forced_blocks_win_over_any_score():
+    """Forced blocks stay even with the worst scores; with init + local = k
+    nothing else is chosen; local 0 and 1 and init 0 give the plain rule."""
+    rng = np.random.default_rng(5)
+    B, G, mb, BS, K = 4, 2, 200, 128, 16
+    lens = np.array([mb * BS, 150 * BS + 3, 40 * BS, 17 * BS], np.int32)
+    scores = rng.standard_normal((B, G, mb)).astype(np.float32)
+    scores[:, :, :3] = -1e30
+    for b in range(B):
+        r = (int(lens[b]) - 1) // BS
+        scores[b, :, r - 5:r + 1] = -1e30
+
+    def run(init, local):
+        p = oracle.Problem(num_seqs=B, num_q_heads=64, num_groups=G, block_size=BS, top_k=K,
+                           max_blocks=mb, num_phys_blocks=1, init_blocks=init,
+                           local_blocks=local)
+        return oracle.block_topk(p, scores, lens)
+
+    plain = run(0, 0)
+    assert np.array_equal(run(0, 1), plain)
+    for b in range(B):
+        r = (int(lens[b]) - 1) // BS
+        for g in range(G):
+            assert list(plain[b, g]) == _brute_select(scores[b, g], r, K)
+    got = run(3, 6)
+    full = run(10, 6)
+    for b in range(B):
+        r = (int(lens[b]) - 1) // BS
+        for g in range(G):
+            sel = set(got[b, g]) - {-1}
+            assert {0, 1, 2} | set(range(r - 5, r + 1)) <= sel
+            assert list(full[b, g]) == list(range(10)) + list(range(r - 5, r + 1))
+    with pytest.raises(ValueError):
+        run(11, 6)  # 17 forced blocks do not fit in k = 16
+    with pytest.raises(ValueError):
+        run(16, 0)  # the recent block needs a place too
+
+
 def test_topk_shard_merge_is_exact():
     """Context sharding of the indexer: each shard's local top-(k-1)
     candidates, merged, give exactly the single-device selection (vLLM blog,
