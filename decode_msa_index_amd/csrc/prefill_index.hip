@@ -14,13 +14,14 @@
 // Work decomposition: a workgroup takes a tile of 256 consecutive (row,
 // group) columns of one sequence (wave w: columns 64w .. 64w+63 as four
 // 16-column MFMA tiles, held as B operands for the whole kernel) and a range
-// of 32 logical blocks.  Per block, the 256 threads stream its 16 KB of
+// of 16 logical blocks (small ranges make many workgroups, so the partial
+// last wave of them is a small share of the run).  Per block, the 256 threads stream its 16 KB of
 // e4m3 keys contiguously into registers (the next block's while the current
 // one computes), then into LDS with the 16-byte chunks swizzled (chunk c of
 // token t at slot c ^ (t % 8), free of bank conflicts both ways); each wave
 // then runs S^T = K Q^T on v_mfma_f32_16x16x32_bf16 for its 64 columns over
 // the block's 8 tiles of 16 tokens, keeping a masked running max per column.
-// The per-block maxima gather in LDS and leave as 128-byte runs per column.
+// The per-block maxima gather in LDS and leave as 64-byte runs per column.
 //
 // Arithmetic: e4m3 keys convert exactly to bf16; products with the bf16
 // index queries are exact and accumulate in fp32.  Blocks past a row's last
@@ -31,7 +32,7 @@
 namespace msa {
 
 constexpr int kCols = 256;   // (row, group) columns per workgroup
-constexpr int kRange = 32;   // logical blocks per workgroup
+constexpr int kRange = 16;   // logical blocks per workgroup
 
 struct PrefillArgs {
   const uint16_t* iq;  // [rows][G][128] bf16
@@ -44,6 +45,49 @@ struct PrefillArgs {
   int tiles_per_seq;  // ceil(R*G / kCols)
   float out_scale;
 };
+
+// S^T for two 16-token tiles of the staged block against the wave's four
+// 16-column tiles, folded into the running maxima m (D row 4r + i of a tile
+// is key 16u + 4r + i, column 16t + n).  The four accumulators of a tile are
+// independent chains, issued interleaved so that no MFMA waits on the one
+// before it; the maxima take both tiles in one three-input max.  MASKED:
+// keys past a column's last visible key count as -inf.
+template <bool FULL>
+__device__ __forceinline__ void block_max(const uint4* __restrict__ stage, const bf16x8 (&qb)[4][4],
+                                          const int (&cpos)[4], int j, int n, int r,
+                                          f32x4 (&m)[4]) {
+#pragma unroll 1
+  for (int u = 0; u < 8; u += 2) {
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tok = 16 * (u + h) + n;
+      const uint4 v0 = stage[tok * 8 + (r ^ (n & 7))];
+      const uint4 v1 = stage[tok * 8 + ((r + 4) ^ (n & 7))];
+      const bf16x8 a[4] = {fp8x8_bf16(v0.x, v0.y), fp8x8_bf16(v0.z, v0.w),
+                           fp8x8_bf16(v1.x, v1.y), fp8x8_bf16(v1.z, v1.w)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[h][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[h][t] = mfma_bf16(a[k], qb[t][k], acc[h][t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x0 = acc[0][t][i], x1 = acc[1][t][i];
+        if constexpr (!FULL) {
+          const int key = j * kBlock + 16 * u + 4 * r + i;
+          x0 = key <= cpos[t] ? x0 : -INFINITY;
+          x1 = key + 16 <= cpos[t] ? x1 : -INFINITY;
+        }
+        m[t][i] = __builtin_fmaxf(m[t][i], __builtin_fmaxf(x0, x1));
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
   __shared__ uint4 stage[2][kBlock * kDim / 16];  // two 16 KB key blocks, swizzled
@@ -97,8 +141,10 @@ __global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
 
   // ---- stream the blocks: registers -> LDS (swizzled) -> MFMA ----
   const int32_t* brow = x.bt + (size_t)b * x.MB;
+  int raw_e = 0;  // table entry of the block in raw
   auto issue = [&](int j, uint4 (&raw)[4]) {
     const int e = brow[j];
+    raw_e = e;
     const int pb = e >= 0 && e < x.P ? e : 0;  // invalid entries are masked below
     const uint4* src = reinterpret_cast<const uint4*>(x.ik + (size_t)pb * (kBlock * kDim));
 #pragma unroll
@@ -114,40 +160,20 @@ __global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
       const int tok = 32 * i + ((int)threadIdx.x >> 3);
       stage[st][tok * 8 + (((int)threadIdx.x & 7) ^ (tok & 7))] = raw[i];
     }
-    __syncthreads();  // the stage is written; the other stage's readers are done
+    const int e = raw_e;  // block j's table entry
+    __syncthreads();      // the stage is written; the other stage's readers are done
     if (j + 1 < jend) issue(j + 1, raw);
-    const int e = brow[j];
     if (e < 0 || e >= x.P) continue;  // invalid table entry: the block stays -inf
     if (j * kBlock > wave_hi) continue;  // no column of this wave sees the block
-    const bool full = j * kBlock + kBlock - 1 <= wave_lo;
+    // wave-uniform: every column of the wave sees the whole block
+    const bool full = __builtin_amdgcn_readfirstlane((int)(j * kBlock + kBlock - 1 <= wave_lo));
     f32x4 m[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) m[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll 2
-    for (int u = 0; u < 8; ++u) {
-      const int tok = 16 * u + n;
-      const uint4 v0 = stage[st][tok * 8 + (r ^ (n & 7))];
-      const uint4 v1 = stage[st][tok * 8 + ((r + 4) ^ (n & 7))];
-      const bf16x8 a0 = fp8x8_bf16(v0.x, v0.y), a1 = fp8x8_bf16(v0.z, v0.w);
-      const bf16x8 a2 = fp8x8_bf16(v1.x, v1.y), a3 = fp8x8_bf16(v1.z, v1.w);
-      const int key0 = j * kBlock + 16 * u + 4 * r;  // D rows 4r + i: keys key0 + i
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mfma_bf16(a0, qb[t][0], acc);
-        acc = mfma_bf16(a1, qb[t][1], acc);
-        acc = mfma_bf16(a2, qb[t][2], acc);
-        acc = mfma_bf16(a3, qb[t][3], acc);
-        if (full) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m[t][i] = fmaxf(m[t][i], acc[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            m[t][i] = key0 + i <= cpos[t] ? fmaxf(m[t][i], acc[i]) : m[t][i];
-        }
-      }
-    }
+    if (full)
+      block_max<true>(stage[st], qb, cpos, j, n, r, m);
+    else
+      block_max<false>(stage[st], qb, cpos, j, n, r, m);
     // max over the lane's 4 keys and the 4 lane groups: lanes 0..15 keep
     // column 16t + n's block maximum
 #pragma unroll
