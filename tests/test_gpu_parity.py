@@ -523,6 +523,23 @@ def test_prefill_chunk(G, H):
     _run_and_check(w, fused=False, name=f"prefill-g{G}-chain")
 
 
+@pytest.mark.parametrize("K,init,local", [(8, 2, 3), (32, 1, 4), (4, 0, 0)])
+def test_prefill_chunk_selection_variants(K, init, local):
+    """A causal chunk (R = 64, G = 8: 1,024 units, so the one-wave attention
+    launch) with other top-k sizes and forced leading / trailing blocks: each
+    row forces its own trailing blocks, through msa_decode and the chain."""
+    import dataclasses
+    R = 64
+    lens = np.array([7000, 3001])
+    qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
+    base = synth.make(f"prefill-k{K}", seed=150 + K, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                      num_q_heads=64, num_groups=8, q_dtype=synth.BF16, kv_dtype=synth.FP8,
+                      plant_per_seq=2, top_k=K)
+    w = dataclasses.replace(base, init_blocks=init, local_blocks=local)
+    _run_and_check(w, fused=True, name=f"prefill-k{K}-i{init}-l{local}")
+    _run_and_check(w, fused=False, name=f"prefill-k{K}-i{init}-l{local}-chain")
+
+
 def test_prefill_scattered_positions():
     """Rows anywhere in the sequence, including ones that see no key or one
     key, block edges and a row past the sequence's end (clamped)."""
