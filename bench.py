@@ -216,6 +216,11 @@ def main():
         f"{graph_ms if graph_ms is None else round(graph_ms, 4)}); index kernel "
         f"{idx_us:.1f} us/launch ({achieved:.0f} GB/s)")
 
+    # the insert half of the step: each sequence's newest token rewritten
+    cw = time_cache_write(w, dws[0], np.arange(w.num_seqs),
+                          np.maximum(w.seq_lens.astype(np.int64) - 1, 0))
+    log(f"[bench] cache write of {cw['tokens']} tokens: {cw['us_per_launch']:.1f} us")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -274,9 +279,67 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "index_mfma_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name), "bytes_per_launch": b_idx},
+        "cache_write": cw,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_cache_write(w, dw, seqs, positions, reps=20):
+    """msa_cache_write of len(positions) new tokens into dw's caches (it
+    overwrites those slots; run it after the other timings): the average
+    launch of a HIP graph of `reps` launches, and the algorithmic bytes per
+    launch -- the new tokens' bf16 (or fp32) K, V and index key read, their
+    quantised codes and scales written, positions and table entries read."""
+    import numpy as np
+    import torch
+
+    import decode_msa_index_amd as msa
+    import synth
+    from tests import parity
+
+    n, G, D, Di = len(positions), w.num_groups, w.head_dim, w.index_dim
+    gen = torch.Generator(device="cuda").manual_seed(0x4357)
+    tdt = torch.float32 if w.q_dtype == synth.F32 else torch.bfloat16
+    idt = torch.float32 if w.index_q_dtype == synth.F32 else torch.bfloat16
+    k_new = torch.randn(n, G, D, device="cuda", generator=gen).to(tdt)
+    v_new = torch.randn(n, G, D, device="cuda", generator=gen).to(tdt)
+    ik_new = torch.randn(n, Di, device="cuda", generator=gen).to(idt)
+    seq_t = parity.dev(np.asarray(seqs, np.int32))
+    pos_t = parity.dev(np.asarray(positions, np.int32))
+    call = lambda: msa.cache_write(dw.p, seq_t, pos_t, k_new, v_new, ik_new, dw.block_table,
+                                   dw.kv_data, dw.kv_scales, dw.ik_data, dw.ik_scales)
+    # a tiny launch issued from Python would time the host call, not the
+    # kernel: `reps` launches are captured in one HIP graph and replayed
+    # between two events
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+
+    def coded(elems, dtype):  # bytes of `elems` cached values in `dtype`
+        return {0: 4 * elems, 2: elems, 3: elems // 2 + elems // 16}[dtype]
+
+    per_token = (2 * G * D * k_new.element_size() + Di * ik_new.element_size() + 8 + 4
+                 + coded(2 * G * D, w.kv_dtype) + coded(Di, w.index_k_dtype))
+    return {"kernel": "cache_write_kernel", "tokens": n, "us_per_launch": us,
+            "bytes_per_launch": n * per_token,
+            "gbps": n * per_token / (us * 1e-6) / 1e9}
 
 
 def run_prefill(args, w):
@@ -314,6 +377,10 @@ def run_prefill(args, w):
     achieved = flops / (idx_us * 1e-6) / 1e12
     log(f"[bench] prefill ms/step {ms_step:.4f}; index contraction {idx_us:.1f} us "
         f"({achieved:.0f} TFLOP/s)")
+    # the insert half: the chunk's own tokens written into the caches
+    cw = time_cache_write(w, dw, np.arange(w.rows) // w.rows_per_seq, w.q_pos)
+    log(f"[bench] cache write of {cw['tokens']} tokens: {cw['us_per_launch']:.1f} us "
+        f"({cw['gbps']:.0f} GB/s)")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -348,6 +415,7 @@ def run_prefill(args, w):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                      "flops_per_launch": flops},
+        "cache_write": cw,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

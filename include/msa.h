@@ -97,7 +97,9 @@ typedef enum {
   MSA_DTYPE_NVFP4 = 3
 } msa_dtype;
 
-/* Problem description, read on the host during the call only. */
+/* Problem description, read on the host during the call only.  Zero-
+ * initialise it (msa_problem p = {0};) and set the fields: the forced-block
+ * counts at the end then default to 0. */
 typedef struct msa_problem {
   int32_t num_seqs;           /* B >= 0 (0: nothing to do) */
   int32_t rows_per_seq;       /* R >= 1 query rows per sequence */
@@ -251,7 +253,7 @@ msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32
                            const void* ik_new, const int32_t* block_table, void* kv_data,
                            void* kv_scales, void* ik_data, void* ik_scales, void* stream);
 
-/* Static description of a status code. *//* Static description of a status code. */
+/* Static description of a status code. */
 const char* msa_status_string(msa_status s);
 
 /* Thread-local detail of the last failure on this thread ("" if none). */
