@@ -94,8 +94,8 @@ def main():
                     help="only copy 1 GiB device-to-device (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        log("bench.py runs on one GPU only: this build has no multi-GPU path "
-            "(see DESIGN.md for how it would shard); run with --gpus 1")
+        log("bench.py runs on one GPU only: the library has no multi-GPU path; "
+            "run with --gpus 1")
         sys.exit(2)
 
     import numpy as np
