@@ -144,6 +144,16 @@ __device__ __forceinline__ f16x8 nvfp4x8_f16(uint32_t w, uint32_t s0, uint32_t s
              v2 * fp8x2_to_f16x2<false>(s1), v3 * fp8x2_to_f16x2<true>(s1));
 }
 
+// 8 E2M1 values (nibbles of w, element 2b in the low nibble of byte b) times
+// one f16 block scale given in both halves of s -> f16x8 (exact, as above).
+__device__ __forceinline__ f16x8 nvfp4x8_f16s(uint32_t w, f16x2 s) {
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return cat(v0 * s, v1 * s, v2 * s, v3 * s);
+}
+
 // ---- lane exchanges -------------------------------------------------------
 
 // Keeps the compiler from moving LDS accesses across this point; the

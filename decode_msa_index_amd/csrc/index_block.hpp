@@ -67,25 +67,111 @@ __device__ __forceinline__ void put_block_scores(const IndexArgs& x, size_t col0
 // visible key), then over i and over the four lane groups, gives the block's
 // score of column l%16 (lanes 0..cols-1 keep them).
 
-constexpr int kStageBytes = 8192;  // LDS per wave: half a block (FP8) staged
+// LDS per wave: half a block staged (FP8 8 KB; NVFP4 4 KB of data plus the
+// block's 1 KB of scales)
+template <int IK>
+constexpr int stage_bytes() {
+  return IK == kFP8 ? 8192 : 5120;
+}
 
 // B operand: the wave's cols index queries, (row, group) pairs col0 ..
-// col0 + cols - 1 (zero columns past cols).
-struct QueryB {
+// col0 + cols - 1 (zero columns past cols).  FP8 keys take them as bf16.
+// NVFP4 keys are dequantised to f16 (cheaper than bf16: the block scale is
+// one packed f16 multiply per two values), so the queries go to f16 too,
+// each column shifted by a power of two 2^sh that puts its largest element
+// in [2^15, 2^16): every element within 2^32 of the column's largest then
+// converts exactly, and unscale = 2^-sh undoes the shift on the pooled
+// score (max-pooling commutes with a positive scale, and a power-of-two
+// scale is exact).
+template <int IK>
+struct QueryB;
+template <>
+struct QueryB<kFP8> {
   bf16x8 b[4];
+  float unscale;
+};
+template <>
+struct QueryB<kNVFP4> {
+  f16x8 b[4];
+  float unscale;
 };
 
-template <int IK>
 __device__ __forceinline__ void load_query_b(const IndexArgs& x, size_t col0, int cols, int lane,
-                                             QueryB& q) {
+                                             QueryB<kFP8>& q) {
+  // loads from a clamped column, masked to zero past cols (no branch, so
+  // nothing waits for them before the block loads are issued)
   const int n = lane & 15, r = lane >> 4;
+  const uint32_t keep = n < cols ? 0xFFFFFFFFu : 0u;
+  const uint16_t* src = x.iq + (col0 + min(n, cols - 1)) * kDim;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int d = IK == kFP8 ? 16 * r + 64 * (c >> 1) + 8 * (c & 1) : 32 * r + 8 * c;
-    q.b[c] = n < cols ? *reinterpret_cast<const bf16x8*>(x.iq + (col0 + n) * kDim + d)
-                      : bf16x8{};
+    uint4 v = *reinterpret_cast<const uint4*>(src + 16 * r + 64 * (c >> 1) + 8 * (c & 1));
+    v.x &= keep;
+    v.y &= keep;
+    v.z &= keep;
+    v.w &= keep;
+    q.b[c] = __builtin_bit_cast(bf16x8, v);
   }
+  q.unscale = 1.0f;
 }
+
+// NVFP4 queries in two steps, so that the block loads can be issued between
+// them: fetch() issues the raw bf16 loads (from a clamped column, masked to
+// zero past cols without a branch), make() converts.
+struct QueryRawNvfp4 {
+  uint4 raw[4];
+  __device__ __forceinline__ void fetch(const IndexArgs& x, size_t col0, int cols, int lane) {
+    const int n = lane & 15, r = lane >> 4;
+    const uint4* src =
+        reinterpret_cast<const uint4*>(x.iq + (col0 + min(n, cols - 1)) * kDim + 32 * r);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = src[c];
+  }
+  __device__ __forceinline__ void make(int cols, int lane, QueryB<kNVFP4>& q) const {
+    const uint32_t keep = (lane & 15) < cols ? 0xFFFFFFFFu : 0u;
+    uint32_t w[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[c][0] = raw[c].x & keep;
+      w[c][1] = raw[c].y & keep;
+      w[c][2] = raw[c].z & keep;
+      w[c][3] = raw[c].w & keep;
+    }
+    // largest bf16 exponent field of column n (its 128 dims sit in lanes n,
+    // n + 16, n + 32, n + 48)
+    uint32_t e = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) e = max(e, max(w[c][k] & 0x7F80u, (w[c][k] >> 16) & 0x7F80u));
+    }
+    e = max(e, (uint32_t)lane_xor<16>((int)e));
+    e = max(e, (uint32_t)lane_xor<32>((int)e));
+    const int emax = (int)(e >> 7);        // biased exponent (0: the column is zero)
+    const int sh = emax ? 142 - emax : 0;  // 2^(emax - 127 + sh) = 2^15
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = ldexpf(__uint_as_float(w[c][k] << 16), sh);
+        const float hi = ldexpf(__uint_as_float(w[c][k] & 0xFFFF0000u), sh);
+        o[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      }
+      q.b[c] = __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+    q.unscale = ldexpf(1.0f, -sh);
+  }
+};
+
+// FP8 queries: nothing to convert (fetch loads them).
+struct QueryRawFp8 {
+  QueryB<kFP8> q;
+  __device__ __forceinline__ void fetch(const IndexArgs& x, size_t col0, int cols, int lane) {
+    load_query_b(x, col0, cols, lane, q);
+  }
+  __device__ __forceinline__ void make(int, int, QueryB<kFP8>& out) const { out = q; }
+};
 
 // Per-lane running maxima of one block (tokens 4r + i of every tile).
 struct TileMax {
@@ -114,7 +200,7 @@ struct HalfRaw<kFP8> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = load_stream(src + i * 64);
   }
-  __device__ __forceinline__ void pool(int j, int h2, int pos, int lane, const QueryB& q,
+  __device__ __forceinline__ void pool(int j, int h2, int pos, int lane, const QueryB<kFP8>& q,
                                        TileMax& tm, uint4* stage) const {
     // token t (0..63) row at 8t chunks; chunk c at slot c ^ (t % 8).  The
     // syncs order the lanes' LDS accesses: reads of the previous half, these
@@ -139,58 +225,92 @@ struct HalfRaw<kFP8> {
   }
 };
 
-template <>
-struct HalfRaw<kNVFP4> {
-  uint4 d[4];     // d[i]: token 16i + lane/4 of the half, 16-byte chunk lane%4
-  uint32_t s[4];  // s[t]: the two e4m3 scales of token 16t + lane%16, dims [32r, +32)
-  __device__ __forceinline__ void issue(const IndexArgs& x, int pb, int h2, int lane) {
-    const uint4* src =
-        reinterpret_cast<const uint4*>(x.ikd + (size_t)pb * (kBlock * kDim / 2)) + h2 * 256 + lane;
-    const uint16_t* ss = reinterpret_cast<const uint16_t*>(
-                             x.iks + (size_t)pb * (kBlock * kDim / 16) +
-                             (size_t)(64 * h2 + (lane & 15)) * (kDim / 16)) + (lane >> 4);
+// NVFP4 keys: the whole block's loads are issued together -- 8 KB of E2M1
+// data as eight 1 KB loads and the block's 1 KB of scales as one -- and the
+// scales are staged in LDS next to the data (each lane needs the scales of
+// other lanes' tokens).
+struct BlockRawNvfp4 {
+  uint4 d[8];  // d[i]: token 16i + lane/4 of the block, 16-byte chunk lane%4
+  uint4 sc;    // the 8 scale bytes of tokens 2 lane and 2 lane + 1
+  __device__ __forceinline__ void issue(const IndexArgs& x, int pb, int lane) {
+    const uint4* src = reinterpret_cast<const uint4*>(x.ikd + (size_t)pb * (kBlock * kDim / 2)) + lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      d[i] = load_stream(src + i * 64);
-      s[i] = __builtin_nontemporal_load(ss + i * 64);
-    }
+    for (int i = 0; i < 8; ++i) d[i] = load_stream(src + i * 64);
+    sc = load_stream(reinterpret_cast<const uint4*>(x.iks + (size_t)pb * (kBlock * kDim / 16)) + lane);
   }
-  // E2M1 value x e4m3 block scale is exact in bf16 (at most 6 significant
-  // bits, inside bf16's range); the tensor scale is folded into out_scale.
-  __device__ __forceinline__ void pool(int j, int h2, int pos, int lane, const QueryB& q,
+  // E2M1 value x e4m3 block scale is exact in f16 (at most 6 significant
+  // bits, inside [2^-10, 2688]); the tensor scale is folded into out_scale.
+  // stage: 4 KB of data (half a block at a time) then the block's 1 KB of
+  // scales.
+  __device__ __forceinline__ void pool(int j, int pos, int lane, const QueryB<kNVFP4>& q,
                                        TileMax& tm, uint4* stage) const {
-    // token t (0..63) row at 4t chunks; chunk p at slot p ^ ((t / 2) % 4)
-    wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * i + (lane >> 2);
-      stage[t * 4 + ((lane & 3) ^ ((t >> 1) & 3))] = d[i];
-    }
-    wave_lds_sync();
     const int n = lane & 15, rg = lane >> 4;
-    const int tok = j * kBlock + 64 * h2 + 4 * rg;
+    const uint16_t* scl = reinterpret_cast<const uint16_t*>(stage + 256);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tt = 16 * t + n;
-      const uint4 v = stage[tt * 4 + (rg ^ ((tt >> 1) & 3))];
-      const f32x2 sc = fp8x2_to_f32x2<false>(s[t]);  // dims [32r, +16), [32r+16, +16)
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mfma_bf16(nvfp4x8_bf16(v.x, sc[0]), q.b[0], acc);
-      acc = mfma_bf16(nvfp4x8_bf16(v.y, sc[0]), q.b[1], acc);
-      acc = mfma_bf16(nvfp4x8_bf16(v.z, sc[1]), q.b[2], acc);
-      acc = mfma_bf16(nvfp4x8_bf16(v.w, sc[1]), q.b[3], acc);
-      fold_tile(tm, acc, tok + 16 * t, pos);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      // token t (0..63) of the half: row at 4t chunks, chunk p at slot p ^ ((t / 2) % 4)
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * i + (lane >> 2);
+        stage[t * 4 + ((lane & 3) ^ ((t >> 1) & 3))] = d[4 * h2 + i];
+      }
+      if (h2 == 0) stage[256 + lane] = sc;
+      wave_lds_sync();
+      const int tok = j * kBlock + 64 * h2 + 4 * rg;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int tt = 16 * t + n;
+        const uint4 v = stage[tt * 4 + (rg ^ ((tt >> 1) & 3))];
+        // scales of dims [32rg, +16) and [32rg + 16, +16) of token 64 h2 + tt
+        const uint32_t s2 = scl[4 * (64 * h2 + tt) + rg];
+        const f16x2 sc2 = fp8x2_to_f16x2<false>(s2);
+        const f16x2 s0 = {sc2[0], sc2[0]}, s1 = {sc2[1], sc2[1]};
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mfma_f16(nvfp4x8_f16s(v.x, s0), q.b[0], acc);
+        acc = mfma_f16(nvfp4x8_f16s(v.y, s0), q.b[1], acc);
+        acc = mfma_f16(nvfp4x8_f16s(v.z, s1), q.b[2], acc);
+        acc = mfma_f16(nvfp4x8_f16s(v.w, s1), q.b[3], acc);
+        fold_tile(tm, acc, tok + 16 * t, pos);
+      }
     }
   }
 };
 
+// FP8 keys: the block as two halves (the FP8 kernel takes one block per
+// wave, so nothing more needs to be in flight).
+struct BlockRawFp8 {
+  HalfRaw<kFP8> h[2];
+  __device__ __forceinline__ void issue(const IndexArgs& x, int pb, int lane) {
+    h[0].issue(x, pb, 0, lane);
+    h[1].issue(x, pb, 1, lane);
+  }
+  __device__ __forceinline__ void pool(int j, int pos, int lane, const QueryB<kFP8>& q,
+                                       TileMax& tm, uint4* stage) const {
+    h[0].pool(j, 0, pos, lane, q, tm, stage);
+    h[1].pool(j, 1, pos, lane, q, tm, stage);
+  }
+};
+
+template <int IK>
+struct BlockRawOf {
+  typedef BlockRawFp8 type;
+  typedef QueryRawFp8 query;
+};
+template <>
+struct BlockRawOf<kNVFP4> {
+  typedef BlockRawNvfp4 type;
+  typedef QueryRawNvfp4 query;
+};
+
 // The block's pooled score of group lane%16, times out_scale (lanes 0..G-1
 // hold groups 0..G-1).
-__device__ __forceinline__ float finish_block(const IndexArgs& x, const TileMax& tm) {
+__device__ __forceinline__ float finish_block(const IndexArgs& x, const TileMax& tm,
+                                             float unscale) {
   float m = fmaxf(fmaxf(tm.m[0], tm.m[1]), fmaxf(tm.m[2], tm.m[3]));
   m = fmaxf(m, lane_xor_f<16>(m));
   m = fmaxf(m, lane_xor_f<32>(m));
-  return m * x.out_scale;
+  return (m * unscale) * x.out_scale;
 }
 
 }  // namespace msa
