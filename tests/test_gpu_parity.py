@@ -5,6 +5,7 @@ oracle only.  Small cases span several blocks, ragged tails and the
 degenerate cases; the full-size cases are the benchmark's workloads in the
 benchmark's launch configuration, with the oracle computed on every output.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -72,6 +73,35 @@ def test_small_ragged(kv, fused):
     w = synth.make("edge", seed=101 + kv, seq_lens=EDGE_LENS, q_dtype=synth.BF16,
                    kv_dtype=kv, plant_per_seq=0)
     _run_and_check(w, fused, f"edge-{synth.DTYPE_NAMES[kv]}")
+
+
+def _scale_bf16(bits: np.ndarray, k: int) -> np.ndarray:
+    """bf16 bit patterns times 2**k, exactly (zeros stay zero)."""
+    b = bits.astype(np.uint32)
+    e = (b >> 7) & 0xFF
+    ne = (e.astype(np.int64) + k).astype(np.uint32)
+    assert np.all((ne[e > 0] >= 1) & (ne[e > 0] <= 254)), "scaled out of bf16's range"
+    return np.where(e > 0, (b & np.uint32(0x807F)) | (ne << 7), b).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
+def test_index_queries_far_outside_f16_range(kv):
+    # NVFP4 keys are scored on f16 MFMA with each index query shifted by a
+    # power of two into f16's range; these queries would overflow (2^60),
+    # flush to zero (2^-60) or lose bits (a 2^30 spread inside one query)
+    # without the shift.  One group's query is zero: all its blocks tie at 0.
+    w = synth.make("iq-range", seed=171 + kv, seq_lens=[5000, 2049, 3000, 700],
+                   q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2)
+    iq = w.index_q.copy()
+    iq[0] = _scale_bf16(iq[0], 60)
+    iq[1] = _scale_bf16(iq[1], -60)
+    iq[2, 1] = 0
+    iq[3, :, :64] = _scale_bf16(iq[3, :, :64], 20)
+    iq[3, :, 64:] = _scale_bf16(iq[3, :, 64:], -10)
+    w = dataclasses.replace(w, index_q=iq)
+    for fused in (False, True):
+        _, same = _run_and_check(w, fused, f"iq-range-{synth.DTYPE_NAMES[kv]}")
+        assert same[2, 1], "a zero query selects the lowest blocks on both sides"
 
 
 def test_tiny_fp32_workload():
