@@ -47,6 +47,7 @@ class MsaProblem(ctypes.Structure):
         ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("index_k_scale", ctypes.c_float),
         ("init_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
+        ("share_seqs", ctypes.c_int32),
     ]
 
 
@@ -75,6 +76,7 @@ class Problem:
     index_k_scale: float = 1.0
     init_blocks: int = 0
     local_blocks: int = 0
+    share_seqs: int = 0
 
     def c(self) -> MsaProblem:
         return MsaProblem(*[getattr(self, f.name) for f in fields(self)])

@@ -43,6 +43,7 @@ msa::Shape shape_of(const msa_problem* p) {
   s.K = p->top_k;
   s.init = p->init_blocks;
   s.local = p->local_blocks > 1 ? p->local_blocks : 1;
+  s.share = p->share_seqs > 1 ? p->share_seqs : 1;
   s.q_dtype = p->q_dtype;
   s.iq_dtype = p->index_q_dtype;
   s.kv_dtype = p->kv_dtype;
@@ -111,6 +112,10 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op) {
   if ((long long)p->init_blocks + (p->local_blocks > 1 ? p->local_blocks : 1) > p->top_k)
     return fail(MSA_ERR_INVALID_ARGUMENT,
                 "init_blocks + max(local_blocks, 1) > top_k: the forced blocks do not fit");
+  if (p->share_seqs < 0 || p->share_seqs > 64)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "share_seqs must be in [0, 64]");
+  if (p->share_seqs > 1 && p->rows_per_seq != 1)
+    return fail(MSA_ERR_UNSUPPORTED, "share_seqs > 1 needs rows_per_seq == 1");
   const int G = p->num_kv_groups, hpg = p->num_q_heads / p->num_kv_groups;
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(MSA_ERR_UNSUPPORTED, "num_kv_groups must be 1, 2, 4 or 8");

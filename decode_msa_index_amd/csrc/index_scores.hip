@@ -110,6 +110,93 @@ __global__ __launch_bounds__(256, 4) void index_mfma_kernel(IndexArgs x) {
 }
 
 // -------------------------------------------------------------------------
+// Shared scan (one row per sequence, share groups of consecutive sequences
+// that may map logical blocks to the same physical blocks -- requests with a
+// common prefix).  One wave per (share group, slice of up to 64 / G of its
+// sequences, logical block j): the slice's 64 or fewer (sequence, group)
+// columns are four MFMA column tiles.  The wave reads the slice's table
+// entries for block j and scores each distinct physical block among them
+// once, for exactly the columns whose sequence maps j to it (and sees it);
+// a prefix block shared by the whole slice is read once for all of them.
+// Each column is scored by the same arithmetic as in index_mfma_kernel, so
+// the scores are those of the unshared scan, bit for bit.
+// -------------------------------------------------------------------------
+constexpr int kShareCols = 64;  // columns per wave (four tiles of 16)
+
+template <int IK>
+__global__ __launch_bounds__(256) void index_shared_kernel(IndexArgs x) {
+  constexpr int CT = kShareCols / 16;
+  __shared__ uint4 stage[4][stage_bytes<IK>() / 16];  // one staging area per wave
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int spw = kShareCols / x.G;  // sequences per slice
+  const int slices = (x.share + spw - 1) / spw;
+  const int grp = blockIdx.y / slices, sl = blockIdx.y % slices;
+  const int b0 = grp * x.share + sl * spw;
+  const int ns = min(min(spw, x.share - sl * spw), x.B - b0);  // the wave's sequences
+  const int j = blockIdx.x * 4 + wave;
+  if (ns <= 0 || j >= x.MB) return;
+  const int cols = ns * x.G, nct = (cols + 15) / 16;
+  const size_t col0 = (size_t)b0 * x.G;  // first (row, group) pair (one row per sequence)
+  // lane i < ns: sequence b0 + i's table entry and last visible key
+  int entry = -1, spos = -1;
+  if (lane < ns) {
+    entry = x.bt[(size_t)(b0 + lane) * x.MB + j];
+    spos = row_last_key(x.lens, x.qpos, b0 + lane, b0 + lane, x.MB);
+  }
+  const bool usable = lane < ns && j * kBlock <= spos && entry >= 0 && entry < x.P;
+  uint64_t pending = __ballot(usable);
+  // per column tile c, this lane's column 16 c + n: its sequence's last key
+  const int n = lane & 15;
+  int posc[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int col = 16 * c + n;
+    const int pc = __shfl(spos, min(col, cols - 1) / x.G, 64);
+    posc[c] = col < cols ? pc : -1;
+  }
+  TileMax tm[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) tm[c].init();
+  if (pending) {
+    QueryB<IK> q[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      if (c < nct) {
+        typename BlockRawOf<IK>::query qr;
+        qr.fetch(x, col0 + 16 * c, min(16, cols - 16 * c), lane);
+        qr.make(min(16, cols - 16 * c), lane, q[c]);
+      } else {
+        q[c] = QueryB<IK>{};
+      }
+    }
+    while (pending) {  // the distinct physical blocks, one at a time
+      const int leader = __builtin_ctzll(pending);
+      const int e = __builtin_amdgcn_readlane(entry, leader);
+      const uint64_t same = __ballot(lane < ns && entry == e) & pending;
+      pending &= ~same;
+      int pact[CT];  // keys a column folds from this block (-1: not its block)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int col = 16 * c + n;
+        pact[c] = (col < cols && ((same >> (col / x.G)) & 1)) ? posc[c] : -1;
+      }
+      typename BlockRawOf<IK>::type raw;
+      raw.issue(x, e, lane);
+      raw.template pool_tiles<CT>(j, pact, nct, lane, q, tm, stage[wave]);
+    }
+    // after the reduction every lane group holds tile c's score of column 16 c + n
+    float v[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) v[c] = finish_block(x, tm[c], q[c].unscale);
+    const int mine = lane >> 4;
+    const float out = mine == 0 ? v[0] : mine == 1 ? v[1] : mine == 2 ? v[2] : v[3];
+    if (lane < cols) x.scores[(col0 + lane) * x.MB + j] = out;
+  } else if (lane < cols) {  // no sequence of the slice sees block j
+    x.scores[(col0 + lane) * x.MB + j] = -INFINITY;
+  }
+}
+
+// -------------------------------------------------------------------------
 // fp32 index keys and queries (small exactness workloads).  One wave per
 // block, two tokens per lane, fp32 FMA.
 // -------------------------------------------------------------------------
@@ -216,6 +303,18 @@ hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* 
   x.row_groups = (s.R + x.rows_per_wave - 1) / x.rows_per_wave;
   x.out_scale = s.index_scale * s.ik_scale;
   const int nseq = s.rows / s.R;
+  x.B = nseq;
+  x.share = s.share;
+  if (s.share > 1 && s.R == 1) {  // shared scan (validated: R == 1)
+    const int spw = kShareCols / s.G;
+    const unsigned ys = (unsigned)(((nseq + s.share - 1) / s.share) * ((s.share + spw - 1) / spw));
+    const dim3 grid((s.MB + 3) / 4, ys);
+    if (s.ik_dtype == kFP8)
+      hipLaunchKernelGGL(index_shared_kernel<kFP8>, grid, dim3(256), 0, st, x);
+    else
+      hipLaunchKernelGGL(index_shared_kernel<kNVFP4>, grid, dim3(256), 0, st, x);
+    return hipGetLastError();
+  }
   const unsigned rgs = (unsigned)(nseq * x.row_groups);
   if (s.ik_dtype == kFP8) {
     constexpr int span = 4 * blocks_per_wave<kFP8>();

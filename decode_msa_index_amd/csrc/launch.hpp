@@ -13,6 +13,7 @@ struct Shape {
   int H, G, hpg;   // query heads, groups, heads per group
   int MB, P, K;    // block-table stride, physical blocks, top-k
   int init, local; // forced blocks: the first `init` and the last `local` (>= 1)
+  int share;       // sequences per share group of the index scan (1: none)
   int q_dtype, iq_dtype, kv_dtype, ik_dtype, out_dtype;
   float sm_scale, index_scale, k_scale, v_scale, ik_scale;
 };

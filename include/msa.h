@@ -125,6 +125,19 @@ typedef struct msa_problem {
   int32_t local_blocks;       /* >= 0: the last max(local_blocks, 1) visible blocks
                                  always kept (0 and 1: the recent block alone);
                                  init_blocks + max(local_blocks, 1) <= top_k */
+  int32_t share_seqs;         /* 0..64; 0 and 1: off.  n > 1: the sequences form
+                                 consecutive share groups of n (the last may be
+                                 shorter) whose block tables may point at the same
+                                 physical blocks, e.g. requests with a common
+                                 prefix.  The index scan then reads each distinct
+                                 physical block of a logical block once for up to
+                                 64 / num_kv_groups sequences of a group (pages
+                                 dequantised once for the requests sharing them:
+                                 blog "Day-0 support for MiniMax-M3.1-Flash",
+                                 section "AMD NVFP4 MSA kernels").  A hint only:
+                                 results are identical for any tables, nothing is
+                                 assumed about them.  Needs rows_per_seq == 1;
+                                 ignored for f32 index keys. */
 } msa_problem;
 
 /*

@@ -165,6 +165,7 @@ class Workload:
     planted: dict = field(default_factory=dict)
     init_blocks: int = 0    # leading blocks always selected
     local_blocks: int = 0   # trailing blocks always selected (0, 1: the recent one)
+    share_seqs: int = 0     # share groups of the index scan (a hint to the kernels only)
     recipe: str = ""
 
     @property
@@ -207,7 +208,7 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
          plant_per_seq: int = 0, plant_add: float = 1.0, bump_blocks: int = 0,
          bump_add: float = 2.0, max_blocks: int | None = None, k_scale: float = 1.0,
          v_scale: float = 1.0, ik_scale: float | None = None,
-         kv_fill: bool = True) -> Workload:
+         kv_fill: bool = True, share_seqs: int = 0, share_blocks: int = 0) -> Workload:
     """Build one seeded workload.
 
     table: "identity" (seq b's block j is physical b*max_blocks+j) or
@@ -217,6 +218,11 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
     bump_blocks: add ``bump_add`` to every index-key element of that many
     random blocks (of sequence 0).
     kv_fill: False leaves the K/V pool zero (timing-only callers).
+    share_seqs, share_blocks: consecutive groups of share_seqs sequences
+    (requests with a common prefix) map their first logical blocks -- up to
+    share_blocks, and short of every member's last block -- to the same
+    physical blocks ("permute" tables only); share_seqs is also passed to the
+    kernels as the share-group hint.
     """
     index_q_dtype = q_dtype if index_q_dtype is None else index_q_dtype
     index_k_dtype = kv_dtype if index_k_dtype is None else index_k_dtype
@@ -231,7 +237,16 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
     G, H, D, Di = num_groups, num_q_heads, head_dim, index_dim
 
     # ---- block table ----
-    P = int(nb.sum()) + extra_phys
+    groups = []  # (first sequence, end, shared blocks)
+    if share_seqs > 1 and share_blocks > 0:
+        if table != "permute":
+            raise ValueError("shared prefixes need a permuted table")
+        for g0 in range(0, num_seqs, share_seqs):
+            g1 = min(num_seqs, g0 + share_seqs)
+            groups.append((g0, g1, int(min(share_blocks, int(nb[g0:g1].min()) - 1))))
+    else:
+        groups = [(b, b + 1, 0) for b in range(num_seqs)]
+    P = int(nb.sum()) - sum((g1 - g0 - 1) * sh for g0, g1, sh in groups) + extra_phys
     P = max(P, 1)
     bt = np.zeros((num_seqs, max_blocks), np.int32)
     if table == "identity":
@@ -241,9 +256,13 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
     else:
         perm = np.random.default_rng([seed, STREAM_TABLE]).permutation(P).astype(np.int32)
         off = 0
-        for b in range(num_seqs):
-            bt[b, : nb[b]] = perm[off: off + nb[b]]
-            off += nb[b]
+        for g0, g1, sh in groups:
+            shared = perm[off: off + sh]
+            off += sh
+            for b in range(g0, g1):
+                bt[b, :sh] = shared
+                bt[b, sh: nb[b]] = perm[off: off + nb[b] - sh]
+                off += nb[b] - sh
 
     # ---- queries ----
     iq_f = normal(seed, STREAM_INDEX_Q, 0, rows * G * Di).reshape(rows, G, Di)
@@ -352,7 +371,8 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
         sm_scale=D ** -0.5, index_scale=Di ** -0.5, k_scale=k_scale, v_scale=v_scale,
         index_k_scale=ik_scale, index_q=index_q, q=q, ik_data=ik_data,
         ik_scales=ik_scales, kv_data=kv_data, kv_scales=kv_scales, block_table=bt,
-        seq_lens=seq_lens.astype(np.int32), q_pos=qp, planted=planted)
+        seq_lens=seq_lens.astype(np.int32), q_pos=qp, planted=planted,
+        share_seqs=share_seqs)
 
 
 # ---------------------------------------------------------------------------

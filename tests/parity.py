@@ -34,7 +34,7 @@ def problem(w: synth.Workload, out_dtype=msa.BF16) -> msa.Problem:
         kv_dtype=w.kv_dtype, index_k_dtype=w.index_k_dtype, out_dtype=out_dtype,
         sm_scale=w.sm_scale, index_scale=w.index_scale, k_scale=w.k_scale,
         v_scale=w.v_scale, index_k_scale=w.index_k_scale, init_blocks=w.init_blocks,
-        local_blocks=w.local_blocks)
+        local_blocks=w.local_blocks, share_seqs=w.share_seqs)
 
 
 def oracle_problem(w: synth.Workload, threads: int = 0):

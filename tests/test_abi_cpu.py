@@ -33,10 +33,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # 15 int32 fields, 5 floats, then the 2 forced-block counts, no padding
-    assert ctypes.sizeof(msa.MsaProblem) == 22 * 4
+    # 15 int32 fields, 5 floats, the 2 forced-block counts, the share-group
+    # size, no padding
+    assert ctypes.sizeof(msa.MsaProblem) == 23 * 4
     assert msa.MsaProblem.init_blocks.offset == 20 * 4
     assert msa.MsaProblem.local_blocks.offset == 21 * 4
+    assert msa.MsaProblem.share_seqs.offset == 22 * 4
 
 
 def good(**kw):
@@ -51,6 +53,9 @@ def test_valid_problem_passes(op):
     # forced blocks that fill the k exactly are fine
     assert msa.check_problem(good(top_k=8, init_blocks=3, local_blocks=5), op) == 0
     assert msa.check_problem(good(top_k=4, init_blocks=3, local_blocks=0), op) == 0
+    # share groups: 0 and 1 mean none, up to 64 sequences per group
+    for n in (0, 1, 2, 64):
+        assert msa.check_problem(good(share_seqs=n), op) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -66,6 +71,8 @@ def test_valid_problem_passes(op):
     (dict(init_blocks=-1), 1), (dict(local_blocks=-2), 1),
     (dict(top_k=16, init_blocks=16), 1),  # no place left for the recent block
     (dict(top_k=8, init_blocks=3, local_blocks=6), 1),
+    (dict(share_seqs=-1), 1), (dict(share_seqs=65), 1),
+    (dict(share_seqs=4, rows_per_seq=2), 2),  # share groups take one row per sequence
 ])
 def test_bad_problems_rejected(kw, code):
     p = good(**kw)

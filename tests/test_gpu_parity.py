@@ -104,6 +104,52 @@ def test_index_queries_far_outside_f16_range(kv):
         assert same[2, 1], "a zero query selects the lowest blocks on both sides"
 
 
+def _decode_outputs(w):
+    dw = parity.DeviceWorkload(w)
+    dw.decode()
+    torch.cuda.synchronize()
+    return dw.scores.cpu(), dw.topk.cpu(), dw.out.cpu()
+
+
+@pytest.mark.parametrize("kv,n,G,H,share_blocks,diverge", [
+    (synth.FP8, 16, 4, 64, 60, False),    # one full group of 16 and a group of 4
+    (synth.FP8, 5, 4, 64, 40, True),      # a member leaves the prefix half way
+    (synth.NVFP4, 5, 4, 64, 40, False),
+    (synth.FP8, 64, 1, 16, 20, False),    # 64 sequences on one wave's columns
+    (synth.FP8, 8, 8, 64, 30, False),
+    (synth.FP8, 16, 4, 64, 0, False),     # the hint over unshared random tables
+])
+def test_shared_prefix_scan(kv, n, G, H, share_blocks, diverge):
+    # requests with common prefixes: the index scan reads each distinct
+    # physical block once per share group slice; the scores, selection and
+    # output must be the oracle's, and bit for bit those of the unshared scan
+    nseq = n + 4 if n < 64 else 64
+    rng = np.random.default_rng(200 + n + G)
+    lens = [int(share_blocks * 128 + rng.integers(1, 2000)) for _ in range(nseq)]
+    if n < 64:
+        lens[-1] = 300  # a short member: sees only the first blocks of the prefix
+    w = synth.make(f"share-{n}", seed=210 + n + G + kv, seq_lens=lens, num_q_heads=H,
+                   num_groups=G, q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2,
+                   share_seqs=n, share_blocks=share_blocks)
+    if share_blocks == 0:
+        w = dataclasses.replace(w, share_seqs=n)
+    if diverge:  # member 1 takes member 2's private blocks for part of the prefix
+        bt = w.block_table.copy()
+        nb2 = (lens[2] + 127) // 128
+        k = min(10, nb2 - share_blocks)
+        bt[1, 20: 20 + k] = bt[2, share_blocks: share_blocks + k]
+        w = dataclasses.replace(w, block_table=bt)
+    shared = int(sum((w.block_table[b, :share_blocks] == w.block_table[(b // n) * n, :share_blocks]).sum()
+                     for b in range(nseq)))
+    say(f"[parity] share-{n}: {nseq} sequences, {shared} (sequence, block) entries shared")
+    _run_and_check(w, True, f"share-{n}-{synth.DTYPE_NAMES[kv]}")
+    _run_and_check(w, False, f"share-{n}-{synth.DTYPE_NAMES[kv]}-chain")
+    s1, k1, o1 = _decode_outputs(w)
+    s0, k0, o0 = _decode_outputs(dataclasses.replace(w, share_seqs=0))
+    assert torch.equal(s1.view(torch.int32), s0.view(torch.int32)), "shared scan scores differ"
+    assert torch.equal(k1, k0) and torch.equal(o1.view(torch.int16), o0.view(torch.int16))
+
+
 def test_tiny_fp32_workload():
     w = synth.tiny()
     dw, same = _run_and_check(w, fused=False, name="tiny-f32")
