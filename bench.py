@@ -16,6 +16,7 @@ and is reported only while the scan's sources are unchanged since then.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -70,7 +71,17 @@ def algorithmic_bytes(w, topk_counts):
     nb = (lens + 127) // 128
     rows, G, MB = w.rows, w.num_groups, w.max_blocks
     qb = 2 if w.q_dtype == 1 else 4
-    index = (int(lens.sum()) * ik_tok + rows * G * 128 * qb + int(nb.sum()) * 4
+    # index keys: each physical block once, for the most tokens any sequence
+    # sees in it (sequences sharing a prefix share its blocks)
+    phys, toks = [], []
+    for b in range(w.num_seqs):
+        j = np.arange(int(nb[b]))
+        phys.append(w.block_table[b, : nb[b]].astype(np.int64))
+        toks.append(np.minimum(128, lens[b] - 128 * j))
+    seen = np.zeros(w.num_phys_blocks, np.int64)
+    if phys:
+        np.maximum.at(seen, np.concatenate(phys), np.concatenate(toks))
+    index = (int(seen.sum()) * ik_tok + rows * G * 128 * qb + int(nb.sum()) * 4
              + rows * G * MB * 4)
     topk = rows * G * MB * 4 + rows * G * w.top_k * 4
     attend = (int(topk_counts) * kv_tok + rows * w.num_q_heads * 128 * qb * 2
@@ -85,7 +96,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_256k",
                     choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "spec4_256k",
-                             "prefill_64k"])
+                             "fp8_share64", "prefill_64k"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,6 +204,23 @@ def main():
     e_idx[1].record()
     torch.cuda.synchronize()
     idx_us = e_idx[0].elapsed_time(e_idx[1]) * 1e3 / args.steps
+    unshared_us = None
+    if w.share_seqs > 1:  # the same scan without the share-group hint
+        plain = []
+        for d in dws:
+            c = parity.DeviceWorkload.__new__(parity.DeviceWorkload)
+            c.__dict__.update(d.__dict__)
+            c.p = dataclasses.replace(d.p, share_seqs=0)
+            plain.append(c)
+        for i in range(args.warmup):
+            plain[i % len(plain)].index_scores()
+        e_idx[0].record()
+        for i in range(args.steps):
+            plain[i % len(plain)].index_scores()
+        e_idx[1].record()
+        torch.cuda.synchronize()
+        unshared_us = e_idx[0].elapsed_time(e_idx[1]) * 1e3 / args.steps
+        log(f"[bench] index scan without the share hint: {unshared_us:.1f} us/launch")
     dws[0].decode(with_scores=True)
     torch.cuda.synchronize()
 
@@ -276,12 +304,17 @@ def main():
         "dense_attention_bytes_ratio": dense_bytes / b_step,
         "kernel_us": {"index_scores": idx_us,
                       "select_attend_and_gaps": ms_step * 1e3 - idx_us},
-        "roofline": {"bound": "hbm", "kernel": "index_mfma_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm",
+                     "kernel": "index_shared_kernel" if w.share_seqs > 1 else "index_mfma_kernel",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name), "bytes_per_launch": b_idx},
         "cache_write": cw,
         "cpu_baseline": cpu,
     }
+    if unshared_us is not None:
+        out["kernel_us"]["index_scores_without_share_hint"] = unshared_us
+        out["config"]["share_seqs"] = w.share_seqs
     print(json.dumps(out), flush=True)
 
 

@@ -196,11 +196,14 @@ struct HalfRaw;
 template <>
 struct HalfRaw<kFP8> {
   uint4 r[8];  // r[i]: token 8i + lane/8 of the half, 16-byte chunk lane%8
+  // STREAM: the bytes are read once (streaming hint); otherwise other waves
+  // of the shared scan read them again soon, from L2.
+  template <bool STREAM = true>
   __device__ __forceinline__ void issue(const IndexArgs& x, int pb, int h2, int lane) {
     const uint4* src =
         reinterpret_cast<const uint4*>(x.ikd + (size_t)pb * (kBlock * kDim)) + h2 * 512 + lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = load_stream(src + i * 64);
+    for (int i = 0; i < 8; ++i) r[i] = STREAM ? load_stream(src + i * 64) : src[i * 64];
   }
   __device__ __forceinline__ void pool(int j, int h2, int pos, int lane, const QueryB<kFP8>& q,
                                        TileMax& tm, uint4* stage) const {
@@ -234,11 +237,14 @@ struct HalfRaw<kFP8> {
 struct BlockRawNvfp4 {
   uint4 d[8];  // d[i]: token 16i + lane/4 of the block, 16-byte chunk lane%4
   uint4 sc;    // the 8 scale bytes of tokens 2 lane and 2 lane + 1
+  template <bool STREAM = true>
   __device__ __forceinline__ void issue(const IndexArgs& x, int pb, int lane) {
     const uint4* src = reinterpret_cast<const uint4*>(x.ikd + (size_t)pb * (kBlock * kDim / 2)) + lane;
+    const uint4* ssrc =
+        reinterpret_cast<const uint4*>(x.iks + (size_t)pb * (kBlock * kDim / 16)) + lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = load_stream(src + i * 64);
-    sc = load_stream(reinterpret_cast<const uint4*>(x.iks + (size_t)pb * (kBlock * kDim / 16)) + lane);
+    for (int i = 0; i < 8; ++i) d[i] = STREAM ? load_stream(src + i * 64) : src[i * 64];
+    sc = STREAM ? load_stream(ssrc) : *ssrc;
   }
   // E2M1 value x e4m3 block scale is exact in f16 (at most 6 significant
   // bits, inside [2^-10, 2688]); the tensor scale is folded into out_scale.
@@ -277,98 +283,21 @@ struct BlockRawNvfp4 {
       }
     }
   }
-  // The block scored for nct <= CT tiles of 16 columns (the shared scan),
-  // as pool_tiles of the FP8 keys.
-  template <int CT>
-  __device__ __forceinline__ void pool_tiles(int j, const int (&pos)[CT], int nct, int lane,
-                                             const QueryB<kNVFP4> (&q)[CT], TileMax (&tm)[CT],
-                                             uint4* stage) const {
-    const int n = lane & 15, rg = lane >> 4;
-    const uint16_t* scl = reinterpret_cast<const uint16_t*>(stage + 256);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * i + (lane >> 2);
-        stage[t * 4 + ((lane & 3) ^ ((t >> 1) & 3))] = d[4 * h2 + i];
-      }
-      if (h2 == 0) stage[256 + lane] = sc;
-      wave_lds_sync();
-      const int tok = j * kBlock + 64 * h2 + 4 * rg;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int tt = 16 * t + n;
-        const uint4 v = stage[tt * 4 + (rg ^ ((tt >> 1) & 3))];
-        const uint32_t s2 = scl[4 * (64 * h2 + tt) + rg];
-        const f16x2 sc2 = fp8x2_to_f16x2<false>(s2);
-        const f16x2 s0 = {sc2[0], sc2[0]}, s1 = {sc2[1], sc2[1]};
-        const f16x8 k0 = nvfp4x8_f16s(v.x, s0), k1 = nvfp4x8_f16s(v.y, s0);
-        const f16x8 k2 = nvfp4x8_f16s(v.z, s1), k3 = nvfp4x8_f16s(v.w, s1);
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          if (c < nct) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            acc = mfma_f16(k0, q[c].b[0], acc);
-            acc = mfma_f16(k1, q[c].b[1], acc);
-            acc = mfma_f16(k2, q[c].b[2], acc);
-            acc = mfma_f16(k3, q[c].b[3], acc);
-            fold_tile(tm[c], acc, tok + 16 * t, pos[c]);
-          }
-        }
-      }
-    }
-  }
 };
 
 // FP8 keys: the block as two halves (the FP8 kernel takes one block per
 // wave, so nothing more needs to be in flight).
 struct BlockRawFp8 {
   HalfRaw<kFP8> h[2];
+  template <bool STREAM = true>
   __device__ __forceinline__ void issue(const IndexArgs& x, int pb, int lane) {
-    h[0].issue(x, pb, 0, lane);
-    h[1].issue(x, pb, 1, lane);
+    h[0].template issue<STREAM>(x, pb, 0, lane);
+    h[1].template issue<STREAM>(x, pb, 1, lane);
   }
   __device__ __forceinline__ void pool(int j, int pos, int lane, const QueryB<kFP8>& q,
                                        TileMax& tm, uint4* stage) const {
     h[0].pool(j, 0, pos, lane, q, tm, stage);
     h[1].pool(j, 1, pos, lane, q, tm, stage);
-  }
-  // The block scored for nct <= CT tiles of 16 columns (the shared scan):
-  // each key chunk is converted once and multiplied with every tile's
-  // queries; tile c folds keys up to pos[c] (per lane: its column's).
-  template <int CT>
-  __device__ __forceinline__ void pool_tiles(int j, const int (&pos)[CT], int nct, int lane,
-                                             const QueryB<kFP8> (&q)[CT], TileMax (&tm)[CT],
-                                             uint4* stage) const {
-    const int n = lane & 15, rg = lane >> 4;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        stage[(8 * i + (lane >> 3)) * 8 + ((lane & 7) ^ (lane >> 3))] = h[h2].r[i];
-      wave_lds_sync();
-      const int tok = j * kBlock + 64 * h2 + 4 * rg;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint4 v0 = stage[(16 * t + n) * 8 + (rg ^ (n & 7))];
-        const uint4 v1 = stage[(16 * t + n) * 8 + ((rg + 4) ^ (n & 7))];
-        const bf16x8 k0 = fp8x8_bf16(v0.x, v0.y), k1 = fp8x8_bf16(v0.z, v0.w);
-        const bf16x8 k2 = fp8x8_bf16(v1.x, v1.y), k3 = fp8x8_bf16(v1.z, v1.w);
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          if (c < nct) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            acc = mfma_bf16(k0, q[c].b[0], acc);
-            acc = mfma_bf16(k1, q[c].b[1], acc);
-            acc = mfma_bf16(k2, q[c].b[2], acc);
-            acc = mfma_bf16(k3, q[c].b[3], acc);
-            fold_tile(tm[c], acc, tok + 16 * t, pos[c]);
-          }
-        }
-      }
-    }
   }
 };
 

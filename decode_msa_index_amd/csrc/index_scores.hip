@@ -112,30 +112,38 @@ __global__ __launch_bounds__(256, 4) void index_mfma_kernel(IndexArgs x) {
 // -------------------------------------------------------------------------
 // Shared scan (one row per sequence, share groups of consecutive sequences
 // that may map logical blocks to the same physical blocks -- requests with a
-// common prefix).  One wave per (share group, slice of up to 64 / G of its
-// sequences, logical block j): the slice's 64 or fewer (sequence, group)
-// columns are four MFMA column tiles.  The wave reads the slice's table
-// entries for block j and scores each distinct physical block among them
-// once, for exactly the columns whose sequence maps j to it (and sees it);
-// a prefix block shared by the whole slice is read once for all of them.
-// Each column is scored by the same arithmetic as in index_mfma_kernel, so
-// the scores are those of the unshared scan, bit for bit.
+// common prefix).  A wave takes a slice of up to share_per_wave(G) sequences
+// of a group (their (sequence, group) columns fit one MFMA column tile) and
+// one logical block j; the four waves of a workgroup take four consecutive
+// slices of the same group and the same j, and every workgroup of block j
+// has an index = j (mod 8), which the dispatcher places on XCD j % 8: all
+// requests for a block the group shares meet in one XCD's L2, at about the
+// same time, and the block comes from HBM once (the loads keep their lines
+// in L2 for that, unlike the streaming loads of index_mfma_kernel).  A wave reads its slice's table entries for j and
+// scores each distinct physical block among them once, for exactly the
+// columns whose sequence maps j to it (and sees it): a shared prefix block
+// is read once per slice, a private block once for its own sequence, and a
+// slice holds few enough sequences that its private blocks (one load after
+// another) stay short.  Each column is scored by the same arithmetic as in
+// index_mfma_kernel, so the scores are those of the unshared scan, bit for
+// bit.
 // -------------------------------------------------------------------------
-constexpr int kShareCols = 64;  // columns per wave (four tiles of 16)
+__host__ __device__ constexpr int share_per_wave(int G) { return G >= 8 ? 2 : 4; }
 
 template <int IK>
-__global__ __launch_bounds__(256) void index_shared_kernel(IndexArgs x) {
-  constexpr int CT = kShareCols / 16;
+__device__ __forceinline__ void index_shared_body(const IndexArgs& x, int wgs_per_group,
+                                                  int wgs_per_block) {
   __shared__ uint4 stage[4][stage_bytes<IK>() / 16];  // one staging area per wave
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int spw = kShareCols / x.G;  // sequences per slice
-  const int slices = (x.share + spw - 1) / spw;
-  const int grp = blockIdx.y / slices, sl = blockIdx.y % slices;
+  // blockIdx.x = ((j / 8) * wgs_per_block + r) * 8 + j % 8
+  const int j = (blockIdx.x / (8 * wgs_per_block)) * 8 + (blockIdx.x & 7);
+  const int r = (blockIdx.x >> 3) % wgs_per_block;
+  const int grp = r / wgs_per_group, sl = 4 * (r % wgs_per_group) + wave;
+  const int spw = share_per_wave(x.G);
   const int b0 = grp * x.share + sl * spw;
   const int ns = min(min(spw, x.share - sl * spw), x.B - b0);  // the wave's sequences
-  const int j = blockIdx.x * 4 + wave;
   if (ns <= 0 || j >= x.MB) return;
-  const int cols = ns * x.G, nct = (cols + 15) / 16;
+  const int cols = ns * x.G;
   const size_t col0 = (size_t)b0 * x.G;  // first (row, group) pair (one row per sequence)
   // lane i < ns: sequence b0 + i's table entry and last visible key
   int entry = -1, spos = -1;
@@ -145,55 +153,44 @@ __global__ __launch_bounds__(256) void index_shared_kernel(IndexArgs x) {
   }
   const bool usable = lane < ns && j * kBlock <= spos && entry >= 0 && entry < x.P;
   uint64_t pending = __ballot(usable);
-  // per column tile c, this lane's column 16 c + n: its sequence's last key
+  // this lane's column n (sequence n / G): its sequence's last key
   const int n = lane & 15;
-  int posc[CT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    const int col = 16 * c + n;
-    const int pc = __shfl(spos, min(col, cols - 1) / x.G, 64);
-    posc[c] = col < cols ? pc : -1;
-  }
-  TileMax tm[CT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c) tm[c].init();
+  const int pc = __shfl(spos, min(n, cols - 1) / x.G, 64);
+  const int posc = n < cols ? pc : -1;
+  TileMax tm;
+  tm.init();
+  float unscale = 1.0f;
   if (pending) {
-    QueryB<IK> q[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      if (c < nct) {
-        typename BlockRawOf<IK>::query qr;
-        qr.fetch(x, col0 + 16 * c, min(16, cols - 16 * c), lane);
-        qr.make(min(16, cols - 16 * c), lane, q[c]);
-      } else {
-        q[c] = QueryB<IK>{};
-      }
-    }
+    typename BlockRawOf<IK>::query qr;
+    qr.fetch(x, col0, cols, lane);
+    QueryB<IK> q;
+    qr.make(cols, lane, q);
+    unscale = q.unscale;
     while (pending) {  // the distinct physical blocks, one at a time
       const int leader = __builtin_ctzll(pending);
       const int e = __builtin_amdgcn_readlane(entry, leader);
       const uint64_t same = __ballot(lane < ns && entry == e) & pending;
       pending &= ~same;
-      int pact[CT];  // keys a column folds from this block (-1: not its block)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const int col = 16 * c + n;
-        pact[c] = (col < cols && ((same >> (col / x.G)) & 1)) ? posc[c] : -1;
-      }
+      // keys this lane's column folds from block e (-1: not its block)
+      const int pact = (n < cols && ((same >> (n / x.G)) & 1)) ? posc : -1;
       typename BlockRawOf<IK>::type raw;
-      raw.issue(x, e, lane);
-      raw.template pool_tiles<CT>(j, pact, nct, lane, q, tm, stage[wave]);
+      raw.template issue<false>(x, e, lane);
+      raw.pool(j, pact, lane, q, tm, stage[wave]);
     }
-    // after the reduction every lane group holds tile c's score of column 16 c + n
-    float v[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) v[c] = finish_block(x, tm[c], q[c].unscale);
-    const int mine = lane >> 4;
-    const float out = mine == 0 ? v[0] : mine == 1 ? v[1] : mine == 2 ? v[2] : v[3];
-    if (lane < cols) x.scores[(col0 + lane) * x.MB + j] = out;
-  } else if (lane < cols) {  // no sequence of the slice sees block j
-    x.scores[(col0 + lane) * x.MB + j] = -INFINITY;
   }
+  const float v = finish_block(x, tm, unscale);  // -inf for columns that see nothing
+  if (lane < cols) x.scores[(col0 + lane) * x.MB + j] = v;
+}
+
+// FP8 keys: held to 128 registers, four waves per SIMD (it fits without
+// spilling); NVFP4 keys need no bound for that.
+__global__ __launch_bounds__(256, 4) void index_shared_fp8_kernel(IndexArgs x, int wgs_per_group,
+                                                                  int wgs_per_block) {
+  index_shared_body<kFP8>(x, wgs_per_group, wgs_per_block);
+}
+__global__ __launch_bounds__(256) void index_shared_nvfp4_kernel(IndexArgs x, int wgs_per_group,
+                                                                 int wgs_per_block) {
+  index_shared_body<kNVFP4>(x, wgs_per_group, wgs_per_block);
 }
 
 // -------------------------------------------------------------------------
@@ -306,13 +303,19 @@ hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* 
   x.B = nseq;
   x.share = s.share;
   if (s.share > 1 && s.R == 1) {  // shared scan (validated: R == 1)
-    const int spw = kShareCols / s.G;
-    const unsigned ys = (unsigned)(((nseq + s.share - 1) / s.share) * ((s.share + spw - 1) / spw));
-    const dim3 grid((s.MB + 3) / 4, ys);
+    const int spw = share_per_wave(s.G);
+    const int wgs_per_group = ((s.share + spw - 1) / spw + 3) / 4;
+    const int groups = (nseq + s.share - 1) / s.share;
+    const long wgs_per_block = (long)groups * wgs_per_group;
+    const long total = wgs_per_block * ((s.MB + 7) / 8 * 8);  // j padded to a multiple of 8
+    if (total > 0x7FFFFFFFL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)total);
     if (s.ik_dtype == kFP8)
-      hipLaunchKernelGGL(index_shared_kernel<kFP8>, grid, dim3(256), 0, st, x);
+      hipLaunchKernelGGL(index_shared_fp8_kernel, grid, dim3(256), 0, st, x, wgs_per_group,
+                         (int)wgs_per_block);
     else
-      hipLaunchKernelGGL(index_shared_kernel<kNVFP4>, grid, dim3(256), 0, st, x);
+      hipLaunchKernelGGL(index_shared_nvfp4_kernel, grid, dim3(256), 0, st, x, wgs_per_group,
+                         (int)wgs_per_block);
     return hipGetLastError();
   }
   const unsigned rgs = (unsigned)(nseq * x.row_groups);

@@ -23,8 +23,25 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def _headline_shape():
     # 8 sequences x 262,144 tokens, 4 groups, 64 heads, top-16, FP8, bf16 queries
+    table = np.random.default_rng(0).permutation(8 * 2048).reshape(8, 2048).astype(np.int32)
     return SimpleNamespace(index_k_dtype=2, kv_dtype=2, q_dtype=1, seq_lens=np.full(8, 262144),
-                           rows=8, num_groups=4, max_blocks=2048, top_k=16, num_q_heads=64)
+                           rows=8, num_seqs=8, num_groups=4, max_blocks=2048, top_k=16,
+                           num_q_heads=64, block_table=table, num_phys_blocks=8 * 2048)
+
+
+def test_shared_blocks_count_once_in_the_scan_bytes():
+    # requests 0 and 1 share physical blocks 0..2 and have private tails of
+    # 10 and 5 tokens (blocks 3, 4); request 2 sees 100 tokens of block 2
+    shape = SimpleNamespace(index_k_dtype=2, kv_dtype=2, q_dtype=1,
+                            seq_lens=np.array([3 * 128 + 10, 3 * 128 + 5, 2 * 128 + 100]),
+                            rows=3, num_seqs=3, num_groups=1, max_blocks=4, top_k=16,
+                            num_q_heads=16,
+                            block_table=np.array([[0, 1, 2, 3], [0, 1, 2, 4], [0, 1, 2, 0]],
+                                                 np.int32),
+                            num_phys_blocks=5)
+    idx, _, _ = bench.algorithmic_bytes(shape, topk_counts=0)
+    small = 3 * 1 * 128 * 2 + (4 + 4 + 3) * 4 + 3 * 1 * 4 * 4
+    assert idx == (3 * 128 + 10 + 5) * 128 + small
 
 
 def test_scan_bytes_of_the_headline_are_the_keys_plus_small_arrays():
