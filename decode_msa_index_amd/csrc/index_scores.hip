@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, 4) void index_mfma_kernel(IndexArgs x) {
 // of a group (their (sequence, group) columns fit one MFMA column tile) and
 // one logical block j; the four waves of a workgroup take four consecutive
 // slices of the same group and the same j, and every workgroup of block j
-// has an index = j (mod 8), which the dispatcher places on XCD j % 8: all
+// has the same index mod 8, which the dispatcher places on one XCD: all
 // requests for a block the group shares meet in one XCD's L2, at about the
 // same time, and the block comes from HBM once (the loads keep their lines
 // in L2 for that, unlike the streaming loads of index_mfma_kernel).  A wave reads its slice's table entries for j and
@@ -135,8 +135,13 @@ __device__ __forceinline__ void index_shared_body(const IndexArgs& x, int wgs_pe
                                                   int wgs_per_block) {
   __shared__ uint4 stage[4][stage_bytes<IK>() / 16];  // one staging area per wave
   const int lane = threadIdx.x & 63, wave = wave_id();
-  // blockIdx.x = ((j / 8) * wgs_per_block + r) * 8 + j % 8
-  const int j = (blockIdx.x / (8 * wgs_per_block)) * 8 + (blockIdx.x & 7);
+  // blockIdx.x = ((jr / 8) * wgs_per_block + r) * 8 + jr % 8 with
+  // jr = MBp - 1 - j (MBp: MB rounded up to a multiple of 8): the last blocks
+  // first, so that the private blocks past a common prefix -- the slices'
+  // longest chains of loads -- start early rather than form the tail
+  const int mbp = (x.MB + 7) / 8 * 8;
+  const int jr = (blockIdx.x / (8 * wgs_per_block)) * 8 + (blockIdx.x & 7);
+  const int j = mbp - 1 - jr;
   const int r = (blockIdx.x >> 3) % wgs_per_block;
   const int grp = r / wgs_per_group, sl = 4 * (r % wgs_per_group) + wave;
   const int spw = share_per_wave(x.G);
