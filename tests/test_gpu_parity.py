@@ -477,6 +477,44 @@ def test_cache_write_is_bit_exact_with_the_oracle(kv, ik, q, iq):
     assert not np.array_equal(ref["kv_data"], w.kv_data)  # the write changed something
 
 
+@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4, synth.F32])
+def test_cache_write_runs_are_bit_exact(kv):
+    # V is stored transposed; aligned runs of 16 consecutive positions of one
+    # sequence are written a dim row at a time, everything else token by
+    # token.  The list mixes both: aligned runs over two blocks, runs that
+    # start 16 before and at a block edge, misaligned runs, a reversed run, a
+    # run broken by a skipped entry, and a short tail.
+    q = synth.F32 if kv == synth.F32 else synth.BF16
+    w, _, _, _ = _cache_write_inputs(kv, kv, q, q, seed=60 + kv)
+    parts = [(3, np.arange(1024, 1280)), (0, np.arange(8, 40)), (3, np.arange(112, 144)),
+             (1, np.arange(15, -1, -1)), (3, np.arange(2000, 2016)), (2, np.arange(0, 5))]
+    seq = np.concatenate([np.full(len(p_), s_, np.int32) for s_, p_ in parts])
+    pos = np.concatenate([p_ for _, p_ in parts]).astype(np.int32)
+    seq[256 + 32 + 32 + 16 + 7] = -1  # breaks the run at 2000 (entry skipped)
+    rng = np.random.default_rng(61 + kv)
+    n, G, D = len(seq), w.num_groups, w.head_dim
+    enc = lambda x: x.astype(np.float32) if q == synth.F32 else synth.encode_bf16(x)
+    new = dict(k=enc(rng.normal(0, 2.0, (n, G, D))), v=enc(rng.normal(0, 2.0, (n, G, D))),
+               ik=enc(rng.normal(0, 2.0, (n, w.index_dim))))
+    ref = {k: (None if getattr(w, k) is None else getattr(w, k).copy())
+           for k in ("kv_data", "kv_scales", "ik_data", "ik_scales")}
+    oracle.cache_write(parity.oracle_problem(w), seq, pos, new["k"], new["v"], new["ik"],
+                       w.block_table, ref["kv_data"], ref["kv_scales"], ref["ik_data"],
+                       ref["ik_scales"])
+    dw = parity.DeviceWorkload(w)
+    say(f"[parity] cache write runs kv={kv}: {n} tokens")
+    msa.cache_write(dw.p, parity.dev(seq), parity.dev(pos), parity.dev(new["k"]),
+                    parity.dev(new["v"]), parity.dev(new["ik"]), dw.block_table, dw.kv_data,
+                    dw.kv_scales, dw.ik_data, dw.ik_scales)
+    torch.cuda.synchronize()
+    for name in ("kv_data", "kv_scales", "ik_data", "ik_scales"):
+        if ref[name] is None:
+            continue
+        got = getattr(dw, name).cpu().numpy().view(np.uint8)
+        want = ref[name].view(np.uint8)
+        assert np.array_equal(got, want), f"{name}: {int((got != want).sum())} bytes differ"
+
+
 def test_cache_write_then_decode_sees_the_new_tokens():
     """A decode step end to end: write every sequence's newest token (and a
     few older ones) into FP8 caches, then msa_decode; the oracle decodes
