@@ -370,7 +370,7 @@ def time_cache_write(w, dw, seqs, positions, reps=20):
 
     per_token = (2 * G * D * k_new.element_size() + Di * ik_new.element_size() + 8 + 4
                  + coded(2 * G * D, w.kv_dtype) + coded(Di, w.index_k_dtype))
-    kernel = "cache_write_token_kernel" if n < 64 else "cache_write_kernel"  # the library's choice
+    kernel = "cache_write_token_kernel" if n < 512 else "cache_write_kernel"  # the library's choice
     return {"kernel": kernel, "tokens": n, "us_per_launch": us,
             "bytes_per_launch": n * per_token,
             "gbps": n * per_token / (us * 1e-6) / 1e9}

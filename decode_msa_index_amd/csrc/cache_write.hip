@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64) void cache_write_token_kernel(CacheWriteArgs a)
 // 64 bytes); the run owns those bytes whole, so no atomics are needed.
 // Otherwise each wave writes its token's V too.
 constexpr int kRun = 16;
-constexpr int kShortList = 64;  // lists shorter than this take cache_write_token_kernel
+constexpr int kShortList = 512;  // lists shorter than this take cache_write_token_kernel
 
 template <int G, bool KV_F32, bool IK_F32>
 __global__ __launch_bounds__(64 * kRun) void cache_write_kernel(CacheWriteArgs a) {

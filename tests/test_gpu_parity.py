@@ -486,11 +486,13 @@ def test_cache_write_runs_are_bit_exact(kv):
     # run broken by a skipped entry, and a short tail.
     q = synth.F32 if kv == synth.F32 else synth.BF16
     w, _, _, _ = _cache_write_inputs(kv, kv, q, q, seed=60 + kv)
-    parts = [(3, np.arange(1024, 1280)), (0, np.arange(8, 40)), (3, np.arange(112, 144)),
+    # (lists of 512 entries or more take the run path: this one has 613)
+    parts = [(3, np.arange(1024, 1536)), (0, np.arange(8, 40)), (3, np.arange(112, 144)),
              (1, np.arange(15, -1, -1)), (3, np.arange(2000, 2016)), (2, np.arange(0, 5))]
     seq = np.concatenate([np.full(len(p_), s_, np.int32) for s_, p_ in parts])
     pos = np.concatenate([p_ for _, p_ in parts]).astype(np.int32)
-    seq[256 + 32 + 32 + 16 + 7] = -1  # breaks the run at 2000 (entry skipped)
+    assert len(seq) >= 512
+    seq[sum(len(p_) for _, p_ in parts[:4]) + 7] = -1  # breaks the run at 2000 (entry skipped)
     rng = np.random.default_rng(61 + kv)
     n, G, D = len(seq), w.num_groups, w.head_dim
     enc = lambda x: x.astype(np.float32) if q == synth.F32 else synth.encode_bf16(x)
