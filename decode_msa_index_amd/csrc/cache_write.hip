@@ -15,15 +15,17 @@
 // where every arithmetic step is one correctly rounded binary32 operation,
 // so the result is a function of the inputs alone.
 //
-// Work decomposition: a wavefront quantises one new token's planes: planes
-// 0..G-1 are the K rows of the G groups, G..2G-1 the V columns (V is stored
-// transposed), 2G the index key.  Lane l takes dims 2l and 2l+1; an NVFP4
-// group of 16 dims is 8 lanes, whose amax is a 3-step lane reduction.  A
-// workgroup takes 16 consecutive list entries; an aligned run of consecutive
-// positions (a prefill chunk) has its V written a dim row at a time (see
-// cache_write_kernel).  V NVFP4 codes written token by token are nibbles
-// shared with the neighbouring token's, written with atomic and/or on their
-// 32-bit word so that two tokens' writes to one byte cannot interfere.
+// Work decomposition: lane l of a wavefront quantises dims 2l and 2l+1 of
+// one new token's plane: planes 0..G-1 are the K rows of the G groups,
+// G..2G-1 the V columns (V is stored transposed), 2G the index key; an
+// NVFP4 group of 16 dims is 8 lanes, whose amax is a 3-step lane
+// reduction.  Short token lists take one wave per (token, plane)
+// (cache_write_token_kernel); long ones take workgroups of 16 consecutive
+// list entries, which write aligned runs of consecutive positions (a
+// prefill chunk) a V dim row at a time (cache_write_kernel).  V NVFP4 codes
+// written token by token are nibbles shared with the neighbouring token's,
+// written with atomic and/or on their 32-bit word so that two tokens'
+// writes to one byte cannot interfere.
 #include "device.hpp"
 #include "launch.hpp"
 
