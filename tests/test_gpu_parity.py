@@ -276,7 +276,6 @@ def test_decode_with_forced_blocks(K, init, local, fused):
     """Decode with leading and trailing blocks always kept: selection (with
     the near-tie rule for the free places) and attention match the oracle,
     through the fused decode and through the three-call chain."""
-    import dataclasses
     base = synth.make("forced", seed=140 + K + init, seq_lens=[20000, 9000, 3 * 128 + 5, 1100],
                       q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3, top_k=K)
     w = dataclasses.replace(base, init_blocks=init, local_blocks=local)
@@ -527,7 +526,6 @@ def test_cache_write_then_decode_sees_the_new_tokens():
     keep = (seq >= 0) & (seq < w.num_seqs) & (pos < w.max_blocks * 128)
     seq, pos = seq[keep], pos[keep]
     new = {k: np.ascontiguousarray(v[keep]) for k, v in new.items()}
-    import dataclasses
     ref = {k: getattr(w, k).copy() for k in ("kv_data", "ik_data")}
     oracle.cache_write(parity.oracle_problem(w), seq, pos, new["k"], new["v"], new["ik"],
                        w.block_table, ref["kv_data"], None, ref["ik_data"], None)
@@ -644,7 +642,6 @@ def test_prefill_chunk_selection_variants(K, init, local):
     """A causal chunk (R = 64, G = 8: 1,024 units, so the one-wave attention
     launch) with other top-k sizes and forced leading / trailing blocks: each
     row forces its own trailing blocks, through msa_decode and the chain."""
-    import dataclasses
     R = 64
     lens = np.array([7000, 3001])
     qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
