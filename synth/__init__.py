@@ -447,15 +447,25 @@ def spec4_256k(seed: int = 0x4D5341 + 7, **kw) -> Workload:
     return w
 
 
-def prefill_64k(seed: int = 0x4D5341 + 6, **kw) -> Workload:
-    cached, chunk = 65536, 4096
-    w = make("prefill_64k", seed=seed, seq_lens=[cached + chunk], rows_per_seq=chunk,
+def _prefill_chunk(name: str, cached: int, seed: int, **kw) -> Workload:
+    chunk = 4096
+    w = make(name, seed=seed, seq_lens=[cached + chunk], rows_per_seq=chunk,
              q_pos=np.arange(cached, cached + chunk, dtype=np.int32), q_dtype=BF16,
              kv_dtype=FP8, **kw)
-    w.recipe = ("chunked prefill: 1 seq, 65536 cached tokens + a 4096-query chunk at "
-                "positions 65536..69631, causal; 64 q heads / 4 groups, D=Di=128, bf16 q, "
-                "e4m3 K/V/index keys, N(0,1), random permutation table")
+    w.recipe = (f"chunked prefill: 1 seq, {cached} cached tokens + a 4096-query chunk at "
+                f"positions {cached}..{cached + chunk - 1}, causal; 64 q heads / 4 groups, "
+                "D=Di=128, bf16 q, e4m3 K/V/index keys, N(0,1), random permutation table")
     return w
+
+
+def prefill_64k(seed: int = 0x4D5341 + 6, **kw) -> Workload:
+    return _prefill_chunk("prefill_64k", 65536, seed, **kw)
+
+
+def prefill_16k(seed: int = 0x4D5341 + 6, **kw) -> Workload:
+    """The prefill_64k chunk over 16,384 cached tokens: the same rows and
+    blocks per row, a quarter of the K/V working set."""
+    return _prefill_chunk("prefill_16k", 16384, seed, **kw)
 
 
 def nvfp4_512k(seed: int = 0x4D5341 + 4, **kw) -> Workload:
