@@ -1,6 +1,5 @@
 // attend_task.hpp -- exact GQA attention over selected KV blocks, as one
-// task of a workgroup: shared by the attention kernels and the persistent
-// decode kernel.
+// task of a workgroup of the attention kernels (sparse_attend.hip).
 //
 // Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
 // primer" and Figure 1): every query head of a GQA group attends exactly the
@@ -72,25 +71,6 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, int row, int h, i
     reinterpret_cast<float*>(a.out)[idx] = v;
   else
     reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
-}
-
-// Dims d0 .. d0+7 of head h (d0 a multiple of 8): one 16-byte store (bf16)
-// or two (f32).
-__device__ __forceinline__ void store_out8(const AttendArgs& a, int row, int h, int d0,
-                                           const float (&o)[8]) {
-  const size_t idx = ((size_t)row * a.H + h) * kDim + d0;
-  if (a.out_f32) {
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx);
-    p[0] = make_float4(o[0], o[1], o[2], o[3]);
-    p[1] = make_float4(o[4], o[5], o[6], o[7]);
-  } else {
-    uint4 w;
-    w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
-    w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + idx) = w;
-  }
 }
 
 // exp2(x - m) that is 0 when both are -inf (an empty partial)
