@@ -73,6 +73,25 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, int row, int h, i
     reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
 }
 
+// Dims d0 .. d0+7 of head h (d0 a multiple of 8): one 16-byte store (bf16)
+// or two (f32).
+__device__ __forceinline__ void store_out8(const AttendArgs& a, int row, int h, int d0,
+                                           const float (&o)[8]) {
+  const size_t idx = ((size_t)row * a.H + h) * kDim + d0;
+  if (a.out_f32) {
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx);
+    p[0] = make_float4(o[0], o[1], o[2], o[3]);
+    p[1] = make_float4(o[4], o[5], o[6], o[7]);
+  } else {
+    uint4 w;
+    w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+    w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + idx) = w;
+  }
+}
+
 // exp2(x - m) that is 0 when both are -inf (an empty partial)
 __device__ __forceinline__ float rescale(float x, float m) {
   return x == -INFINITY ? 0.0f : exp2f(x - m);
@@ -572,18 +591,43 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     if (SELECT && a.clear) clear_row(a, u, NW);
   }
 
-  // ---- normalise and store: heads 4qd+i, dims 16 (dt0 + d) + n ----
+  // ---- normalise and store (heads 4qd+i, dims 16 (dt0 + d) + n) ----
   float inv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     inv[i] = timed_out ? __builtin_nanf("") : (cl[i] > 0.0f ? a.v_scale / cl[i] : 0.0f);
+  if constexpr (NW <= 4) {
+    // 8 consecutive dims of one head per lane: the wave's values meet in
+    // LDS -- each wave its own dims, so a wave-level sync orders the
+    // accesses -- and leave as 16-byte stores.  (Eight-wave workgroups keep
+    // the element stores: the extra registers cost them more than they save.)
+    __shared__ float ob[kHeadsPad][kDim + 4];  // +4: rows start on different banks
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * qd + i;
-    if (h < a.hpg) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int d = 0; d < DTW; ++d)
-        store_out(a, row, g * a.hpg + h, (dt0 + d) * 16 + n, co[d][i] * inv[i]);
+      for (int d = 0; d < DTW; ++d) ob[4 * qd + i][(dt0 + d) * 16 + n] = co[d][i] * inv[i];
+    }
+    wave_lds_sync();
+    constexpr int CPH = 2 * DTW;  // 8-dim chunks of a head in the wave's dims
+#pragma unroll
+    for (int c0 = 0; c0 < kHeadsPad * CPH; c0 += 64) {
+      const int c = c0 + lane, h = c / CPH, d0 = dt0 * 16 + (c % CPH) * 8;
+      if (c < kHeadsPad * CPH && h < a.hpg) {
+        const float4 lo = *reinterpret_cast<const float4*>(&ob[h][d0]);
+        const float4 hi = *reinterpret_cast<const float4*>(&ob[h][d0 + 4]);
+        const float o[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        store_out8(a, row, g * a.hpg + h, d0, o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * qd + i;
+      if (h < a.hpg) {
+#pragma unroll
+        for (int d = 0; d < DTW; ++d)
+          store_out(a, row, g * a.hpg + h, (dt0 + d) * 16 + n, co[d][i] * inv[i]);
+      }
     }
   }
   if (a.lse && wave == 0 && n == 0) {
