@@ -425,11 +425,12 @@ def test_nan_in_cache_reaches_the_output_without_stalling_the_merge():
     assert int(torch.count_nonzero(dw.ws_decode)) == 0
 
 
-def _cache_write_inputs(kv, ik, q_dtype, iq_dtype, seed, spikes=True):
+def _cache_write_inputs(kv, ik, q_dtype, iq_dtype, seed, spikes=True, G=4, H=64):
     lens = [900, 300, 129, 5000]
     w = synth.make("cw", seed=seed, seq_lens=lens, q_dtype=q_dtype, index_q_dtype=iq_dtype,
                    kv_dtype=kv, index_k_dtype=ik, k_scale=0.75, v_scale=1.25,
-                   ik_scale=0.5 if ik != synth.NVFP4 else None, plant_per_seq=1)
+                   ik_scale=0.5 if ik != synth.NVFP4 else None, plant_per_seq=1,
+                   num_groups=G, num_q_heads=H)
     # block boundaries, both tokens of a V nibble pair, a sequence's last
     # key, and tokens out of range (skipped)
     seq = np.array([0, 0, 0, 1, 1, 2, 2, 3, 3, 3, -1, 4, 0], np.int32)
@@ -476,15 +477,16 @@ def test_cache_write_is_bit_exact_with_the_oracle(kv, ik, q, iq):
     assert not np.array_equal(ref["kv_data"], w.kv_data)  # the write changed something
 
 
-@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4, synth.F32])
-def test_cache_write_runs_are_bit_exact(kv):
+@pytest.mark.parametrize("kv,G,H", [(synth.FP8, 4, 64), (synth.NVFP4, 4, 64), (synth.F32, 4, 64),
+                                    (synth.FP8, 8, 64), (synth.NVFP4, 1, 16), (synth.F32, 2, 16)])
+def test_cache_write_runs_are_bit_exact(kv, G, H):
     # V is stored transposed; aligned runs of 16 consecutive positions of one
     # sequence are written a dim row at a time, everything else token by
     # token.  The list mixes both: aligned runs over two blocks, runs that
     # start 16 before and at a block edge, misaligned runs, a reversed run, a
     # run broken by a skipped entry, and a short tail.
     q = synth.F32 if kv == synth.F32 else synth.BF16
-    w, _, _, _ = _cache_write_inputs(kv, kv, q, q, seed=60 + kv)
+    w, _, _, _ = _cache_write_inputs(kv, kv, q, q, seed=60 + kv + G, G=G, H=H)
     # (lists of 512 entries or more take the run path: this one has 613)
     parts = [(3, np.arange(1024, 1536)), (0, np.arange(8, 40)), (3, np.arange(112, 144)),
              (1, np.arange(15, -1, -1)), (3, np.arange(2000, 2016)), (2, np.arange(0, 5))]
