@@ -118,6 +118,7 @@ def _decode_outputs(w):
     (synth.FP8, 64, 1, 16, 20, False),    # 64 sequences on one wave's columns
     (synth.FP8, 8, 8, 64, 30, False),
     (synth.FP8, 16, 4, 64, 0, False),     # the hint over unshared random tables
+    (synth.NVFP4, 16, 4, 64, 60, "qpos"),  # rows ending inside the shared prefix
 ])
 def test_shared_prefix_scan(kv, n, G, H, share_blocks, diverge):
     # requests with common prefixes: the index scan reads each distinct
@@ -133,7 +134,11 @@ def test_shared_prefix_scan(kv, n, G, H, share_blocks, diverge):
                    share_seqs=n, share_blocks=share_blocks)
     if share_blocks == 0:
         w = dataclasses.replace(w, share_seqs=n)
-    if diverge:  # member 1 takes member 2's private blocks for part of the prefix
+    if diverge == "qpos":  # query rows at earlier positions, some deep inside the prefix
+        qp = np.array([L - 1 - (rng.integers(0, L) if b % 3 == 0 else 0)
+                       for b, L in enumerate(lens)], np.int32)
+        w = dataclasses.replace(w, q_pos=qp)
+    elif diverge:  # member 1 takes member 2's private blocks for part of the prefix
         bt = w.block_table.copy()
         nb2 = (lens[2] + 127) // 128
         k = min(10, nb2 - share_blocks)
