@@ -229,6 +229,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
                                             const Partials& part, int u, int split,
                                             uint32_t* sel_lds) {
   __shared__ int32_t sel_w[SELECT ? NW : 1][32];  // SELECT: each wave's copy of the selection
+  __shared__ uint4 vsl[KV == kNVFP4 ? NW : 1][64];  // NVFP4: each wave's block of V scales
   // sel_lds (SELECT): [256] scratch, [MB] keys, [MB] table row
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int row = u / a.G, g = u % a.G, b = row / a.R;
@@ -318,7 +319,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     // ---- loads: K rows kappa(u, n), V^T rows dt*16+n; 32 dims / tokens each ----
     uint4 kraw[16], vraw[16];
     uint32_t ksc[8];
-    uint4 vsc[16];
+    uint4 vsc;  // NVFP4: 16 bytes of the block's V scales (staged in LDS for the P V step)
     if constexpr (KV == kFP8) {
       const uint8_t* kb = kvd + kplane * (kBlock * kDim);
       const uint8_t* vb = kvd + vplane * (kBlock * kDim);
@@ -347,12 +348,11 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
         ksc[t] = *reinterpret_cast<const uint16_t*>(ks + kappa * (kDim / 16) + qd * 2);
       }
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < 8; ++dt)
         vraw[dt] = *reinterpret_cast<const uint4*>(vb + (dt * 16 + n) * (kBlock / 2) + qd * 16);
-        const uint4* sp = reinterpret_cast<const uint4*>(vs + dt * kBlock + qd * 32);
-        vsc[2 * dt] = sp[0];
-        vsc[2 * dt + 1] = sp[1];
-      }
+      // the block's 1 KB of V scales ([d/16][t]), 16 bytes per lane: every
+      // lane needs 8 of them per 8-key chunk, and 16 lanes the same ones
+      vsc = reinterpret_cast<const uint4*>(vs)[lane];
     }
 
     // ---- S^T = K Q^T ----
@@ -416,6 +416,11 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
 
     // ---- O += P V ----
+    if constexpr (KV == kNVFP4) {  // the V scales through the wave's LDS slice
+      wave_lds_sync();  // the previous block's reads are done
+      vsl[wave][lane] = vsc;
+      wave_lds_sync();
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -426,8 +431,10 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
           vop = (c & 1) ? fp8x8_f16(r.z, r.w) : fp8x8_f16(r.x, r.y);
         } else {
           const uint32_t w = c == 0 ? vraw[dt].x : c == 1 ? vraw[dt].y : c == 2 ? vraw[dt].z : vraw[dt].w;
-          const uint4 sv = vsc[2 * dt + (c >> 1)];
-          vop = (c & 1) ? nvfp4x8_f16(w, sv.z, sv.w) : nvfp4x8_f16(w, sv.x, sv.y);
+          // scales of keys 32 qd + 8 c .. +7 in dim row dt (one per 16 dims)
+          const uint2 sv = *reinterpret_cast<const uint2*>(
+              reinterpret_cast<const uint8_t*>(vsl[wave]) + dt * kBlock + 32 * qd + 8 * c);
+          vop = nvfp4x8_f16(w, sv.x, sv.y);
         }
         oacc[dt] = mfma_f16(pop[c], vop, oacc[dt]);
       }
