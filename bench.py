@@ -96,7 +96,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_256k",
                     choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "spec4_256k",
-                             "fp8_share64", "prefill_64k", "prefill_16k"])
+                             "fp8_share64", "fp8_dcp45_shard", "prefill_64k", "prefill_16k"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -433,6 +433,22 @@ def fp8_share64(seed: int = 0x4D5341 + 9, **kw) -> Workload:
     return w
 
 
+def fp8_dcp45_shard(seed: int = 0x4D5341 + 10, **kw) -> Workload:
+    """One GPU's share of a context-parallel (DCP, 4 GPUs) indexer step over
+    45 requests of U[30,720, 215,040] tokens: each GPU scores a quarter of
+    every request's context for all 4 index heads."""
+    rng = np.random.default_rng([seed, STREAM_TABLE, 2])
+    full = rng.integers(30720, 215041, size=45)
+    lens = ((full + 3) // 4).tolist()
+    w = make("fp8_dcp45_shard", seed=seed, seq_lens=lens, q_dtype=BF16, kv_dtype=FP8,
+             plant_per_seq=8, plant_add=1.0, **kw)
+    w.recipe = ("one GPU's quarter of a 4-way context-parallel step: 45 requests, each a "
+                "quarter of U[30720, 215040] tokens, 64 q heads / 4 groups, D=Di=128, bf16 q, "
+                "e4m3 K/V/index keys, N(0,1), 8 planted blocks per request, random "
+                "permutation table")
+    return w
+
+
 def spec4_256k(seed: int = 0x4D5341 + 7, **kw) -> Workload:
     """Speculative decode: the 256K batch-8 caches with 4 query rows per
     sequence at its last 4 positions (each row its own causal end)."""
