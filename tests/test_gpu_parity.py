@@ -155,6 +155,53 @@ def test_shared_prefix_scan(kv, n, G, H, share_blocks, diverge):
     assert torch.equal(k1, k0) and torch.equal(o1.view(torch.int16), o0.view(torch.int16))
 
 
+def test_context_shards_merge_to_the_full_selection():
+    # Context parallelism of the indexer (the pages' DCP): shard k of 4 holds
+    # a contiguous quarter of every sequence's blocks and scores it with its
+    # own block table.  Each shard's pooled scores must be those of the full
+    # scan, bit for bit, and the shards' local top-(k-1) candidates
+    # (score desc, block asc), merged, must give the full selection.
+    w = synth.make("dcp", seed=230, seq_lens=[20000, 9000, 16385], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, plant_per_seq=3)
+    dw = parity.DeviceWorkload(w)
+    dw.index_scores()
+    dw.block_topk()
+    torch.cuda.synchronize()
+    full = dw.scores.cpu().numpy()
+    sel = dw.topk.cpu().numpy()
+    nb = (w.seq_lens.astype(np.int64) + 127) // 128
+    K, S = w.top_k, 4
+    cands = [[[] for _ in range(w.num_groups)] for _ in range(w.num_seqs)]
+    for k in range(S):
+        lo = [int(k * n // S) for n in nb]
+        hi = [int((k + 1) * n // S) for n in nb]
+        mbk = max(1, max(h - l for l, h in zip(lo, hi)))
+        bt = np.zeros((w.num_seqs, mbk), np.int32)
+        lens = np.zeros(w.num_seqs, np.int32)
+        for b in range(w.num_seqs):
+            bt[b, : hi[b] - lo[b]] = w.block_table[b, lo[b]: hi[b]]
+            lens[b] = max(0, min(int(w.seq_lens[b]) - 128 * lo[b], 128 * (hi[b] - lo[b])))
+        p = dataclasses.replace(dw.p, max_blocks_per_seq=mbk)
+        sk = torch.empty(w.num_seqs, w.num_groups, mbk, dtype=torch.float32, device="cuda")
+        msa.index_scores(p, dw.index_q, dw.ik_data, dw.ik_scales, parity.dev(bt),
+                         parity.dev(lens), None, sk)
+        torch.cuda.synchronize()
+        sk = sk.cpu().numpy()
+        for b in range(w.num_seqs):
+            n = hi[b] - lo[b]
+            got, want = sk[b, :, :n], full[b, :, lo[b]: hi[b]]
+            assert np.array_equal(got.view(np.int32), want.view(np.int32)), (k, b)
+            for g in range(w.num_groups):  # local candidates, the recent block excluded
+                js = [j for j in range(lo[b], hi[b]) if j != nb[b] - 1]
+                js.sort(key=lambda j: (-float(full[b, g, j]), j))
+                cands[b][g] += [(float(full[b, g, j]), j) for j in js[: K - 1]]
+    for b in range(w.num_seqs):
+        for g in range(w.num_groups):
+            merged = sorted(cands[b][g], key=lambda c: (-c[0], c[1]))[: K - 1]
+            want = sorted([j for _, j in merged] + [int(nb[b] - 1)])
+            assert [int(x) for x in sel[b, g] if x >= 0] == want, (b, g)
+
+
 def test_tiny_fp32_workload():
     w = synth.tiny()
     dw, same = _run_and_check(w, fused=False, name="tiny-f32")
