@@ -15,10 +15,11 @@
 // group) columns of one sequence (wave w: columns 64w .. 64w+63 as four
 // 16-column MFMA tiles, held as B operands for the whole kernel) and a range
 // of 16 logical blocks (small ranges make many workgroups, so the partial
-// last wave of them is a small share of the run).  Per block, the 256 threads stream its 16 KB of
-// e4m3 keys contiguously into registers (the next block's while the current
-// one computes), then into LDS with the 16-byte chunks swizzled (chunk c of
-// token t at slot c ^ (t % 8), free of bank conflicts both ways); each wave
+// last wave of them is a small share of the run).  Per block, the 256 threads
+// move its 16 KB of e4m3 keys from HBM straight into LDS with LDS-direct
+// loads (the next block's while the current one computes), each lane fetching
+// the 16-byte chunk that belongs at its LDS slot, so the chunks land swizzled
+// (chunk c of token t at slot c ^ (t % 8), free of bank conflicts); each wave
 // then runs S^T = K Q^T on v_mfma_f32_16x16x32_bf16 for its 64 columns over
 // the block's 8 tiles of 16 tokens, keeping a masked running max per column.
 // The per-block maxima gather in LDS and leave as 64-byte runs per column.
@@ -33,6 +34,18 @@ namespace msa {
 
 constexpr int kCols = 256;   // (row, group) columns per workgroup
 constexpr int kRange = 16;   // logical blocks per workgroup
+
+// 16 bytes per lane from global memory straight into LDS (no registers):
+// lane i's bytes land at wave_base + 16 i, so wave_base must be the same
+// for the whole wave.
+__device__ __forceinline__ void load_lds16(const uint4* src, uint4* wave_base) {
+  __builtin_amdgcn_global_load_lds(
+      (__attribute__((address_space(1))) void*)(const_cast<uint4*>(src)),
+      (__attribute__((address_space(3))) void*)wave_base, 16, 0, 0);
+}
+// wait until every vector-memory operation of this thread has completed,
+// LDS-direct loads included
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 struct PrefillArgs {
   const uint16_t* iq;  // [rows][G][128] bf16
@@ -90,7 +103,11 @@ __device__ __forceinline__ void block_max(const uint4* __restrict__ stage, const
 }
 
 __global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
-  __shared__ uint4 stage[2][kBlock * kDim / 16];  // two 16 KB key blocks, swizzled
+  // two 16 KB key blocks, swizzled; two arrays rather than one [2][...] so
+  // that the compiler sees the reads of one and the LDS-direct loads into the
+  // other as disjoint and does not wait for those loads before the reads
+  __shared__ uint4 stage0[kBlock * kDim / 16];
+  __shared__ uint4 stage1[kBlock * kDim / 16];
   __shared__ float smax[kCols][kRange + 1];       // per-column block maxima (+1: no bank conflicts)
   __shared__ int s_pos_max;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -139,41 +156,40 @@ __global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
   // blocks this workgroup computes: [j0, jend)
   const int jend = min(j1, s_pos_max < 0 ? j0 : s_pos_max / kBlock + 1);
 
-  // ---- stream the blocks: registers -> LDS (swizzled) -> MFMA ----
+  // ---- stream the blocks: HBM -> LDS (swizzled, no registers) -> MFMA ----
   const int32_t* brow = x.bt + (size_t)b * x.MB;
-  int raw_e = 0;  // table entry of the block in raw
-  auto issue = [&](int j, uint4 (&raw)[4]) {
+  int next_e = 0;  // table entry of the block being loaded
+  auto issue = [&](int j, uint4* stg) {
     const int e = brow[j];
-    raw_e = e;
+    next_e = e;
     const int pb = e >= 0 && e < x.P ? e : 0;  // invalid entries are masked below
     const uint4* src = reinterpret_cast<const uint4*>(x.ik + (size_t)pb * (kBlock * kDim));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = load_stream(src + i * 256 + threadIdx.x);
-  };
-  uint4 raw[4];
-  if (j0 < jend) issue(j0, raw);
-  for (int j = j0; j < jend; ++j) {
-    const int st = (j - j0) & 1;
-    // thread t holds chunk t%8 of tokens 32i + t/8; chunk c of token k at slot c ^ (k%8)
+    // slot s = 256 i + thread of the stage holds chunk (s % 8) ^ (tok % 8) of
+    // token tok = s / 8; the wave's 64 slots of instruction i are contiguous
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 32 * i + ((int)threadIdx.x >> 3);
-      stage[st][tok * 8 + (((int)threadIdx.x & 7) ^ (tok & 7))] = raw[i];
+      const int slot = 256 * i + (int)threadIdx.x;
+      const int tok = slot >> 3, c = (slot & 7) ^ (tok & 7);
+      load_lds16(src + tok * 8 + c, stg + 256 * i + 64 * wave);
     }
-    const int e = raw_e;  // block j's table entry
-    __syncthreads();      // the stage is written; the other stage's readers are done
-    if (j + 1 < jend) issue(j + 1, raw);
-    if (e < 0 || e >= x.P) continue;  // invalid table entry: the block stays -inf
-    if (j * kBlock > wave_hi) continue;  // no column of this wave sees the block
+  };
+  // block j from stage `cur`, while block j + 1 loads into `nxt`
+  auto step = [&](int j, const uint4* cur, uint4* nxt) {
+    const int e = next_e;  // block j's table entry
+    wait_vm_all();         // this thread's part of block j is in LDS
+    __syncthreads();       // every part is; the other stage's readers are done
+    if (j + 1 < jend) issue(j + 1, nxt);
+    if (e < 0 || e >= x.P) return;     // invalid table entry: the block stays -inf
+    if (j * kBlock > wave_hi) return;  // no column of this wave sees the block
     // wave-uniform: every column of the wave sees the whole block
     const bool full = __builtin_amdgcn_readfirstlane((int)(j * kBlock + kBlock - 1 <= wave_lo));
     f32x4 m[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) m[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (full)
-      block_max<true>(stage[st], qb, cpos, j, n, r, m);
+      block_max<true>(cur, qb, cpos, j, n, r, m);
     else
-      block_max<false>(stage[st], qb, cpos, j, n, r, m);
+      block_max<false>(cur, qb, cpos, j, n, r, m);
     // max over the lane's 4 keys and the 4 lane groups: lanes 0..15 keep
     // column 16t + n's block maximum
 #pragma unroll
@@ -183,6 +199,11 @@ __global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
       v = fmaxf(v, lane_xor_f<32>(v));
       if (r == 0) smax[64 * wave + 16 * t + n][j - j0] = v * x.out_scale;
     }
+  };
+  if (j0 < jend) issue(j0, stage0);
+  for (int j = j0; j < jend; j += 2) {  // jend is the same for the whole workgroup
+    step(j, stage0, stage1);
+    if (j + 1 < jend) step(j + 1, stage1, stage0);
   }
   __syncthreads();
   // ---- column c's blocks [j0, j1): one contiguous run each ----
