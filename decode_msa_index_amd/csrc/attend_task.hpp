@@ -92,6 +92,13 @@ __device__ __forceinline__ void store_out8(const AttendArgs& a, int row, int h, 
   }
 }
 
+// 2^x on the hardware exp2 instruction alone, without the library's scaling
+// for results below 2^-126 (those may come out as 0 rather than subnormal).
+// Used for the attention weights 2^(s - max): a weight that small rounds to
+// 0 in f16 for the P V product either way, and cannot change the fp32 row
+// sum, which already holds the weight 1 of the row's maximum.
+__device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp2(x - m) that is 0 when both are -inf (an empty partial)
 __device__ __forceinline__ float rescale(float x, float m) {
   return x == -INFINITY ? 0.0f : exp2f(x - m);
@@ -397,7 +404,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sacc[t][i] - Mn);
+        const float p = exp2_weight(sacc[t][i] - Mn);
         lsum += p;
         pop[t >> 1][4 * (t & 1) + i] = (_Float16)p;
       }
