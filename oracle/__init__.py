@@ -69,8 +69,6 @@ def lib():
         L.msa_oracle_bf16.restype = ctypes.c_double
         L.msa_oracle_bf16.argtypes = [ctypes.c_uint16]
         L.msa_oracle_index_scores.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
-        L.msa_oracle_token_scores.argtypes = [P, vp, vp, vp, vp, vp, vp,
-                                              ctypes.c_int32, ctypes.c_int32, vp]
         L.msa_oracle_block_topk.argtypes = [P, vp, vp, vp, vp]
         L.msa_oracle_sparse_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_oracle_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -145,22 +143,6 @@ def index_scores(p: Problem, index_q, ik_data, ik_scales, block_table, seq_lens,
     rc = lib().msa_oracle_index_scores(ctypes.byref(pc), _ptr(index_q), _ptr(ik_data),
                                        _ptr(ik_scales), _ptr(block_table), _ptr(seq_lens),
                                        _ptr(q_pos), _ptr(out))
-    if rc:
-        raise ValueError("oracle rejected the problem")
-    return out
-
-
-def token_scores(p: Problem, index_q, ik_data, ik_scales, block_table, seq_lens,
-                 row: int, group: int, q_pos=None) -> np.ndarray:
-    b = row // p.rows_per_seq
-    pos = int(seq_lens[b]) - 1
-    if q_pos is not None:
-        pos = min(pos, int(q_pos[row]))
-    out = np.empty(max(pos + 1, 0), np.float32)
-    pc = p.c()
-    rc = lib().msa_oracle_token_scores(ctypes.byref(pc), _ptr(index_q), _ptr(ik_data),
-                                       _ptr(ik_scales), _ptr(block_table), _ptr(seq_lens),
-                                       _ptr(q_pos), row, group, _ptr(out))
     if rc:
         raise ValueError("oracle rejected the problem")
     return out

@@ -166,14 +166,29 @@ static int check_problem(const msa_oracle_problem* p) {
 }
 
 /* Last visible key of the query row: keys t <= pos and t < seq_len are
- * visible.  Decode rows see the whole cache, including the token just
- * inserted.  A negative result means the row sees no key at all. */
+ * visible, and only keys the block table reaches (t < max_blocks * block_size:
+ * a row cannot see a block it has no table entry for).  Decode rows see the
+ * whole cache, including the token just inserted.  A negative result means
+ * the row sees no key at all.  (The pages say nothing of a sequence longer
+ * than its table; this is the reading the library's header documents.) */
 static int64_t row_pos(const msa_oracle_problem* p, const int32_t* seq_lens,
                        const int32_t* q_pos, int64_t row) {
   int64_t b = row / p->rows_per_seq;
-  int64_t last = (int64_t)seq_lens[b] - 1;
+  int64_t reach = (int64_t)p->max_blocks * p->block_size;
+  int64_t last = (int64_t)seq_lens[b] < reach ? (int64_t)seq_lens[b] : reach;
+  last -= 1;
   if (q_pos && (int64_t)q_pos[row] < last) return q_pos[row];
   return last;
+}
+
+/* Physical block of logical block j of sequence b, or -1 when the table
+ * entry lies outside the pool [0, num_phys_blocks): such a block holds no
+ * key (pooled score -inf, nothing to attend).  The pages are silent on
+ * malformed tables; this is the reading the library's header documents. */
+static int64_t phys_block(const msa_oracle_problem* p, const int32_t* block_table,
+                          int64_t b, int64_t j) {
+  int64_t pb = block_table[b * (int64_t)p->max_blocks + j];
+  return (pb < 0 || pb >= p->num_phys_blocks) ? -1 : pb;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -226,19 +241,15 @@ int msa_oracle_threads_used(void) { return g_threads_used; }
 /* Step 1+2: index scores and block max-pool                                */
 /* ------------------------------------------------------------------------ */
 
-/* Score of token t for (row, group): the dot product of the group's index
- * query with the shared index key, times the score scale, in double, then
- * rounded once to binary32.  One index query per GQA group, one index-key
+/* Score of the token in slot `slot` of physical block pb for (row, group):
+ * the dot product of the group's index query with the shared index key,
+ * times the score scale, in double, then rounded once to binary32.  One index query per GQA group, one index-key
  * head shared by all groups (vLLM blog, "MSA primer"; API reference of
  * MiniMaxM3SparseAttention: the indexer is built with scale = head_dim^-0.5
  * and num_index_heads = num_kv_heads). */
 static float token_score(const msa_oracle_problem* p, const void* index_q,
-                         const void* ik_data, const void* ik_scales,
-                         const int32_t* block_table, int64_t row, int g, int64_t t) {
-  int64_t b = row / p->rows_per_seq;
-  int64_t j = t / p->block_size;
-  int slot = (int)(t % p->block_size);
-  int64_t pb = block_table[b * (int64_t)p->max_blocks + j];
+                         const void* ik_data, const void* ik_scales, int64_t pb,
+                         int64_t row, int g, int slot) {
   size_t qoff = ((size_t)row * (size_t)p->num_groups + (size_t)g) * (size_t)p->index_dim;
   double dot = 0.0;
   for (int d = 0; d < p->index_dim; ++d) {
@@ -259,7 +270,7 @@ typedef struct {
 /* Max-pool: the score of logical block j is the largest token score over
  * the block's visible tokens (sparse_score_type "max" in the API reference
  * of MiniMaxM3SparseAttention.__init__).  Blocks past the row's last visible
- * block get -inf. */
+ * block, and blocks whose table entry is outside the pool, get -inf. */
 static void score_unit(void* c_, int64_t unit) {
   score_ctx* c = (score_ctx*)c_;
   const msa_oracle_problem* p = c->p;
@@ -275,10 +286,11 @@ static void score_unit(void* c_, int64_t unit) {
     }
     int64_t t1 = t0 + p->block_size - 1;
     if (t1 > pos) t1 = pos;
-    float best = -INFINITY;
-    for (int64_t t = t0; t <= t1; ++t) {
-      float s = token_score(p, c->index_q, c->ik_data, c->ik_scales,
-                            c->block_table, row, g, t);
+    int64_t pb = phys_block(p, c->block_table, row / p->rows_per_seq, j);
+    float best = -INFINITY;  /* the max over no token: an empty block */
+    for (int64_t t = t0; pb >= 0 && t <= t1; ++t) {
+      float s = token_score(p, c->index_q, c->ik_data, c->ik_scales, pb, row, g,
+                            (int)(t - t0));
       if (s > best) best = s;
     }
     out[j] = best;
@@ -295,19 +307,6 @@ int msa_oracle_index_scores(const msa_oracle_problem* p, const void* index_q,
   score_ctx c = {p, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos, scores};
   int64_t units = (int64_t)p->num_seqs * p->rows_per_seq * p->num_groups;
   fan_out(p->num_threads, units, score_unit, &c);
-  return 0;
-}
-
-int msa_oracle_token_scores(const msa_oracle_problem* p, const void* index_q,
-                            const void* ik_data, const void* ik_scales,
-                            const int32_t* block_table, const int32_t* seq_lens,
-                            const int32_t* q_pos, int32_t row, int32_t group,
-                            float* out) {
-  if (check_problem(p) || !index_q || !ik_data || !block_table || !seq_lens || !out)
-    return -1;
-  int64_t pos = row_pos(p, seq_lens, q_pos, row);
-  for (int64_t t = 0; t <= pos; ++t)
-    out[t] = token_score(p, index_q, ik_data, ik_scales, block_table, row, group, t);
   return 0;
 }
 
@@ -440,7 +439,8 @@ static void attend_unit(void* c_, int64_t unit) {
   for (int i = 0; i < p->top_k; ++i) {
     int32_t j = sel[i];
     if (j < 0) continue;
-    int64_t pb = c->block_table[b * (int64_t)p->max_blocks + j];
+    int64_t pb = phys_block(p, c->block_table, b, j);
+    if (pb < 0) continue; /* an entry outside the pool holds no key */
     for (int t = 0; t < p->block_size; ++t) {
       int64_t tok = (int64_t)j * p->block_size + t;
       if (tok > pos) break;

@@ -194,6 +194,167 @@ def test_cache_write_nvfp4_representable_values_come_back_exactly():
         assert np.array_equal(sc, s_codes[0, g])
 
 
+# An independent NVFP4 writer in numpy, written from the quantiser's
+# definition (per 16 consecutive elements of one token: s = e4m3(amax /
+# (6 scale)), element e2m1(x / (e4m3value(s) scale)), every step one binary32
+# operation, 0 codes when the group scale is 0) and the cache layouts the
+# library header documents.  Rounding to e4m3 is torch's float8 cast after a
+# clamp at 448 (saturation); rounding to e2m1 is a threshold table whose
+# midpoints go to the even code.
+def _e2m1_codes(y: np.ndarray) -> np.ndarray:
+    a = np.abs(y.astype(np.float64))
+    code = np.zeros(a.shape, np.uint8)
+    for thr, c, inclusive in [(0.25, 1, False), (0.75, 2, True), (1.25, 3, False),
+                              (1.75, 4, True), (2.5, 5, False), (3.5, 6, True),
+                              (5.0, 7, False)]:
+        code = np.where(a >= thr if inclusive else a > thr, np.uint8(c), code)
+    return (code | (np.signbit(y).astype(np.uint8) << 3)).astype(np.uint8)
+
+
+def _nvfp4_group_codes(x: np.ndarray, scale: float):
+    """x [n] float32 (n a multiple of 16) -> e2m1 codes [n], e4m3 scale codes [n/16]."""
+    sc = np.float32(scale)
+    g = x.astype(np.float32).reshape(-1, 16)
+    amax = np.abs(g).max(axis=1)
+    sv = amax / (np.float32(6.0) * sc)
+    s_code = torch.from_numpy(np.minimum(sv, np.float32(448.0))).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    s_val = torch.from_numpy(s_code.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    sg = (s_val * sc).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = g / sg[:, None]
+    q = np.where(sg[:, None] == 0, np.uint8(0), _e2m1_codes(y))
+    return q.reshape(-1), s_code
+
+
+def _put_nibble(buf: np.ndarray, elem: int, code: int):
+    b = elem // 2
+    buf[b] = (buf[b] & 0xF0) | code if elem % 2 == 0 else (buf[b] & 0x0F) | (code << 4)
+
+
+def _numpy_nvfp4_write(w, seq, pos, new):
+    """Expected NVFP4 caches after writing the new tokens (both K/V and
+    index keys NVFP4)."""
+    P, G, BS, D, Di = w.num_phys_blocks, w.num_groups, w.block_size, w.head_dim, w.index_dim
+    kvd = w.kv_data.copy().reshape(P, 2, G, -1)
+    kvs = w.kv_scales.copy().reshape(P, 2, G, -1)
+    ikd = w.ik_data.copy().reshape(P, BS, Di // 2)
+    iks = w.ik_scales.copy().reshape(P, BS, Di // 16)
+    bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    for i, (b, p_) in enumerate(zip(seq, pos)):
+        if b < 0 or b >= w.num_seqs or p_ < 0 or p_ >= w.max_blocks * BS:
+            continue
+        pb = int(w.block_table[b, p_ // BS])
+        if pb < 0 or pb >= P:
+            continue
+        t = int(p_ % BS)
+        for g in range(G):
+            qk, sk = _nvfp4_group_codes(bf(new["k"][i, g]), w.k_scale)
+            for d in range(D):  # K: [t][d/2], scales [t][d/16]
+                _put_nibble(kvd[pb, 0, g], t * D + d, int(qk[d]))
+            kvs[pb, 0, g, t * (D // 16): (t + 1) * (D // 16)] = sk
+            qv, sv = _nvfp4_group_codes(bf(new["v"][i, g]), w.v_scale)
+            for d in range(D):  # V: [d][t/2], scales [d/16][t]
+                _put_nibble(kvd[pb, 1, g], d * BS + t, int(qv[d]))
+            for c in range(D // 16):
+                kvs[pb, 1, g, c * BS + t] = sv[c]
+        qi, si = _nvfp4_group_codes(bf(new["ik"][i]), w.index_k_scale)
+        row = ikd[pb, t]
+        for d in range(Di):
+            _put_nibble(row, d, int(qi[d]))
+        iks[pb, t] = si
+    return {"kv_data": kvd.reshape(w.kv_data.shape), "kv_scales": kvs.reshape(w.kv_scales.shape),
+            "ik_data": ikd.reshape(w.ik_data.shape), "ik_scales": iks.reshape(w.ik_scales.shape)}
+
+
+def _nvfp4_tokens(w):
+    """New tokens at block edges, both tokens of V nibble pairs (even and odd
+    slot of one block), and entries out of range (skipped)."""
+    seq = np.array([0, 0, 0, 0, 1, 1, 2, -1, 3, 0], np.int32)
+    pos = np.array([0, 1, 898, 899, 128, 255, 127, 5, 5, w.max_blocks * 128], np.int32)
+    return seq, pos
+
+
+def test_cache_write_nvfp4_matches_an_independent_writer_on_every_plane():
+    """General values (normal, with a spread of magnitudes, exact zeros and
+    groups that are all zero): the oracle's NVFP4 K, V and index-key bytes,
+    data and scales, equal those of the independent numpy writer byte for
+    byte -- every plane, the transposed V with its shared nibble bytes and
+    [d/16][t] scales included."""
+    w, _, _, _ = _cache_write_case(synth.NVFP4, synth.NVFP4, synth.BF16, synth.BF16, seed=8)
+    seq, pos = _nvfp4_tokens(w)
+    rng = np.random.default_rng(17)
+    n, G, D = len(seq), w.num_groups, w.head_dim
+
+    def vals(*shape):
+        x = rng.normal(0, 1.5, shape) * np.exp2(rng.integers(-12, 4, shape))
+        x[rng.random(shape) < 0.05] = 0.0
+        return x
+
+    kx, vx, ix = vals(n, G, D), vals(n, G, D), vals(n, w.index_dim)
+    kx[1, 0, 16:32] = 0.0  # a group with amax 0: scale code 0, data 0
+    new = dict(k=synth.encode_bf16(kx), v=synth.encode_bf16(vx), ik=synth.encode_bf16(ix))
+    got = _oracle_write(w, seq, pos, new)
+    want = _numpy_nvfp4_write(w, seq, pos, new)
+    for name in ("kv_data", "kv_scales", "ik_data", "ik_scales"):
+        diff = int((got[name] != want[name]).sum())
+        assert diff == 0, f"{name}: {diff} bytes differ"
+    assert not np.array_equal(got["kv_data"], w.kv_data)
+
+
+def test_cache_write_nvfp4_grid_values_come_back_through_an_independent_reader():
+    """Values on the format's grid (e4m3(s) * e2m1(q) * scale, each group
+    holding a +-6 element) for K, V and the index key, written for tokens that
+    share V nibble bytes: read back with the test's own decoders of the
+    documented layouts, every written element is exactly the input value and
+    every element of other slots is unchanged."""
+    import dataclasses
+    w, _, _, _ = _cache_write_case(synth.NVFP4, synth.NVFP4, synth.BF16, synth.BF16, seed=9)
+    w = dataclasses.replace(w, k_scale=2.0 ** -8, v_scale=2.0 ** -7, index_k_scale=2.0 ** -6)
+    seq, pos = _nvfp4_tokens(w)
+    rng = np.random.default_rng(10)
+    n, G, D, Di = len(seq), w.num_groups, w.head_dim, w.index_dim
+
+    def grid(shape, scale):
+        s_codes = rng.integers(0x20, 0x50, shape[:-1] + (shape[-1] // 16,))
+        q_codes = rng.integers(0, 16, shape)
+        q_codes[..., ::16] = np.where(rng.random(q_codes[..., ::16].shape) < 0.5, 7, 15)
+        e4 = np.vectorize(oracle.e4m3)(s_codes)
+        e2 = np.vectorize(oracle.e2m1)(q_codes)
+        x = np.repeat(e4, 16, axis=-1) * e2 * scale
+        assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+        bx = synth.encode_bf16(x.astype(np.float32))
+        assert np.array_equal((bx.astype(np.uint32) << 16).view(np.float32), x)  # bf16-exact
+        return x, bx
+
+    kx, kb = grid((n, G, D), w.k_scale)
+    vx, vb = grid((n, G, D), w.v_scale)
+    ix, ib = grid((n, Di), w.index_k_scale)
+    got = _oracle_write(w, seq, pos, dict(k=kb, v=vb, ik=ib))
+    w2 = dataclasses.replace(w, kv_data=got["kv_data"], kv_scales=got["kv_scales"],
+                             ik_data=got["ik_data"], ik_scales=got["ik_scales"])
+    K0, V0 = _kv_f64(w)
+    K1, V1 = _kv_f64(w2)  # [P, G, BS, D], tensor scales applied
+    I0 = _index_keys_f64(w) * w.index_k_scale
+    I1 = _index_keys_f64(w2) * w.index_k_scale  # [P, BS, Di]
+    written = set()
+    for i, (b, p_) in enumerate(zip(seq, pos)):
+        if b < 0 or b >= w.num_seqs or p_ >= w.max_blocks * 128:
+            continue
+        pb, t = int(w.block_table[b, p_ // 128]), int(p_ % 128)
+        written.add((pb, t))
+        for g in range(G):
+            np.testing.assert_array_equal(K1[pb, g, t], kx[i, g])
+            np.testing.assert_array_equal(V1[pb, g, t], vx[i, g])
+        np.testing.assert_array_equal(I1[pb, t], ix[i])
+    keep = np.ones((w.num_phys_blocks, 128), bool)
+    for pb, t in written:
+        keep[pb, t] = False
+    assert np.array_equal(K1.transpose(0, 2, 1, 3)[keep], K0.transpose(0, 2, 1, 3)[keep])
+    assert np.array_equal(V1.transpose(0, 2, 1, 3)[keep], V0.transpose(0, 2, 1, 3)[keep])
+    assert np.array_equal(I1[keep], I0[keep])
+
+
 def test_bf16_matches_torch():
     rng = np.random.default_rng(1)
     bits = np.concatenate([rng.integers(0, 1 << 16, 20000),
@@ -375,6 +536,93 @@ def test_q_pos_limits_visible_tokens():
     got = oracle.index_scores(p, iq, ik, None, bt, lens, q_pos=qp)
     assert got[0, 0, 3] == 0.0 and got[1, 0, 3] == 80.0
     assert np.all(got[2, :, 2:] == -np.inf) and np.isfinite(got[2, 0, 1])
+
+
+# ---------------------------------------------------------------------------
+# rows longer than their block table; table entries outside the pool (the
+# readings the library header documents: a row sees only keys its table
+# reaches, and an entry outside [0, P) is an empty block)
+# ---------------------------------------------------------------------------
+
+def test_rows_are_clamped_at_the_table_reach():
+    """Sequences longer than max_blocks * BS, and a query position past it,
+    see the keys t < max_blocks * BS only: every output equals that of the
+    same caches with the lengths cut to the table's reach, and the cut case
+    matches the brute-force scores and the dense attention."""
+    import dataclasses
+    base = _small_workload(synth.FP8, lens=(700, 517, 129), top_k=3, plant=1)
+    MB = 4  # reach: 512 tokens
+    bt = np.ascontiguousarray(base.block_table[:, :MB])
+    cut = dataclasses.replace(base, max_blocks=MB, block_table=bt,
+                              seq_lens=np.array([512, 512, 129], np.int32))
+    long_ = dataclasses.replace(cut, seq_lens=np.array([700, 10517, 129], np.int32))
+    a = oracle.decode(_oracle_problem(long_), long_.index_q, long_.ik_data, long_.ik_scales,
+                      long_.q, long_.kv_data, long_.kv_scales, long_.block_table,
+                      long_.seq_lens)
+    c = oracle.decode(_oracle_problem(cut), cut.index_q, cut.ik_data, cut.ik_scales, cut.q,
+                      cut.kv_data, cut.kv_scales, cut.block_table, cut.seq_lens)
+    for x, y in zip(a, c):
+        assert np.array_equal(x, y)
+    keys = _index_keys_f64(cut) * cut.index_k_scale
+    iq = _decode_plain(cut.index_q, cut.index_q_dtype)
+    for b in range(cut.num_seqs):
+        L = int(cut.seq_lens[b])
+        nb = (L + 127) // 128
+        s = (keys[cut.block_table[b, :nb]].reshape(nb * 128, -1)[:L] @ iq[b].T
+             * cut.index_scale).astype(np.float32)
+        for j in range(nb):
+            np.testing.assert_array_max_ulp(c[0][b, :, j], s[j * 128: (j + 1) * 128].max(0), 1)
+        assert all((c[1][b, g] >= 0).sum() == min(3, nb) and nb - 1 in c[1][b, g]
+                   for g in range(cut.num_groups))
+        ref = _dense_attention(cut, b, [[j for j in c[1][b, g] if j >= 0]
+                                        for g in range(cut.num_groups)])
+        np.testing.assert_allclose(c[2][b], ref, rtol=1e-12, atol=1e-12)
+    # positions past the reach clamp the same way
+    qp = np.array([5000, 300, 128], np.int32)
+    qpc = np.array([511, 300, 128], np.int32)
+    pa = oracle.decode(_oracle_problem(long_), long_.index_q, long_.ik_data, long_.ik_scales,
+                       long_.q, long_.kv_data, long_.kv_scales, long_.block_table,
+                       long_.seq_lens, qp)
+    pc = oracle.decode(_oracle_problem(cut), cut.index_q, cut.ik_data, cut.ik_scales, cut.q,
+                       cut.kv_data, cut.kv_scales, cut.block_table, cut.seq_lens, qpc)
+    for x, y in zip(pa, pc):
+        assert np.array_equal(x, y)
+
+
+def test_out_of_pool_table_entries_are_empty_blocks():
+    """Entries -1, P and -5 (one of them a recent block) score -inf, are
+    never dereferenced and add nothing to the attention; a sequence whose
+    whole table is invalid gets -inf scores, the plain selection, a zero
+    output and lse -inf."""
+    import dataclasses
+    w = _small_workload(synth.FP8, lens=(900, 517, 300), top_k=4, plant=2)
+    p = _oracle_problem(w)
+    s0 = oracle.index_scores(p, w.index_q, w.ik_data, w.ik_scales, w.block_table, w.seq_lens)
+    bt = w.block_table.copy()
+    bad = {(0, 2): -1, (0, 6): w.num_phys_blocks, (1, 4): -5}  # (1, 4): sequence 1's recent block
+    for (b, j), v in bad.items():
+        bt[b, j] = v
+    bt[2, :] = -1
+    wb = dataclasses.replace(w, block_table=bt)
+    s, k, o, lse = oracle.decode(p, wb.index_q, wb.ik_data, wb.ik_scales, wb.q, wb.kv_data,
+                                 wb.kv_scales, bt, wb.seq_lens)
+    for b in range(2):
+        for j in range(w.max_blocks):
+            if (b, j) in bad:
+                assert np.all(s[b, :, j] == -np.inf)
+            else:
+                assert np.array_equal(s[b, :, j], s0[b, :, j])
+    assert np.all(s[2] == -np.inf)
+    for b in range(3):
+        recent = (int(w.seq_lens[b]) - 1) // 128
+        for g in range(w.num_groups):
+            assert list(k[b, g]) == _brute_select(s[b, g], recent, w.top_k)
+    valid = lambda b, j: j >= 0 and (b, j) not in bad
+    for b in range(2):
+        ref = _dense_attention(w, b, [[j for j in k[b, g] if valid(b, j)]
+                                      for g in range(w.num_groups)])
+        np.testing.assert_allclose(o[b], ref, rtol=1e-12, atol=1e-12)
+    assert np.all(o[2] == 0.0) and np.all(lse[2] == -np.inf)
 
 
 # ---------------------------------------------------------------------------
