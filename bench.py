@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device (counter calibration) and exit")
+    ap.add_argument("--calibrate-read", action="store_true",
+                    help="only time the read probe over the workload's index-key blocks "
+                         "(the scan's bytes and access pattern, no arithmetic) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py runs on one GPU only: the library has no multi-GPU path; "
@@ -125,25 +128,21 @@ def main():
 
     import decode_msa_index_amd as msa
     import synth
-    from tests import parity
+    from decode_msa_index_amd import harness
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     msa.lib()
     t0 = time.time()
     w = getattr(synth, args.workload)()
     log(f"[bench] generated {w.name} in {time.time() - t0:.1f}s: {w.recipe}")
+    if args.calibrate_read:
+        return calibrate_read(args, w)
     if w.rows_per_seq >= 16:  # a prefill chunk: its own line (rows/s, MFMA roofline)
         return run_prefill(args, w)
 
-    dws = [parity.DeviceWorkload(w)]
+    dws = [harness.DeviceWorkload(w)]
     for _ in range(1, args.layers):
-        d = parity.DeviceWorkload.__new__(parity.DeviceWorkload)
-        d.__dict__.update(dws[0].__dict__)
-        d.ik_data = dws[0].ik_data.clone()
-        d.kv_data = dws[0].kv_data.clone()
-        d.ik_scales = None if dws[0].ik_scales is None else dws[0].ik_scales.clone()
-        d.kv_scales = None if dws[0].kv_scales is None else dws[0].kv_scales.clone()
-        dws.append(d)
+        dws.append(dws[0].copy_with_new_caches())
     torch.cuda.synchronize()
     log(f"[bench] {args.layers} cache copies resident; "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -208,7 +207,7 @@ def main():
     if w.share_seqs > 1:  # the same scan without the share-group hint
         plain = []
         for d in dws:
-            c = parity.DeviceWorkload.__new__(parity.DeviceWorkload)
+            c = harness.DeviceWorkload.__new__(harness.DeviceWorkload)
             c.__dict__.update(d.__dict__)
             c.p = dataclasses.replace(d.p, share_seqs=0)
             plain.append(c)
@@ -255,7 +254,7 @@ def main():
         threads = max(1, min(16, os.cpu_count() or 1))
 
         def time_oracle(nthreads, seconds):
-            p = parity.oracle_problem(w, nthreads)
+            p = oracle.Problem(**w.problem_fields(), num_threads=nthreads)
             reps, t_c0 = 0, time.perf_counter()
             while True:
                 oracle.decode(p, w.index_q, w.ik_data, w.ik_scales, w.q, w.kv_data,
@@ -318,6 +317,69 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def calibrate_read(args, w):
+    """Read ceiling of the scan's access pattern: the read probe
+    (libmsa_probe.so) streams exactly the index-key blocks the scan reads, in
+    the scan's order, one wave per 16 KB block with every load 1 KB of
+    consecutive bytes, and does no arithmetic.  Rotated over --layers cache
+    copies like the decode steps; also timed over the same blocks in physical
+    order, and with 2 and 4 blocks in flight per wave."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from decode_msa_index_amd import harness
+    from decode_msa_index_amd.build import PROBE_LIB
+
+    assert w.index_k_dtype == 2, "the read probe covers FP8 index keys (16 KB blocks)"
+    L = ctypes.CDLL(PROBE_LIB)
+    L.msa_probe_read_blocks.restype = ctypes.c_int
+    L.msa_probe_read_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nb = (w.seq_lens.astype(np.int64) + 127) // 128
+    order = np.concatenate([w.block_table[b, : nb[b]] for b in range(w.num_seqs)]).astype(np.int32)
+    n = len(order)
+    copies = [harness.dev(w.ik_data)]
+    for _ in range(1, args.layers):
+        copies.append(copies[0].clone())
+    orders = {"scan order": harness.dev(order), "physical order": harness.dev(np.sort(order))}
+    sink = torch.zeros(n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    results = []
+    for name, o in orders.items():
+        for bpw in (1, 2, 4):
+            def launch(i):
+                rc = L.msa_probe_read_blocks(copies[i % len(copies)].data_ptr(), o.data_ptr(), n,
+                                             bpw, sink.data_ptr(), stream)
+                assert rc == 0, rc
+            for i in range(args.warmup):
+                launch(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(args.steps):
+                launch(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            gbps = n * 16384 / (us * 1e-6) / 1e9
+            log(f"[bench] read probe, {name}, {bpw} block(s) per wave: {us:.2f} us per launch, "
+                f"{gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
+            results.append({"order": name, "blocks_per_wave": bpw, "us_per_launch": us,
+                            "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS})
+    print(json.dumps({"calibrate_read": w.name, "bytes_per_launch": n * 16384,
+                      "cache_copies": args.layers, "steps": args.steps, "results": results}),
+          flush=True)
+
+
+def row_last_key(w, r: int) -> int:
+    """The last key query row r sees (negative: none): its position, the
+    sequence's end and the block table's reach, whichever comes first."""
+    b = r // w.rows_per_seq
+    last = min(int(w.seq_lens[b]), w.max_blocks * w.block_size) - 1
+    return min(int(w.q_pos[r]), last) if w.q_pos is not None else last
+
+
 def time_cache_write(w, dw, seqs, positions, reps=20):
     """msa_cache_write of len(positions) new tokens into dw's caches (it
     overwrites those slots; run it after the other timings): the average
@@ -329,7 +391,7 @@ def time_cache_write(w, dw, seqs, positions, reps=20):
 
     import decode_msa_index_amd as msa
     import synth
-    from tests import parity
+    from decode_msa_index_amd import harness
 
     n, G, D, Di = len(positions), w.num_groups, w.head_dim, w.index_dim
     gen = torch.Generator(device="cuda").manual_seed(0x4357)
@@ -338,8 +400,8 @@ def time_cache_write(w, dw, seqs, positions, reps=20):
     k_new = torch.randn(n, G, D, device="cuda", generator=gen).to(tdt)
     v_new = torch.randn(n, G, D, device="cuda", generator=gen).to(tdt)
     ik_new = torch.randn(n, Di, device="cuda", generator=gen).to(idt)
-    seq_t = parity.dev(np.asarray(seqs, np.int32))
-    pos_t = parity.dev(np.asarray(positions, np.int32))
+    seq_t = harness.dev(np.asarray(seqs, np.int32))
+    pos_t = harness.dev(np.asarray(positions, np.int32))
     call = lambda: msa.cache_write(dw.p, seq_t, pos_t, k_new, v_new, ik_new, dw.block_table,
                                    dw.kv_data, dw.kv_scales, dw.ik_data, dw.ik_scales)
     # a tiny launch issued from Python would time the host call, not the
@@ -383,10 +445,10 @@ def run_prefill(args, w):
     import numpy as np
     import torch
 
-    from tests import parity
+    from decode_msa_index_amd import harness
 
     PEAK_BF16_TFLOPS = 2500.0
-    dw = parity.DeviceWorkload(w)
+    dw = harness.DeviceWorkload(w)
     torch.cuda.synchronize()
     for _ in range(max(1, args.warmup)):
         dw.decode(with_scores=False)
@@ -406,7 +468,7 @@ def run_prefill(args, w):
     idx_us = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
     # algorithmic flops of the index contraction: every row against its
     # visible keys, G groups x 128 dims, multiply + add
-    seen = np.array([parity.row_pos(w, r) + 1 for r in range(w.rows)], np.int64).clip(0)
+    seen = np.array([row_last_key(w, r) + 1 for r in range(w.rows)], np.int64).clip(0)
     flops = 2.0 * 128 * w.num_groups * float(seen.sum())
     achieved = flops / (idx_us * 1e-6) / 1e12
     log(f"[bench] prefill ms/step {ms_step:.4f}; index contraction {idx_us:.1f} us "
@@ -419,9 +481,11 @@ def run_prefill(args, w):
     if not args.no_cpu_baseline:
         import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
-        sample = list(range(0, w.rows, max(1, w.rows // 64)))[:64]
-        ws = parity.subset_rows(w, sample)
-        p = parity.oracle_problem(ws, threads)
+        sample = np.asarray(list(range(0, w.rows, max(1, w.rows // 64)))[:64], np.int64)
+        ws = dataclasses.replace(  # the same caches, the sampled query rows
+            w, rows_per_seq=len(sample), index_q=np.ascontiguousarray(w.index_q[sample]),
+            q=np.ascontiguousarray(w.q[sample]), q_pos=np.ascontiguousarray(w.q_pos[sample]))
+        p = oracle.Problem(**ws.problem_fields(), num_threads=threads)
         reps, t_c0 = 0, time.perf_counter()
         while True:
             oracle.decode(p, ws.index_q, ws.ik_data, ws.ik_scales, ws.q, ws.kv_data,

@@ -19,11 +19,11 @@ F32, BF16, FP8_E4M3, NVFP4 = 0, 1, 2, 3
 OP_INDEX, OP_TOPK, OP_ATTEND, OP_DECODE, OP_CACHE_WRITE = 0, 1, 2, 3, 4
 
 STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
-          3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
+          3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP", 5: "MSA_ERR_DEVICE_WAIT"}
 
 EXPORTS = ["msa_check_problem", "msa_workspace_bytes", "msa_index_scores", "msa_block_topk",
-           "msa_sparse_attend", "msa_decode", "msa_cache_write", "msa_status_string",
-           "msa_last_error"]
+           "msa_sparse_attend", "msa_decode", "msa_cache_write", "msa_workspace_status",
+           "msa_set_merge_spin_limit", "msa_status_string", "msa_last_error"]
 
 
 class MsaError(RuntimeError):
@@ -112,6 +112,10 @@ def lib():
                                  ctypes.c_size_t, vp]
         L.msa_cache_write.restype = ctypes.c_int
         L.msa_cache_write.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.msa_workspace_status.restype = ctypes.c_int
+        L.msa_workspace_status.argtypes = [vp, vp]
+        L.msa_set_merge_spin_limit.restype = None
+        L.msa_set_merge_spin_limit.argtypes = [i32]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_last_error.restype = ctypes.c_char_p
@@ -198,6 +202,21 @@ def cache_write(p: Problem, token_seq, token_pos, k_new, v_new, ik_new, block_ta
                                  _ptr(k_new), _ptr(v_new), _ptr(ik_new), _ptr(block_table),
                                  _ptr(kv_data), _ptr(kv_scales), _ptr(ik_data),
                                  _ptr(ik_scales), _stream(stream)))
+
+
+def workspace_status(workspace, stream=None) -> int:
+    """Waits for the stream and returns the workspace's status code (0, or
+    5 = MSA_ERR_DEVICE_WAIT after a split-K merge gave up); raises on other
+    errors."""
+    rc = lib().msa_workspace_status(_ptr(workspace), _stream(stream))
+    if rc not in (0, 5):
+        _check(rc)
+    return rc
+
+
+def set_merge_spin_limit(polls: int) -> None:
+    """Test hook: polls before a split-K merge gives up (negative: at once)."""
+    lib().msa_set_merge_spin_limit(polls)
 
 
 def new_workspace(p: Problem, op: int, device="cuda"):

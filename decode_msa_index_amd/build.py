@@ -1,4 +1,5 @@
-"""Build the HIP library (libmsa.so) in-tree with hipcc for gfx950."""
+"""Build the HIP library (libmsa.so) in-tree with hipcc for gfx950, and the
+benchmark's read-bandwidth probe (libmsa_probe.so) beside it."""
 from __future__ import annotations
 
 import os
@@ -11,6 +12,9 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.cpp", "index_scores.hip", "block_topk.hip", "sparse_attend.hip",
            "prefill_index.hip", "cache_write.hip"]
+# the benchmark's read-bandwidth probe: a library of its own, not the product
+PROBE_SOURCES = ["read_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libmsa_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,18 +33,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -1,5 +1,6 @@
 // api.cpp -- the C ABI declared in include/msa.h: host-side validation, then
-// launches on the caller's stream.  No allocation, no state across calls.
+// launches on the caller's stream.  No allocation, no state across calls
+// (apart from the merge spin limit, a test hook).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -7,10 +8,9 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/msa.h"
-#include "launch.hpp"
+#include "api_internal.hpp"
 
-namespace {
+namespace msa_api {
 
 thread_local char g_err[512] = "";
 
@@ -27,9 +27,12 @@ msa_status fail(msa_status st, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr size_t kAlign = 256;
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-enum Op { kOpIndex = 0, kOpTopk = 1, kOpAttend = 2, kOpDecode = 3, kOpCacheWrite = 4 };
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSA_OK;
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 msa::Shape shape_of(const msa_problem* p) {
   msa::Shape s;
@@ -57,31 +60,29 @@ msa::Shape shape_of(const msa_problem* p) {
   return s;
 }
 
-struct WsLayout {
-  size_t scores, attend, total;
-};
-
-// Device scratch: msa_sparse_attend needs room for the split-K partial
-// states when it splits a (row, group) over several workgroups; msa_decode
-// needs the pooled scores before that.
+// Device scratch.  msa_sparse_attend needs room for the split-K partial
+// states when it splits a (row, group) over several workgroups, behind a
+// status header; msa_decode needs the header and the partials, then the
+// pooled scores.
 WsLayout ws_layout(const msa_problem* p, int op) {
   WsLayout w{};
   if (op != kOpAttend && op != kOpDecode) return w;
   const msa::Shape s = shape_of(p);
-  size_t off = 0;
-  if (op == kOpDecode) {
-    w.scores = off;
-    off += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
-  }
-  w.attend = off;
-  off += round_up(msa::attend_workspace_bytes(s, msa::attend_config(s)));
-  w.total = off;
+  const size_t attend = round_up(msa::attend_workspace_bytes(s, msa::attend_config(s)));
+  if (op == kOpAttend && attend == 0) return w;
+  w.status = 0;
+  w.attend = msa::kStatusBytes;
+  w.scores = w.attend + attend;
+  w.total = w.scores;
+  if (op == kOpDecode) w.total += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
   return w;
 }
 
 bool pos_finite(float x) { return std::isfinite(x) && x > 0.0f; }
 
-}  // namespace
+}  // namespace msa_api
+
+using namespace msa_api;
 
 extern "C" {
 
@@ -207,10 +208,6 @@ static msa_status check_attend_args(const msa_problem* p, const void* q, const v
   return MSA_OK;
 }
 
-static msa_status hip_status(hipError_t e, const char* what) {
-  if (e == hipSuccess) return MSA_OK;
-  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
 
 msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* ik_data,
                             const void* ik_scales, const int32_t* block_table,
@@ -270,41 +267,29 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
   const msa::Shape s = shape_of(p);
   return hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table,
                                               seq_lens, q_pos, topk_idx, out, lse,
-                                              static_cast<char*>(workspace) + w.attend,
+                                              static_cast<char*>(workspace) + w.status,
                                               (hipStream_t)stream),
                     "sparse attend launch");
 }
 
-msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
-                      const void* ik_scales, const void* q, const void* kv_data,
-                      const void* kv_scales, const int32_t* block_table,
-                      const int32_t* seq_lens, const int32_t* q_pos, float* block_scores,
-                      int32_t* topk_idx, void* out, float* lse, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  msa_status st = msa_check_problem(p, kOpDecode);
-  if (st != MSA_OK) return st;
-  st = check_index_args(p, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos);
-  if (st != MSA_OK) return st;
-  st = check_attend_args(p, q, kv_data, kv_scales, block_table, seq_lens, q_pos, out, lse);
-  if (st != MSA_OK) return st;
-  OPTIONAL(block_scores, 4);
-  REQUIRE(topk_idx, 4);
-  const WsLayout w = ws_layout(p, kOpDecode);
-  if (w.total) {
-    REQUIRE(workspace, kAlign);
-    if (workspace_bytes < w.total)
-      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
-                  workspace_bytes, w.total);
-  } else {
-    OPTIONAL(workspace, kAlign);
-  }
-  if (p->num_seqs == 0) return MSA_OK;
+}  // extern "C"
+
+namespace msa_api {
+
+// The decode step on a workspace the caller (or the library's static scratch)
+// provides; arguments already validated.
+msa_status decode_impl(const msa_problem* p, const void* index_q, const void* ik_data,
+                              const void* ik_scales, const void* q, const void* kv_data,
+                              const void* kv_scales, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* q_pos, float* block_scores,
+                              int32_t* topk_idx, void* out, float* lse, char* ws,
+                              const WsLayout& w, hipStream_t hs) {
   const msa::Shape s = shape_of(p);
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t hs = (hipStream_t)stream;
   void* aws = ws + w.attend;
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + w.status);
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
   float* ws_scores = block_scores ? nullptr : scores;  // cleared again after use
+  msa_status st;
   if (msa::select_fusable(s)) {
     // two launches: the index scan, then selection + attention in one kernel
     st = hip_status(msa::launch_index_scores(s, index_q, ik_data, ik_scales, block_table,
@@ -312,7 +297,7 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
                     "index scores launch");
     if (st != MSA_OK) return st;
     return hip_status(msa::launch_select_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
-                                                q_pos, scores, topk_idx, out, lse, aws,
+                                                q_pos, scores, topk_idx, out, lse, aws, status,
                                                 ws_scores, hs),
                       "select + attend launch");
   }
@@ -325,12 +310,75 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
                   "block top-k launch");
   if (st != MSA_OK) return st;
   st = hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
-                                            q_pos, topk_idx, out, lse, aws, hs),
+                                            q_pos, topk_idx, out, lse, ws + w.status, hs),
                   "sparse attend launch");
   if (st != MSA_OK || block_scores) return st;
-  return hip_status(msa::launch_zero_fill(ws + w.scores, w.attend - w.scores, hs),
+  return hip_status(msa::launch_zero_fill(ws + w.scores, w.total - w.scores, hs),
                     "workspace clear launch");
 }
+
+msa_status check_decode_args(const msa_problem* p, const void* index_q,
+                                    const void* ik_data, const void* ik_scales, const void* q,
+                                    const void* kv_data, const void* kv_scales,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* q_pos, const float* block_scores,
+                                    const int32_t* topk_idx, const void* out, const float* lse) {
+  msa_status st = msa_check_problem(p, kOpDecode);
+  if (st != MSA_OK) return st;
+  st = check_index_args(p, index_q, ik_data, ik_scales, block_table, seq_lens, q_pos);
+  if (st != MSA_OK) return st;
+  st = check_attend_args(p, q, kv_data, kv_scales, block_table, seq_lens, q_pos, out, lse);
+  if (st != MSA_OK) return st;
+  OPTIONAL(block_scores, 4);
+  REQUIRE(topk_idx, 4);
+  return MSA_OK;
+}
+
+}  // namespace msa_api
+
+extern "C" {
+
+msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
+                      const void* ik_scales, const void* q, const void* kv_data,
+                      const void* kv_scales, const int32_t* block_table,
+                      const int32_t* seq_lens, const int32_t* q_pos, float* block_scores,
+                      int32_t* topk_idx, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  msa_status st = check_decode_args(p, index_q, ik_data, ik_scales, q, kv_data, kv_scales,
+                                    block_table, seq_lens, q_pos, block_scores, topk_idx, out,
+                                    lse);
+  if (st != MSA_OK) return st;
+  const WsLayout w = ws_layout(p, kOpDecode);
+  REQUIRE(workspace, kAlign);
+  if (workspace_bytes < w.total)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                workspace_bytes, w.total);
+  if (p->num_seqs == 0) return MSA_OK;
+  return decode_impl(p, index_q, ik_data, ik_scales, q, kv_data, kv_scales, block_table,
+                     seq_lens, q_pos, block_scores, topk_idx, out, lse,
+                     static_cast<char*>(workspace), w, (hipStream_t)stream);
+}
+
+msa_status msa_workspace_status(const void* workspace, void* stream) {
+  clear_error();
+  const char* base = static_cast<const char*>(workspace);
+  if (!base) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(base, kAlign)) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  uint32_t word = 0;
+  hipStream_t hs = (hipStream_t)stream;
+  msa_status st = hip_status(hipMemcpyAsync(&word, base, sizeof word, hipMemcpyDeviceToHost, hs),
+                             "status read");
+  if (st != MSA_OK) return st;
+  st = hip_status(hipStreamSynchronize(hs), "status read");
+  if (st != MSA_OK) return st;
+  if (word != 0)
+    return fail(MSA_ERR_DEVICE_WAIT,
+                "a split-K merge gave up waiting for partial states; outputs of that call are "
+                "NaN and the workspace must be zero-filled again before reuse");
+  return MSA_OK;
+}
+
+void msa_set_merge_spin_limit(int32_t polls) { msa::set_merge_spin_limit(polls); }
 
 msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32_t* token_seq,
                            const int32_t* token_pos, const void* k_new, const void* v_new,
@@ -367,6 +415,7 @@ const char* msa_status_string(msa_status s) {
     case MSA_ERR_UNSUPPORTED: return "unsupported problem";
     case MSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MSA_ERR_HIP: return "HIP error";
+    case MSA_ERR_DEVICE_WAIT: return "a device-side wait gave up";
     default: return "unknown status";
   }
 }

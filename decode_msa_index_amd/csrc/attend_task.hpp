@@ -127,9 +127,11 @@ __device__ __forceinline__ float rescale(float x, float m) {
 // rows (heads) 4*(l/16)+i, columns (dims) 16*dt + l%16.
 // ---------------------------------------------------------------------------
 struct Partials {
-  float* o;   // [rows*G][S][8 dim tiles][64 lanes][4]: unnormalised outputs, lane-major
-  float* ml;  // [rows*G][S][16 heads][2]: running max (log2 domain) and denominator
+  float* o;          // [rows*G][S][8 dim tiles][64 lanes][4]: unnormalised outputs, lane-major
+  float* ml;         // [rows*G][S][16 heads][2]: running max (log2 domain) and denominator
+  uint32_t* status;  // the workspace's status word: non-zero once a merge has given up
   int S;
+  int spin_limit;    // polls of one batch before a merger gives up (< 0: at once)
 };
 
 // Host side: the argument blocks of an attention launch.
@@ -165,12 +167,15 @@ inline AttendArgs make_attend_args(const Shape& s, const int32_t* block_table,
 // Split-K scratch inside the attention workspace (attend_workspace_bytes):
 // [ml: units*S*16*2][o: units*S*16*128] floats.  Zero before a launch, and
 // zero again after it (the merging workgroup clears what it read).
-inline Partials make_partials(const Shape& s, const AttendConfig& c, void* workspace) {
+inline Partials make_partials(const Shape& s, const AttendConfig& c, void* workspace,
+                              uint32_t* status, int spin_limit) {
   const size_t units = (size_t)s.rows * s.G;
   Partials part;
   part.S = c.splits;
   part.ml = static_cast<float*>(workspace);
   part.o = part.ml + units * c.splits * kHeadsPad * 2;
+  part.status = status;
+  part.spin_limit = spin_limit;
   return part;
 }
 
@@ -215,7 +220,8 @@ __device__ __forceinline__ bool all_landed(f32x4 v) {
   return w.x != 0u && w.y != 0u && w.z != 0u && w.w != 0u;
 }
 // Polls of one batch of partials before the merger gives up (each poll is a
-// device-memory round trip, about a microsecond).
+// device-memory round trip, about a microsecond): the default of
+// Partials::spin_limit.
 constexpr int kSpinLimit = 1 << 20;
 
 // Returns the unit's row of the scores to 0 once every reader is done with
@@ -246,6 +252,10 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
   const int per_wg = (count + part.S - 1) / part.S;
   const int e0 = split * per_wg, e1 = min(count, e0 + per_wg);
   const int n = lane & 15, qd = lane >> 4;
+  // the merging split reads the workspace's status word early: a workspace
+  // a merge gave up on holds partial words that may still land late, so its
+  // partials are not trusted again until the caller clears it
+  const uint32_t poisoned = (part.S > 1 && split == part.S - 1) ? *part.status : 0u;
 
   // Q^T operand: head n of the group, dims qd*32 + 8c + e (zero past hpg);
   // loaded first so that its latency overlaps the selection
@@ -526,12 +536,12 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
     return;
   }
-  bool timed_out = false;
+  bool timed_out = poisoned != 0u || part.spin_limit < 0;
   if (part.S > 1) {
     // merge the other splits' partials, a batch at a time, into (co, cm, cl)
     constexpr int CH = 128 / (4 * DTW + 8);  // partials whose words a batch holds
     const size_t ubase = (size_t)u * part.S;
-    for (int sp0 = 0; sp0 < part.S - 1; sp0 += CH) {
+    for (int sp0 = 0; sp0 < part.S - 1 && !timed_out; sp0 += CH) {
       f32x4 po[CH][DTW], pm[CH][2];
       for (int tries = 0;; ++tries) {
         // the loads below must be issued again on every pass: without this
@@ -557,7 +567,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
           }
         }
         if (__ballot(!ok) == 0) break;
-        if (tries >= kSpinLimit) {  // never expected: the output becomes NaN
+        if (tries >= part.spin_limit) {  // never expected: the output becomes NaN
           timed_out = true;
           break;
         }
@@ -588,10 +598,15 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
     // return the partials read to zero: the workspace is left as found.  The
     // max / denominator words are shared by all waves: none may be cleared
-    // while another wave is still polling them.
+    // while another wave is still polling them.  After a timeout nothing is
+    // cleared (a late partial could land after the clearing); the status
+    // word marks the workspace instead, for the host to read and to clear.
     __syncthreads();
+    if (timed_out) {
+      if (threadIdx.x == 0) *part.status = 1u;
+    }
 #pragma unroll 1
-    for (int sp = 0; sp < part.S - 1; ++sp) {
+    for (int sp = 0; sp < part.S - 1 && !timed_out; ++sp) {
       f32x4* zo = reinterpret_cast<f32x4*>(part.o + (ubase + sp) * (kHeadsPad * kDim));
 #pragma unroll
       for (int d = 0; d < DTW; ++d) zo[(dt0 + d) * 64 + lane] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -602,7 +617,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
       }
     }
     // every split has finished its selection: the scores row is free
-    if (SELECT && a.clear) clear_row(a, u, NW);
+    if (SELECT && a.clear && !timed_out) clear_row(a, u, NW);
   }
 
   // ---- normalise and store (heads 4qd+i, dims 16 (dt0 + d) + n) ----

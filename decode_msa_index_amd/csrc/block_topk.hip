@@ -46,16 +46,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + x - v;
 }
 
-// Candidate keys live in LDS (kLds) when the row's block count fits, else
-// they are re-read from global memory in every pass.
-constexpr int kLdsKeys = 16384;
-
-template <bool kLds>
+// The row's keys are re-read from global memory in every radix pass (rows
+// this long do not fit in LDS).
 __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
     int K, int init, int local) {
-  extern __shared__ uint32_t keys[];  // kLds: one order key per candidate block
   __shared__ uint32_t hist[4][256];
   __shared__ uint32_t scan_sm[4];
   __shared__ uint32_t pick[2];
@@ -81,26 +77,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   if (need == 0) return;
   const int ncand = c1 - c0;  // free blocks c0 .. c1-1 compete for `need` places
   const float* sc = s + c0;
-  auto key_at = [&](int jj) -> uint32_t {
-    if constexpr (kLds) return keys[jj];
-    else return order_key(sc[jj]);
-  };
-  if constexpr (kLds) {
-    // read the row once, 4 loads in flight per thread per round
-    for (int base = 0; base < ncand; base += 4 * 256) {
-      float v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jj = base + k * 256 + tid;
-        v[k] = jj < ncand ? sc[jj] : 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jj = base + k * 256 + tid;
-        if (jj < ncand) keys[jj] = order_key(v[k]);
-      }
-    }
-  }
+  auto key_at = [&](int jj) -> uint32_t { return order_key(sc[jj]); };
   uint32_t prefix = 0, pmask = 0, rem = (uint32_t)need;
   for (int pass = 3; pass >= 0; --pass) {
     const int shift = pass * 8;
@@ -181,7 +158,7 @@ hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t*
                        sizeof(uint32_t) * (256 + s.MB), st, scores, seq_lens, q_pos, topk, s.R,
                        s.G, s.MB, s.K, s.init, s.local);
   } else {
-    hipLaunchKernelGGL(block_topk_kernel<false>, dim3(s.rows * s.G), dim3(256), 0, st, scores,
+    hipLaunchKernelGGL(block_topk_kernel, dim3(s.rows * s.G), dim3(256), 0, st, scores,
                        seq_lens, q_pos, topk, s.R, s.G, s.MB, s.K, s.init, s.local);
   }
   return hipGetLastError();

@@ -48,6 +48,18 @@ struct AttendConfig {
 AttendConfig attend_config(const Shape& s);
 size_t attend_workspace_bytes(const Shape& s, const AttendConfig& c);
 
+// Workspace status header: 256 bytes at the front of every workspace that
+// holds split-K partials; word 0 becomes non-zero when a merge gives up
+// waiting (its partials are then no longer trusted until it is cleared).
+constexpr size_t kStatusBytes = 256;
+
+// Polls of one batch of split-K partials before a merger gives up (< 0: the
+// merger gives up at once, a test of the failure path).
+void set_merge_spin_limit(int polls);
+int merge_spin_limit();
+
+// workspace: status header (kStatusBytes) followed by the split-K partials;
+// both are cleared before the launch.
 hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_data,
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
@@ -63,7 +75,8 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, float* clear_scores, hipStream_t st);
+                                void* workspace, uint32_t* status, float* clear_scores,
+                                hipStream_t st);
 // Quantises new tokens' K, V and index keys into their cache slots
 // (cache_write.hip).
 hipError_t launch_cache_write(const Shape& s, int num_tokens, const int32_t* token_seq,
@@ -73,10 +86,6 @@ hipError_t launch_cache_write(const Shape& s, int num_tokens, const int32_t* tok
 // Clears bytes (a multiple of 4) with a fill kernel.
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 
-hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const void* q,
-                                    const void* kv_data, const void* kv_scales,
-                                    const int32_t* block_table, const int32_t* seq_lens,
-                                    const int32_t* q_pos, const int32_t* topk, void* out,
-                                    float* lse, void* workspace, hipStream_t st);
+
 
 }  // namespace msa

@@ -3,8 +3,10 @@
 // Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
 // primer"): keep the top-k blocks by pooled index score, the most recent
 // block always among them.  The recent block counts inside the k.  The
-// indexer's init_blocks / local_blocks settings (same blog, the sparse
-// attention layer's constructor) add more always-kept blocks: read here as
+// indexer's init_blocks / local_blocks settings (vLLM API reference of
+// vllm.models.minimax_m3.nvidia.model, the MiniMaxM3SparseAttention
+// constructor, which fills them from sparse_init_block / sparse_local_block)
+// add more always-kept blocks: read here as
 // the first `init` blocks and the last `local` (>= 1, the recent one
 // included) blocks of 0..rb, all inside the k.  When rb + 1 > k the free
 // candidates are then the contiguous blocks c0 = init .. c1 - 1 with

@@ -15,6 +15,7 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -213,19 +214,28 @@ static long resident_capacity(const void* kernel, int threads, size_t lds) {
   return (long)per_cu * cus;
 }
 
+static std::atomic<int> g_spin_limit{kSpinLimit};
+void set_merge_spin_limit(int polls) { g_spin_limit.store(polls); }
+int merge_spin_limit() { return g_spin_limit.load(); }
+
+// workspace: the split-K partials; status: the workspace's status word.
+// zero_partials: the status header and the partials after it are cleared
+// first (msa_sparse_attend's layout: header, then partials).
 template <int KVT, int NWV, bool SELECT>
 static hipError_t launch_kernel(const Shape& s, int splits, const AttendArgs& a, const void* q,
                                 const void* kv_data, const void* kv_scales, void* workspace,
-                                bool zero_partials, hipStream_t st) {
+                                uint32_t* status, bool zero_partials, hipStream_t st) {
   const int units = s.rows * s.G;
   const void* fn = reinterpret_cast<const void*>(&attend_mfma_kernel<KVT, NWV, SELECT>);
   const size_t lds = SELECT ? select_dyn_lds(s) : 0;
   // the merging workgroup of a split unit waits for the unit's other
   // workgroups: split only when the whole grid can be resident at once
   if (splits > 1 && (long)units * splits > resident_capacity(fn, 64 * NWV, lds)) splits = 1;
-  const Partials part = make_partials(s, AttendConfig{NWV, splits}, workspace);
+  const Partials part =
+      make_partials(s, AttendConfig{NWV, splits}, workspace, status, merge_spin_limit());
   if (splits > 1 && zero_partials) {
-    const hipError_t e = launch_zero_fill(part.ml, attend_workspace_bytes(s, AttendConfig{NWV, splits}), st);
+    const hipError_t e = launch_zero_fill(
+        status, kStatusBytes + attend_workspace_bytes(s, AttendConfig{NWV, splits}), st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((attend_mfma_kernel<KVT, NWV, SELECT>), dim3(units * splits), dim3(64 * NWV),
@@ -240,11 +250,12 @@ static hipError_t launch_kernel(const Shape& s, int splits, const AttendArgs& a,
 template <bool SELECT>
 static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const AttendArgs& a,
                               const void* q, const void* kv_data, const void* kv_scales,
-                              void* workspace, bool zero_partials, hipStream_t st) {
+                              void* workspace, uint32_t* status, bool zero_partials,
+                              hipStream_t st) {
   if (c.splits < 1 || c.splits > kMaxSplits) return hipErrorInvalidValue;
 #define MSA_ATTEND_LAUNCH(KVT, NWV) \
   return launch_kernel<KVT, NWV, SELECT>(s, c.splits, a, q, kv_data, kv_scales, workspace, \
-                                         zero_partials, st)
+                                         status, zero_partials, st)
   if (s.kv_dtype == kFP8) {
     switch (c.nw) {
       case 1: MSA_ATTEND_LAUNCH(kFP8, 1);
@@ -263,38 +274,33 @@ static hipError_t launch_mfma(const Shape& s, const AttendConfig& c, const Atten
 #undef MSA_ATTEND_LAUNCH
 }
 
-hipError_t launch_sparse_attend_cfg(const Shape& s, const AttendConfig& c, const void* q,
-                                    const void* kv_data, const void* kv_scales,
-                                    const int32_t* block_table, const int32_t* seq_lens,
-                                    const int32_t* q_pos, const int32_t* topk, void* out,
-                                    float* lse, void* workspace, hipStream_t st) {
+hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_data,
+                                const void* kv_scales, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* q_pos,
+                                const int32_t* topk, void* out, float* lse, void* workspace,
+                                hipStream_t st) {
   const AttendArgs a = make_attend_args(s, block_table, seq_lens, q_pos, topk, nullptr, nullptr, out, lse);
   if (s.kv_dtype == kF32) {
     hipLaunchKernelGGL(attend_f32_kernel, dim3(s.rows * s.G), dim3(64), 0, st, q,
                        (const float*)kv_data, (int)(s.q_dtype == kBF16), a);
     return hipGetLastError();
   }
-  return launch_mfma<false>(s, c, a, q, kv_data, kv_scales, workspace, true, st);
-}
-
-hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_data,
-                                const void* kv_scales, const int32_t* block_table,
-                                const int32_t* seq_lens, const int32_t* q_pos,
-                                const int32_t* topk, void* out, float* lse, void* workspace,
-                                hipStream_t st) {
-  return launch_sparse_attend_cfg(s, attend_config(s), q, kv_data, kv_scales, block_table,
-                                  seq_lens, q_pos, topk, out, lse, workspace, st);
+  uint32_t* status = static_cast<uint32_t*>(workspace);
+  return launch_mfma<false>(s, attend_config(s), a, q, kv_data, kv_scales,
+                            static_cast<char*>(workspace) + kStatusBytes, status, true, st);
 }
 
 hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_data,
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, float* clear_scores, hipStream_t st) {
+                                void* workspace, uint32_t* status, float* clear_scores,
+                                hipStream_t st) {
   AttendArgs a =
       make_attend_args(s, block_table, seq_lens, q_pos, nullptr, scores, topk_out, out, lse);
   a.clear = reinterpret_cast<uint32_t*>(clear_scores);
-  return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace, false, st);
+  return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace, status,
+                           false, st);
 }
 
 }  // namespace msa

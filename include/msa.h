@@ -23,7 +23,8 @@
  * Conventions
  * ---------------------------------------------------------------------------
  * All data pointers are DEVICE pointers owned by the caller; the library
- * allocates and frees nothing and keeps no state between calls.  Every call
+ * allocates and frees nothing and keeps no state between calls (apart from
+ * the test hook msa_set_merge_spin_limit).  Every call
  * validates its arguments on the host, synchronously, before anything is
  * launched, then enqueues its kernels on `stream` (a hipStream_t; NULL is the
  * default stream) and returns without waiting.  Device-side data (block-table
@@ -87,7 +88,9 @@ typedef enum {
   MSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, inconsistent sizes */
   MSA_ERR_UNSUPPORTED = 2,      /* a shape or dtype combination not built */
   MSA_ERR_WORKSPACE_TOO_SMALL = 3,
-  MSA_ERR_HIP = 4               /* a HIP launch or runtime call failed */
+  MSA_ERR_HIP = 4,              /* a HIP launch or runtime call failed */
+  MSA_ERR_DEVICE_WAIT = 5       /* msa_workspace_status: a split-K merge gave up
+                                   waiting (see msa_workspace_bytes) */
 } msa_status;
 
 typedef enum {
@@ -153,16 +156,26 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  *     group) is split over several workgroups (0 when it is not);
  *   - msa_decode: B*R*G*MB words for the pooled scores, then that;
  *   - the other calls: 0.
- * Every region is rounded up to 256 bytes.  The workspace is caller-owned
- * device memory, 256-byte aligned.  msa_decode requires it to be zero-filled
- * before its first use (e.g. hipMemset once after allocation): the
- * workgroups of its attention kernel hand partial states to each other
- * through it, and a word still zero means "not yet written".  Every
- * msa_decode and msa_sparse_attend call leaves the workspace zero-filled
- * again, so one zero fill serves any sequence of calls and problem shapes;
- * msa_sparse_attend itself needs no initialisation (it clears what it uses).
- * Calls that share a workspace must not overlap.  A call whose size is 0
- * accepts a NULL workspace.
+ * Every region is rounded up to 256 bytes, and a workspace that holds
+ * partial states starts with a 256-byte status header.  The workspace is
+ * caller-owned device memory, 256-byte aligned.  msa_decode requires it to
+ * be zero-filled before its first use (e.g. hipMemset once after
+ * allocation): the workgroups of its attention kernel hand partial states to
+ * each other through it, and a word still zero means "not yet written".
+ * Every msa_decode and msa_sparse_attend call leaves the workspace
+ * zero-filled again, so one zero fill serves any sequence of calls and
+ * problem shapes; msa_sparse_attend itself needs no initialisation (it
+ * clears what it uses).  Calls that share a workspace must not overlap.  A
+ * call whose size is 0 accepts a NULL workspace.
+ *
+ * Failure mode: the workgroup that merges a (row, group)'s partial states
+ * waits for them with a bounded poll (about a second).  Should it ever give
+ * up, that (row, group)'s out and lse become NaN, the call has already
+ * returned MSA_OK, and the workspace is marked in its status header instead
+ * of being cleared (a partial state could still land after a clearing).
+ * msa_workspace_status reads the mark; later msa_decode calls on a marked
+ * workspace give NaN for every split (row, group) until the caller
+ * zero-fills it again.
  */
 msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
 
@@ -186,9 +199,10 @@ msa_status msa_index_scores(const msa_problem* p, const void* index_q, const voi
  * always kept).  For row r with last visible block rb = pos / BS: if
  * rb + 1 <= K all blocks 0..rb are kept.  Otherwise the forced blocks are
  * kept -- 0 .. init_blocks-1 and the last L = max(local_blocks, 1) blocks
- * rb-L+1 .. rb (the indexer's sparse_init_block / sparse_local_block
- * settings, named in the blog's sparse attention layer; read as blocks
- * always kept inside the k) -- plus the K - init_blocks - L best of the
+ * rb-L+1 .. rb (the indexer's init_blocks / local_blocks, which the API
+ * reference of MiniMaxM3SparseAttention's constructor fills from
+ * sparse_init_block / sparse_local_block; read as blocks always kept inside
+ * the k) -- plus the K - init_blocks - L best of the
  * free blocks init_blocks .. rb-L by (block_scores descending, block index
  * ascending).  With init_blocks = local_blocks = 0 that is rb plus the K-1
  * best of 0..rb-1.  Output ascending, -1 padded.  Deterministic: ties go to
@@ -265,6 +279,24 @@ msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32
                            const int32_t* token_pos, const void* k_new, const void* v_new,
                            const void* ik_new, const int32_t* block_table, void* kv_data,
                            void* kv_scales, void* ik_data, void* ik_scales, void* stream);
+
+/*
+ * Status of a workspace after the calls enqueued on `stream` so far: waits
+ * for the stream, reads the status header of `workspace` (a decode or attend
+ * workspace of at least 256 bytes) and returns MSA_ERR_DEVICE_WAIT if a
+ * split-K merge gave up waiting on it (see msa_workspace_bytes), MSA_OK
+ * otherwise.  Synchronous: not for use inside a captured graph.
+ */
+msa_status msa_workspace_status(const void* workspace, void* stream);
+
+/*
+ * Test hook for the failure path above: polls of one batch of partial states
+ * before a merging workgroup gives up, for launches enqueued after the call
+ * (default 2^20; a negative value makes every merge give up at once, so that
+ * the NaN outputs and the status mark can be checked while every kernel
+ * still runs to its normal end).  Process-wide; not for production use.
+ */
+void msa_set_merge_spin_limit(int32_t polls);
 
 /* Static description of a status code. */
 const char* msa_status_string(msa_status s);

@@ -346,8 +346,9 @@ typedef struct {
  * most recent block always kept, at most 2,048 keys).  The recent block is
  * the one holding the row's own position; it counts inside the k.
  *
- * The indexer also takes sparse_init_block and sparse_local_block (vLLM
- * blog, "MiniMaxM3SparseAttention" constructor: init_blocks and
+ * The indexer also takes sparse_init_block and sparse_local_block (vLLM API
+ * reference of vllm.models.minimax_m3.nvidia.model, the
+ * MiniMaxM3SparseAttention constructor: passed on as init_blocks and
  * local_blocks, both 0 unless configured; nothing more is said of them).
  * Read here as blocks that are always kept besides the recent one, inside
  * the k like it: the first init_blocks blocks 0 .. init_blocks-1 and the

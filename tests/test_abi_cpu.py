@@ -109,20 +109,24 @@ def test_workspace_sizes():
     d = msa.workspace_bytes(p, msa.OP_DECODE)
     scores = 8 * 4 * 2049 * 4
     assert d % 256 == 0 and a % 256 == 0
-    # decode: the pooled scores rounded up to 256, then the attention's part
+    # decode: the attention's part (status header + partials), then the
+    # pooled scores rounded up to 256
     assert d - a == -(-scores // 256) * 256
-    # split partials: 16 heads x (128 outputs + max + denominator) per split
+    # a 256-byte status header, then the split partials: 16 heads x (128
+    # outputs + max + denominator) per split
     units = 8 * 4
-    S = a // (units * 16 * 130 * 4)
-    assert S >= 2 and a == -(-(units * S * 16 * 130 * 4) // 256) * 256
+    S = (a - 256) // (units * 16 * 130 * 4)
+    assert S >= 2 and a == 256 + -(-(units * S * 16 * 130 * 4) // 256) * 256
     big = good(num_seqs=512, max_blocks_per_seq=16)
     assert msa.workspace_bytes(big, msa.OP_ATTEND) == 0  # enough (row, group)s: no split
+    assert msa.workspace_bytes(big, msa.OP_DECODE) == 256 + 512 * 4 * 16 * 4
 
 
 def test_status_strings():
     L = msa.lib()
     assert L.msa_status_string(0) == b"ok"
     assert L.msa_status_string(3) == b"workspace too small"
+    assert L.msa_status_string(5) == b"a device-side wait gave up"
 
 
 def test_cache_write_rejects_bad_arguments_before_launch():

@@ -54,9 +54,10 @@ def _run_and_check(w, fused, name):
     o = dw.out.float().cpu().numpy()
     serr = parity.check_scores(w, s, s_ref)
     same = parity.check_selection(w, s_ref, k_ref, k)
-    aerr = parity.check_attention(w, o, o_ref, mask=same)
+    aerr = parity.check_decode_attention(w, o, o_ref, same, k)
+    parity.record(name, same, serr, aerr)
     say(f"[parity] {name}: score err {serr:.3f} of bound, {int(same.sum())}/{same.size} "
-        f"selections identical, attention max-abs {aerr:.2e}")
+        f"selections identical, attention max-abs {aerr:.2e} (every unit)")
     return dw, same
 
 
@@ -592,9 +593,109 @@ def test_cache_write_then_decode_sees_the_new_tokens():
     dw.decode()
     torch.cuda.synchronize()
     s_ref, k_ref, o_ref, _ = _oracle_all(w2)
-    parity.check_scores(w2, dw.scores.cpu().numpy(), s_ref)
-    same = parity.check_selection(w2, s_ref, k_ref, dw.topk.cpu().numpy())
-    parity.check_attention(w2, dw.out.float().cpu().numpy(), o_ref, mask=same)
+    serr = parity.check_scores(w2, dw.scores.cpu().numpy(), s_ref)
+    k = dw.topk.cpu().numpy()
+    same = parity.check_selection(w2, s_ref, k_ref, k)
+    aerr = parity.check_decode_attention(w2, dw.out.float().cpu().numpy(), o_ref, same, k)
+    parity.record("cache-write-fp8-then-decode", same, serr, aerr)
+
+
+def test_nvfp4_cache_write_then_decode_sees_the_new_tokens():
+    """The same end-to-end step with NVFP4 K/V and index keys: the write
+    (data and scales of every plane, V's shared nibble bytes) and a decode
+    over the written caches agree with the oracle's write and decode."""
+    w, seq, pos, new = _cache_write_inputs(synth.NVFP4, synth.NVFP4, synth.BF16, synth.BF16,
+                                           seed=78, spikes=False)
+    keep = (seq >= 0) & (seq < w.num_seqs) & (pos < w.max_blocks * 128)
+    seq, pos = seq[keep], pos[keep]
+    new = {k: np.ascontiguousarray(v[keep]) for k, v in new.items()}
+    ref = {k: getattr(w, k).copy() for k in ("kv_data", "kv_scales", "ik_data", "ik_scales")}
+    oracle.cache_write(parity.oracle_problem(w), seq, pos, new["k"], new["v"], new["ik"],
+                       w.block_table, ref["kv_data"], ref["kv_scales"], ref["ik_data"],
+                       ref["ik_scales"])
+    dw = parity.DeviceWorkload(w)
+    msa.cache_write(dw.p, parity.dev(seq), parity.dev(pos), parity.dev(new["k"]),
+                    parity.dev(new["v"]), parity.dev(new["ik"]), dw.block_table, dw.kv_data,
+                    dw.kv_scales, dw.ik_data, dw.ik_scales)
+    torch.cuda.synchronize()
+    for name in ref:
+        got = getattr(dw, name).cpu().numpy().view(np.uint8)
+        assert np.array_equal(got, ref[name].view(np.uint8)), f"{name} differs after the write"
+    w2 = dataclasses.replace(w, **ref)
+    say("[parity] NVFP4 decode after the cache write")
+    dw.decode()
+    torch.cuda.synchronize()
+    s_ref, k_ref, o_ref, _ = _oracle_all(w2)
+    serr = parity.check_scores(w2, dw.scores.cpu().numpy(), s_ref)
+    k = dw.topk.cpu().numpy()
+    same = parity.check_selection(w2, s_ref, k_ref, k)
+    aerr = parity.check_decode_attention(w2, dw.out.float().cpu().numpy(), o_ref, same, k)
+    parity.record("cache-write-nvfp4-then-decode", same, serr, aerr)
+
+
+@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
+@pytest.mark.parametrize("fused", [False, True])
+def test_out_of_pool_entries_and_rows_past_the_table(kv, fused):
+    """The header's two device-data rules against the oracle: table entries
+    outside [0, P) (-1, P, -7; one of them a recent block, one sequence whose
+    whole table is invalid) are empty blocks, and sequences longer than
+    max_blocks * 128 (one with a query position past that too) see only the
+    keys their table reaches."""
+    lens = [5000, 2049, 64 * 128, 3000, 700]
+    base = synth.make("pool", seed=191 + kv, seq_lens=lens, q_dtype=synth.BF16, kv_dtype=kv,
+                      plant_per_seq=2)
+    bt = base.block_table.copy()
+    P = base.num_phys_blocks
+    bt[0, 3], bt[0, 20] = -1, P
+    bt[1, 16] = -7  # sequence 1's recent block
+    bt[4, :] = -1   # nothing valid at all
+    # sequences 2 and 3 claim more tokens than the table reaches (40 blocks)
+    MB = 40
+    bt = np.ascontiguousarray(bt[:, :MB])
+    w = dataclasses.replace(base, max_blocks=MB, block_table=bt,
+                            seq_lens=np.array([5000, 2049, 100000, 40 * 128 + 77, 700], np.int32),
+                            rows_per_seq=1, q_pos=np.array([4999, 2048, 90000, 6000, 699], np.int32))
+    dw, same = _run_and_check(w, fused, f"pool-{synth.DTYPE_NAMES[kv]}-{'fused' if fused else 'chain'}")
+    o = dw.out.float().cpu().numpy()
+    assert np.all(o[4] == 0.0) and np.all(dw.lse.cpu().numpy()[4] == -np.inf)
+    assert np.all(dw.scores.cpu().numpy()[4] == -np.inf)
+
+
+def test_merge_timeout_is_reported():
+    """The split-K merge's failure path, forced from the host: with the
+    merge told to give up at once (every kernel still runs to its end), the
+    split units' outputs are NaN, the workspace is marked and
+    msa_workspace_status reports it; later decodes on the marked workspace
+    stay NaN; after the caller clears it, decodes are exact again.
+    msa_sparse_attend clears its own workspace at every call."""
+    w = synth.make("timeout", seed=93, seq_lens=[20000, 9000], q_dtype=synth.BF16,
+                   kv_dtype=synth.FP8, plant_per_seq=2)
+    dw = parity.DeviceWorkload(w)
+    dw.decode(with_scores=False)
+    torch.cuda.synchronize()
+    ref = dw.out.float().clone()
+    assert msa.workspace_status(dw.ws_decode) == 0
+    say("[parity] forced merge timeout")
+    try:
+        msa.set_merge_spin_limit(-1)
+        dw.decode(with_scores=False)
+        assert msa.workspace_status(dw.ws_decode) == 5
+        assert torch.isnan(dw.out.float()).all()
+        dw.sparse_attend()
+        assert msa.workspace_status(dw.ws_attend) == 5
+    finally:
+        msa.set_merge_spin_limit(1 << 20)
+    dw.decode(with_scores=False)  # the marked workspace stays marked
+    assert msa.workspace_status(dw.ws_decode) == 5
+    assert torch.isnan(dw.out.float()).all()
+    dw.ws_decode.zero_()
+    dw.decode(with_scores=False)
+    assert msa.workspace_status(dw.ws_decode) == 0
+    assert torch.equal(dw.out.float(), ref)
+    assert int(torch.count_nonzero(dw.ws_decode)) == 0
+    dw.sparse_attend()  # clears its workspace first
+    assert msa.workspace_status(dw.ws_attend) == 0
+    assert torch.isfinite(dw.out.float()).all()
 
 
 def test_one_workspace_across_shapes():
@@ -735,7 +836,8 @@ def test_prefill_64k_sampled_rows():
     o = dw.out.float().cpu().numpy()[rows]
     serr = parity.check_scores(ws, s, s_ref)
     same = parity.check_selection(ws, s_ref, k_ref, k)
-    aerr = parity.check_attention(ws, o, o_ref, mask=same)
+    aerr = parity.check_decode_attention(ws, o, o_ref, same, k)
+    parity.record("prefill_64k (sampled rows)", same, serr, aerr)
     say(f"[parity] prefill_64k: score err {serr:.3f} of bound, {int(same.sum())}/{same.size} "
         f"selections identical, attention max-abs {aerr:.2e}")
 
