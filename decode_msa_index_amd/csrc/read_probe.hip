@@ -39,6 +39,11 @@ __global__ __launch_bounds__(256) void read_blocks_kernel(const uint8_t* __restr
 #pragma unroll
     for (int k = 0; k < 16; ++k) x ^= v[i][k].x ^ v[i][k].y ^ v[i][k].z ^ v[i][k].w;
   }
+  // reduce over the wave first: every lane's loads then feed the one store
+  // (a value only lane 0 used would let the compiler move the loads under
+  // the lane-0 branch, and read 16 bytes per load instead of 1 KB)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
   if (lane == 0) sink[w] = x;
 }
 

@@ -70,7 +70,14 @@ _E2M1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, 0, -.5, -1, -1.5, -2, -3, -4, -6], 
 
 
 def index_keys_abs(w: synth.Workload, pblocks: np.ndarray) -> np.ndarray:
-    """|dequantised index keys| of the given physical blocks, [n, BS, Di] fp32."""
+    """|dequantised index keys| of the given physical blocks, [n, BS, Di] fp32
+    (zeros for table entries outside the pool: such a block holds no key)."""
+    pblocks = np.asarray(pblocks)
+    bad = (pblocks < 0) | (pblocks >= w.num_phys_blocks)
+    if bad.any():
+        v = index_keys_abs(w, np.where(bad, 0, pblocks))
+        v[bad] = 0.0
+        return v
     if w.index_k_dtype == synth.NVFP4:
         d = w.ik_data[pblocks]
         s = torch.from_numpy(np.ascontiguousarray(w.ik_scales[pblocks])).view(

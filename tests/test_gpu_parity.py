@@ -492,8 +492,14 @@ def _cache_write_inputs(kv, ik, q_dtype, iq_dtype, seed, spikes=True, G=4, H=64)
     rng = np.random.default_rng(seed)
     n, G, D = len(seq), w.num_groups, w.head_dim
 
+    # with spikes: a wide spread and saturating values (the write's edge
+    # cases); without: the cached values' own N(0, 1) scale, since the
+    # attention bound of the decode that follows is absolute (bf16 rounding
+    # alone exceeds 1e-2 on outputs of magnitude 4 and more)
+    sigma = 2.0 if spikes else 1.0
+
     def vals(*shape):
-        x = rng.normal(0, 2.0, shape) * np.where(rng.random(shape) < 0.1, 1e-3, 1.0)
+        x = rng.normal(0, sigma, shape) * np.where(rng.random(shape) < 0.1, 1e-3, 1.0)
         if spikes:
             x[rng.random(shape) < 0.01] = 3000.0  # saturating values
         return x.astype(np.float32)
