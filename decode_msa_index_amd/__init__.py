@@ -22,7 +22,8 @@ STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
           3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP", 5: "MSA_ERR_DEVICE_WAIT"}
 
 EXPORTS = ["msa_check_problem", "msa_workspace_bytes", "msa_index_scores", "msa_block_topk",
-           "msa_sparse_attend", "msa_decode", "msa_cache_write", "msa_workspace_status",
+           "msa_sparse_attend", "msa_decode", "msa_decode_static", "msa_cache_write",
+           "msa_workspace_status",
            "msa_set_merge_spin_limit", "msa_status_string", "msa_last_error"]
 
 
@@ -110,6 +111,9 @@ def lib():
         L.msa_decode.restype = ctypes.c_int
         L.msa_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+        L.msa_decode_static.restype = ctypes.c_int
+        L.msa_decode_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp]
         L.msa_cache_write.restype = ctypes.c_int
         L.msa_cache_write.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_workspace_status.restype = ctypes.c_int
@@ -191,6 +195,17 @@ def decode(p: Problem, index_q, ik_data, ik_scales, q, kv_data, kv_scales, block
                             _ptr(q), _ptr(kv_data), _ptr(kv_scales), _ptr(block_table),
                             _ptr(seq_lens), _ptr(q_pos), _ptr(block_scores), _ptr(topk_idx),
                             _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def decode_static(p: Problem, index_q, ik_data, ik_scales, q, kv_data, kv_scales, block_table,
+                  seq_lens, q_pos, block_scores, topk_idx, out, lse, stream=None):
+    """msa_decode on the library's own static scratch (no workspace)."""
+    pc = p.c()
+    _check(lib().msa_decode_static(ctypes.byref(pc), _ptr(index_q), _ptr(ik_data),
+                                   _ptr(ik_scales), _ptr(q), _ptr(kv_data), _ptr(kv_scales),
+                                   _ptr(block_table), _ptr(seq_lens), _ptr(q_pos),
+                                   _ptr(block_scores), _ptr(topk_idx), _ptr(out), _ptr(lse),
+                                   _stream(stream)))
 
 
 def cache_write(p: Problem, token_seq, token_pos, k_new, v_new, ik_new, block_table, kv_data,

@@ -362,7 +362,12 @@ msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_
 msa_status msa_workspace_status(const void* workspace, void* stream) {
   clear_error();
   const char* base = static_cast<const char*>(workspace);
-  if (!base) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!base) {  // msa_decode_static's scratch on the current device
+    char* ws = nullptr;
+    msa_status st = static_scratch(&ws);
+    if (st != MSA_OK) return st;
+    base = ws;
+  }
   if (!aligned(base, kAlign)) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
   uint32_t word = 0;
   hipStream_t hs = (hipStream_t)stream;

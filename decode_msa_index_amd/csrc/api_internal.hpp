@@ -42,4 +42,7 @@ msa_status decode_impl(const msa_problem* p, const void* index_q, const void* ik
                        int32_t* topk_idx, void* out, float* lse, char* ws, const WsLayout& w,
                        hipStream_t hs);
 
+// The current device's copy of msa_decode_static's scratch array.
+msa_status static_scratch(char** out);
+
 }  // namespace msa_api

@@ -281,9 +281,33 @@ msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32
                            void* kv_scales, void* ik_data, void* ik_scales, void* stream);
 
 /*
+ * msa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, semantics and results as msa_decode
+ * (its attention may differ from the three-call chain's to rounding in the
+ * same way), minus the workspace: its scratch is a device array of
+ * MSA_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  A problem whose msa_workspace_bytes(p, 3) exceeds that is
+ * rejected with MSA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued
+ * (passing block_scores does not shrink the need: the size is that of the
+ * decode workspace).  The call allocates nothing: it clears the scratch
+ * region it needs with a fill kernel, then enqueues the decode.  Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ * msa_workspace_status(NULL, stream) reads the array's status header.
+ */
+#define MSA_STATIC_SCRATCH_BYTES (16u << 20)
+msa_status msa_decode_static(const msa_problem* p, const void* index_q, const void* ik_data,
+                             const void* ik_scales, const void* q, const void* kv_data,
+                             const void* kv_scales, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* q_pos, float* block_scores,
+                             int32_t* topk_idx, void* out, float* lse, void* stream);
+
+/*
  * Status of a workspace after the calls enqueued on `stream` so far: waits
  * for the stream, reads the status header of `workspace` (a decode or attend
- * workspace of at least 256 bytes) and returns MSA_ERR_DEVICE_WAIT if a
+ * workspace of at least 256 bytes; NULL: msa_decode_static's scratch on the
+ * current device) and returns MSA_ERR_DEVICE_WAIT if a
  * split-K merge gave up waiting on it (see msa_workspace_bytes), MSA_OK
  * otherwise.  Synchronous: not for use inside a captured graph.
  */
