@@ -54,7 +54,7 @@ struct AttendArgs {
   const int32_t* qpos;
   const int32_t* topk;    // selection input (attend only)
   const float* scores;    // pooled scores (select + attend, written by an earlier kernel)
-  uint32_t* clear;        // SELECT: [units][MB] words the last reader zeroes (nullable)
+  uint32_t* clear;        // select + attend: [units][MB] words the last reader zeroes (nullable)
   int32_t* topk_out;      // selection output (select + attend), may be null
   void* out;
   float* lse;
@@ -231,19 +231,26 @@ __device__ __forceinline__ void clear_row(const AttendArgs& a, int u, int nw) {
   for (int jj = threadIdx.x; jj < a.MB; jj += 64 * nw) row[jj] = 0u;
 }
 
+// Where a task's selection comes from.
+enum SelMode {
+  kSelGiven = 0,  // topk_idx, an input
+  kSelScores = 1  // made here from pooled scores an earlier kernel wrote
+};
+
 // One attention task: (row, group) unit u, split `split` of part.S, run by
-// the calling workgroup of NW waves.  sel_lds: the dynamic LDS of a SELECT
-// kernel.  Returns early (all threads of the workgroup together) where it
-// has nothing more to do.
-template <int KV, int NW, bool SELECT>
+// the calling workgroup of NW waves.  sel_lds: the dynamic LDS of a
+// selecting kernel.  Returns early (all threads of the workgroup together)
+// where it has nothing more to do.
+template <int KV, int NW, int SEL>
 __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
                                             const uint8_t* __restrict__ kvd,
                                             const uint8_t* __restrict__ kvs, const AttendArgs& a,
                                             const Partials& part, int u, int split,
                                             uint32_t* sel_lds) {
+  constexpr bool SELECT = SEL != kSelGiven;
   __shared__ int32_t sel_w[SELECT ? NW : 1][32];  // SELECT: each wave's copy of the selection
   __shared__ uint4 vsl[KV == kNVFP4 ? NW : 1][64];  // NVFP4: each wave's block of V scales
-  // sel_lds (SELECT): [256] scratch, [MB] keys, [MB] table row
+  // sel_lds (SELECT): [256] scratch, [MB] keys, then (kSelScores) [MB] table row
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int row = u / a.G, g = u % a.G, b = row / a.R;
   const int pos = row_last_key(a.lens, a.qpos, row, b, a.MB);
@@ -270,7 +277,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
   }
 
-  if constexpr (SELECT) {
+  if constexpr (SEL == kSelScores) {
     // every thread loads a share of the row's scores (as order keys) and of
     // its block-table entries, in one round that does not wait for the row
     // length, and keeps its largest key; the workgroup then selects
@@ -536,7 +543,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
     return;
   }
-  bool timed_out = poisoned != 0u || part.spin_limit < 0;
+  bool timed_out = poisoned != 0u || (part.S > 1 && part.spin_limit < 0);
   if (part.S > 1) {
     // merge the other splits' partials, a batch at a time, into (co, cm, cl)
     constexpr int CH = 128 / (4 * DTW + 8);  // partials whose words a batch holds

@@ -37,13 +37,6 @@ struct IndexArgs {
   float out_scale;    // index_scale * index_k_scale (NVFP4: times the tensor scale)
 };
 
-// Lanes 0..cols-1 store block j's scores of the wave's columns: column c is
-// (row, group) pair col0 + c of the [rows][G] order.
-__device__ __forceinline__ void put_block_scores(const IndexArgs& x, size_t col0, int cols, int j,
-                                                 int lane, float v) {
-  if (lane < cols) x.scores[(col0 + lane) * x.MB + j] = v;
-}
-
 // The scores of a 16-token tile come from MFMA: S = K Q^T as
 // v_mfma_f32_16x16x32_bf16 with the tile's tokens as A rows, the wave's
 // index queries as B columns -- the G groups of up to 16 / G rows of one
@@ -320,6 +313,81 @@ __device__ __forceinline__ float finish_block(const IndexArgs& x, const TileMax&
   m = fmaxf(m, lane_xor_f<16>(m));
   m = fmaxf(m, lane_xor_f<32>(m));
   return (m * unscale) * x.out_scale;
+}
+
+// Blocks a wave of the decode scan takes in one run (the next block's loads
+// in flight while one is scored): one for FP8 keys (16 KB per block), four
+// for NVFP4 keys (9 KB per block, more conversion work per byte).
+template <int IK>
+constexpr int blocks_per_wave() {
+  return IK == kFP8 ? 1 : 4;
+}
+
+// One wave of the decode scan: row group rg (rows rg * rows_per_wave ..) of
+// sequence b, blocks j0 + 4 i (i < blocks_per_wave); scores to x.scores
+// ([rows][G][MB]).
+template <int IK>
+__device__ __forceinline__ void scan_wave_blocks(const IndexArgs& x, int b, int rg, int j0,
+                                                 uint4* stage) {
+  constexpr int NB = blocks_per_wave<IK>();
+  const int lane = threadIdx.x & 63;
+  const int r0 = rg * x.rows_per_wave, nr = min(x.rows_per_wave, x.R - r0);
+  const int cols = nr * x.G;
+  const size_t col0 = ((size_t)b * x.R + r0) * x.G;  // first (row, group) pair
+  if (j0 >= x.MB) return;
+  auto put = [&](int j, float v) {
+    if (lane < cols) x.scores[(col0 + lane) * x.MB + j] = v;
+  };
+  // table entries of the wave's blocks, lane i holding block i's (issued
+  // alongside the length loads)
+  int entry = -1;
+  if (lane < NB && j0 + 4 * lane < x.MB) entry = x.bt[(size_t)b * x.MB + j0 + 4 * lane];
+  // this lane's column: its row's last visible key (-1 past the columns)
+  const int n = lane & 15;
+  const int pos = n < cols ? row_last_key(x.lens, x.qpos, b * x.R + r0 + n / x.G, b, x.MB) : -1;
+  int pos_max = pos;  // the wave's furthest-seeing column
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) pos_max = max(pos_max, __shfl_xor(pos_max, o, 64));
+  // the wave's blocks with keys to see: a prefix of its run (blocks past
+  // every column's last key, or past the table, score -inf unread)
+  int live = 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    live += (j0 + 4 * i < x.MB && (j0 + 4 * i) * kBlock <= pos_max) ? 1 : 0;
+  for (int i = live; i < NB && j0 + 4 * i < x.MB; ++i) put(j0 + 4 * i, -INFINITY);
+  if (live == 0) return;
+  // physical block of the wave's i-th block, -1 for an entry outside the pool
+  auto phys = [&](int i) {
+    const int e = __builtin_amdgcn_readlane(entry, i);
+    return (e < 0 || e >= x.P) ? -1 : e;
+  };
+  // Every load of the loop is issued unconditionally (a branch around an
+  // issue makes the compiler wait for all loads in flight where the paths
+  // join, which would serialise the blocks): loads for an unusable block
+  // read physical block 0 (in range; the result is not used).
+  typename BlockRawOf<IK>::query qraw;
+  qraw.fetch(x, col0, cols, lane);
+  typename BlockRawOf<IK>::type buf[2];
+  int pb = phys(0);
+  buf[0].issue(x, max(pb, 0), lane);
+  QueryB<IK> q;
+  qraw.make(cols, lane, q);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (i >= live) break;
+    const int j = j0 + 4 * i;
+    const int pb_next = i + 1 < live ? phys(i + 1) : -1;
+    if (i + 1 < NB) buf[(i + 1) & 1].issue(x, max(pb_next, 0), lane);
+    if (pb < 0) {  // an entry outside the pool: the block contributes nothing
+      put(j, -INFINITY);
+    } else {
+      TileMax tm;
+      tm.init();
+      buf[i & 1].pool(j, pos, lane, q, tm, stage);
+      put(j, finish_block(x, tm, q.unscale));
+    }
+    pb = pb_next;
+  }
 }
 
 }  // namespace msa

@@ -41,72 +41,11 @@ namespace msa {
 // block, more conversion work per byte).
 // -------------------------------------------------------------------------
 template <int IK>
-constexpr int blocks_per_wave() {
-  return IK == kFP8 ? 1 : 4;
-}
-
-template <int IK>
 __global__ __launch_bounds__(256, 4) void index_mfma_kernel(IndexArgs x) {
-  constexpr int NB = blocks_per_wave<IK>();
   __shared__ uint4 stage[4][stage_bytes<IK>() / 16];  // one staging area per wave
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wave = wave_id();
   const int b = blockIdx.y / x.row_groups, rg = blockIdx.y % x.row_groups;
-  const int r0 = rg * x.rows_per_wave, nr = min(x.rows_per_wave, x.R - r0);
-  const int cols = nr * x.G;
-  const size_t col0 = ((size_t)b * x.R + r0) * x.G;  // first (row, group) pair
-  const int j0 = blockIdx.x * (4 * NB) + wave;     // the wave's blocks: j0 + 4 i
-  if (j0 >= x.MB) return;
-  // table entries of the wave's blocks, lane i holding block i's (issued
-  // alongside the length loads)
-  int entry = -1;
-  if (lane < NB && j0 + 4 * lane < x.MB) entry = x.bt[(size_t)b * x.MB + j0 + 4 * lane];
-  // this lane's column: its row's last visible key (-1 past the columns)
-  const int n = lane & 15;
-  const int pos = n < cols ? row_last_key(x.lens, x.qpos, b * x.R + r0 + n / x.G, b, x.MB) : -1;
-  int pos_max = pos;  // the wave's furthest-seeing column
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) pos_max = max(pos_max, __shfl_xor(pos_max, o, 64));
-  // the wave's blocks with keys to see: a prefix of its run (blocks past
-  // every column's last key, or past the table, score -inf unread)
-  int live = 0;
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    live += (j0 + 4 * i < x.MB && (j0 + 4 * i) * kBlock <= pos_max) ? 1 : 0;
-  for (int i = live; i < NB && j0 + 4 * i < x.MB; ++i)
-    put_block_scores(x, col0, cols, j0 + 4 * i, lane, -INFINITY);
-  if (live == 0) return;
-  // physical block of the wave's i-th block, -1 for an entry outside the pool
-  auto phys = [&](int i) {
-    const int e = __builtin_amdgcn_readlane(entry, i);
-    return (e < 0 || e >= x.P) ? -1 : e;
-  };
-  // Every load of the loop is issued unconditionally (a branch around an
-  // issue makes the compiler wait for all loads in flight where the paths
-  // join, which would serialise the blocks): loads for an unusable block
-  // read physical block 0 (in range; the result is not used).
-  typename BlockRawOf<IK>::query qraw;
-  qraw.fetch(x, col0, cols, lane);
-  typename BlockRawOf<IK>::type buf[2];
-  int pb = phys(0);
-  buf[0].issue(x, max(pb, 0), lane);
-  QueryB<IK> q;
-  qraw.make(cols, lane, q);
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    if (i >= live) break;
-    const int j = j0 + 4 * i;
-    const int pb_next = i + 1 < live ? phys(i + 1) : -1;
-    if (i + 1 < NB) buf[(i + 1) & 1].issue(x, max(pb_next, 0), lane);
-    if (pb < 0) {  // an entry outside the pool: the block contributes nothing
-      put_block_scores(x, col0, cols, j, lane, -INFINITY);
-    } else {
-      TileMax tm;
-      tm.init();
-      buf[i & 1].pool(j, pos, lane, q, tm, stage[wave]);
-      put_block_scores(x, col0, cols, j, lane, finish_block(x, tm, q.unscale));
-    }
-    pb = pb_next;
-  }
+  scan_wave_blocks<IK>(x, b, rg, blockIdx.x * (4 * blocks_per_wave<IK>()) + wave, stage[wave]);
 }
 
 // -------------------------------------------------------------------------

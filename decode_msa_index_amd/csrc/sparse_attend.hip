@@ -26,8 +26,8 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvd,
     const uint8_t* __restrict__ kvs, AttendArgs a, Partials part) {
   extern __shared__ uint32_t sel_lds[];
-  attend_task<KV, NW, SELECT>(q, kvd, kvs, a, part, blockIdx.x / part.S,
-                                     blockIdx.x % part.S, sel_lds);
+  attend_task<KV, NW, SELECT ? kSelScores : kSelGiven>(q, kvd, kvs, a, part, blockIdx.x / part.S,
+                                                      blockIdx.x % part.S, sel_lds);
 }
 
 __global__ void zero_fill_kernel(int32_t* p, int n) {
