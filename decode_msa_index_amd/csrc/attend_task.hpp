@@ -224,6 +224,11 @@ __device__ __forceinline__ bool all_landed(f32x4 v) {
 // Partials::spin_limit.
 constexpr int kSpinLimit = 1 << 20;
 
+// The state arithmetic below writes every multiply-add as an explicit fmaf:
+// a sum of two products left to the compiler may be fused either way, and
+// the kernels that attend a unit (given selection, selection made in-kernel)
+// must round it alike.
+
 // Returns the unit's row of the scores to 0 once every reader is done with
 // it, so that the workspace is left as the call found it.
 __device__ __forceinline__ void clear_row(const AttendArgs& a, int u, int nw) {
@@ -277,6 +282,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
   }
 
+  int sorted_sel = -1;  // SELECT: lane l's entry of the ascending selection
   if constexpr (SEL == kSelScores) {
     // every thread loads a share of the row's scores (as order keys) and of
     // its block-table entries, in one round that does not wait for the row
@@ -310,10 +316,11 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
     group_select<NW>(keys, rb, a.K, a.init, a.local, tmax, gsl, sel_lds, sel_w[wave]);
     if (a.clear && part.S == 1) clear_row(a, u, NW);
-    if (split == 0 && wave == 0 && a.topk_out) {  // the stored selection ascends
-      const int v = sort_selection(lane < a.K ? sel_w[0][lane] : -1, a.K);
-      if (lane < a.K) a.topk_out[(size_t)u * a.K + lane] = v;
-    }
+    // the selection in ascending order, as msa_block_topk stores it: the
+    // blocks are then attended in the same order as from a given selection
+    sorted_sel = sort_selection(lane < a.K ? sel_w[wave][lane] : -1, a.K);
+    if (split == 0 && wave == 0 && a.topk_out && lane < a.K)
+      a.topk_out[(size_t)u * a.K + lane] = sorted_sel;
   }
 
   float M = -INFINITY, Lr = 0.0f;
@@ -326,7 +333,8 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
   int my_j = -1, my_pb = -1;
   {
     const int sidx = e0 + wave + NW * lane;
-    if (lane < 32 && sidx < e1) my_j = SELECT ? sel_w[wave][sidx] : a.topk[(size_t)u * a.K + sidx];
+    const int sel_e = SELECT ? __shfl(sorted_sel, min(sidx, 63), 64) : -1;
+    if (lane < 32 && sidx < e1) my_j = SELECT ? sel_e : a.topk[(size_t)u * a.K + sidx];
     if (my_j >= 0 && my_j <= rb)
       my_pb = SELECT ? reinterpret_cast<const int32_t*>(sel_lds + 256 + a.MB)[my_j]
                      : a.bt[(size_t)b * a.MB + my_j];
@@ -400,20 +408,24 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     }
 
     // ---- online softmax update (head n lives in lanes n, n+16, n+32, n+48) ----
+    // Keys past the row's last visible one (only in its last block) are
+    // masked to -inf.  The scale is positive, so the largest scaled logit is
+    // the scaled largest raw one, and each weight takes one fma before exp2.
+    // (A branch that skips the mask for full blocks, or one that skips the
+    // rescale when no maximum moved, costs more registers than it saves.)
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 32 * qd + 8 * (t >> 1) + 4 * (t & 1) + i;
-        const float v = key < nvalid ? sacc[t][i] * a.scale_log2 : -INFINITY;
-        sacc[t][i] = v;
-        mx = fmaxf(mx, v);
+        if (key >= nvalid) sacc[t][i] = -INFINITY;
+        mx = fmaxf(mx, sacc[t][i]);
       }
     }
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float Mn = fmaxf(M, mx);
+    const float Mn = fmaxf(M, mx * a.scale_log2);
     const float alpha = rescale(M, Mn);
     float lsum = 0.0f;
     f16x8 pop[4];
@@ -421,22 +433,24 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2_weight(sacc[t][i] - Mn);
+        const float p = exp2_weight(fmaf(sacc[t][i], a.scale_log2, -Mn));
         lsum += p;
         pop[t >> 1][4 * (t & 1) + i] = (_Float16)p;
       }
     }
     lsum += shfl_xor(lsum, 16);
     lsum += shfl_xor(lsum, 32);
-    Lr = Lr * alpha + lsum;
+    Lr = fmaf(Lr, alpha, lsum);
     M = Mn;
-    float alpha_o[4];
+    {
+      float alpha_o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * qd + i, 64);
+      for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * qd + i, 64);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha_o[i];
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha_o[i];
+      }
     }
 
     // ---- O += P V ----
@@ -506,7 +520,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f[v][i] = rescale(f[v][i], cm[i]);
-        cl[i] += f[v][i] * l[v][i];
+        cl[i] = fmaf(f[v][i], l[v][i], cl[i]);
       }
     }
 #pragma unroll
@@ -516,7 +530,7 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
       for (int v = 0; v < NW; ++v) {
         const f32x4 x = st_o[v][wave * DTW + d][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) co[d][i] += f[v][i] * x[i];
+        for (int i = 0; i < 4; ++i) co[d][i] = fmaf(f[v][i], x[i], co[d][i]);
       }
     }
   }
@@ -592,13 +606,13 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
             fa[i] = rescale(cm[i], mx);
             fb[i] = rescale(sm[i], mx);
             cm[i] = mx;
-            cl[i] = cl[i] * fa[i] + sl[i] * fb[i];
+            cl[i] = fmaf(sl[i], fb[i], cl[i] * fa[i]);
           }
 #pragma unroll
           for (int d = 0; d < DTW; ++d) {
             const f32x4 x = decode_partial(po[c][d]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) co[d][i] = co[d][i] * fa[i] + x[i] * fb[i];
+            for (int i = 0; i < 4; ++i) co[d][i] = fmaf(x[i], fb[i], co[d][i] * fa[i]);
           }
         }
       }

@@ -14,9 +14,10 @@
  *                      (and optional leading / trailing blocks)
  *   msa_sparse_attend  exact GQA attention over the blocks   (main attention)
  *   msa_decode         the three in one call
- * msa_decode's scores and selection are bitwise those of the three-call
- * chain; its attention output agrees with the chain's to rounding.  A fifth
- * call writes new tokens into the caches the others read:
+ * msa_decode's scores, selection, outputs and lse are bitwise those of the
+ * three-call chain (both attend the selected blocks in ascending order with
+ * the same launch shape).  A fifth call writes new tokens into the caches
+ * the others read:
  *   msa_cache_write    quantise new K / V / index keys into their slots
  *
  * ---------------------------------------------------------------------------

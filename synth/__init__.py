@@ -45,6 +45,7 @@ NVFP4_TENSOR_SCALE = 8.0 / (6.0 * 448.0)
 
 STREAM_INDEX_Q, STREAM_Q, STREAM_IK, STREAM_KV = 1, 2, 3, 4
 STREAM_TABLE, STREAM_LENS, STREAM_PLANT = 5, 6, 7
+STREAM_SHARED_Q = 8
 
 
 def build(force: bool = True) -> str:
@@ -208,7 +209,8 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
          plant_per_seq: int = 0, plant_add: float = 1.0, bump_blocks: int = 0,
          bump_add: float = 2.0, max_blocks: int | None = None, k_scale: float = 1.0,
          v_scale: float = 1.0, ik_scale: float | None = None,
-         kv_fill: bool = True, share_seqs: int = 0, share_blocks: int = 0) -> Workload:
+         kv_fill: bool = True, share_seqs: int = 0, share_blocks: int = 0,
+         share_corr: float = 0.0) -> Workload:
     """Build one seeded workload.
 
     table: "identity" (seq b's block j is physical b*max_blocks+j) or
@@ -223,6 +225,11 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
     share_blocks, and short of every member's last block -- to the same
     physical blocks ("permute" tables only); share_seqs is also passed to the
     kernels as the share-group hint.
+    share_corr: rho in [0, 1) for groups with a shared prefix: every member's
+    queries and index queries become rho * (the group's common draw) +
+    sqrt(1 - rho^2) * (its own draw) -- requests continuing one prompt -- and
+    plant_per_seq blocks are planted once per group, inside the shared
+    prefix, along the common index query's direction instead of per member.
     """
     index_q_dtype = q_dtype if index_q_dtype is None else index_q_dtype
     index_k_dtype = kv_dtype if index_k_dtype is None else index_k_dtype
@@ -267,6 +274,18 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
     # ---- queries ----
     iq_f = normal(seed, STREAM_INDEX_Q, 0, rows * G * Di).reshape(rows, G, Di)
     q_f = normal(seed, STREAM_Q, 0, rows * H * D).reshape(rows, H, D)
+    corr_groups = [(g0, g1, sh) for g0, g1, sh in groups if g1 - g0 > 1 and sh > 0] \
+        if share_corr > 0 else []
+    if corr_groups:
+        if rows_per_seq != 1:
+            raise ValueError("share_corr needs rows_per_seq == 1")
+        rho = float(share_corr)
+        own = math.sqrt(1.0 - rho * rho)
+        per = G * Di + H * D
+        for n, (g0, g1, _) in enumerate(corr_groups):
+            c = normal(seed, STREAM_SHARED_Q, n * per, per)
+            iq_f[g0:g1] = rho * c[:G * Di].reshape(1, G, Di) + own * iq_f[g0:g1]
+            q_f[g0:g1] = rho * c[G * Di:].reshape(1, H, D) + own * q_f[g0:g1]
     index_q = _encode_plain(iq_f, index_q_dtype)
     q = _encode_plain(q_f, q_dtype)
 
@@ -277,7 +296,21 @@ def make(name: str = "custom", *, seed: int = 0x4D5341, seq_lens=None, num_seqs:
     if plant_per_seq:
         iq_vals = (index_q.astype(np.uint32) << 16).view(np.float32) \
             if index_q_dtype == BF16 else index_q.astype(np.float32)
+        in_corr = set()
+        for g0, g1, sh in corr_groups:  # once per group, inside the shared prefix
+            in_corr.update(range(g0, g1))
+            choices = rng_p.choice(sh, size=min(plant_per_seq, sh), replace=False)
+            js = sorted(int(c) for c in choices)
+            u = np.sign(iq_vals[g0 * rows_per_seq:g1 * rows_per_seq].astype(np.float64)
+                        .sum(axis=(0, 1))).astype(np.float32)
+            u[u == 0] = 1.0
+            for b in range(g0, g1):
+                planted[b] = js
+            for j in js:
+                add_vec[int(bt[g0, j])] = plant_add * u
         for b in range(num_seqs):
+            if b in in_corr:
+                continue
             recent = int(nb[b]) - 1
             choices = rng_p.choice(recent, size=min(plant_per_seq, recent), replace=False)
             planted[b] = sorted(int(c) for c in choices)

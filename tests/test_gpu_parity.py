@@ -357,34 +357,36 @@ def test_sparse_attend_on_oracle_selection():
 
 
 def test_decode_equals_chain_and_is_deterministic():
-    """The fused decode makes the same selection as the three-kernel chain
-    and stores the same scores; its attention visits the selected blocks in
-    another order (the fused selection is not sorted before use), so its
-    outputs agree with the chain's to rounding: within 2 bf16 ulps, lse to
-    1e-5 relative.  Repeated decodes are bit-identical."""
-    w = synth.make("det", seed=44, seq_lens=[20000, 7000, 300], q_dtype=synth.BF16,
-                   kv_dtype=synth.FP8, plant_per_seq=4)
-    dw = parity.DeviceWorkload(w)
-    say("[parity] chain vs decode vs decode")
-    dw.chain()
-    torch.cuda.synchronize()
-    chain = (dw.scores.clone(), dw.topk.clone(), dw.out.float().clone(), dw.lse.clone())
-    first = None
-    for with_scores in (True, True, False):
-        dw.decode(with_scores=with_scores)
+    """The fused decode makes the same selection as the three-kernel chain,
+    stores the same scores and attends the selected blocks in the same
+    (ascending) order with the same launch shape, so its outputs and lse are
+    bit-identical to the chain's, on a shape that splits each (row, group)
+    over several workgroups and on one that does not.  Repeated decodes are
+    bit-identical."""
+    for lens in ([20000, 7000, 300], [9000] * 80):
+        w = synth.make("det", seed=44, seq_lens=lens, q_dtype=synth.BF16,
+                       kv_dtype=synth.FP8, plant_per_seq=4)
+        dw = parity.DeviceWorkload(w)
+        say(f"[parity] chain vs decode vs decode, {len(lens)} sequences")
+        dw.chain()
         torch.cuda.synchronize()
-        if with_scores:
-            assert torch.equal(dw.scores, chain[0])
-        assert torch.equal(dw.topk, chain[1])
-        out = dw.out.float()
-        assert torch.all((out - chain[2]).abs() <= 2.0 ** -7 * chain[2].abs() + 1e-6)
-        assert torch.allclose(dw.lse, chain[3], rtol=1e-5, atol=1e-6)
-        now = (dw.topk.clone(), dw.out.view(torch.uint8).clone(), dw.lse.clone())
-        if first is None:
-            first = now
-        else:
-            assert all(torch.equal(x, y) for x, y in zip(first, now)), "decode not deterministic"
-        assert int(torch.count_nonzero(dw.ws_decode)) == 0, "workspace not left zero-filled"
+        chain = (dw.scores.clone(), dw.topk.clone(), dw.out.view(torch.uint8).clone(),
+                 dw.lse.clone())
+        first = None
+        for with_scores in (True, True, False):
+            dw.decode(with_scores=with_scores)
+            torch.cuda.synchronize()
+            if with_scores:
+                assert torch.equal(dw.scores, chain[0])
+            assert torch.equal(dw.topk, chain[1])
+            assert torch.equal(dw.out.view(torch.uint8), chain[2]), "decode out != chain out"
+            assert torch.equal(dw.lse, chain[3]), "decode lse != chain lse"
+            now = (dw.topk.clone(), dw.out.view(torch.uint8).clone(), dw.lse.clone())
+            if first is None:
+                first = now
+            else:
+                assert all(torch.equal(x, y) for x, y in zip(first, now)), "decode not deterministic"
+            assert int(torch.count_nonzero(dw.ws_decode)) == 0, "workspace not left zero-filled"
 
 
 def test_decode_in_graph_replays_match_eager():
