@@ -96,7 +96,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_256k",
                     choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "spec4_256k",
-                             "fp8_share64", "fp8_dcp45_shard", "prefill_64k", "prefill_16k"])
+                             "fp8_share64", "fp8_dcp45_shard", "prefill_64k", "prefill_16k",
+                             "prefill_64k_nvfp4"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -441,7 +442,8 @@ def time_cache_write(w, dw, seqs, positions, reps=20):
 def run_prefill(args, w):
     """Chunked prefill (many query rows per sequence): one step = one
     msa_decode call over all rows; the dominant kernel is the MFMA index
-    contraction, reported against the bf16 dense MFMA peak."""
+    contraction (bf16 MFMA for FP8 index keys, f16 for NVFP4), reported
+    against the 2.5 PFLOP/s dense peak both share."""
     import numpy as np
     import torch
 
@@ -503,7 +505,8 @@ def run_prefill(args, w):
                   "sparse attention)",
         "value": w.rows / (ms_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if w.index_k_dtype == 3 else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "recipe": w.recipe, "rows": w.rows,
                    "context_tokens": int(w.seq_lens.sum()), "kv_groups": w.num_groups,
                    "q_heads": w.num_q_heads, "top_k": w.top_k},

@@ -215,8 +215,8 @@ hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* 
                                const int32_t* seq_lens, const int32_t* q_pos,
                                float* scores, hipStream_t st) {
   if (prefill_index_supported(s)) {
-    return launch_prefill_index_scores(s, index_q, ik_data, block_table, seq_lens, q_pos,
-                                       scores, st);
+    return launch_prefill_index_scores(s, index_q, ik_data, ik_scales, block_table, seq_lens,
+                                       q_pos, scores, st);
   }
   if (s.ik_dtype == kF32) {
     switch (s.G) {

@@ -34,7 +34,7 @@ hipError_t launch_index_scores(const Shape& s, const void* index_q, const void* 
 // index scan (prefill_index.hip), used by launch_index_scores when supported.
 bool prefill_index_supported(const Shape& s);
 hipError_t launch_prefill_index_scores(const Shape& s, const void* index_q, const void* ik_data,
-                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const void* ik_scales, const int32_t* block_table, const int32_t* seq_lens,
                                        const int32_t* q_pos, float* scores, hipStream_t st);
 
 hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,

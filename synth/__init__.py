@@ -496,19 +496,25 @@ def spec4_256k(seed: int = 0x4D5341 + 7, **kw) -> Workload:
     return w
 
 
-def _prefill_chunk(name: str, cached: int, seed: int, **kw) -> Workload:
+def _prefill_chunk(name: str, cached: int, seed: int, kv_dtype: int = FP8, **kw) -> Workload:
     chunk = 4096
     w = make(name, seed=seed, seq_lens=[cached + chunk], rows_per_seq=chunk,
              q_pos=np.arange(cached, cached + chunk, dtype=np.int32), q_dtype=BF16,
-             kv_dtype=FP8, **kw)
+             kv_dtype=kv_dtype, **kw)
+    fmt = "e4m3" if kv_dtype == FP8 else "NVFP4 (quantised from N(0,1))"
     w.recipe = (f"chunked prefill: 1 seq, {cached} cached tokens + a 4096-query chunk at "
                 f"positions {cached}..{cached + chunk - 1}, causal; 64 q heads / 4 groups, "
-                "D=Di=128, bf16 q, e4m3 K/V/index keys, N(0,1), random permutation table")
+                f"D=Di=128, bf16 q, {fmt} K/V/index keys, N(0,1), random permutation table")
     return w
 
 
 def prefill_64k(seed: int = 0x4D5341 + 6, **kw) -> Workload:
     return _prefill_chunk("prefill_64k", 65536, seed, **kw)
+
+
+def prefill_64k_nvfp4(seed: int = 0x4D5341 + 6, **kw) -> Workload:
+    """The prefill_64k chunk with NVFP4 K/V and index keys."""
+    return _prefill_chunk("prefill_64k_nvfp4", 65536, seed, kv_dtype=NVFP4, **kw)
 
 
 def prefill_16k(seed: int = 0x4D5341 + 6, **kw) -> Workload:

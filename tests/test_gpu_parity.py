@@ -785,19 +785,44 @@ def test_decode_long_block_table_unfused_path():
 # many query rows per sequence (chunked prefill): the MFMA form of the scan
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("G,H", [(4, 64), (8, 64), (1, 16)])
-def test_prefill_chunk(G, H):
+@pytest.mark.parametrize("G,H,kv", [(4, 64, synth.FP8), (8, 64, synth.FP8), (1, 16, synth.FP8),
+                                    (4, 64, synth.NVFP4), (8, 64, synth.NVFP4),
+                                    (1, 16, synth.NVFP4)])
+def test_prefill_chunk(G, H, kv):
     """A causal chunk of R = 80 rows ending at each sequence's last key: more
     columns than one tile (G >= 4), more blocks than one block range, ragged
-    lengths."""
+    lengths; FP8 and NVFP4 index keys (both on the MFMA indexer)."""
     R = 80
     lens = np.array([5000, 9003])
     qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
-    w = synth.make(f"prefill-g{G}", seed=91 + G, seq_lens=lens, rows_per_seq=R, q_pos=qp,
-                   num_q_heads=H, num_groups=G, q_dtype=synth.BF16, kv_dtype=synth.FP8,
+    w = synth.make(f"prefill-g{G}", seed=91 + G + 10 * kv, seq_lens=lens, rows_per_seq=R,
+                   q_pos=qp, num_q_heads=H, num_groups=G, q_dtype=synth.BF16, kv_dtype=kv,
                    plant_per_seq=3)
-    _run_and_check(w, fused=True, name=f"prefill-g{G}")
-    _run_and_check(w, fused=False, name=f"prefill-g{G}-chain")
+    tag = "" if kv == synth.FP8 else "-nvfp4"
+    _run_and_check(w, fused=True, name=f"prefill-g{G}{tag}")
+    _run_and_check(w, fused=False, name=f"prefill-g{G}{tag}-chain")
+
+
+def test_prefill_nvfp4_queries_far_outside_f16_range():
+    """The NVFP4 MFMA indexer shifts each (row, group) query by its own power
+    of two into f16's range: rows of a 32-row chunk with queries at 2^60,
+    2^-60, a 2^30 spread inside one query, and a zero query (its blocks all
+    tie at 0 and the lowest are kept)."""
+    R = 32
+    lens = np.array([4000])
+    qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
+    w = synth.make("prefill-iq-range", seed=177, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                   q_dtype=synth.BF16, kv_dtype=synth.NVFP4, plant_per_seq=2)
+    iq = w.index_q.copy()
+    iq[0::4] = _scale_bf16(iq[0::4], 60)
+    iq[1::4] = _scale_bf16(iq[1::4], -60)
+    iq[2::4, 1] = 0
+    iq[3::4, :, :64] = _scale_bf16(iq[3::4, :, :64], 20)
+    iq[3::4, :, 64:] = _scale_bf16(iq[3::4, :, 64:], -10)
+    w = dataclasses.replace(w, index_q=iq)
+    for fused in (False, True):
+        _, same = _run_and_check(w, fused, "prefill-iq-range-nvfp4")
+        assert same[2::4, 1].all(), "a zero query selects the lowest blocks on both sides"
 
 
 @pytest.mark.parametrize("K,init,local", [(8, 2, 3), (32, 1, 4), (4, 0, 0)])
@@ -816,14 +841,15 @@ def test_prefill_chunk_selection_variants(K, init, local):
     _run_and_check(w, fused=False, name=f"prefill-k{K}-i{init}-l{local}-chain")
 
 
-def test_prefill_scattered_positions():
+@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
+def test_prefill_scattered_positions(kv):
     """Rows anywhere in the sequence, including ones that see no key or one
     key, block edges and a row past the sequence's end (clamped)."""
     qp = np.array([-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 2900,
                    2998, 2999, 5000, 40, 300, 1700, 3, 64, 2222, 2500], np.int32)
-    w = synth.make("prefill-scatter", seed=97, seq_lens=[3000], rows_per_seq=len(qp),
-                   q_pos=qp, q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=2)
-    _run_and_check(w, fused=True, name="prefill-scatter")
+    w = synth.make("prefill-scatter", seed=97 + kv, seq_lens=[3000], rows_per_seq=len(qp),
+                   q_pos=qp, q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2)
+    _run_and_check(w, fused=True, name=f"prefill-scatter-{synth.DTYPE_NAMES[kv]}")
 
 
 def test_prefill_64k_sampled_rows():
