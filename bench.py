@@ -99,14 +99,18 @@ def main():
                              "fp8_share64", "fp8_dcp45_shard", "prefill_64k", "prefill_16k",
                              "prefill_64k_nvfp4"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
+    ap.add_argument("--share-corr", type=float, default=0.0,
+                    help="fp8_share64 only: correlation of the requests' queries with their "
+                         "group's common draw (requests continuing one prompt)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device (counter calibration) and exit")
     ap.add_argument("--calibrate-read", action="store_true",
-                    help="only time the read probe over the workload's index-key blocks "
-                         "(the scan's bytes and access pattern, no arithmetic) and exit")
+                    help="only time the read probes (the scan's index-key blocks and the "
+                         "attention's selected K/V, each with its kernel's access pattern "
+                         "and no arithmetic) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py runs on one GPU only: the library has no multi-GPU path; "
@@ -134,7 +138,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     msa.lib()
     t0 = time.time()
-    w = getattr(synth, args.workload)()
+    if args.share_corr:
+        if args.workload != "fp8_share64":
+            log("--share-corr applies to the fp8_share64 workload only")
+            sys.exit(2)
+        w = synth.fp8_share64(share_corr=args.share_corr)
+        w.recipe += f"; queries {args.share_corr} x the group's common draw"
+    else:
+        w = getattr(synth, args.workload)()
     log(f"[bench] generated {w.name} in {time.time() - t0:.1f}s: {w.recipe}")
     if args.calibrate_read:
         return calibrate_read(args, w)
@@ -236,6 +247,21 @@ def main():
                     sel_tokens += min(128, L - 128 * int(j))
     b_idx, b_topk, b_att = algorithmic_bytes(w, sel_tokens)
     b_step = b_idx + b_topk + b_att
+    share_sel = None
+    if w.share_seqs > 1:  # selected K/V blocks: requested vs distinct per group
+        kv_blk = 2 * 128 * 128 * (1 if w.kv_dtype == 2 else 0.5625)
+        req, distinct = 0, set()
+        for r in range(w.rows):
+            b = r // w.rows_per_seq
+            for gi in range(w.num_groups):
+                for j in topk[r, gi]:
+                    if 0 <= j < w.max_blocks:
+                        req += 1
+                        distinct.add((gi, int(w.block_table[b, j])))
+        share_sel = {"blocks_requested": req, "blocks_distinct": len(distinct),
+                     "kv_bytes_requested": req * kv_blk, "kv_bytes_distinct": len(distinct) * kv_blk}
+        log(f"[bench] selected K/V blocks: {req} requested, {len(distinct)} distinct "
+            f"({req * kv_blk / 1e6:.1f} MB vs {len(distinct) * kv_blk / 1e6:.1f} MB)")
     achieved = b_idx / (idx_us * 1e-6) / 1e9
     tokens = int(w.seq_lens.astype(np.int64).sum())
     dense_bytes = tokens * (256 if w.kv_dtype == 2 else 144) * w.num_groups
@@ -315,16 +341,41 @@ def main():
     if unshared_us is not None:
         out["kernel_us"]["index_scores_without_share_hint"] = unshared_us
         out["config"]["share_seqs"] = w.share_seqs
+    if share_sel is not None:
+        out["share_selection"] = share_sel
     print(json.dumps(out), flush=True)
 
 
+def _time_launches(launch, steps, warmup):
+    """Mean time (us) of `steps` launches after `warmup`, from HIP events on
+    the current stream."""
+    import torch
+    for i in range(warmup):
+        launch(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
 def calibrate_read(args, w):
-    """Read ceiling of the scan's access pattern: the read probe
-    (libmsa_probe.so) streams exactly the index-key blocks the scan reads, in
-    the scan's order, one wave per 16 KB block with every load 1 KB of
-    consecutive bytes, and does no arithmetic.  Rotated over --layers cache
-    copies like the decode steps; also timed over the same blocks in physical
-    order, and with 2 and 4 blocks in flight per wave."""
+    """Read ceilings of the two memory-bound kernels' access patterns, timed
+    with the read probes (libmsa_probe.so), which do no arithmetic:
+
+    * the scan: exactly the index-key blocks the scan reads, in the scan's
+      order, one wave per 16 KB block with every load 1 KB of consecutive
+      bytes; also over the same blocks in physical order, and with 2 and 4
+      blocks in flight per wave (decode workloads, FP8 index keys);
+    * the attention: the K and V planes of every selected block, one wave per
+      (row, group) in selection order, as the one-wave attention launch (512
+      or more units) reads them; the attention kernel itself (given the same
+      selection) is timed beside it (FP8 caches).
+
+    Decode workloads rotate over --layers cache copies like the decode steps;
+    prefill chunks use one copy, like their benchmark line."""
     import ctypes
 
     import numpy as np
@@ -333,44 +384,80 @@ def calibrate_read(args, w):
     from decode_msa_index_amd import harness
     from decode_msa_index_amd.build import PROBE_LIB
 
-    assert w.index_k_dtype == 2, "the read probe covers FP8 index keys (16 KB blocks)"
     L = ctypes.CDLL(PROBE_LIB)
-    L.msa_probe_read_blocks.restype = ctypes.c_int
-    L.msa_probe_read_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    nb = (w.seq_lens.astype(np.int64) + 127) // 128
-    order = np.concatenate([w.block_table[b, : nb[b]] for b in range(w.num_seqs)]).astype(np.int32)
-    n = len(order)
-    copies = [harness.dev(w.ik_data)]
-    for _ in range(1, args.layers):
-        copies.append(copies[0].clone())
-    orders = {"scan order": harness.dev(order), "physical order": harness.dev(np.sort(order))}
-    sink = torch.zeros(n, dtype=torch.int32, device="cuda")
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    L.msa_probe_read_blocks.restype = ci
+    L.msa_probe_read_blocks.argtypes = [vp, vp, ci, ci, vp, vp]
+    L.msa_probe_read_kv.restype = ci
+    L.msa_probe_read_kv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, vp]
     stream = torch.cuda.current_stream().cuda_stream
-    results = []
-    for name, o in orders.items():
-        for bpw in (1, 2, 4):
-            def launch(i):
-                rc = L.msa_probe_read_blocks(copies[i % len(copies)].data_ptr(), o.data_ptr(), n,
-                                             bpw, sink.data_ptr(), stream)
-                assert rc == 0, rc
-            for i in range(args.warmup):
-                launch(i)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for i in range(args.steps):
-                launch(i)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / args.steps
-            gbps = n * 16384 / (us * 1e-6) / 1e9
-            log(f"[bench] read probe, {name}, {bpw} block(s) per wave: {us:.2f} us per launch, "
-                f"{gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
-            results.append({"order": name, "blocks_per_wave": bpw, "us_per_launch": us,
-                            "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS})
-    print(json.dumps({"calibrate_read": w.name, "bytes_per_launch": n * 16384,
-                      "cache_copies": args.layers, "steps": args.steps, "results": results}),
-          flush=True)
+    prefill = w.rows_per_seq >= 16
+    layers = 1 if prefill else args.layers
+    out = {"calibrate_read": w.name, "cache_copies": layers, "steps": args.steps}
+
+    if w.index_k_dtype == 2 and not prefill:
+        nb = (w.seq_lens.astype(np.int64) + 127) // 128
+        order = np.concatenate([w.block_table[b, : nb[b]] for b in range(w.num_seqs)]).astype(np.int32)
+        n = len(order)
+        copies = [harness.dev(w.ik_data)]
+        for _ in range(1, layers):
+            copies.append(copies[0].clone())
+        orders = {"scan order": harness.dev(order), "physical order": harness.dev(np.sort(order))}
+        sink = torch.zeros(n, dtype=torch.int32, device="cuda")
+        results = []
+        for name, o in orders.items():
+            for bpw in (1, 2, 4):
+                def launch(i):
+                    rc = L.msa_probe_read_blocks(copies[i % len(copies)].data_ptr(), o.data_ptr(),
+                                                 n, bpw, sink.data_ptr(), stream)
+                    assert rc == 0, rc
+                us = _time_launches(launch, args.steps, args.warmup)
+                gbps = n * 16384 / (us * 1e-6) / 1e9
+                log(f"[bench] read probe, {name}, {bpw} block(s) per wave: {us:.2f} us per "
+                    f"launch, {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
+                results.append({"order": name, "blocks_per_wave": bpw, "us_per_launch": us,
+                                "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS})
+        out["scan"] = {"bytes_per_launch": n * 16384, "results": results}
+        del copies
+
+    if w.kv_dtype == 2 and w.rows * w.num_groups >= 512:  # the one-wave attention launch
+        base = harness.DeviceWorkload(w)
+        base.index_scores()
+        base.block_topk()
+        torch.cuda.synchronize()
+        dws = [base] + [base.copy_with_new_caches() for _ in range(1, layers)]
+        units = w.rows * w.num_groups
+        topk = base.topk.cpu().numpy()
+        bt = w.block_table
+        sel = 0
+        for u in range(units):  # blocks the probe reads (valid entries only)
+            b = (u // w.num_groups) // w.rows_per_seq
+            js = topk.reshape(units, w.top_k)[u]
+            js = js[(js >= 0) & (js < w.max_blocks)]
+            sel += int(np.count_nonzero((bt[b, js] >= 0) & (bt[b, js] < w.num_phys_blocks)))
+        sink = torch.zeros(units, dtype=torch.int32, device="cuda")
+
+        def probe(i):
+            d = dws[i % len(dws)]
+            rc = L.msa_probe_read_kv(d.kv_data.data_ptr(), base.topk.data_ptr(),
+                                     base.block_table.data_ptr(), units, w.top_k, w.num_groups,
+                                     w.rows_per_seq, w.max_blocks, w.num_phys_blocks,
+                                     sink.data_ptr(), stream)
+            assert rc == 0, rc
+
+        def attend(i):
+            dws[i % len(dws)].sparse_attend(topk=base.topk)
+
+        us_probe = _time_launches(probe, args.steps, args.warmup)
+        us_attend = _time_launches(attend, args.steps, args.warmup)
+        nbytes = sel * 2 * 16384
+        log(f"[bench] K/V read probe: {sel} selected blocks, {nbytes / 1e6:.1f} MB, "
+            f"{us_probe:.1f} us per launch ({nbytes / (us_probe * 1e-6) / 1e9:.0f} GB/s); "
+            f"the attention on the same selection: {us_attend:.1f} us")
+        out["kv"] = {"selected_blocks": sel, "bytes_per_launch": nbytes,
+                     "probe_us_per_launch": us_probe, "attend_us_per_launch": us_attend,
+                     "probe_gbps": nbytes / (us_probe * 1e-6) / 1e9}
+    print(json.dumps(out), flush=True)
 
 
 def row_last_key(w, r: int) -> int:

@@ -1,11 +1,20 @@
-// read_probe.hip -- a measurement probe, not part of the MSA library: it
-// reads the same 16 KB index-key blocks a decode scan reads, in the scan's
-// order and with its access pattern (one wave per block, every load
-// instruction 1 KB of consecutive bytes, all of a block's loads issued
-// before anything waits), and does no arithmetic on them.  Its time per
-// byte is the read bandwidth that this access pattern reaches, the ceiling
-// the scan is measured against.  Built as its own library (libmsa_probe.so)
-// for the benchmark's --calibrate-read mode.
+// read_probe.hip -- measurement probes, not part of the MSA library.
+//
+// msa_probe_read_blocks reads the same 16 KB index-key blocks a decode scan
+// reads, in the scan's order and with its access pattern (one wave per
+// block, every load instruction 1 KB of consecutive bytes, all of a block's
+// loads issued before anything waits), and does no arithmetic on them.  Its
+// time per byte is the read bandwidth that this access pattern reaches, the
+// ceiling the scan is measured against.
+//
+// msa_probe_read_kv reads what the one-wave attention launch reads: one
+// wave per (row, group) walks the unit's selected blocks in selection order
+// and reads each block's K and V planes (16 KB each, 32 loads of 1 KB issued
+// together), again with no arithmetic: the floor of that kernel's time set
+// by its K/V reads alone.
+//
+// Built as its own library (libmsa_probe.so) for the benchmark's
+// --calibrate-read mode.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +56,38 @@ __global__ __launch_bounds__(256) void read_blocks_kernel(const uint8_t* __restr
   if (lane == 0) sink[w] = x;
 }
 
+// One wave per unit u = row * G + g: the K plane (p, 0, g) and the V plane
+// (p, 1, g) of every selected block, p = bt[b][j] for j = topk[u][e].
+// Entries outside [0, MB) and table entries outside [0, P) are skipped.
+__global__ __launch_bounds__(64) void read_kv_kernel(const uint8_t* __restrict__ kv,
+                                                     const int32_t* __restrict__ topk,
+                                                     const int32_t* __restrict__ bt, int K, int G,
+                                                     int R, int MB, int P,
+                                                     uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x;
+  const int u = blockIdx.x, row = u / G, g = u % G, b = row / R;
+  uint32_t x = 0;
+  for (int e = 0; e < K; ++e) {
+    const int j = topk[(size_t)u * K + e];
+    if (j < 0 || j >= MB) continue;
+    const int p = bt[(size_t)b * MB + j];
+    if (p < 0 || p >= P) continue;
+    const u32x4v* kp = reinterpret_cast<const u32x4v*>(kv + (((size_t)p * 2 + 0) * G + g) * 16384) + lane;
+    const u32x4v* vp = reinterpret_cast<const u32x4v*>(kv + (((size_t)p * 2 + 1) * G + g) * 16384) + lane;
+    u32x4v v[32];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] = kp[k * 64];
+      v[16 + k] = vp[k * 64];
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
+  if (lane == 0) sink[u] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +108,19 @@ hipError_t msa_probe_read_blocks(const void* base, const int32_t* order, int nbl
     case 4: hipLaunchKernelGGL(read_blocks_kernel<4>, grid, block, 0, st, b, order, nblocks, sink); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// Reads the K and V planes (16 KB each, FP8 cache) of every selected block of
+// units (row, group) pairs: kv = [P][2][G][16 KB], topk = [units][K], bt =
+// [rows / R][MB].  sink: one uint32 per unit.
+hipError_t msa_probe_read_kv(const void* kv, const int32_t* topk, const int32_t* bt, int units,
+                             int K, int G, int R, int MB, int P, uint32_t* sink, void* stream) {
+  if (units <= 0) return hipSuccess;
+  if (K < 1 || G < 1 || R < 1 || MB < 1 || P < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kv_kernel, dim3((unsigned)units), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(kv), topk, bt,
+                     K, G, R, MB, P, sink);
   return hipGetLastError();
 }
 
