@@ -369,6 +369,9 @@ def calibrate_read(args, w):
       order, one wave per 16 KB block with every load 1 KB of consecutive
       bytes; also over the same blocks in physical order, and with 2 and 4
       blocks in flight per wave (decode workloads, FP8 index keys);
+    * NVFP4 index keys: the scan's blocks as the cache stores them (8 KB of
+      E2M1 data and 1 KB of scales in two arrays), the data alone, and the
+      same bytes as one 9 KB record per block;
     * the attention: the K and V planes of every selected block, one wave per
       (row, group) in selection order, as the one-wave attention launch (512
       or more units) reads them; the attention kernel itself (given the same
@@ -390,6 +393,8 @@ def calibrate_read(args, w):
     L.msa_probe_read_blocks.argtypes = [vp, vp, ci, ci, vp, vp]
     L.msa_probe_read_kv.restype = ci
     L.msa_probe_read_kv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, vp]
+    L.msa_probe_read_records.restype = ci
+    L.msa_probe_read_records.argtypes = [vp, vp, vp, ci, ci, ci, vp, vp]
     stream = torch.cuda.current_stream().cuda_stream
     prefill = w.rows_per_seq >= 16
     layers = 1 if prefill else args.layers
@@ -419,6 +424,43 @@ def calibrate_read(args, w):
                                 "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS})
         out["scan"] = {"bytes_per_launch": n * 16384, "results": results}
         del copies
+
+    if w.index_k_dtype == 3 and not prefill:  # NVFP4 index keys: record layouts
+        nb = (w.seq_lens.astype(np.int64) + 127) // 128
+        order = np.concatenate([w.block_table[b, : nb[b]] for b in range(w.num_seqs)]).astype(np.int32)
+        assert order.min() >= 0 and order.max() < w.num_phys_blocks
+        n = len(order)
+        P = w.num_phys_blocks
+        data = harness.dev(np.ascontiguousarray(w.ik_data.reshape(P, 8192)))
+        scl = harness.dev(np.ascontiguousarray(w.ik_scales.reshape(P, 1024)))
+        rec9 = torch.cat([data, scl], dim=1).contiguous()  # one 9 KB record per block
+        layouts = {"8 KB data + 1 KB scales (the cache's layout)": ([data], [scl], 8, 1),
+                   "8 KB data only": ([data], [None], 8, 0),
+                   "one 9 KB record per block": ([rec9], [None], 9, 0)}
+        for name in layouts:  # rotate over copies like the decode steps
+            bases, sides, rk, sk = layouts[name]
+            for _ in range(1, layers):
+                bases.append(bases[0].clone())
+                sides.append(None if sides[0] is None else sides[0].clone())
+        o = harness.dev(order)
+        sink = torch.zeros(n, dtype=torch.int32, device="cuda")
+        results = []
+        for name, (bases, sides, rk, sk) in layouts.items():
+            def launch(i):
+                sd = sides[i % len(sides)]
+                rc = L.msa_probe_read_records(bases[i % len(bases)].data_ptr(),
+                                              None if sd is None else sd.data_ptr(), o.data_ptr(),
+                                              n, rk, sk, sink.data_ptr(), stream)
+                assert rc == 0, rc
+            us = _time_launches(launch, args.steps, args.warmup)
+            nbytes = n * (rk + sk) * 1024
+            gbps = nbytes / (us * 1e-6) / 1e9
+            log(f"[bench] record probe, {name}: {us:.2f} us per launch, {nbytes / 1e6:.1f} MB, "
+                f"{gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
+            results.append({"layout": name, "us_per_launch": us, "bytes_per_launch": nbytes,
+                            "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS})
+        out["nvfp4_records"] = {"blocks": n, "results": results}
+        del layouts
 
     if w.kv_dtype == 2 and w.rows * w.num_groups >= 512:  # the one-wave attention launch
         base = harness.DeviceWorkload(w)

@@ -13,6 +13,13 @@
 // together), again with no arithmetic: the floor of that kernel's time set
 // by its K/V reads alone.
 //
+// msa_probe_read_records reads one record per block in the same one-wave,
+// 1 KB-per-load pattern: `rec_bytes` at base + order[i] * rec_bytes, plus,
+// optionally, `side_bytes` more at side + order[i] * side_bytes.  With 8 KB
+// records and 1 KB side records it reads what the NVFP4 scan reads (E2M1
+// data, e4m3 scales); with 9 KB records and no side records, the same bytes
+// stored as one record per block.
+//
 // Built as its own library (libmsa_probe.so) for the benchmark's
 // --calibrate-read mode.
 #include <hip/hip_runtime.h>
@@ -88,6 +95,35 @@ __global__ __launch_bounds__(64) void read_kv_kernel(const uint8_t* __restrict__
   if (lane == 0) sink[u] = x;
 }
 
+// One wave per block: R 1 KB chunks of the record, then S of the side record
+// (R <= 16, S <= 1), all issued before any is used.
+template <int R, int S>
+__global__ __launch_bounds__(256) void read_records_kernel(const uint8_t* __restrict__ base,
+                                                           const uint8_t* __restrict__ side,
+                                                           const int32_t* __restrict__ order,
+                                                           int nblocks, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= nblocks) return;
+  const size_t b = (size_t)order[w];
+  const u32x4v* src = reinterpret_cast<const u32x4v*>(base + b * (R * 1024)) + lane;
+  u32x4v v[R + S];
+#pragma unroll
+  for (int k = 0; k < R; ++k) v[k] = __builtin_nontemporal_load(src + k * 64);
+  if constexpr (S > 0) {
+    const u32x4v* ssrc = reinterpret_cast<const u32x4v*>(side + b * (S * 1024)) + lane;
+#pragma unroll
+    for (int k = 0; k < S; ++k) v[R + k] = __builtin_nontemporal_load(ssrc + k * 64);
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int k = 0; k < R + S; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
+  if (lane == 0) sink[w] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +143,30 @@ hipError_t msa_probe_read_blocks(const void* base, const int32_t* order, int nbl
     case 2: hipLaunchKernelGGL(read_blocks_kernel<2>, grid, block, 0, st, b, order, nblocks, sink); break;
     case 4: hipLaunchKernelGGL(read_blocks_kernel<4>, grid, block, 0, st, b, order, nblocks, sink); break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Reads nblocks records: block i is rec_kib KB at base + order[i] * rec_kib
+// KB, plus side_kib KB at side + order[i] * side_kib KB.  Supported:
+// (rec_kib, side_kib) = (8, 1), (8, 0), (9, 0).  sink: one uint32 per block.
+hipError_t msa_probe_read_records(const void* base, const void* side, const int32_t* order,
+                                  int nblocks, int rec_kib, int side_kib, uint32_t* sink,
+                                  void* stream) {
+  if (nblocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((nblocks + 3) / 4)), block(256);
+  const uint8_t* b = static_cast<const uint8_t*>(base);
+  const uint8_t* sd = static_cast<const uint8_t*>(side);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rec_kib == 8 && side_kib == 1) {
+    if (!sd) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((read_records_kernel<8, 1>), grid, block, 0, st, b, sd, order, nblocks, sink);
+  } else if (rec_kib == 8 && side_kib == 0) {
+    hipLaunchKernelGGL((read_records_kernel<8, 0>), grid, block, 0, st, b, sd, order, nblocks, sink);
+  } else if (rec_kib == 9 && side_kib == 0) {
+    hipLaunchKernelGGL((read_records_kernel<9, 0>), grid, block, 0, st, b, sd, order, nblocks, sink);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
