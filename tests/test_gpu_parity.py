@@ -852,18 +852,20 @@ def test_prefill_scattered_positions(kv):
     _run_and_check(w, fused=True, name=f"prefill-scatter-{synth.DTYPE_NAMES[kv]}")
 
 
-def test_prefill_64k_sampled_rows():
+@pytest.mark.parametrize("name", ["prefill_64k", "prefill_64k_nvfp4"])
+def test_prefill_64k_sampled_rows(name):
     """The full chunked-prefill shape (65536 cached + 4096 queries, causal),
-    all rows on the GPU; the oracle computes a sample of rows one by one."""
-    say("[parity] generating prefill_64k")
-    w = synth.prefill_64k()
+    FP8 and NVFP4, all rows on the GPU; the oracle computes a sample of rows
+    one by one."""
+    say(f"[parity] generating {name}")
+    w = getattr(synth, name)()
     dw = parity.DeviceWorkload(w)
-    say("[parity] prefill_64k: GPU msa_decode over 4096 rows")
+    say(f"[parity] {name}: GPU msa_decode over 4096 rows")
     dw.decode()
     torch.cuda.synchronize()
     rows = [0, 1, 127, 128, 1000, 2047, 2048, 3333, 4094, 4095]
     ws = parity.subset_rows(w, rows)
-    say(f"[parity] prefill_64k: oracle on rows {rows}")
+    say(f"[parity] {name}: oracle on rows {rows}")
     s_ref, k_ref, o_ref, l_ref = _oracle_all(ws)
     s = dw.scores.cpu().numpy()[rows]
     k = dw.topk.cpu().numpy()[rows]
@@ -871,9 +873,28 @@ def test_prefill_64k_sampled_rows():
     serr = parity.check_scores(ws, s, s_ref)
     same = parity.check_selection(ws, s_ref, k_ref, k)
     aerr = parity.check_decode_attention(ws, o, o_ref, same, k)
-    parity.record("prefill_64k (sampled rows)", same, serr, aerr)
-    say(f"[parity] prefill_64k: score err {serr:.3f} of bound, {int(same.sum())}/{same.size} "
+    parity.record(f"{name} (sampled rows)", same, serr, aerr)
+    say(f"[parity] {name}: score err {serr:.3f} of bound, {int(same.sum())}/{same.size} "
         f"selections identical, attention max-abs {aerr:.2e}")
+    # every row, against properties that hold at any size: the selection is
+    # the top-(k-1) of the row's own pooled scores by (score desc, block asc)
+    # plus its recent block, ascending; scores are -inf past the recent
+    # block; outputs and lse are finite
+    S = dw.scores.cpu().numpy()
+    K = dw.topk.cpu().numpy()
+    assert np.isfinite(dw.out.float().cpu().numpy()).all()
+    assert np.isfinite(dw.lse.cpu().numpy()).all()
+    for r in range(w.rows):
+        rb = parity.row_pos(w, r) // w.block_size
+        assert np.all(S[r, :, rb + 1:] == -np.inf)
+        for g in range(w.num_groups):
+            sel = K[r, g]
+            assert np.all(np.diff(sel) > 0) and sel[-1] == rb
+            cand = S[r, g, :rb]
+            order = np.lexsort((np.arange(rb), -cand))[: w.top_k - 1]
+            assert np.array_equal(np.sort(order), sel[:-1]), (r, g)
+    say(f"[parity] {name}: all {w.rows} rows x {w.num_groups} groups select their own top-"
+        f"{w.top_k - 1} + recent block")
 
 
 # ---------------------------------------------------------------------------
