@@ -233,7 +233,14 @@ constexpr int kSpinLimit = 1 << 20;
 // it, so that the workspace is left as the call found it.
 __device__ __forceinline__ void clear_row(const AttendArgs& a, int u, int nw) {
   uint32_t* row = a.clear + (size_t)u * a.MB;
-  for (int jj = threadIdx.x; jj < a.MB; jj += 64 * nw) row[jj] = 0u;
+  const int nt = 64 * nw;
+  // words up to the first 16-byte boundary, 16-byte stores, then the tail
+  const int head = min(a.MB, (int)(((16 - (reinterpret_cast<uintptr_t>(row) & 15)) & 15) >> 2));
+  if ((int)threadIdx.x < head) row[threadIdx.x] = 0u;
+  uint4* v = reinterpret_cast<uint4*>(row + head);
+  const int nv = (a.MB - head) >> 2;
+  for (int i = threadIdx.x; i < nv; i += nt) v[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int jj = head + 4 * nv + (int)threadIdx.x; jj < a.MB; jj += nt) row[jj] = 0u;
 }
 
 // Where a task's selection comes from.
@@ -615,28 +622,9 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
         }
       }
     }
-    // return the partials read to zero: the workspace is left as found.  The
-    // max / denominator words are shared by all waves: none may be cleared
-    // while another wave is still polling them.  After a timeout nothing is
-    // cleared (a late partial could land after the clearing); the status
-    // word marks the workspace instead, for the host to read and to clear.
-    __syncthreads();
-    if (timed_out) {
-      if (threadIdx.x == 0) *part.status = 1u;
-    }
-#pragma unroll 1
-    for (int sp = 0; sp < part.S - 1 && !timed_out; ++sp) {
-      f32x4* zo = reinterpret_cast<f32x4*>(part.o + (ubase + sp) * (kHeadsPad * kDim));
-#pragma unroll
-      for (int d = 0; d < DTW; ++d) zo[(dt0 + d) * 64 + lane] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (wave == 0 && n == 0) {
-        f32x4* zm = reinterpret_cast<f32x4*>(part.ml + (ubase + sp) * (kHeadsPad * 2));
-        zm[2 * qd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        zm[2 * qd + 1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-    }
-    // every split has finished its selection: the scores row is free
-    if (SELECT && a.clear && !timed_out) clear_row(a, u, NW);
+    // one verdict for the workgroup (each wave polled its own words), and
+    // every wave is past its polls before any of them clears a shared word
+    timed_out = __syncthreads_or(timed_out ? 1 : 0) != 0;
   }
 
   // ---- normalise and store (heads 4qd+i, dims 16 (dt0 + d) + n) ----
@@ -687,6 +675,32 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
             timed_out ? __builtin_nanf("")
                       : (cl[i] > 0.0f ? (cm[i] + log2f(cl[i])) * 0.69314718055994531f : -INFINITY);
     }
+  }
+
+  // ---- the merger, after its output: return the partials it read to zero,
+  // so the workspace is left as found (all waves are past their polls: the
+  // barrier after the merge).  After a timeout nothing is cleared (a late
+  // partial could land after the clearing); the status word marks the
+  // workspace instead, for the host to read and to clear. ----
+  if (part.S > 1) {
+    const size_t ubase = (size_t)u * part.S;
+    if (timed_out) {
+      if (threadIdx.x == 0) *part.status = 1u;
+      return;
+    }
+#pragma unroll 1
+    for (int sp = 0; sp < part.S - 1; ++sp) {
+      f32x4* zo = reinterpret_cast<f32x4*>(part.o + (ubase + sp) * (kHeadsPad * kDim));
+#pragma unroll
+      for (int d = 0; d < DTW; ++d) zo[(dt0 + d) * 64 + lane] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (wave == 0 && n == 0) {
+        f32x4* zm = reinterpret_cast<f32x4*>(part.ml + (ubase + sp) * (kHeadsPad * 2));
+        zm[2 * qd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        zm[2 * qd + 1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    // every split has finished its selection: the scores row is free
+    if (SELECT && a.clear) clear_row(a, u, NW);
   }
 }
 
