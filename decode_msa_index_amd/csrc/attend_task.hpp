@@ -108,10 +108,12 @@ __device__ __forceinline__ float rescale(float x, float m) {
 // FP8 / NVFP4 cache, bf16 queries: MFMA tiles.
 //
 // Grid: (row, group) x S splits; a workgroup of NW waves takes a contiguous
-// share of the row's selection entries and wave w of it takes every NW-th
-// entry of that share.  With SELECT the workgroup first makes the group's
-// selection itself from the pooled scores (select_wave.hpp; every split
-// recomputes it, which costs no extra latency) and split 0 also stores it.
+// share of the row's selection entries (in ascending block order, so a
+// selection made here and a given one are attended alike) and wave w of it
+// takes every NW-th entry of that share.  With SELECT the workgroup first
+// makes the group's selection itself from the pooled scores
+// (select_wave.hpp; every split recomputes it, which costs no extra latency)
+// and split 0 also stores it.
 // For each block a wave computes S^T = K Q^T on MFMA, updates its running
 // max / denominator (online softmax, fp32) and accumulates P V on MFMA into
 // the rescaled running output.  The NW states then meet in LDS, where wave w
@@ -120,9 +122,9 @@ __device__ __forceinline__ float rescale(float x, float m) {
 // their combined states with device-scope stores and leave; split S-1 (the
 // highest workgroup id of the unit, so the other splits are already
 // dispatched when it runs) polls for those states -- each word is encoded so
-// that zero means "not yet written" -- merges them into its own and stores
-// the output.  The launch makes sure all workgroups of the grid can be
-// resident at once.
+// that zero means "not yet written" -- merges them into its own, stores the
+// output and then returns what it read to zero.  The launch makes sure all
+// workgroups of the grid can be resident at once.
 // Running state layout per lane l: max and denominator of head l%16; output
 // rows (heads) 4*(l/16)+i, columns (dims) 16*dt + l%16.
 // ---------------------------------------------------------------------------
