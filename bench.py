@@ -116,6 +116,9 @@ def main():
         log("bench.py runs on one GPU only: the library has no multi-GPU path; "
             "run with --gpus 1")
         sys.exit(2)
+    if args.share_corr and args.workload != "fp8_share64":
+        log("--share-corr applies to the fp8_share64 workload only")
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -139,9 +142,6 @@ def main():
     msa.lib()
     t0 = time.time()
     if args.share_corr:
-        if args.workload != "fp8_share64":
-            log("--share-corr applies to the fp8_share64 workload only")
-            sys.exit(2)
         w = synth.fp8_share64(share_corr=args.share_corr)
         w.recipe += f"; queries {args.share_corr} x the group's common draw"
     else:

@@ -64,3 +64,10 @@ def test_counter_traffic_is_reported_only_for_its_workload_and_sources(monkeypat
     assert bench.measured_traffic("nvfp4_512k") is None
     monkeypatch.setattr(bench, "scan_fingerprint", lambda: "0" * 16)
     assert bench.measured_traffic(t["workload"]) is None
+
+
+def test_share_correlation_applies_to_the_share_workload_only():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "fp8_256k",
+                        "--share-corr", "0.9"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "fp8_share64" in r.stderr and r.stdout == ""
