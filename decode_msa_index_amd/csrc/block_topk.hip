@@ -8,6 +8,12 @@
 // rest is the best of the free blocks c0 .. c1-1; ties go to the lower block
 // index, which makes the selection unique and deterministic.
 //
+// Few (row, group) units with long rows (decode batches: a few dozen rows of
+// thousands of blocks): one workgroup of four waves per unit runs the
+// selection the fused attention kernel runs (group_select), so that the
+// chip is not left with one busy wave per unit.  Many units (prefill chunks,
+// large batches) or short rows: one wavefront per unit (wave_select_keys).
+//
 // Rows of more than 16,000 blocks: one 256-thread workgroup per (row,
 // group).  The row's scores are read as order-preserving 32-bit keys; the
 // best free candidates are found
@@ -135,6 +141,52 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 
 constexpr int kWaveSelectMax = 16000;  // keys + histogram stay under 64 KB of LDS
 
+// One unit per workgroup of NW waves: the row's scores as order keys in LDS
+// (each thread also keeps the largest key of the free candidates it loaded),
+// then the workgroup selection of select_wave.hpp and the ascending store.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void block_topk_group_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
+    int K, int init, int local) {
+  extern __shared__ uint32_t lds[];  // [256] scratch, then [MB] keys
+  __shared__ GroupSelectLds<NW> gsl;
+  __shared__ int32_t sel_w[NW][32];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int u = blockIdx.x, row = u / G, b = row / R;
+  const float* s = scores + (size_t)u * MB;
+  uint32_t* keys = lds + 256;
+  const int pos = row_last_key(lens, qpos, row, b, MB);
+  const int rb = pos < 0 ? -1 : pos / kBlock;
+  const int c0 = init, c1 = rb + 1 - local;  // the free candidates
+  uint32_t tmax = 0u;
+  for (int base = 0; base < MB; base += 8 * 64 * NW) {
+    float v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = s[min(base + r * 64 * NW + (int)threadIdx.x, MB - 1)];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int jj = base + r * 64 * NW + (int)threadIdx.x;
+      if (jj < MB) {
+        const uint32_t k = order_key(v[r]);
+        keys[jj] = k;
+        if (jj >= c0 && jj < c1) tmax = max(tmax, k);
+      }
+    }
+  }
+  group_select<NW>(keys, rb, K, init, local, tmax, gsl, lds, sel_w[wave]);
+  if (wave == 0) {
+    const int v = sort_selection(lane < K ? sel_w[0][lane] : -1, K);
+    if (lane < K) topk[(size_t)u * K + lane] = v;
+  }
+}
+
+// The workgroup form pays where one wave per unit would leave most of the
+// chip idle on a long row.
+static bool use_group_select(const Shape& s) {
+  return s.MB >= 512 && s.MB <= 8064 && (long)s.rows * s.G < 512;
+}
+
 __global__ __launch_bounds__(64) void block_topk_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qpos, int32_t* __restrict__ topk, int R, int G, int MB,
@@ -153,7 +205,11 @@ __global__ __launch_bounds__(64) void block_topk_wave_kernel(
 
 hipError_t launch_block_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
                              const int32_t* q_pos, int32_t* topk, hipStream_t st) {
-  if (s.MB <= kWaveSelectMax) {
+  if (use_group_select(s)) {
+    hipLaunchKernelGGL(block_topk_group_kernel<4>, dim3(s.rows * s.G), dim3(256),
+                       sizeof(uint32_t) * (256 + s.MB), st, scores, seq_lens, q_pos, topk, s.R,
+                       s.G, s.MB, s.K, s.init, s.local);
+  } else if (s.MB <= kWaveSelectMax) {
     hipLaunchKernelGGL(block_topk_wave_kernel, dim3(s.rows * s.G), dim3(64),
                        sizeof(uint32_t) * (256 + s.MB), st, scores, seq_lens, q_pos, topk, s.R,
                        s.G, s.MB, s.K, s.init, s.local);

@@ -261,13 +261,19 @@ def test_speculative_rows_share_one_scan(kv, R, G, H):
     _run_and_check(w, fused=True, name=f"spec-r{R}-g{G}-{synth.DTYPE_NAMES[kv]}")
 
 
-@pytest.mark.parametrize("MB", [700, 17000])
-def test_block_topk_bit_exact_with_ties(MB):
+# (MB, B): the selection kernel's three forms -- one wave per unit (short
+# rows, or 512 and more units), a four-wave workgroup per unit (few units on
+# long rows), and the radix workgroup for rows too long for LDS
+TOPK_FORMS = [(300, 9), (700, 9), (700, 130), (17000, 9)]
+
+
+@pytest.mark.parametrize("MB,B", TOPK_FORMS)
+def test_block_topk_bit_exact_with_ties(MB, B):
     """Selection kernel alone, on oracle-independent scores with many exact
-    ties: identical to the oracle's selection.  MB = 17000 takes the
-    workgroup-wide path used for rows too long for LDS."""
+    ties: identical to the oracle's selection, in each of the kernel's
+    forms."""
     rng = np.random.default_rng(5)
-    B, G = 9, 4
+    G = 4
     lens = rng.integers(1, min(MB, 3000) * 128 + 1, B).astype(np.int32)
     lens[0], lens[1], lens[2] = min(MB, 3000) * 128, 1, 17 * 128
     scores = rng.integers(-6, 7, (B, G, MB)).astype(np.float32) * 0.25
@@ -292,14 +298,15 @@ def test_block_topk_bit_exact_with_ties(MB):
         assert np.array_equal(out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("MB", [700, 17000])
-def test_block_topk_forced_blocks_bit_exact(MB):
+@pytest.mark.parametrize("MB,B", [(mb, 2 * b) for mb, b in TOPK_FORMS])
+def test_block_topk_forced_blocks_bit_exact(MB, B):
     """Leading (init) and trailing (local) blocks always kept: the selection
     kernel alone matches the oracle exactly, for every top-k the attention
     accepts, forced sets that leave few or no free places, and the score
-    pattern that sends the wave-level selection down its radix path."""
+    pattern that sends the wave-level selection down its radix path, in each
+    of the kernel's forms."""
     rng = np.random.default_rng(6)
-    B, G = 8, 2
+    G = 2
     n = min(MB, 3000)
     lens = rng.integers(1, n * 128 + 1, B).astype(np.int32)
     lens[0], lens[1], lens[2], lens[3] = n * 128, 1, 9 * 128, 33 * 128 + 1
