@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--chain", action="store_true",
+                    help="also time the steps as the three-call chain (index scores, block "
+                         "top-k, sparse attend)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device (counter calibration) and exit")
     ap.add_argument("--calibrate-read", action="store_true",
@@ -201,6 +204,20 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t_g) * 1e3 / (reps * len(dws))
+
+    # ---- optional: the same steps as the three-call chain (msa_index_scores,
+    # msa_block_topk, msa_sparse_attend), eager ----
+    chain_ms = None
+    if args.chain:
+        for i in range(args.warmup):
+            dws[i % len(dws)].chain()
+        torch.cuda.synchronize()
+        t_c = time.perf_counter()
+        for i in range(args.steps):
+            dws[i % len(dws)].chain()
+        torch.cuda.synchronize()
+        chain_ms = (time.perf_counter() - t_c) * 1e3 / args.steps
+        log(f"[bench] three-call chain: {chain_ms:.4f} ms per step")
 
     # ---- timed region 3: the dominant kernel (index scan), launched back to
     # back between two HIP events on the launch stream (the average launch
@@ -323,6 +340,7 @@ def main():
         },
         "ms_per_step_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "ms_per_step_graph": graph_ms,
+        "ms_per_step_chain": chain_ms,
         "hbm_gbps_step": b_step / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": b_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "tokens_scanned_per_s": tokens / (ms_step * 1e-3),
