@@ -658,7 +658,7 @@ def run_prefill(args, w):
                    "context_tokens": int(w.seq_lens.sum()), "kv_groups": w.num_groups,
                    "q_heads": w.num_q_heads, "top_k": w.top_k},
         "kernel_us": {"index_contraction": idx_us,
-                      "select_attend_and_gaps": ms_step * 1e3 - idx_us},
+                      "topk_attend_and_gaps": ms_step * 1e3 - idx_us},
         "roofline": {"bound": "mfma", "kernel": "prefill_index_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.cpp", "static_scratch.cpp", "index_scores.hip", "block_topk.hip",
-           "sparse_attend.hip", "prefill_index.hip", "cache_write.hip"]
+           "sparse_attend.hip", "k2q_attend.hip", "prefill_index.hip", "cache_write.hip"]
 # the benchmark's read-bandwidth probe: a library of its own, not the product
 PROBE_SOURCES = ["read_probe.hip"]
 PROBE_LIB = os.path.join(HERE, "libmsa_probe.so")

@@ -1,0 +1,634 @@
+// k2q_attend.hip -- sparse attention of a chunk of many query rows, grouped
+// by key block.
+//
+// Method (vLLM blog "Day-0 support for MiniMax-M3.1-Flash", section "MSA
+// primer": every query head attends exactly its group's selected blocks; the
+// vLLM API reference of the MiniMax-M3 model, class MiniMaxM3Model: the
+// indexer's top-k buffer is token-major [tokens, index heads, top-k] and is
+// inverted by a key-to-query CSR builder, build_k2q_csr, before the sparse
+// prefill attention).
+//
+// A prefill chunk selects the same few hundred blocks of a sequence over and
+// over: 4,096 rows over 544 blocks request every (group, block) about 120
+// times.  Gathered per (row, group), that is 8.6 GB of K/V for 71 MB of
+// distinct blocks, each block dequantised again for every row.  Here the
+// selection is inverted instead, and every block is read and dequantised
+// once per chunk of up to kChunkRows rows that selected it:
+//   1. build:   workgroups over slices of a sequence's rows count the valid
+//               entries of topk_idx per (group, block) in LDS histograms and
+//               reserve their places in each block's bucket with one global
+//               atomic per block and slice; one workgroup per (sequence,
+//               group) scans the counts into bucket starts and a table of
+//               work chunks (up to kChunkRows entries of one block each);
+//               every entry then lands at its bucket start + place;
+//   2. attend:  one workgroup per chunk stages its block in LDS, K as bf16
+//               and V as f16 (both exact); each wave computes one entry at a
+//               time -- the entry's (up to 16) heads over that block: S^T =
+//               K Q^T and O = P V on MFMA, the block's softmax in fp32 --
+//               with the next entry's queries already in flight.  It stores
+//               a partial per entry: the normalised output O / l in f16 and
+//               (max, sum) in fp32;
+//   3. merge:   one wave per (row, group) takes the row's largest partial
+//               maximum M, then sums the partials weighted by
+//               l 2^(max - M) in selection order (fp32), scales by v_scale
+//               and stores the output and lse.
+// Which wave takes which entry depends on the order of atomics; the
+// arithmetic of an entry and the merge order do not, so the results are
+// deterministic.  They
+// differ from a per-row gather by the f16 rounding of each block's
+// normalised output (relative 2^-11), which the merge weights by at most 1.
+#include "attend_task.hpp"
+#include "device.hpp"
+#include "launch.hpp"
+
+#include <algorithm>
+
+namespace msa {
+
+constexpr int kChunkRows = 64;  // entries (rows) per work chunk
+constexpr int kK2qWaves = 8;    // waves per attend workgroup (two workgroups per CU)
+constexpr int kMergeWaves = 4;  // (row, group) units per merge workgroup
+constexpr int kScanThreads = 1024;
+constexpr int kCountThreads = 256;
+constexpr int kCountPairs = 16;  // entries per thread of a count workgroup
+constexpr size_t kPartialOBytes = (size_t)kHeadsPad * kDim * 2;   // f16 [4][64 lanes][8]
+constexpr size_t kPartialMlBytes = (size_t)kHeadsPad * 2 * 4;     // f32 [16 heads][max, sum]
+constexpr int kK2qMinRows = 64;
+constexpr int kK2qMaxBlocks = 8192;  // the count's LDS histogram of MB words
+
+// Buffers inside the workspace (after its status header).  Per (sequence,
+// group) bg: entries [bg * R * K, +R * K), chunks [bg * max_chunks, +max_chunks).
+struct K2qBufs {
+  int32_t* counts;    // [B*G][MB] entries per block
+  int32_t* starts;    // [B*G][MB] index of a block's first entry in `entries`
+  int32_t* place;     // [pairs] an entry's place in its bucket, -1: not attended
+  int32_t* entries;   // [B*G][R*K] entry ids (u * K + slot), grouped by block
+  int2* chunks;       // [B*G][max_chunks] (block, chunk within the block)
+  int32_t* nchunks;   // [B*G] chunks in use
+  float* ml;          // [pairs][16][2]: max (log2 domain) and sum of each head
+  uint4* o;           // [pairs][4][64] of 8 f16
+  int max_chunks;     // per (sequence, group)
+  int slices;         // count workgroups per (sequence, group)
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct K2qSizes {
+  long long bg, pairs, max_chunks;
+};
+static K2qSizes k2q_sizes(const Shape& s) {
+  K2qSizes z;
+  z.bg = (long long)(s.rows / s.R) * s.G;
+  z.pairs = (long long)s.rows * s.G * s.K;
+  const long long per = (long long)s.R * s.K;  // entries of one (sequence, group)
+  z.max_chunks = per / kChunkRows + std::min<long long>(s.MB, per) + 1;
+  return z;
+}
+
+// Offsets of the buffers from the start of the region; the region's size.
+static size_t k2q_layout(const Shape& s, size_t off[8]) {
+  const K2qSizes z = k2q_sizes(s);
+  const size_t sz[8] = {4 * (size_t)(z.bg * s.MB), 4 * (size_t)(z.bg * s.MB), 4 * (size_t)z.pairs,
+                        4 * (size_t)z.pairs, 8 * (size_t)(z.bg * z.max_chunks), 4 * (size_t)z.bg,
+                        kPartialMlBytes * z.pairs, kPartialOBytes * z.pairs};
+  size_t at = 0;
+  for (int i = 0; i < 8; ++i) {
+    off[i] = at;
+    at += align256(sz[i]);
+  }
+  return at;
+}
+
+// Many rows per sequence, an MFMA cache, block tables the build's LDS holds.
+bool k2q_eligible(const Shape& s) {
+  return (s.kv_dtype == kFP8 || s.kv_dtype == kNVFP4) && s.R >= kK2qMinRows &&
+         s.MB <= kK2qMaxBlocks;
+}
+
+size_t k2q_workspace_bytes(const Shape& s) {
+  size_t off[8];
+  return k2q_layout(s, off);
+}
+
+// The entries the per-row kernels attend: slot sidx below min(K, rb + 1)
+// holding a block 0 <= j <= rb whose table entry lies in [0, P).  Returns j,
+// or -1.
+__device__ __forceinline__ int k2q_entry(const AttendArgs& a, int row, int b, int u, int sidx) {
+  const int pos = row_last_key(a.lens, a.qpos, row, b, a.MB);
+  const int rb = pos < 0 ? -1 : pos / kBlock;
+  if (sidx >= min(a.K, rb + 1)) return -1;
+  const int j = a.topk[(size_t)u * a.K + sidx];
+  if (j < 0 || j > rb) return -1;
+  const int pb = a.bt[(size_t)b * a.MB + j];
+  return (pb >= 0 && pb < a.P) ? j : -1;
+}
+
+// ---- 1. build ---------------------------------------------------------------------
+__device__ __forceinline__ void scan_threads(uint32_t& e, uint32_t& c, uint32_t* sm) {
+  // exclusive scans of e and c over the workgroup: wave scans, then the
+  // wave totals
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t xe = e, xc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ye = __shfl_up(xe, o, 64), yc = __shfl_up(xc, o, 64);
+    if (lane >= o) {
+      xe += ye;
+      xc += yc;
+    }
+  }
+  if (lane == 63) {
+    sm[wave] = xe;
+    sm[16 + wave] = xc;
+  }
+  __syncthreads();
+  uint32_t be = 0, bc = 0;
+  for (int v = 0; v < wave; ++v) {
+    be += sm[v];
+    bc += sm[16 + v];
+  }
+  e = be + xe - e;
+  c = bc + xc - c;
+}
+
+// (sequence, group, slice of rows): LDS histogram per block, one global
+// atomic per block to reserve the slice's places, then each entry's place.
+__global__ __launch_bounds__(kCountThreads) void k2q_count_kernel(AttendArgs a, K2qBufs w) {
+  extern __shared__ int32_t hist[];  // [MB]
+  const int tid = threadIdx.x;
+  const int bg = blockIdx.x / w.slices, slice = blockIdx.x % w.slices;
+  const int b = bg / a.G, g = bg % a.G;
+  const int rows_per = (a.R + w.slices - 1) / w.slices;
+  const int r0 = slice * rows_per, r1 = min(a.R, r0 + rows_per);
+  const int n = max(0, r1 - r0) * a.K;  // <= kCountThreads * kCountPairs
+  for (int x = tid; x < a.MB; x += kCountThreads) hist[x] = 0;
+  __syncthreads();
+  int jj[kCountPairs], lp[kCountPairs];
+#pragma unroll
+  for (int k = 0; k < kCountPairs; ++k) {
+    const int i = tid + k * kCountThreads;
+    jj[k] = -1;
+    if (i < n) {
+      const int row = b * a.R + r0 + i / a.K, u = row * a.G + g;
+      jj[k] = k2q_entry(a, row, b, u, i % a.K);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kCountPairs; ++k) lp[k] = jj[k] >= 0 ? atomicAdd(&hist[jj[k]], 1) : -1;
+  __syncthreads();
+  for (int x = tid; x < a.MB; x += kCountThreads) {
+    const int c = hist[x];
+    if (c > 0) hist[x] = atomicAdd(&w.counts[(size_t)bg * a.MB + x], c);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kCountPairs; ++k) {
+    const int i = tid + k * kCountThreads;
+    if (i < n) {
+      const int row = b * a.R + r0 + i / a.K;
+      w.place[((size_t)row * a.G + g) * a.K + i % a.K] = jj[k] >= 0 ? hist[jj[k]] + lp[k] : -1;
+    }
+  }
+}
+
+// (sequence, group): bucket starts and the table of work chunks.
+__global__ __launch_bounds__(kScanThreads) void k2q_scan_kernel(AttendArgs a, K2qBufs w) {
+  __shared__ uint32_t sm[32];
+  const int tid = threadIdx.x, bg = blockIdx.x;
+  const int* cnt = w.counts + (size_t)bg * a.MB;
+  const int per = (a.MB + kScanThreads - 1) / kScanThreads;
+  const int x0 = min(a.MB, tid * per), x1 = min(a.MB, x0 + per);
+  uint32_t se = 0, sc = 0;
+  for (int x = x0; x < x1; ++x) {
+    se += (uint32_t)cnt[x];
+    sc += ((uint32_t)cnt[x] + kChunkRows - 1) / kChunkRows;
+  }
+  scan_threads(se, sc, sm);
+  const size_t ebase = (size_t)bg * a.R * a.K;
+  int2* chunks = w.chunks + (size_t)bg * w.max_chunks;
+  for (int x = x0; x < x1; ++x) {
+    const int n = cnt[x];
+    w.starts[(size_t)bg * a.MB + x] = (int)(ebase + se);
+    const int nch = (n + kChunkRows - 1) / kChunkRows;
+    for (int k = 0; k < nch; ++k) chunks[sc + k] = make_int2(x, k);
+    se += n;
+    sc += nch;
+  }
+  if (tid == kScanThreads - 1) w.nchunks[bg] = (int)sc;  // past every chunk
+}
+
+__global__ __launch_bounds__(256) void k2q_scatter_kernel(AttendArgs a, K2qBufs w, int pairs) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= pairs) return;
+  const int place = w.place[i];
+  if (place < 0) return;
+  const int u = i / a.K, row = u / a.G, g = u % a.G, b = row / a.R;
+  w.entries[w.starts[((size_t)b * a.G + g) * a.MB + a.topk[i]] + place] = i;
+}
+
+// ---- 2. attend ------------------------------------------------------------------
+// LDS: K as bf16 [key][16 chunks of 8 dims], V^T as f16 [dim][16 chunks of 8
+// key positions]; chunk c of row r sits at c ^ (r & 15), so that the 16
+// lanes of an MFMA operand read (16 rows, one chunk) hit 16 distinct
+// 16-byte bank groups.
+//
+// Operand layout (v_mfma_f32_16x16x32: A lane l holds A[l%16][8(l/16)+e],
+// B lane l holds B[8(l/16)+e][l%16], D lane l holds D[4(l/16)+i][l%16]).
+// S^T tile t holds keys 16t .. 16t+15 in natural order; in k-step c lane l
+// (n = l%16, qd = l/16) holds dims 32qd + 8c .. +7 of both K and Q (the
+// contraction order is free as long as the operands agree), and ends with
+// keys 16t + 4qd + i of head n.  Its P V operand
+// for key chunk c is the f16 of tiles 2c and 2c+1: contraction position
+// 32c + 8qd + e stands for key 32c + 16(e/4) + 4qd + e%4.  V^T is staged in
+// that position order: within each 32-key group, key 16a + 4q + i sits at
+// position 8q + 4a + i.
+__device__ __forceinline__ int k_slot(int key, int c) { return key * 16 + (c ^ (key & 15)); }
+__device__ __forceinline__ int v_slot(int d, int c) { return d * 16 + (c ^ (d & 15)); }
+
+// Four f16 values of keys t0 .. t0+3 (t0 % 4 == 0) of V^T row d.
+__device__ __forceinline__ void v_put4(uint4* v_lds, int d, int t0, uint2 val) {
+  const int r = t0 & 31;
+  const int c = 4 * (t0 >> 5) + ((r & 15) >> 2);
+  reinterpret_cast<uint2*>(v_lds)[2 * v_slot(d, c) + (r >> 4)] = val;
+}
+
+__device__ __forceinline__ uint2 f16x4_bits(f16x2 a, f16x2 b) {
+  return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+// Stages plane (pb, g) of K and of V into LDS: all 64 * NW threads.
+template <int KV, int NT>
+__device__ __forceinline__ void stage_block(const uint8_t* __restrict__ kvd,
+                                            const uint8_t* __restrict__ kvs, size_t kplane,
+                                            size_t vplane, uint4* k_lds, uint4* v_lds) {
+  const int tid = threadIdx.x;
+  if constexpr (KV == kFP8) {
+    const uint4* kb = reinterpret_cast<const uint4*>(kvd + kplane * (kBlock * kDim));
+    const uint4* vb = reinterpret_cast<const uint4*>(kvd + vplane * (kBlock * kDim));
+    constexpr int R = 1024 / NT;  // 16-byte pieces per thread and plane
+    uint4 kr[R], vr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      kr[r] = kb[tid + r * NT];
+      vr[r] = vb[tid + r * NT];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // K piece x: key x/8, dims 16 (x%8) .. +15 -> chunks 2(x%8), 2(x%8)+1
+      const int x = tid + r * NT, key = x >> 3, part = x & 7;
+      k_lds[k_slot(key, 2 * part)] = __builtin_bit_cast(uint4, fp8x8_bf16(kr[r].x, kr[r].y));
+      k_lds[k_slot(key, 2 * part + 1)] = __builtin_bit_cast(uint4, fp8x8_bf16(kr[r].z, kr[r].w));
+      // V^T piece x: dim x/8, keys 16 (x%8) .. +15
+      const int d = x >> 3, t0 = 16 * (x & 7);
+      const uint32_t wv[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v_put4(v_lds, d, t0 + 4 * q,
+               f16x4_bits(fp8x2_to_f16x2<false>(wv[q]), fp8x2_to_f16x2<true>(wv[q])));
+    }
+  } else {
+    // NVFP4: data [t][64 B] (K) and [d][64 B] (V^T, keys as nibbles, low
+    // nibble first); e4m3 scales K [t][d/16], V [d/16][t]
+    const uint4* kb = reinterpret_cast<const uint4*>(kvd + kplane * (kBlock * kDim / 2));
+    const uint4* vb = reinterpret_cast<const uint4*>(kvd + vplane * (kBlock * kDim / 2));
+    const uint8_t* ks = kvs + kplane * (kBlock * kDim / 16);
+    const uint8_t* vs = kvs + vplane * (kBlock * kDim / 16);
+    constexpr int R = 512 / NT;
+    uint4 kr[R], vr[R], vsc[R][2];
+    uint32_t ksc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int x = tid + r * NT;
+      kr[r] = kb[x];
+      vr[r] = vb[x];
+      // K piece x: key x/4, dims 32 (x%4) .. +31: scales 2 (x%4), +1 of the key
+      ksc[r] = *reinterpret_cast<const uint16_t*>(ks + (x >> 2) * (kDim / 16) + 2 * (x & 3));
+      // V piece x: dim x/4, keys 32 (x%4) .. +31: 32 scale bytes of row d/16
+      const uint4* sp = reinterpret_cast<const uint4*>(vs + ((x >> 2) >> 4) * kBlock + 32 * (x & 3));
+      vsc[r][0] = sp[0];
+      vsc[r][1] = sp[1];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int x = tid + r * NT;
+      const int key = x >> 2, part = x & 3;
+      const f32x2 sc = fp8x2_to_f32x2<false>(ksc[r]);
+      const uint32_t wk[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        k_lds[k_slot(key, 4 * part + c)] = __builtin_bit_cast(uint4, nvfp4x8_bf16(wk[c], sc[c >> 1]));
+      const int d = x >> 2, t0 = 32 * part;
+      const uint32_t wv[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+      const uint32_t sb[8] = {vsc[r][0].x, vsc[r][0].y, vsc[r][0].z, vsc[r][0].w,
+                              vsc[r][1].x, vsc[r][1].y, vsc[r][1].z, vsc[r][1].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // keys t0 + 8m .. +7 with scale bytes 8m .. 8m+7
+        const f16x8 h = nvfp4x8_f16(wv[m], sb[2 * m], sb[2 * m + 1]);
+        const uint4 hb = __builtin_bit_cast(uint4, h);
+        v_put4(v_lds, d, t0 + 8 * m, make_uint2(hb.x, hb.y));
+        v_put4(v_lds, d, t0 + 8 * m + 4, make_uint2(hb.z, hb.w));
+      }
+    }
+  }
+}
+
+
+// The B operand of S^T = K Q^T: head n of the group, dims 32qd + 8c .. +7.
+// Lanes past the group's heads load its last head instead (their results
+// are never used); the loads are unconditional, so that a wait for them is
+// counted exactly.
+__device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, const AttendArgs& a,
+                                       int row, int g, int n, int qd, bf16x8 (&qo)[4]) {
+  const uint4* qp = reinterpret_cast<const uint4*>(
+      q + ((size_t)row * a.H + (size_t)g * a.hpg + min(n, a.hpg - 1)) * kDim + qd * 32);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qo[c] = __builtin_bit_cast(bf16x8, qp[c]);
+}
+
+// Both operands come from LDS for every entry: held in registers across
+// entries, the block's K operands alone (128 registers) would cut the waves
+// per SIMD from four to one.
+template <int KV>
+__global__ __launch_bounds__(64 * kK2qWaves) void k2q_attend_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvd,
+    const uint8_t* __restrict__ kvs, AttendArgs a, K2qBufs w) {
+  constexpr int NW = kK2qWaves;
+  __shared__ uint4 k_lds[kBlock * 16];
+  __shared__ uint4 v_lds[kDim * 16];
+  const int bg = blockIdx.x / w.max_chunks, c = blockIdx.x % w.max_chunks;
+  if (c >= w.nchunks[bg]) return;
+  const int2 ch = w.chunks[(size_t)bg * w.max_chunks + c];
+  const int j = ch.x, g = bg % a.G, b = bg / a.G;
+  const int pb = a.bt[(size_t)b * a.MB + j];  // in [0, P): the count checked it
+  const int s0 = w.starts[(size_t)bg * a.MB + j];
+  const int e0 = s0 + ch.y * kChunkRows;
+  const int e1 = min(s0 + w.counts[(size_t)bg * a.MB + j], e0 + kChunkRows);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n = lane & 15, qd = lane >> 4;
+  // the wave's entries e0 + wave + NW i, lane i holding entry i's id and
+  // last visible key (loaded while the block is staged)
+  const int cnt = (e1 - e0 - wave + NW - 1) / NW;
+  int my_pair = 0, my_pos = 0;
+  if (lane < cnt) {
+    my_pair = w.entries[e0 + wave + NW * lane];
+    my_pos = row_last_key(a.lens, a.qpos, my_pair / a.K / a.G, b, a.MB);
+  }
+  stage_block<KV, 64 * NW>(kvd, kvs, ((size_t)pb * 2 + 0) * a.G + g,
+                           ((size_t)pb * 2 + 1) * a.G + g, k_lds, v_lds);
+  __syncthreads();
+  const float cs = a.scale_log2;
+  // one entry: entry `it` of the wave, its queries in qop
+  auto attend_entry = [&](int it, const bf16x8 (&qop)[4]) {
+    // the staged operands are read from LDS again for every entry (kept in
+    // registers across entries they would take the whole register file)
+    asm volatile("" ::: "memory");
+    const int pair = __shfl(my_pair, it, 64);
+    const int nvalid = min(kBlock, __shfl(my_pos, it, 64) - j * kBlock + 1);  // >= 1
+    // ---- S^T = K Q^T ----
+    f32x4 sacc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      sacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        sacc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, k_lds[k_slot(16 * t + n, 4 * qd + cc)]),
+                            qop[cc], sacc[t]);
+    }
+    // ---- the block's softmax (head n lives in lanes n, n+16, n+32, n+48):
+    // the maximum of the raw dot products, then 2^(s c - m c) with one fma
+    // per weight (c > 0 keeps the maximum where it is) ----
+    float mraw = -INFINITY;
+    if (nvalid == kBlock) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        mraw = fmaxf(mraw, fmaxf(fmaxf(sacc[t][0], sacc[t][1]), fmaxf(sacc[t][2], sacc[t][3])));
+    } else {  // the row's own recent block: keys past its position are masked
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = 16 * t + 4 * qd + i < nvalid ? sacc[t][i] : -INFINITY;
+          sacc[t][i] = v;
+          mraw = fmaxf(mraw, v);
+        }
+      }
+    }
+    mraw = fmaxf(mraw, shfl_xor(mraw, 16));
+    mraw = fmaxf(mraw, shfl_xor(mraw, 32));
+    const float mc = mraw * cs;  // the block's maximum, log2 domain
+    float lsum = 0.0f;
+    f16x8 pop[4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2_weight(fmaf(sacc[t][i], cs, -mc));
+        lsum += p;
+        pop[t >> 1][4 * (t & 1) + i] = (_Float16)p;
+      }
+    }
+    lsum += shfl_xor(lsum, 16);
+    lsum += shfl_xor(lsum, 32);
+    // ---- O = P V, two 16-dim tiles at a time ----
+    f32x4 oacc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      if ((dt & 1) == 0) asm volatile("" ::: "memory");
+      oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        oacc[dt] = mfma_f16(pop[cc], __builtin_bit_cast(f16x8, v_lds[v_slot(16 * dt + n, 4 * cc + qd)]),
+                            oacc[dt]);
+    }
+    // ---- the partial: O / l of heads 4qd+i, dims 16 dt + n, lane-major ----
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) inv[i] = __builtin_amdgcn_rcpf(__shfl(lsum, 4 * qd + i, 64));
+    uint4* po = w.o + (size_t)pair * 256;
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      f16x8 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = (_Float16)(oacc[2 * p2][i] * inv[i]);
+        h[4 + i] = (_Float16)(oacc[2 * p2 + 1][i] * inv[i]);
+      }
+      // streaming stores: the partials are read once, by the merge, and
+      // should not push the queries out of the caches
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, h),
+                                  reinterpret_cast<u32x4_t*>(po + p2 * 64 + lane));
+    }
+    if (lane < 16)
+      __builtin_nontemporal_store(f32x2{mc, lsum},
+                                  reinterpret_cast<f32x2*>(w.ml + (size_t)pair * (kHeadsPad * 2)) + lane);
+  };
+  // two query buffers: entry it + 1's queries load while entry it is computed
+  auto q_of = [&](int it, bf16x8 (&qo)[4]) {
+    load_q(q, a, __shfl(my_pair, min(it, cnt - 1), 64) / a.K / a.G, g, n, qd, qo);
+  };
+  bf16x8 qa[4], qb[4];
+  if (cnt > 0) q_of(0, qa);
+  for (int it = 0; it < cnt; it += 2) {
+    q_of(it + 1, qb);
+    attend_entry(it, qa);
+    if (it + 1 >= cnt) break;
+    q_of(it + 2, qa);
+    attend_entry(it + 1, qb);
+  }
+}
+
+// ---- 3. merge -------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kMergeWaves) void k2q_merge_kernel(AttendArgs a, K2qBufs w,
+                                                                    int units) {
+  __shared__ float ob[kMergeWaves][kHeadsPad][kDim + 4];
+  __shared__ float4 mls[kMergeWaves][32 * 8];  // the unit's (max, sum) records
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int u = blockIdx.x * kMergeWaves + wave;
+  if (u >= units) return;
+  const int row = u / a.G, g = u % a.G;
+  const int n = lane & 15, qd = lane >> 4;
+  const uint64_t valid =
+      __ballot(lane < a.K && w.place[(size_t)u * a.K + min(lane, a.K - 1)] >= 0);
+  // the unit's K (max, sum) records, 128 bytes each, into LDS in one round
+  {
+    const float4* src = reinterpret_cast<const float4*>(w.ml + (size_t)u * a.K * (kHeadsPad * 2));
+    float4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = src[min(lane + 64 * k, 8 * a.K - 1)];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lane + 64 * k < 8 * a.K) mls[wave][lane + 64 * k] = r[k];
+    wave_lds_sync();
+  }
+  // (max, sum) of heads 4qd .. 4qd+3 in partial s: 32 bytes at 32 qd
+  auto ml_of = [&](int s, float (&m)[4], float (&l)[4]) {
+    const float4 x = mls[wave][8 * s + 2 * qd], y = mls[wave][8 * s + 2 * qd + 1];
+    m[0] = x.x; l[0] = x.y; m[1] = x.z; l[1] = x.w;
+    m[2] = y.x; l[2] = y.y; m[3] = y.z; l[3] = y.w;
+  };
+  // pass 1: the largest partial maximum of each head
+  float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int s = 0; s < a.K; ++s) {
+    if ((valid >> s) & 1) {
+      float m[4], l[4];
+      ml_of(s, m, l);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], m[i]);
+    }
+  }
+  // pass 2: sum of the partials weighted by l 2^(max - M), ascending slots
+  float L[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 co[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) co[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int BATCH = 4;
+  for (int s0 = 0; s0 < a.K; s0 += BATCH) {
+    uint4 po[BATCH][4];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int s = s0 + k;
+      if (s < a.K && ((valid >> s) & 1)) {
+        const uint4* src = w.o + ((size_t)u * a.K + s) * 256;
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) po[k][p2] = src[p2 * 64 + lane];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int s = s0 + k;
+      if (s < a.K && ((valid >> s) & 1)) {
+        float m[4], l[4], wt[4];
+        ml_of(s, m, l);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wt[i] = l[i] * exp2f(m[i] - M[i]);
+          L[i] += wt[i];
+        }
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const f16x8 h = __builtin_bit_cast(f16x8, po[k][p2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            co[2 * p2][i] = fmaf((float)h[i], wt[i], co[2 * p2][i]);
+            co[2 * p2 + 1][i] = fmaf((float)h[4 + i], wt[i], co[2 * p2 + 1][i]);
+          }
+        }
+      }
+    }
+  }
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) inv[i] = L[i] > 0.0f ? a.v_scale / L[i] : 0.0f;
+  // heads 4qd+i, dims 16 dt + n -> 8 consecutive dims of one head per lane
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) ob[wave][4 * qd + i][dt * 16 + n] = co[dt][i] * inv[i];
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int c0 = 0; c0 < kHeadsPad * 16; c0 += 64) {
+    const int cidx = c0 + lane, h = cidx >> 4, d0 = (cidx & 15) * 8;
+    if (h < a.hpg) {
+      const float4 lo = *reinterpret_cast<const float4*>(&ob[wave][h][d0]);
+      const float4 hi = *reinterpret_cast<const float4*>(&ob[wave][h][d0 + 4]);
+      const float o[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      store_out8(a, row, g * a.hpg + h, d0, o);
+    }
+  }
+  if (a.lse && n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * qd + i;
+      if (h < a.hpg)
+        a.lse[(size_t)row * a.H + (size_t)g * a.hpg + h] =
+            L[i] > 0.0f ? (M[i] + log2f(L[i])) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+}
+
+// ---- launch ----------------------------------------------------------------------
+
+hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
+                             const void* kv_data, const void* kv_scales, void* region,
+                             hipStream_t st) {
+  size_t off[8];
+  k2q_layout(s, off);
+  const K2qSizes z = k2q_sizes(s);
+  if (z.pairs == 0) return hipSuccess;
+  char* base = static_cast<char*>(region);
+  K2qBufs w;
+  w.counts = reinterpret_cast<int32_t*>(base + off[0]);
+  w.starts = reinterpret_cast<int32_t*>(base + off[1]);
+  w.place = reinterpret_cast<int32_t*>(base + off[2]);
+  w.entries = reinterpret_cast<int32_t*>(base + off[3]);
+  w.chunks = reinterpret_cast<int2*>(base + off[4]);
+  w.nchunks = reinterpret_cast<int32_t*>(base + off[5]);
+  w.ml = reinterpret_cast<float*>(base + off[6]);
+  w.o = reinterpret_cast<uint4*>(base + off[7]);
+  w.max_chunks = (int)z.max_chunks;
+  const int rows_per = std::max(1, kCountThreads * kCountPairs / s.K);
+  w.slices = (s.R + rows_per - 1) / rows_per;
+  hipError_t e = launch_zero_fill(w.counts, 4 * (size_t)(z.bg * s.MB), st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2q_count_kernel, dim3((unsigned)(z.bg * w.slices)), dim3(kCountThreads),
+                     sizeof(int32_t) * (size_t)s.MB, st, a, w);
+  hipLaunchKernelGGL(k2q_scan_kernel, dim3((unsigned)z.bg), dim3(kScanThreads), 0, st, a, w);
+  hipLaunchKernelGGL(k2q_scatter_kernel, dim3((unsigned)((z.pairs + 255) / 256)), dim3(256), 0, st,
+                     a, w, (int)z.pairs);
+  const dim3 agrid((unsigned)(z.bg * z.max_chunks));
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const uint8_t* kd = static_cast<const uint8_t*>(kv_data);
+  const uint8_t* ks = static_cast<const uint8_t*>(kv_scales);
+  if (s.kv_dtype == kFP8)
+    hipLaunchKernelGGL(k2q_attend_kernel<kFP8>, agrid, dim3(64 * kK2qWaves), 0, st, qp, kd, ks, a, w);
+  else
+    hipLaunchKernelGGL(k2q_attend_kernel<kNVFP4>, agrid, dim3(64 * kK2qWaves), 0, st, qp, kd, ks, a, w);
+  const int units = s.rows * s.G;
+  hipLaunchKernelGGL(k2q_merge_kernel, dim3((unsigned)((units + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(64 * kMergeWaves), 0, st, a, w, units);
+  return hipGetLastError();
+}
+
+}  // namespace msa

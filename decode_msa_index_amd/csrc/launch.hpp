@@ -77,6 +77,15 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
                                 void* workspace, uint32_t* status, float* clear_scores,
                                 hipStream_t st);
+// Chunks of many rows per sequence (chunked prefill): the attention grouped
+// by key block (k2q_attend.hip).  launch_sparse_attend takes this path when
+// k2q_eligible; its workspace after the status header is the path's own.
+struct AttendArgs;
+bool k2q_eligible(const Shape& s);
+size_t k2q_workspace_bytes(const Shape& s);
+hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
+                             const void* kv_data, const void* kv_scales, void* region,
+                             hipStream_t st);
 // Quantises new tokens' K, V and index keys into their cache slots
 // (cache_write.hip).
 hipError_t launch_cache_write(const Shape& s, int num_tokens, const int32_t* token_seq,

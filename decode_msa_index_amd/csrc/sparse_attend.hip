@@ -165,8 +165,10 @@ AttendConfig attend_config(const Shape& s) {
   return c;
 }
 
-// [ml: units*S*16*2][o: units*S*16*128] floats
+// [ml: units*S*16*2][o: units*S*16*128] floats; the key-block path's own
+// buffers for chunked prefill
 size_t attend_workspace_bytes(const Shape& s, const AttendConfig& c) {
+  if (k2q_eligible(s)) return k2q_workspace_bytes(s);
   if (c.splits <= 1) return 0;
   const size_t units = (size_t)s.rows * s.G;
   return sizeof(float) * units * c.splits * kHeadsPad * (kDim + 2);
@@ -183,7 +185,7 @@ static size_t select_static_lds(int nw) {
 // The fused kernel needs the row's keys in LDS: block tables whose rows fit
 // in 64 KB of dynamic LDS, with the whole workgroup inside gfx950's 160 KB.
 bool select_fusable(const Shape& s) {
-  if (s.kv_dtype == kF32) return false;
+  if (s.kv_dtype == kF32 || k2q_eligible(s)) return false;
   const size_t dyn = select_dyn_lds(s);
   return dyn <= 65536 && dyn + select_static_lds(attend_config(s).nw) <= 160 * 1024;
 }
@@ -285,6 +287,8 @@ hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_da
                        (const float*)kv_data, (int)(s.q_dtype == kBF16), a);
     return hipGetLastError();
   }
+  if (k2q_eligible(s))
+    return launch_k2q_attend(s, a, q, kv_data, kv_scales, static_cast<char*>(workspace) + kStatusBytes, st);
   uint32_t* status = static_cast<uint32_t*>(workspace);
   return launch_mfma<false>(s, attend_config(s), a, q, kv_data, kv_scales,
                             static_cast<char*>(workspace) + kStatusBytes, status, true, st);

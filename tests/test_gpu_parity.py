@@ -859,6 +859,99 @@ def test_prefill_scattered_positions(kv):
     _run_and_check(w, fused=True, name=f"prefill-scatter-{synth.DTYPE_NAMES[kv]}")
 
 
+# ---------------------------------------------------------------------------
+# chunked prefill (64+ rows per sequence): the attention grouped by key block
+# ---------------------------------------------------------------------------
+
+SCATTER_QP = [-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 2900,
+              2998, 2999, 5000, 40, 300, 1700, 3, 64, 2222, 2500]
+
+
+@pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
+def test_key_block_attention_edge_cases(kv):
+    """Two sequences of 72 rows: one at scattered positions (rows that see no
+    key or one key, block edges, positions past the end), one causal at its
+    end; an out-of-pool table entry in each sequence, one of them the recent
+    block of some rows.  Through msa_decode and the chain, then
+    msa_sparse_attend on a given selection with malformed entries (-1, past
+    the row's recent block, a duplicate, attended twice as by the oracle):
+    outputs and lse against the oracle."""
+    R = 72
+    lens = np.array([3000, 4100])
+    qp = np.concatenate([np.array((SCATTER_QP * 3)[:R]),
+                         np.arange(lens[1] - R, lens[1])]).astype(np.int32)
+    base = synth.make(f"k2q-edge-{kv}", seed=211 + kv, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                      q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2)
+    bt = base.block_table.copy()
+    bt[0, 5] = -1
+    bt[1, 31] = base.num_phys_blocks  # the recent block of sequence 1's rows 4000 .. 4095
+    w = dataclasses.replace(base, block_table=bt)
+    tag = synth.DTYPE_NAMES[kv]
+    _run_and_check(w, fused=True, name=f"k2q-edge-{tag}")
+    dw, _ = _run_and_check(w, fused=False, name=f"k2q-edge-{tag}-chain")
+    # a given selection with malformed entries, inside each row's first
+    # min(K, rb + 1) slots (the entries the kernels read)
+    k_given = dw.topk.cpu().numpy().copy()
+    for r in range(w.rows):
+        rb = parity.row_pos(w, r) // w.block_size
+        if rb >= 3:
+            k_given[r, 0, 1] = -1
+            if w.max_blocks - 1 > rb:  # a block the row does not see, inside the table
+                k_given[r, 1, 0] = w.max_blocks - 1
+            k_given[r, 2, 1] = k_given[r, 2, 0]
+    import oracle
+    o_ref, l_ref = oracle.sparse_attend(parity.oracle_problem(w), w.q, w.kv_data, w.kv_scales,
+                                        w.block_table, w.seq_lens,
+                                        np.ascontiguousarray(k_given, np.int32), w.q_pos)
+    say(f"[parity] k2q-edge-{tag}: sparse_attend on a malformed given selection")
+    dw.sparse_attend(topk=parity.dev(k_given))
+    torch.cuda.synchronize()
+    parity.check_attention(w, dw.out.float().cpu().numpy(), o_ref)
+    lse = dw.lse.cpu().numpy()
+    assert np.array_equal(np.isinf(lse), np.isinf(l_ref))
+    fin = np.isfinite(l_ref)
+    np.testing.assert_allclose(lse[fin], l_ref[fin], rtol=0, atol=2e-3)
+
+
+def test_key_block_attention_many_chunks_per_block():
+    """200 causal rows with the first block forced for every row: bucket 0
+    of each group holds 200 entries, four work chunks; local_blocks = 2.
+    Through msa_decode and the chain."""
+    R = 200
+    lens = np.array([20000])
+    qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
+    base = synth.make("k2q-chunks", seed=233, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                      q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3)
+    w = dataclasses.replace(base, init_blocks=1, local_blocks=2)
+    dw, _ = _run_and_check(w, fused=True, name="k2q-chunks")
+    assert np.all(dw.topk.cpu().numpy()[:, :, 0] == 0)
+    _run_and_check(w, fused=False, name="k2q-chunks-chain")
+
+
+def test_key_block_attention_is_deterministic_and_equals_the_chain():
+    """Which wave attends which entry follows the order of atomics; the
+    results do not: repeated msa_decode calls and the three-call chain give
+    bit-identical outputs and lse."""
+    R = 96
+    lens = np.array([9000, 6100])
+    qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
+    w = synth.make("k2q-det", seed=47, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                   q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3)
+    dw = parity.DeviceWorkload(w)
+    say("[parity] k2q: chain vs decode vs decode")
+    dw.chain()
+    torch.cuda.synchronize()
+    ref = (dw.out.view(torch.uint8).clone(), dw.lse.clone(), dw.topk.clone())
+    for _ in range(2):
+        dw.out.zero_()
+        dw.lse.zero_()
+        dw.decode()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.topk, ref[2])
+        assert torch.equal(dw.out.view(torch.uint8), ref[0])
+        assert torch.equal(dw.lse, ref[1])
+
+
 @pytest.mark.parametrize("name", ["prefill_64k", "prefill_64k_nvfp4"])
 def test_prefill_64k_sampled_rows(name):
     """The full chunked-prefill shape (65536 cached + 4096 queries, causal),
