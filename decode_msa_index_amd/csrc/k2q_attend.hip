@@ -27,11 +27,13 @@
 //               K Q^T and O = P V on MFMA, the block's softmax in fp32 --
 //               with the next entry's queries already in flight.  It stores
 //               a partial per entry: the normalised output O / l in f16 and
-//               (max, sum) in fp32;
-//   3. merge:   one wave per (row, group) takes the row's largest partial
-//               maximum M, then sums the partials weighted by
+//               (max, sum) in fp32, the sum l being that of the f16 weights
+//               the P V product uses (a ninth MFMA tile against ones);
+//   3. merge:   one workgroup per (row, group) takes the row's largest
+//               partial maximum M, then sums the partials weighted by
 //               l 2^(max - M) in selection order (fp32), scales by v_scale
-//               and stores the output and lse.
+//               and stores the output and lse; each wave a quarter of the
+//               dims, with all of its loads in flight at once.
 // Which wave takes which entry depends on the order of atomics; the
 // arithmetic of an entry and the merge order do not, so the results are
 // deterministic.  They
@@ -46,14 +48,20 @@
 namespace msa {
 
 constexpr int kChunkRows = 64;  // entries (rows) per work chunk
-constexpr int kK2qWaves = 8;    // waves per attend workgroup (two workgroups per CU)
-constexpr int kMergeWaves = 4;  // (row, group) units per merge workgroup
+// Entries a wave attends at once (each operand read from LDS feeds that many
+// MFMAs).  Two measured no faster on the 4,096-row chunk: the kernel is bound
+// by its HBM traffic, not by LDS.
+constexpr int kK2qEntries = 1;
 constexpr int kScanThreads = 1024;
 constexpr int kCountThreads = 256;
 constexpr int kCountPairs = 16;  // entries per thread of a count workgroup
 constexpr size_t kPartialOBytes = (size_t)kHeadsPad * kDim * 2;   // f16 [4][64 lanes][8]
 constexpr size_t kPartialMlBytes = (size_t)kHeadsPad * 2 * 4;     // f32 [16 heads][max, sum]
-constexpr int kK2qMinRows = 64;
+// Rows per sequence from which the grouping pays: measured on a 65,536-token
+// context (G = 4, top-16) against the per-(row, group) kernel, 0.177 against
+// 0.191 ms per step at 384 rows and 1.05 against 1.36 ms at 4,096 rows; at
+// 256 rows and fewer the fixed cost of the extra launches dominates.
+constexpr int kK2qMinRows = 384;
 constexpr int kK2qMaxBlocks = 8192;  // the count's LDS histogram of MB words
 
 // Buffers inside the workspace (after its status header).  Per (sequence,
@@ -65,7 +73,7 @@ struct K2qBufs {
   int32_t* entries;   // [B*G][R*K] entry ids (u * K + slot), grouped by block
   int2* chunks;       // [B*G][max_chunks] (block, chunk within the block)
   int32_t* nchunks;   // [B*G] chunks in use
-  float* ml;          // [pairs][16][2]: max (log2 domain) and sum of each head
+  float* ml;          // [pairs][2][16]: the 16 heads' maxima (log2 domain), then sums
   uint4* o;           // [pairs][4][64] of 8 f16
   int max_chunks;     // per (sequence, group)
   int slices;         // count workgroups per (sequence, group)
@@ -334,6 +342,10 @@ __device__ __forceinline__ void stage_block(const uint8_t* __restrict__ kvd,
 }
 
 
+__device__ __forceinline__ f16x8 ones_f16x8() {
+  return __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+}
+
 // The B operand of S^T = K Q^T: head n of the group, dims 32qd + 8c .. +7.
 // Lanes past the group's heads load its last head instead (their results
 // are never used); the loads are unconditional, so that a wait for them is
@@ -346,14 +358,22 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, const Att
   for (int c = 0; c < 4; ++c) qo[c] = __builtin_bit_cast(bf16x8, qp[c]);
 }
 
-// Both operands come from LDS for every entry: held in registers across
-// entries, the block's K operands alone (128 registers) would cut the waves
-// per SIMD from four to one.
-template <int KV>
-__global__ __launch_bounds__(64 * kK2qWaves) void k2q_attend_kernel(
+// Both operands come from LDS for every group of entries: held in registers
+// across entries, the block's K operands alone (128 registers) would cut the
+// waves per SIMD to one.  A wave takes E entries at a time, so that every
+// operand read from LDS feeds E MFMAs.
+template <int E>
+struct K2qShape {
+  static constexpr int waves = E == 1 ? 8 : 4;  // per workgroup; two workgroups per CU (LDS)
+  static constexpr int waves_per_simd = E == 1 ? 4 : 2;
+};
+
+template <int KV, int E>
+__global__ __launch_bounds__(64 * K2qShape<E>::waves)
+__attribute__((amdgpu_waves_per_eu(K2qShape<E>::waves_per_simd))) void k2q_attend_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvd,
     const uint8_t* __restrict__ kvs, AttendArgs a, K2qBufs w) {
-  constexpr int NW = kK2qWaves;
+  constexpr int NW = K2qShape<E>::waves;
   __shared__ uint4 k_lds[kBlock * 16];
   __shared__ uint4 v_lds[kDim * 16];
   const int bg = blockIdx.x / w.max_chunks, c = blockIdx.x % w.max_chunks;
@@ -378,206 +398,206 @@ __global__ __launch_bounds__(64 * kK2qWaves) void k2q_attend_kernel(
                            ((size_t)pb * 2 + 1) * a.G + g, k_lds, v_lds);
   __syncthreads();
   const float cs = a.scale_log2;
-  // one entry: entry `it` of the wave, its queries in qop
-  auto attend_entry = [&](int it, const bf16x8 (&qop)[4]) {
-    // the staged operands are read from LDS again for every entry (kept in
-    // registers across entries they would take the whole register file)
+  // entries it0 .. it0+E-1 of the wave (past the last: repeats of it, not
+  // stored), their queries in qop
+  auto attend_group = [&](int it0, const bf16x8 (&qop)[E][4]) {
+    // the staged operands are read from LDS again for every group
     asm volatile("" ::: "memory");
-    const int pair = __shfl(my_pair, it, 64);
-    const int nvalid = min(kBlock, __shfl(my_pos, it, 64) - j * kBlock + 1);  // >= 1
+    int pair[E], nvalid[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int ii = min(it0 + e, cnt - 1);
+      pair[e] = __shfl(my_pair, ii, 64);
+      nvalid[e] = min(kBlock, __shfl(my_pos, ii, 64) - j * kBlock + 1);  // >= 1
+    }
     // ---- S^T = K Q^T ----
-    f32x4 sacc[8];
+    f32x4 sacc[E][8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      sacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        sacc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, k_lds[k_slot(16 * t + n, 4 * qd + cc)]),
-                            qop[cc], sacc[t]);
+      for (int e = 0; e < E; ++e) sacc[e][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const bf16x8 kk = __builtin_bit_cast(bf16x8, k_lds[k_slot(16 * t + n, 4 * qd + cc)]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) sacc[e][t] = mfma_bf16(kk, qop[e][cc], sacc[e][t]);
+      }
     }
-    // ---- the block's softmax (head n lives in lanes n, n+16, n+32, n+48):
+    // ---- each block softmax (head n lives in lanes n, n+16, n+32, n+48):
     // the maximum of the raw dot products, then 2^(s c - m c) with one fma
     // per weight (c > 0 keeps the maximum where it is) ----
-    float mraw = -INFINITY;
-    if (nvalid == kBlock) {
+    f16x8 pop[E][4];
+    float mc[E];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        mraw = fmaxf(mraw, fmaxf(fmaxf(sacc[t][0], sacc[t][1]), fmaxf(sacc[t][2], sacc[t][3])));
-    } else {  // the row's own recent block: keys past its position are masked
+    for (int e = 0; e < E; ++e) {
+      float mraw = -INFINITY;
+      if (nvalid[e] == kBlock) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          mraw = fmaxf(mraw, fmaxf(fmaxf(sacc[e][t][0], sacc[e][t][1]),
+                                   fmaxf(sacc[e][t][2], sacc[e][t][3])));
+      } else {  // the row's own recent block: keys past its position are masked
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = 16 * t + 4 * qd + i < nvalid[e] ? sacc[e][t][i] : -INFINITY;
+            sacc[e][t][i] = v;
+            mraw = fmaxf(mraw, v);
+          }
+        }
+      }
+      mraw = fmaxf(mraw, shfl_xor(mraw, 16));
+      mraw = fmaxf(mraw, shfl_xor(mraw, 32));
+      mc[e] = mraw * cs;  // the block's maximum, log2 domain
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = 16 * t + 4 * qd + i < nvalid ? sacc[t][i] : -INFINITY;
-          sacc[t][i] = v;
-          mraw = fmaxf(mraw, v);
-        }
+        for (int i = 0; i < 4; ++i)
+          pop[e][t >> 1][4 * (t & 1) + i] = (_Float16)exp2_weight(fmaf(sacc[e][t][i], cs, -mc[e]));
       }
     }
-    mraw = fmaxf(mraw, shfl_xor(mraw, 16));
-    mraw = fmaxf(mraw, shfl_xor(mraw, 32));
-    const float mc = mraw * cs;  // the block's maximum, log2 domain
-    float lsum = 0.0f;
-    f16x8 pop[4];
+    // ---- O = P V, two 16-dim tiles at a time, and the row sums l = P 1
+    // (of the same f16 weights) as a ninth tile: they arrive in the output
+    // layout, head 4qd+i in every lane of row group qd ----
+    f32x4 oacc[E][8], lacc[E];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int e = 0; e < E; ++e) {
+      lacc[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2_weight(fmaf(sacc[t][i], cs, -mc));
-        lsum += p;
-        pop[t >> 1][4 * (t & 1) + i] = (_Float16)p;
-      }
+      for (int cc = 0; cc < 4; ++cc) lacc[e] = mfma_f16(pop[e][cc], ones_f16x8(), lacc[e]);
     }
-    lsum += shfl_xor(lsum, 16);
-    lsum += shfl_xor(lsum, 32);
-    // ---- O = P V, two 16-dim tiles at a time ----
-    f32x4 oacc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       if ((dt & 1) == 0) asm volatile("" ::: "memory");
-      oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        oacc[dt] = mfma_f16(pop[cc], __builtin_bit_cast(f16x8, v_lds[v_slot(16 * dt + n, 4 * cc + qd)]),
-                            oacc[dt]);
-    }
-    // ---- the partial: O / l of heads 4qd+i, dims 16 dt + n, lane-major ----
-    float inv[4];
+      for (int e = 0; e < E; ++e) oacc[e][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = __builtin_amdgcn_rcpf(__shfl(lsum, 4 * qd + i, 64));
-    uint4* po = w.o + (size_t)pair * 256;
+      for (int cc = 0; cc < 4; ++cc) {
+        const f16x8 vv = __builtin_bit_cast(f16x8, v_lds[v_slot(16 * dt + n, 4 * cc + qd)]);
 #pragma unroll
-    for (int p2 = 0; p2 < 4; ++p2) {
-      f16x8 h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[i] = (_Float16)(oacc[2 * p2][i] * inv[i]);
-        h[4 + i] = (_Float16)(oacc[2 * p2 + 1][i] * inv[i]);
+        for (int e = 0; e < E; ++e) oacc[e][dt] = mfma_f16(pop[e][cc], vv, oacc[e][dt]);
       }
-      // streaming stores: the partials are read once, by the merge, and
-      // should not push the queries out of the caches
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, h),
-                                  reinterpret_cast<u32x4_t*>(po + p2 * 64 + lane));
     }
-    if (lane < 16)
-      __builtin_nontemporal_store(f32x2{mc, lsum},
-                                  reinterpret_cast<f32x2*>(w.ml + (size_t)pair * (kHeadsPad * 2)) + lane);
+    // ---- the partials: O / l of heads 4qd+i, dims 16 dt + n, lane-major ----
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e > 0 && it0 + e >= cnt) break;
+      float inv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) inv[i] = __builtin_amdgcn_rcpf(lacc[e][i]);
+      uint4* po = w.o + (size_t)pair[e] * 256;
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        f16x8 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = (_Float16)(oacc[e][2 * p2][i] * inv[i]);
+          h[4 + i] = (_Float16)(oacc[e][2 * p2 + 1][i] * inv[i]);
+        }
+        // streaming stores: the partials are read once, by the merge, and
+        // should not push the queries out of the caches
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, h),
+                                    reinterpret_cast<u32x4_t*>(po + p2 * 64 + lane));
+      }
+      // (max, sum) record: [16 maxima][16 sums]
+      float* pml = w.ml + (size_t)pair[e] * (kHeadsPad * 2);
+      if (lane < 16) __builtin_nontemporal_store(mc[e], pml + lane);
+      if (n == 0) __builtin_nontemporal_store(lacc[e], reinterpret_cast<f32x4*>(pml + 16) + qd);
+    }
   };
-  // two query buffers: entry it + 1's queries load while entry it is computed
-  auto q_of = [&](int it, bf16x8 (&qo)[4]) {
-    load_q(q, a, __shfl(my_pair, min(it, cnt - 1), 64) / a.K / a.G, g, n, qd, qo);
+  // two query buffers: group it + E's queries load while group it is computed
+  auto q_of = [&](int it0, bf16x8 (&qo)[E][4]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      load_q(q, a, __shfl(my_pair, min(it0 + e, cnt - 1), 64) / a.K / a.G, g, n, qd, qo[e]);
   };
-  bf16x8 qa[4], qb[4];
+  bf16x8 qa[E][4], qb[E][4];
   if (cnt > 0) q_of(0, qa);
-  for (int it = 0; it < cnt; it += 2) {
-    q_of(it + 1, qb);
-    attend_entry(it, qa);
-    if (it + 1 >= cnt) break;
-    q_of(it + 2, qa);
-    attend_entry(it + 1, qb);
+  for (int it = 0; it < cnt; it += 2 * E) {
+    q_of(it + E, qb);
+    attend_group(it, qa);
+    if (it + E >= cnt) break;
+    q_of(it + 2 * E, qa);
+    attend_group(it + E, qb);
   }
 }
 
 // ---- 3. merge -------------------------------------------------------------------
-__global__ __launch_bounds__(64 * kMergeWaves) void k2q_merge_kernel(AttendArgs a, K2qBufs w,
-                                                                    int units) {
-  __shared__ float ob[kMergeWaves][kHeadsPad][kDim + 4];
-  __shared__ float4 mls[kMergeWaves][32 * 8];  // the unit's (max, sum) records
+// One workgroup per (row, group); wave w takes dims 32w .. 32w+31 of all
+// 16 heads from every partial (one 16-byte load per lane and partial, all
+// issued at once), weighted by l 2^(max - M) and summed in ascending slot
+// order, then stores those dims.
+__global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w) {
+  __shared__ f32x4 mls[32 * 8];            // the unit's records: [slot][8 x 4 floats]
+  __shared__ float ob[4][kHeadsPad][36];   // each wave's 16 heads x 32 dims
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int u = blockIdx.x * kMergeWaves + wave;
-  if (u >= units) return;
-  const int row = u / a.G, g = u % a.G;
+  const int u = blockIdx.x, row = u / a.G, g = u % a.G;
   const int n = lane & 15, qd = lane >> 4;
   const uint64_t valid =
       __ballot(lane < a.K && w.place[(size_t)u * a.K + min(lane, a.K - 1)] >= 0);
-  // the unit's K (max, sum) records, 128 bytes each, into LDS in one round
-  {
-    const float4* src = reinterpret_cast<const float4*>(w.ml + (size_t)u * a.K * (kHeadsPad * 2));
-    float4 r[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = src[min(lane + 64 * k, 8 * a.K - 1)];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (lane + 64 * k < 8 * a.K) mls[wave][lane + 64 * k] = r[k];
-    wave_lds_sync();
+  {  // the K (max, sum) records, 128 bytes each
+    const f32x4* src = reinterpret_cast<const f32x4*>(w.ml + (size_t)u * a.K * (kHeadsPad * 2));
+    if ((int)threadIdx.x < 8 * a.K) mls[threadIdx.x] = src[threadIdx.x];
   }
-  // (max, sum) of heads 4qd .. 4qd+3 in partial s: 32 bytes at 32 qd
-  auto ml_of = [&](int s, float (&m)[4], float (&l)[4]) {
-    const float4 x = mls[wave][8 * s + 2 * qd], y = mls[wave][8 * s + 2 * qd + 1];
-    m[0] = x.x; l[0] = x.y; m[1] = x.z; l[1] = x.w;
-    m[2] = y.x; l[2] = y.y; m[3] = y.z; l[3] = y.w;
-  };
-  // pass 1: the largest partial maximum of each head
-  float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  // this wave's 16-byte piece of partials 0 .. 15 (dt = 2 wave, 2 wave + 1)
+  uint4 po[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    if (s < a.K && ((valid >> s) & 1)) po[s] = w.o[((size_t)u * a.K + s) * 256 + wave * 64 + lane];
+  __syncthreads();
+  // heads 4qd .. 4qd+3: the largest partial maximum, then the weights
+  f32x4 M = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   for (int s = 0; s < a.K; ++s) {
     if ((valid >> s) & 1) {
-      float m[4], l[4];
-      ml_of(s, m, l);
+      const f32x4 m = mls[8 * s + qd];
 #pragma unroll
       for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], m[i]);
     }
   }
-  // pass 2: sum of the partials weighted by l 2^(max - M), ascending slots
-  float L[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4 co[8];
+  f32x4 L = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, c0 = L, c1 = L;
+  auto add = [&](int s, uint4 piece) {
+    const f32x4 m = mls[8 * s + qd], l = mls[8 * s + 4 + qd];
+    const f16x8 h = __builtin_bit_cast(f16x8, piece);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) co[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr int BATCH = 4;
-  for (int s0 = 0; s0 < a.K; s0 += BATCH) {
-    uint4 po[BATCH][4];
+    for (int i = 0; i < 4; ++i) {
+      const float wt = l[i] * exp2f(m[i] - M[i]);
+      L[i] += wt;
+      c0[i] = fmaf((float)h[i], wt, c0[i]);
+      c1[i] = fmaf((float)h[4 + i], wt, c1[i]);
+    }
+  };
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
+  for (int s = 0; s < 16; ++s)
+    if (s < a.K && ((valid >> s) & 1)) add(s, po[s]);
+  for (int s0 = 16; s0 < a.K; s0 += 16) {  // top-k above 16: the next 16 partials
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
       const int s = s0 + k;
-      if (s < a.K && ((valid >> s) & 1)) {
-        const uint4* src = w.o + ((size_t)u * a.K + s) * 256;
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) po[k][p2] = src[p2 * 64 + lane];
-      }
+      if (s < a.K && ((valid >> s) & 1)) po[k] = w.o[((size_t)u * a.K + s) * 256 + wave * 64 + lane];
     }
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int s = s0 + k;
-      if (s < a.K && ((valid >> s) & 1)) {
-        float m[4], l[4], wt[4];
-        ml_of(s, m, l);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wt[i] = l[i] * exp2f(m[i] - M[i]);
-          L[i] += wt[i];
-        }
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) {
-          const f16x8 h = __builtin_bit_cast(f16x8, po[k][p2]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            co[2 * p2][i] = fmaf((float)h[i], wt[i], co[2 * p2][i]);
-            co[2 * p2 + 1][i] = fmaf((float)h[4 + i], wt[i], co[2 * p2 + 1][i]);
-          }
-        }
-      }
-    }
+    for (int k = 0; k < 16; ++k)
+      if (s0 + k < a.K && ((valid >> (s0 + k)) & 1)) add(s0 + k, po[k]);
   }
-  float inv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) inv[i] = L[i] > 0.0f ? a.v_scale / L[i] : 0.0f;
-  // heads 4qd+i, dims 16 dt + n -> 8 consecutive dims of one head per lane
+  // heads 4qd+i, dims 32 wave + 16 t + n -> 8 consecutive dims of one head per lane
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) ob[wave][4 * qd + i][dt * 16 + n] = co[dt][i] * inv[i];
+    const float inv = L[i] > 0.0f ? a.v_scale / L[i] : 0.0f;
+    ob[wave][4 * qd + i][n] = c0[i] * inv;
+    ob[wave][4 * qd + i][16 + n] = c1[i] * inv;
   }
   wave_lds_sync();
-#pragma unroll
-  for (int c0 = 0; c0 < kHeadsPad * 16; c0 += 64) {
-    const int cidx = c0 + lane, h = cidx >> 4, d0 = (cidx & 15) * 8;
+  {
+    const int h = lane >> 2, d0 = (lane & 3) * 8;
     if (h < a.hpg) {
       const float4 lo = *reinterpret_cast<const float4*>(&ob[wave][h][d0]);
       const float4 hi = *reinterpret_cast<const float4*>(&ob[wave][h][d0 + 4]);
       const float o[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      store_out8(a, row, g * a.hpg + h, d0, o);
+      store_out8(a, row, g * a.hpg + h, 32 * wave + d0, o);
     }
   }
-  if (a.lse && n == 0) {
+  if (a.lse && wave == 0 && n == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * qd + i;
@@ -621,13 +641,13 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint8_t* kd = static_cast<const uint8_t*>(kv_data);
   const uint8_t* ks = static_cast<const uint8_t*>(kv_scales);
+  constexpr int E = kK2qEntries;
+  const dim3 ablock(64 * K2qShape<E>::waves);
   if (s.kv_dtype == kFP8)
-    hipLaunchKernelGGL(k2q_attend_kernel<kFP8>, agrid, dim3(64 * kK2qWaves), 0, st, qp, kd, ks, a, w);
+    hipLaunchKernelGGL((k2q_attend_kernel<kFP8, E>), agrid, ablock, 0, st, qp, kd, ks, a, w);
   else
-    hipLaunchKernelGGL(k2q_attend_kernel<kNVFP4>, agrid, dim3(64 * kK2qWaves), 0, st, qp, kd, ks, a, w);
-  const int units = s.rows * s.G;
-  hipLaunchKernelGGL(k2q_merge_kernel, dim3((unsigned)((units + kMergeWaves - 1) / kMergeWaves)),
-                     dim3(64 * kMergeWaves), 0, st, a, w, units);
+    hipLaunchKernelGGL((k2q_attend_kernel<kNVFP4, E>), agrid, ablock, 0, st, qp, kd, ks, a, w);
+  hipLaunchKernelGGL(k2q_merge_kernel, dim3((unsigned)(s.rows * s.G)), dim3(256), 0, st, a, w);
   return hipGetLastError();
 }
 

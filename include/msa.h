@@ -16,7 +16,7 @@
  *   msa_decode         the three in one call
  * msa_decode's scores, selection, outputs and lse are bitwise those of the
  * three-call chain (both attend the selected blocks in ascending order with
- * the same launch shape).  A fifth call writes new tokens into the caches
+ * the same launch shape, or both take the key-block path below).  A fifth call writes new tokens into the caches
  * the others read:
  *   msa_cache_write    quantise new K / V / index keys into their slots
  *
@@ -154,7 +154,10 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
 /*
  * Workspace bytes a call needs for problem p (op as for msa_check_problem):
  *   - msa_sparse_attend: room for the split-K partial states when a (row,
- *     group) is split over several workgroups (0 when it is not);
+ *     group) is split over several workgroups (0 when it is not); for a
+ *     chunk of 384 or more rows per sequence over an FP8 or NVFP4 cache, the
+ *     key-block path's buffers instead (see msa_sparse_attend): about 4.3 KB
+ *     per (row, group, top-k slot), 1.1 GB for 4,096 rows at G = 4, top-16;
  *   - msa_decode: B*R*G*MB words for the pooled scores, then that;
  *   - the other calls: 0.
  * Every region is rounded up to 256 bytes, and a workspace that holds
@@ -220,7 +223,14 @@ msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
  * blocks: out = sum_t softmax_t(sm_scale * k_scale * q.k_t) * v_scale * v_t,
  * with fp32 softmax state, split over the selected blocks (across the waves
  * of a workgroup and, for small batches, across workgroups, one of which
- * merges the others' partial states).  topk_idx: the first
+ * merges the others' partial states).  A chunk of 384 or more rows per
+ * sequence over an FP8 or NVFP4 cache (chunked prefill) is grouped by key
+ * block instead (API reference, MiniMaxM3Model: the top-k buffer inverted by
+ * build_k2q_csr): each selected block is read and dequantised once per up to
+ * 64 rows that selected it, each (row, group, block) leaves a partial whose
+ * normalised output is rounded to f16, and each row's partials are merged in
+ * selection order with fp32 weights; out and lse then differ from a per-row
+ * gather by that rounding (relative 2^-11 of each partial).  topk_idx: the first
  * min(top_k, last visible block + 1) entries of a row are read; an entry
  * outside [0, last visible block] contributes nothing (msa_block_topk never
  * writes one).  kv_scales is required for NVFP4 and ignored otherwise.  lse
@@ -235,12 +245,12 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
 
 /*
  * The whole decode step (blog, "MSA primer"): msa_index_scores ->
- * msa_block_topk -> msa_sparse_attend, with the same scores and selection;
- * the attention may visit the selected blocks in another order, so out and
- * lse agree with the three calls' to rounding.  For FP8 or NVFP4 caches
- * and block tables of up to 8064 blocks per row (about a million tokens) it
- * is two kernels, the scan and then selection + attention in one; otherwise
- * the three kernels run in turn.
+ * msa_block_topk -> msa_sparse_attend; scores, selection, out and lse are
+ * bitwise the three calls'.  For FP8 or NVFP4 caches and block tables of up
+ * to 8064 blocks per row (about a million tokens) it is two kernels, the
+ * scan and then selection + attention in one; chunks of 384 or more rows
+ * per sequence, longer tables and fp32 caches run the three calls' kernels
+ * in turn.
  * topk_idx receives the selection; block_scores (nullable) receives the
  * pooled scores.  workspace: msa_workspace_bytes(p, 3) bytes, zero-filled
  * before its first use (see msa_workspace_bytes) and left zero-filled.
@@ -284,9 +294,8 @@ msa_status msa_cache_write(const msa_problem* p, int32_t num_tokens, const int32
 /*
  * msa_decode without a workspace, for callers that cannot allocate device
  * memory (code under graph capture, tight serving loops, harnesses that
- * forbid allocation).  Same arguments, semantics and results as msa_decode
- * (its attention may differ from the three-call chain's to rounding in the
- * same way), minus the workspace: its scratch is a device array of
+ * forbid allocation).  Same arguments, semantics and results as msa_decode,
+ * minus the workspace: its scratch is a device array of
  * MSA_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
  * process ends.  A problem whose msa_workspace_bytes(p, 3) exceeds that is
  * rejected with MSA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued

@@ -860,7 +860,7 @@ def test_prefill_scattered_positions(kv):
 
 
 # ---------------------------------------------------------------------------
-# chunked prefill (64+ rows per sequence): the attention grouped by key block
+# chunked prefill (384+ rows per sequence): the attention grouped by key block
 # ---------------------------------------------------------------------------
 
 SCATTER_QP = [-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 2900,
@@ -869,22 +869,22 @@ SCATTER_QP = [-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 29
 
 @pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
 def test_key_block_attention_edge_cases(kv):
-    """Two sequences of 72 rows: one at scattered positions (rows that see no
+    """Two sequences of 384 rows: one at scattered positions (rows that see no
     key or one key, block edges, positions past the end), one causal at its
     end; an out-of-pool table entry in each sequence, one of them the recent
     block of some rows.  Through msa_decode and the chain, then
     msa_sparse_attend on a given selection with malformed entries (-1, past
     the row's recent block, a duplicate, attended twice as by the oracle):
     outputs and lse against the oracle."""
-    R = 72
+    R = 384
     lens = np.array([3000, 4100])
-    qp = np.concatenate([np.array((SCATTER_QP * 3)[:R]),
+    qp = np.concatenate([np.array((SCATTER_QP * 16)[:R]),
                          np.arange(lens[1] - R, lens[1])]).astype(np.int32)
     base = synth.make(f"k2q-edge-{kv}", seed=211 + kv, seq_lens=lens, rows_per_seq=R, q_pos=qp,
                       q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2)
     bt = base.block_table.copy()
     bt[0, 5] = -1
-    bt[1, 31] = base.num_phys_blocks  # the recent block of sequence 1's rows 4000 .. 4095
+    bt[1, 31] = base.num_phys_blocks  # the recent block of sequence 1's rows 3968 .. 4095
     w = dataclasses.replace(base, block_table=bt)
     tag = synth.DTYPE_NAMES[kv]
     _run_and_check(w, fused=True, name=f"k2q-edge-{tag}")
@@ -914,10 +914,10 @@ def test_key_block_attention_edge_cases(kv):
 
 
 def test_key_block_attention_many_chunks_per_block():
-    """200 causal rows with the first block forced for every row: bucket 0
-    of each group holds 200 entries, four work chunks; local_blocks = 2.
+    """400 causal rows with the first block forced for every row: bucket 0
+    of each group holds 400 entries, seven work chunks; local_blocks = 2.
     Through msa_decode and the chain."""
-    R = 200
+    R = 400
     lens = np.array([20000])
     qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
     base = synth.make("k2q-chunks", seed=233, seq_lens=lens, rows_per_seq=R, q_pos=qp,
@@ -932,7 +932,7 @@ def test_key_block_attention_is_deterministic_and_equals_the_chain():
     """Which wave attends which entry follows the order of atomics; the
     results do not: repeated msa_decode calls and the three-call chain give
     bit-identical outputs and lse."""
-    R = 96
+    R = 384
     lens = np.array([9000, 6100])
     qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
     w = synth.make("k2q-det", seed=47, seq_lens=lens, rows_per_seq=R, q_pos=qp,
