@@ -71,7 +71,7 @@ struct K2qBufs {
   int32_t* starts;    // [B*G][MB] index of a block's first entry in `entries`
   int32_t* place;     // [pairs] an entry's place in its bucket, -1: not attended
   int32_t* entries;   // [B*G][R*K] entry ids (u * K + slot), grouped by block
-  int2* chunks;       // [B*G][max_chunks] (block, chunk within the block)
+  int4* chunks;       // [B*G][max_chunks] (block j, first entry, end, physical block)
   int32_t* nchunks;   // [B*G] chunks in use
   float* ml;          // [pairs][2][16]: the 16 heads' maxima (log2 domain), then sums
   uint4* o;           // [pairs][4][64] of 8 f16
@@ -97,7 +97,7 @@ static K2qSizes k2q_sizes(const Shape& s) {
 static size_t k2q_layout(const Shape& s, size_t off[8]) {
   const K2qSizes z = k2q_sizes(s);
   const size_t sz[8] = {4 * (size_t)(z.bg * s.MB), 4 * (size_t)(z.bg * s.MB), 4 * (size_t)z.pairs,
-                        4 * (size_t)z.pairs, 8 * (size_t)(z.bg * z.max_chunks), 4 * (size_t)z.bg,
+                        4 * (size_t)z.pairs, 16 * (size_t)(z.bg * z.max_chunks), 4 * (size_t)z.bg,
                         kPartialMlBytes * z.pairs, kPartialOBytes * z.pairs};
   size_t at = 0;
   for (int i = 0; i < 8; ++i) {
@@ -213,12 +213,17 @@ __global__ __launch_bounds__(kScanThreads) void k2q_scan_kernel(AttendArgs a, K2
   }
   scan_threads(se, sc, sm);
   const size_t ebase = (size_t)bg * a.R * a.K;
-  int2* chunks = w.chunks + (size_t)bg * w.max_chunks;
+  const int b = bg / a.G;
+  int4* chunks = w.chunks + (size_t)bg * w.max_chunks;
   for (int x = x0; x < x1; ++x) {
     const int n = cnt[x];
-    w.starts[(size_t)bg * a.MB + x] = (int)(ebase + se);
+    const int start = (int)(ebase + se);
+    w.starts[(size_t)bg * a.MB + x] = start;
     const int nch = (n + kChunkRows - 1) / kChunkRows;
-    for (int k = 0; k < nch; ++k) chunks[sc + k] = make_int2(x, k);
+    // a non-empty bucket's table entry is in [0, P): the count checked it
+    const int pb = nch > 0 ? a.bt[(size_t)b * a.MB + x] : 0;
+    for (int k = 0; k < nch; ++k)
+      chunks[sc + k] = make_int4(x, start + k * kChunkRows, start + min(n, (k + 1) * kChunkRows), pb);
     se += n;
     sc += nch;
   }
@@ -377,13 +382,12 @@ __attribute__((amdgpu_waves_per_eu(K2qShape<E>::waves_per_simd))) void k2q_atten
   __shared__ uint4 k_lds[kBlock * 16];
   __shared__ uint4 v_lds[kDim * 16];
   const int bg = blockIdx.x / w.max_chunks, c = blockIdx.x % w.max_chunks;
-  if (c >= w.nchunks[bg]) return;
-  const int2 ch = w.chunks[(size_t)bg * w.max_chunks + c];
-  const int j = ch.x, g = bg % a.G, b = bg / a.G;
-  const int pb = a.bt[(size_t)b * a.MB + j];  // in [0, P): the count checked it
-  const int s0 = w.starts[(size_t)bg * a.MB + j];
-  const int e0 = s0 + ch.y * kChunkRows;
-  const int e1 = min(s0 + w.counts[(size_t)bg * a.MB + j], e0 + kChunkRows);
+  // the chunk's descriptor is read together with the count (a slot past the
+  // count holds stale bytes and is not used)
+  const int nchunks = w.nchunks[bg];
+  const int4 ch = w.chunks[(size_t)bg * w.max_chunks + c];
+  if (c >= nchunks) return;
+  const int j = ch.x, e0 = ch.y, e1 = ch.z, pb = ch.w, g = bg % a.G, b = bg / a.G;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int n = lane & 15, qd = lane >> 4;
   // the wave's entries e0 + wave + NW i, lane i holding entry i's id and
@@ -394,6 +398,14 @@ __attribute__((amdgpu_waves_per_eu(K2qShape<E>::waves_per_simd))) void k2q_atten
     my_pair = w.entries[e0 + wave + NW * lane];
     my_pos = row_last_key(a.lens, a.qpos, my_pair / a.K / a.G, b, a.MB);
   }
+  // the first group's queries load while the block is staged
+  auto q_of = [&](int it0, bf16x8 (&qo)[E][4]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      load_q(q, a, __shfl(my_pair, min(it0 + e, cnt - 1), 64) / a.K / a.G, g, n, qd, qo[e]);
+  };
+  bf16x8 qa[E][4], qb[E][4];
+  if (cnt > 0) q_of(0, qa);
   stage_block<KV, 64 * NW>(kvd, kvs, ((size_t)pb * 2 + 0) * a.G + g,
                            ((size_t)pb * 2 + 1) * a.G + g, k_lds, v_lds);
   __syncthreads();
@@ -507,13 +519,6 @@ __attribute__((amdgpu_waves_per_eu(K2qShape<E>::waves_per_simd))) void k2q_atten
     }
   };
   // two query buffers: group it + E's queries load while group it is computed
-  auto q_of = [&](int it0, bf16x8 (&qo)[E][4]) {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      load_q(q, a, __shfl(my_pair, min(it0 + e, cnt - 1), 64) / a.K / a.G, g, n, qd, qo[e]);
-  };
-  bf16x8 qa[E][4], qb[E][4];
-  if (cnt > 0) q_of(0, qa);
   for (int it = 0; it < cnt; it += 2 * E) {
     q_of(it + E, qb);
     attend_group(it, qa);
@@ -540,11 +545,14 @@ __global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w)
     const f32x4* src = reinterpret_cast<const f32x4*>(w.ml + (size_t)u * a.K * (kHeadsPad * 2));
     if ((int)threadIdx.x < 8 * a.K) mls[threadIdx.x] = src[threadIdx.x];
   }
-  // this wave's 16-byte piece of partials 0 .. 15 (dt = 2 wave, 2 wave + 1)
+  // this wave's 16-byte piece of partials 0 .. 15 (dt = 2 wave, 2 wave + 1),
+  // loaded whether or not the slot holds one (the record exists either way;
+  // an unused slot's bytes are never read), so that these loads need not
+  // wait for the validity bits
   uint4 po[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s)
-    if (s < a.K && ((valid >> s) & 1)) po[s] = w.o[((size_t)u * a.K + s) * 256 + wave * 64 + lane];
+    if (s < a.K) po[s] = load_stream(w.o + ((size_t)u * a.K + s) * 256 + wave * 64 + lane);
   __syncthreads();
   // heads 4qd .. 4qd+3: the largest partial maximum, then the weights
   f32x4 M = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -574,7 +582,7 @@ __global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w)
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int s = s0 + k;
-      if (s < a.K && ((valid >> s) & 1)) po[k] = w.o[((size_t)u * a.K + s) * 256 + wave * 64 + lane];
+      if (s < a.K) po[k] = load_stream(w.o + ((size_t)u * a.K + s) * 256 + wave * 64 + lane);
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k)
@@ -623,7 +631,7 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
   w.starts = reinterpret_cast<int32_t*>(base + off[1]);
   w.place = reinterpret_cast<int32_t*>(base + off[2]);
   w.entries = reinterpret_cast<int32_t*>(base + off[3]);
-  w.chunks = reinterpret_cast<int2*>(base + off[4]);
+  w.chunks = reinterpret_cast<int4*>(base + off[4]);
   w.nchunks = reinterpret_cast<int32_t*>(base + off[5]);
   w.ml = reinterpret_cast<float*>(base + off[6]);
   w.o = reinterpret_cast<uint4*>(base + off[7]);
