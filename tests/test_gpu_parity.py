@@ -928,6 +928,21 @@ def test_key_block_attention_many_chunks_per_block():
     _run_and_check(w, fused=False, name="k2q-chunks-chain")
 
 
+def test_key_block_attention_1024_rows():
+    """1,024 causal rows against the oracle on every row (G = 2 with 4 heads
+    per group keeps the oracle small): each of the chunk's recent blocks is
+    the forced block of 128 rows and spans several work chunks.  Through
+    msa_decode and the chain."""
+    R = 1024
+    lens = np.array([4000])
+    qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
+    w = synth.make("k2q-1024", seed=239, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                   num_q_heads=8, num_groups=2, q_dtype=synth.BF16, kv_dtype=synth.FP8,
+                   plant_per_seq=3)
+    _run_and_check(w, fused=True, name="k2q-1024")
+    _run_and_check(w, fused=False, name="k2q-1024-chain")
+
+
 def test_key_block_attention_is_deterministic_and_equals_the_chain():
     """Which wave attends which entry follows the order of atomics; the
     results do not: repeated msa_decode calls and the three-call chain give
