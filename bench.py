@@ -622,6 +622,16 @@ def run_prefill(args, w):
     achieved = flops / (idx_us * 1e-6) / 1e12
     log(f"[bench] prefill ms/step {ms_step:.4f}; index contraction {idx_us:.1f} us "
         f"({achieved:.0f} TFLOP/s)")
+    # the attention alone on the step's selection (msa_sparse_attend: for
+    # chunks of 384+ rows the key-block lists, attention and merge)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        dw.sparse_attend()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    att_us = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    log(f"[bench] sparse attention on the step's selection: {att_us:.1f} us")
     # the insert half: the chunk's own tokens written into the caches
     cw = time_cache_write(w, dw, np.arange(w.rows) // w.rows_per_seq, w.q_pos)
     log(f"[bench] cache write of {cw['tokens']} tokens: {cw['us_per_launch']:.1f} us "
@@ -658,7 +668,8 @@ def run_prefill(args, w):
                    "context_tokens": int(w.seq_lens.sum()), "kv_groups": w.num_groups,
                    "q_heads": w.num_q_heads, "top_k": w.top_k},
         "kernel_us": {"index_contraction": idx_us,
-                      "topk_attend_and_gaps": ms_step * 1e3 - idx_us},
+                      "topk_attend_and_gaps": ms_step * 1e3 - idx_us,
+                      "sparse_attend": att_us},
         "roofline": {"bound": "mfma", "kernel": "prefill_index_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
