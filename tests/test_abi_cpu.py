@@ -122,6 +122,28 @@ def test_workspace_sizes():
     assert msa.workspace_bytes(big, msa.OP_DECODE) == 256 + 512 * 4 * 16 * 4
 
 
+def test_workspace_sizes_of_the_key_block_path():
+    """A chunk of 384+ rows per sequence over an FP8 or NVFP4 cache takes
+    the key-block attention, whose workspace holds per (row, group, slot) a
+    4 KB f16 partial, a 128-byte (max, sum) record and two list words, plus
+    small per-block arrays and the chunk table; 383 rows take the per-row
+    kernel, which needs none at 512+ (row, group) units."""
+    def sizes(R, kv=2):
+        p = good(num_seqs=1, rows_per_seq=R, max_blocks_per_seq=544, num_phys_blocks=544,
+                 kv_dtype=kv)
+        return msa.workspace_bytes(p, msa.OP_ATTEND), msa.workspace_bytes(p, msa.OP_DECODE)
+    assert sizes(383)[0] == 0
+    for kv in (2, 3):
+        a, d = sizes(4096, kv)
+        slots = 4096 * 4 * 16
+        per_slot = 4096 + 128 + 8
+        assert slots * per_slot < a - 256 < slots * per_slot * 1.001
+        # decode adds the pooled scores
+        assert d - a == -(-(4096 * 4 * 544 * 4) // 256) * 256
+    a384, _ = sizes(384)
+    assert a384 > 384 * 4 * 16 * (4096 + 128 + 8)
+
+
 def test_status_strings():
     L = msa.lib()
     assert L.msa_status_string(0) == b"ok"

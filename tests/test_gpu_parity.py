@@ -928,6 +928,22 @@ def test_key_block_attention_many_chunks_per_block():
     _run_and_check(w, fused=False, name="k2q-chunks-chain")
 
 
+@pytest.mark.parametrize("G,H,kv", [(8, 64, synth.NVFP4), (1, 16, synth.FP8)])
+def test_key_block_attention_groups(G, H, kv):
+    """384 causal rows with G = 8 (8 heads per group: half of each MFMA
+    column tile is padding) over NVFP4, and G = 1 over FP8; through
+    msa_decode and the chain."""
+    R = 384
+    lens = np.array([6000])
+    qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
+    w = synth.make(f"k2q-g{G}", seed=251 + G, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                   num_q_heads=H, num_groups=G, q_dtype=synth.BF16, kv_dtype=kv,
+                   plant_per_seq=3)
+    tag = synth.DTYPE_NAMES[kv]
+    _run_and_check(w, fused=True, name=f"k2q-g{G}-{tag}")
+    _run_and_check(w, fused=False, name=f"k2q-g{G}-{tag}-chain")
+
+
 def test_key_block_attention_1024_rows():
     """1,024 causal rows against the oracle on every row (G = 2 with 4 heads
     per group keeps the oracle small): each of the chunk's recent blocks is
