@@ -36,9 +36,9 @@
 //               dims, with all of its loads in flight at once.
 // Which wave takes which entry depends on the order of atomics; the
 // arithmetic of an entry and the merge order do not, so the results are
-// deterministic.  They
-// differ from a per-row gather by the f16 rounding of each block's
-// normalised output (relative 2^-11), which the merge weights by at most 1.
+// deterministic.  They differ from a per-row gather by the f16 rounding of
+// each block's normalised output (relative 2^-11), which the merge weights
+// by at most 1.
 #include "attend_task.hpp"
 #include "device.hpp"
 #include "launch.hpp"
@@ -250,11 +250,10 @@ __global__ __launch_bounds__(256) void k2q_scatter_kernel(AttendArgs a, K2qBufs 
 // S^T tile t holds keys 16t .. 16t+15 in natural order; in k-step c lane l
 // (n = l%16, qd = l/16) holds dims 32qd + 8c .. +7 of both K and Q (the
 // contraction order is free as long as the operands agree), and ends with
-// keys 16t + 4qd + i of head n.  Its P V operand
-// for key chunk c is the f16 of tiles 2c and 2c+1: contraction position
-// 32c + 8qd + e stands for key 32c + 16(e/4) + 4qd + e%4.  V^T is staged in
-// that position order: within each 32-key group, key 16a + 4q + i sits at
-// position 8q + 4a + i.
+// keys 16t + 4qd + i of head n.  Its P V operand for key chunk c is the f16
+// of tiles 2c and 2c+1: contraction position 32c + 8qd + e stands for key
+// 32c + 16(e/4) + 4qd + e%4.  V^T is staged in that position order: within
+// each 32-key group, key 16a + 4q + i sits at position 8q + 4a + i.
 __device__ __forceinline__ int k_slot(int key, int c) { return key * 16 + (c ^ (key & 15)); }
 __device__ __forceinline__ int v_slot(int d, int c) { return d * 16 + (c ^ (d & 15)); }
 
@@ -345,7 +344,6 @@ __device__ __forceinline__ void stage_block(const uint8_t* __restrict__ kvd,
     }
   }
 }
-
 
 __device__ __forceinline__ f16x8 ones_f16x8() {
   return __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
