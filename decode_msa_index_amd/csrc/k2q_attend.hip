@@ -616,14 +616,18 @@ __global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w)
 
 // ---- launch ----------------------------------------------------------------------
 
+// workspace: the status header, then this path's buffers.  The header and
+// the counts are cleared first (one fill: they are adjacent); after the
+// merge the split zone is cleared again (lists and the first records live
+// there), so that a later call of any shape finds it zero.
 hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
-                             const void* kv_data, const void* kv_scales, void* region,
+                             const void* kv_data, const void* kv_scales, void* workspace,
                              hipStream_t st) {
   size_t off[8];
-  k2q_layout(s, off);
+  const size_t region_bytes = k2q_layout(s, off);
   const K2qSizes z = k2q_sizes(s);
   if (z.pairs == 0) return hipSuccess;
-  char* base = static_cast<char*>(region);
+  char* base = static_cast<char*>(workspace) + kStatusBytes;
   K2qBufs w;
   w.counts = reinterpret_cast<int32_t*>(base + off[0]);
   w.starts = reinterpret_cast<int32_t*>(base + off[1]);
@@ -636,7 +640,7 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
   w.max_chunks = (int)z.max_chunks;
   const int rows_per = std::max(1, kCountThreads * kCountPairs / s.K);
   w.slices = (s.R + rows_per - 1) / rows_per;
-  hipError_t e = launch_zero_fill(w.counts, 4 * (size_t)(z.bg * s.MB), st);
+  hipError_t e = launch_zero_fill(workspace, kStatusBytes + off[1], st);  // header + counts
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k2q_count_kernel, dim3((unsigned)(z.bg * w.slices)), dim3(kCountThreads),
                      sizeof(int32_t) * (size_t)s.MB, st, a, w);
@@ -654,7 +658,9 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
   else
     hipLaunchKernelGGL((k2q_attend_kernel<kNVFP4, E>), agrid, ablock, 0, st, qp, kd, ks, a, w);
   hipLaunchKernelGGL(k2q_merge_kernel, dim3((unsigned)(s.rows * s.G)), dim3(256), 0, st, a, w);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_zero_fill(base, std::min(region_bytes, kSplitZoneBytes), st);
 }
 
 }  // namespace msa

@@ -52,6 +52,12 @@ size_t attend_workspace_bytes(const Shape& s, const AttendConfig& c);
 // holds split-K partials; word 0 becomes non-zero when a merge gives up
 // waiting (its partials are then no longer trusted until it is cleared).
 constexpr size_t kStatusBytes = 256;
+// The split-K partials of every launch shape lie in the first
+// kSplitZoneBytes after the status header: attend_config splits a (row,
+// group) only below 256 units, into at most ceil(256 / units) workgroups, so
+// units * splits <= 510.  This zone (with the header) is the part of a
+// workspace that must be zero when a call starts; every call leaves it so.
+constexpr size_t kSplitZoneBytes = (size_t)512 * kHeadsPad * (128 + 2) * sizeof(float);  // 128 dims + max + sum
 
 // Polls of one batch of split-K partials before a merger gives up (< 0: the
 // merger gives up at once, a test of the failure path).
@@ -79,12 +85,13 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 hipStream_t st);
 // Chunks of many rows per sequence (chunked prefill): the attention grouped
 // by key block (k2q_attend.hip).  launch_sparse_attend takes this path when
-// k2q_eligible; its workspace after the status header is the path's own.
+// k2q_eligible; its workspace after the status header is the path's own
+// (cleared in the header and the split zone, not beyond).
 struct AttendArgs;
 bool k2q_eligible(const Shape& s);
 size_t k2q_workspace_bytes(const Shape& s);
 hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
-                             const void* kv_data, const void* kv_scales, void* region,
+                             const void* kv_data, const void* kv_scales, void* workspace,
                              hipStream_t st);
 // Quantises new tokens' K, V and index keys into their cache slots
 // (cache_write.hip).

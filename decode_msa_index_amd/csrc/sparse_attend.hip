@@ -162,6 +162,7 @@ AttendConfig attend_config(const Shape& s) {
   c.splits = sp;
   const int per_wg = (s.K + sp - 1) / sp;
   c.nw = per_wg >= 8 ? 8 : per_wg >= 4 ? 4 : per_wg >= 2 ? 2 : 1;
+  // units * splits <= 510 whenever splits >= 2 (kSplitZoneBytes)
   return c;
 }
 
@@ -288,7 +289,7 @@ hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_da
     return hipGetLastError();
   }
   if (k2q_eligible(s))
-    return launch_k2q_attend(s, a, q, kv_data, kv_scales, static_cast<char*>(workspace) + kStatusBytes, st);
+    return launch_k2q_attend(s, a, q, kv_data, kv_scales, workspace, st);
   uint32_t* status = static_cast<uint32_t*>(workspace);
   return launch_mfma<false>(s, attend_config(s), a, q, kv_data, kv_scales,
                             static_cast<char*>(workspace) + kStatusBytes, status, true, st);

@@ -162,15 +162,18 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  *   - the other calls: 0.
  * Every region is rounded up to 256 bytes, and a workspace that holds
  * partial states starts with a 256-byte status header.  The workspace is
- * caller-owned device memory, 256-byte aligned.  msa_decode requires it to
- * be zero-filled before its first use (e.g. hipMemset once after
- * allocation): the workgroups of its attention kernel hand partial states to
+ * caller-owned device memory, 256-byte aligned.  msa_decode requires its
+ * first 256 + 4,259,840 bytes (all of it, if smaller) to be zero-filled
+ * before its first use (e.g. hipMemset once after allocation): the status
+ * header and the zone where the split-K partial states of any problem shape
+ * live -- the workgroups of the attention kernel hand partial states to
  * each other through it, and a word still zero means "not yet written".
- * Every msa_decode and msa_sparse_attend call leaves the workspace
- * zero-filled again, so one zero fill serves any sequence of calls and
- * problem shapes; msa_sparse_attend itself needs no initialisation (it
- * clears what it uses).  Calls that share a workspace must not overlap.  A
- * call whose size is 0 accepts a NULL workspace.
+ * Every msa_decode and msa_sparse_attend call leaves that part zero-filled
+ * again, so one zero fill serves any sequence of calls and problem shapes;
+ * past it a call may leave its scratch (the key-block path's lists and
+ * partials).  msa_sparse_attend itself needs no initialisation (it clears
+ * what it uses).  Calls that share a workspace must not overlap.  A call
+ * whose size is 0 accepts a NULL workspace.
  *
  * Failure mode: the workgroup that merges a (row, group)'s partial states
  * waits for them with a bounded poll (about a second).  Should it ever give

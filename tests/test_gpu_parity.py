@@ -713,13 +713,26 @@ def test_merge_timeout_is_reported():
     assert torch.isfinite(dw.out.float()).all()
 
 
+# the status header and the split-K zone after it (launch.hpp: 512 (row,
+# group) splits x 16 heads x (128 + 2) floats): the part of a workspace every
+# call must find, and leave, zero
+SPLIT_ZONE_BYTES = 256 + 512 * 16 * 130 * 4
+
+
 def test_one_workspace_across_shapes():
-    """msa_decode leaves its workspace zero-filled, so one workspace (zeroed
-    once) serves calls of different shapes in any order."""
+    """msa_decode leaves the status header and the split-K zone of its
+    workspace zero-filled, so one workspace (zeroed once) serves calls of
+    different shapes in any order: two split-K decode shapes and a 384-row
+    prefill chunk whose key-block attention writes lists and partials over
+    the zone and beyond (and clears the zone after use)."""
+    R = 384
+    qp = np.arange(5000 - R, 5000).astype(np.int32)
     ws_ = [synth.make("shapeA", seed=61, seq_lens=[9000, 40000, 128, 1], q_dtype=synth.BF16,
                       kv_dtype=synth.FP8, plant_per_seq=3),
            synth.make("shapeB", seed=62, seq_lens=[70000, 3000], q_dtype=synth.BF16,
-                      kv_dtype=synth.FP8, num_q_heads=32, num_groups=8, top_k=8)]
+                      kv_dtype=synth.FP8, num_q_heads=32, num_groups=8, top_k=8),
+           synth.make("shapeC", seed=63, seq_lens=[5000], rows_per_seq=R, q_pos=qp,
+                      q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3)]
     dws = [parity.DeviceWorkload(w) for w in ws_]
     refs = []
     for dw in dws:  # each shape alone, on its own freshly zeroed workspace
@@ -728,15 +741,16 @@ def test_one_workspace_across_shapes():
         refs.append((dw.topk.clone(), dw.out.clone()))
     shared = torch.zeros(max(int(dw.ws_decode.numel()) for dw in dws), dtype=torch.uint8,
                          device="cuda")
-    for k in (0, 1, 0, 1, 1, 0):
+    assert shared.numel() > SPLIT_ZONE_BYTES
+    for k in (0, 1, 2, 0, 1, 2, 2, 1, 0):
         dw = dws[k]
-        say(f"[parity] shared workspace, shape {'AB'[k]}")
+        say(f"[parity] shared workspace, shape {'ABC'[k]}")
         dw.ws_decode = shared
         dw.decode(with_scores=False)
         torch.cuda.synchronize()
         assert torch.equal(dw.topk, refs[k][0])
         assert torch.equal(dw.out.view(torch.uint8), refs[k][1].view(torch.uint8))
-        assert int(torch.count_nonzero(shared)) == 0
+        assert int(torch.count_nonzero(shared[:SPLIT_ZONE_BYTES])) == 0
 
 
 def test_empty_batch_and_errors():
