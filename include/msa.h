@@ -184,8 +184,9 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * workspace give NaN for every split (row, group) until the caller
  * zero-fills it again.  msa_sparse_attend, and msa_decode calls that run the
  * three calls' kernels (block tables over 8064 blocks per row, chunks of 384
- * or more rows per sequence), clear the header and the zone they use at
- * the start of the call, like a caller's zero fill.
+ * or more rows per sequence), clear the header and the zone at the start of
+ * any call that uses them (split-K partials or the key-block path), like a
+ * caller's zero fill.
  */
 msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
 
