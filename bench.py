@@ -96,11 +96,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_256k",
                     choices=["fp8_256k", "fp8_long", "fp8_b32", "nvfp4_512k", "spec4_256k",
-                             "fp8_share64", "fp8_dcp45_shard", "prefill_64k", "prefill_16k",
-                             "prefill_64k_nvfp4"])
+                             "fp8_share64", "nvfp4_share64", "fp8_dcp45_shard", "prefill_64k",
+                             "prefill_16k", "prefill_64k_nvfp4"])
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated per step")
     ap.add_argument("--share-corr", type=float, default=0.0,
-                    help="fp8_share64 only: correlation of the requests' queries with their "
+                    help="fp8_share64 / nvfp4_share64 only: correlation of the requests' queries with their "
                          "group's common draw (requests continuing one prompt)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -119,8 +119,8 @@ def main():
         log("bench.py runs on one GPU only: the library has no multi-GPU path; "
             "run with --gpus 1")
         sys.exit(2)
-    if args.share_corr and args.workload != "fp8_share64":
-        log("--share-corr applies to the fp8_share64 workload only")
+    if args.share_corr and args.workload not in ("fp8_share64", "nvfp4_share64"):
+        log("--share-corr applies to the fp8_share64 and nvfp4_share64 workloads only")
         sys.exit(2)
 
     import numpy as np
@@ -145,7 +145,7 @@ def main():
     msa.lib()
     t0 = time.time()
     if args.share_corr:
-        w = synth.fp8_share64(share_corr=args.share_corr)
+        w = getattr(synth, args.workload)(share_corr=args.share_corr)
         w.recipe += f"; queries {args.share_corr} x the group's common draw"
     else:
         w = getattr(synth, args.workload)()

@@ -450,20 +450,31 @@ def fp8_256k(seed: int = 0x4D5341 + 5, **kw) -> Workload:
     return w
 
 
-def fp8_share64(seed: int = 0x4D5341 + 9, **kw) -> Workload:
+def _share64(name: str, kv_dtype: int, seed: int, **kw) -> Workload:
     """64 requests with a common 128K-token prefix (the same physical blocks
     in every block table) and private continuations of U[1, 8192] tokens,
     declared as one share group of 64."""
     pre = 131072
     rng = np.random.default_rng([seed, STREAM_TABLE, 1])
     lens = (pre + rng.integers(1, 8193, size=64)).tolist()
-    w = make("fp8_share64", seed=seed, seq_lens=lens, q_dtype=BF16, kv_dtype=FP8,
+    w = make(name, seed=seed, seq_lens=lens, q_dtype=BF16, kv_dtype=kv_dtype,
              plant_per_seq=8, plant_add=1.0, share_seqs=64, share_blocks=pre // 128, **kw)
+    fmt = "e4m3 K/V/index keys, N(0,1)" if kv_dtype == FP8 else \
+        "NVFP4 K/V/index keys quantised from N(0,1)"
     w.recipe = ("64 requests sharing a 131072-token prefix (same physical blocks) plus "
                 "U[1, 8192] private tokens each, one share group of 64, 64 q heads / 4 "
-                "groups, D=Di=128, bf16 q, e4m3 K/V/index keys, N(0,1), 8 planted blocks "
+                f"groups, D=Di=128, bf16 q, {fmt}, 8 planted blocks "
                 "per request, random permutation table")
     return w
+
+
+def fp8_share64(seed: int = 0x4D5341 + 9, **kw) -> Workload:
+    return _share64("fp8_share64", FP8, seed, **kw)
+
+
+def nvfp4_share64(seed: int = 0x4D5341 + 11, **kw) -> Workload:
+    """The shared-prefix batch with NVFP4 K/V and index keys."""
+    return _share64("nvfp4_share64", NVFP4, seed, **kw)
 
 
 def fp8_dcp45_shard(seed: int = 0x4D5341 + 10, **kw) -> Workload:
