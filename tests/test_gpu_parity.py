@@ -39,9 +39,13 @@ def _oracle_all(w, threads=0):
                          w.block_table, w.seq_lens, w.q_pos)
 
 
-def _run_and_check(w, fused, name):
-    say(f"[parity] {name}: oracle on {w.rows} rows")
-    s_ref, k_ref, o_ref, l_ref = _oracle_all(w)
+def _run_and_check(w, fused, name, ref=None):
+    """ref: the oracle's (scores, selection, out, lse) of w, when the caller
+    already has them."""
+    if ref is None:
+        say(f"[parity] {name}: oracle on {w.rows} rows")
+        ref = _oracle_all(w)
+    s_ref, k_ref, o_ref, l_ref = ref
     dw = parity.DeviceWorkload(w)
     say(f"[parity] {name}: GPU {'msa_decode' if fused else 'three-call chain'}")
     if fused:
@@ -956,6 +960,29 @@ def test_key_block_attention_groups(G, H, kv):
     tag = synth.DTYPE_NAMES[kv]
     _run_and_check(w, fused=True, name=f"k2q-g{G}-{tag}")
     _run_and_check(w, fused=False, name=f"k2q-g{G}-{tag}-chain")
+
+
+@pytest.mark.parametrize("K,init,local,kv", [(32, 2, 3, synth.FP8), (32, 0, 0, synth.NVFP4),
+                                           (4, 0, 0, synth.FP8), (1, 0, 0, synth.FP8)])
+def test_key_block_attention_top_k(K, init, local, kv):
+    """384 causal rows per sequence with top-k other than 16: 32 (the merge
+    takes its partials in two batches of 16; count slices of 128 rows), with
+    and without forced blocks, 4, and 1 (only each row's recent block, always
+    the masked case).  Two sequences (G = 2, 4 heads per group), one of them
+    shorter than 32 blocks (rows whose whole past is selected).  Through msa_decode and the chain,
+    against one oracle run."""
+    R = 384
+    lens = np.array([5500, 3000])
+    qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
+    base = synth.make(f"k2q-k{K}", seed=263 + K + kv, seq_lens=lens, rows_per_seq=R, q_pos=qp,
+                      num_q_heads=8, num_groups=2, top_k=K, q_dtype=synth.BF16, kv_dtype=kv,
+                      plant_per_seq=3)
+    w = dataclasses.replace(base, init_blocks=init, local_blocks=local)
+    tag = f"k2q-k{K}-i{init}-l{local}-{synth.DTYPE_NAMES[kv]}"
+    say(f"[parity] {tag}: oracle on {w.rows} rows")
+    ref = _oracle_all(w)
+    _run_and_check(w, fused=True, name=tag, ref=ref)
+    _run_and_check(w, fused=False, name=tag + "-chain", ref=ref)
 
 
 def test_key_block_attention_1024_rows():
