@@ -1024,6 +1024,55 @@ def test_key_block_attention_is_deterministic_and_equals_the_chain():
         assert torch.equal(dw.lse, ref[1])
 
 
+def test_key_block_attention_8000_blocks():
+    """A 384-row chunk over a 1,040,000-token context (8,125 blocks, near the
+    key-block path's 8,192-block limit): each thread of the list scan takes 8
+    blocks and the count's histogram spans 32 KB of LDS.  Rows at the end of
+    the context plus a few far back.  The oracle on sampled rows; every row's
+    selection against its own pooled scores; msa_decode equal to the chain
+    bit for bit."""
+    R, L = 384, 1_040_000
+    qp = np.arange(L - R, L).astype(np.int32)
+    qp[[5, 77, 200, 311]] = [0, 127, 128, 500_000]
+    w = synth.make("k2q-8000", seed=271, seq_lens=[L], rows_per_seq=R, q_pos=qp,
+                   num_q_heads=8, num_groups=2, q_dtype=synth.BF16, kv_dtype=synth.FP8,
+                   plant_per_seq=6)
+    assert w.max_blocks == 8125
+    dw = parity.DeviceWorkload(w)
+    say("[parity] k2q-8000: GPU three-call chain, then msa_decode")
+    dw.chain()
+    torch.cuda.synchronize()
+    ref = (dw.out.view(torch.uint8).clone(), dw.lse.clone(), dw.topk.clone())
+    dw.out.zero_()
+    dw.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(dw.topk, ref[2])
+    assert torch.equal(dw.out.view(torch.uint8), ref[0])
+    assert torch.equal(dw.lse, ref[1])
+    rows = [0, 5, 77, 128, 200, 311, 383]
+    ws = parity.subset_rows(w, rows)
+    say(f"[parity] k2q-8000: oracle on rows {rows}")
+    s_ref, k_ref, o_ref, l_ref = _oracle_all(ws)
+    serr = parity.check_scores(ws, dw.scores.cpu().numpy()[rows], s_ref)
+    same = parity.check_selection(ws, s_ref, k_ref, dw.topk.cpu().numpy()[rows])
+    aerr = parity.check_decode_attention(ws, dw.out.float().cpu().numpy()[rows], o_ref, same,
+                                         dw.topk.cpu().numpy()[rows])
+    parity.record("k2q-8000 (sampled rows)", same, serr, aerr)
+    S = dw.scores.cpu().numpy()
+    K = dw.topk.cpu().numpy()
+    assert np.isfinite(dw.out.float().cpu().numpy()).all()
+    for r in range(w.rows):
+        rb = parity.row_pos(w, r) // w.block_size
+        for g in range(w.num_groups):
+            sel = K[r, g][K[r, g] >= 0]
+            if rb + 1 <= w.top_k:
+                assert np.array_equal(sel, np.arange(rb + 1)), (r, g)
+                continue
+            cand = S[r, g, :rb]
+            order = np.lexsort((np.arange(rb), -cand))[: w.top_k - 1]
+            assert np.array_equal(np.sort(order), sel[:-1]) and sel[-1] == rb, (r, g)
+
+
 @pytest.mark.parametrize("name", ["prefill_64k", "prefill_64k_nvfp4"])
 def test_prefill_64k_sampled_rows(name):
     """The full chunked-prefill shape (65536 cached + 4096 queries, causal),
