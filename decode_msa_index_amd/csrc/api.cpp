@@ -3,6 +3,7 @@
 // (apart from the merge spin limit, a test hook).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -313,7 +314,12 @@ msa_status decode_impl(const msa_problem* p, const void* index_q, const void* ik
                                             q_pos, topk_idx, out, lse, ws + w.status, hs),
                   "sparse attend launch");
   if (st != MSA_OK || block_scores) return st;
-  return hip_status(msa::launch_zero_fill(ws + w.scores, w.total - w.scores, hs),
+  // the scores that lie inside the part of the workspace every call leaves
+  // zero (the status header and the split zone) are cleared again; past it
+  // (a large attention scratch before them) they may stay
+  const size_t zero_end = std::min(w.total, msa::kStatusBytes + msa::kSplitZoneBytes);
+  if (zero_end <= w.scores) return MSA_OK;
+  return hip_status(msa::launch_zero_fill(ws + w.scores, zero_end - w.scores, hs),
                     "workspace clear launch");
 }
 

@@ -15,12 +15,13 @@
 // selection is inverted instead, and every block is read and dequantised
 // once per chunk of up to kChunkRows rows that selected it:
 //   1. build:   workgroups over slices of a sequence's rows count the valid
-//               entries of topk_idx per (group, block) in LDS histograms and
-//               reserve their places in each block's bucket with one global
-//               atomic per block and slice; one workgroup per (sequence,
-//               group) scans the counts into bucket starts and a table of
-//               work chunks (up to kChunkRows entries of one block each);
-//               every entry then lands at its bucket start + place;
+//               entries of topk_idx per (group, block) in LDS histograms,
+//               each entry taking its place in its slice's part of the
+//               bucket, and store the whole histogram; one workgroup per
+//               (sequence, group) adds the slices' counts into bucket starts,
+//               each slice's offset in the bucket and a table of work chunks
+//               (up to kChunkRows entries of one block each); every entry
+//               then lands at bucket start + slice offset + place;
 //   2. attend:  one workgroup per chunk stages its block in LDS, K as bf16
 //               and V as f16 (both exact); each wave computes one entry at a
 //               time -- the entry's (up to 16) heads over that block: S^T =
@@ -64,12 +65,12 @@ constexpr size_t kPartialMlBytes = (size_t)kHeadsPad * 2 * 4;     // f32 [16 hea
 constexpr int kK2qMinRows = 384;
 constexpr int kK2qMaxBlocks = 8192;  // the count's LDS histogram of MB words
 
-// Buffers inside the workspace (after its status header).  Per (sequence,
+// Buffers inside the workspace (after its status header and the split zone).  Per (sequence,
 // group) bg: entries [bg * R * K, +R * K), chunks [bg * max_chunks, +max_chunks).
 struct K2qBufs {
-  int32_t* counts;    // [B*G][MB] entries per block
+  int32_t* counts;    // [B*G][slices][MB] a slice's entries per block, then its offset
   int32_t* starts;    // [B*G][MB] index of a block's first entry in `entries`
-  int32_t* place;     // [pairs] an entry's place in its bucket, -1: not attended
+  int32_t* place;     // [pairs] an entry's place in its slice's part of the bucket, -1: not attended
   int32_t* entries;   // [B*G][R*K] entry ids (u * K + slot), grouped by block
   int4* chunks;       // [B*G][max_chunks] (block j, first entry, end, physical block)
   int32_t* nchunks;   // [B*G] chunks in use
@@ -77,6 +78,7 @@ struct K2qBufs {
   uint4* o;           // [pairs][4][64] of 8 f16
   int max_chunks;     // per (sequence, group)
   int slices;         // count workgroups per (sequence, group)
+  int rows_per;       // rows of a slice
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -94,9 +96,14 @@ static K2qSizes k2q_sizes(const Shape& s) {
 }
 
 // Offsets of the buffers from the start of the region; the region's size.
+// Rows per count workgroup (a slice) and slices per (sequence, group).
+static int k2q_rows_per(const Shape& s) { return std::max(1, kCountThreads * kCountPairs / s.K); }
+static int k2q_slices(const Shape& s) { return (s.R + k2q_rows_per(s) - 1) / k2q_rows_per(s); }
+
 static size_t k2q_layout(const Shape& s, size_t off[8]) {
   const K2qSizes z = k2q_sizes(s);
-  const size_t sz[8] = {4 * (size_t)(z.bg * s.MB), 4 * (size_t)(z.bg * s.MB), 4 * (size_t)z.pairs,
+  const size_t sz[8] = {4 * (size_t)(z.bg * k2q_slices(s) * s.MB), 4 * (size_t)(z.bg * s.MB),
+                        4 * (size_t)z.pairs,
                         4 * (size_t)z.pairs, 16 * (size_t)(z.bg * z.max_chunks), 4 * (size_t)z.bg,
                         kPartialMlBytes * z.pairs, kPartialOBytes * z.pairs};
   size_t at = 0;
@@ -113,9 +120,11 @@ bool k2q_eligible(const Shape& s) {
          s.MB <= kK2qMaxBlocks;
 }
 
+// After the status header: the split zone, left alone, then the path's own
+// buffers.
 size_t k2q_workspace_bytes(const Shape& s) {
   size_t off[8];
-  return k2q_layout(s, off);
+  return kSplitZoneBytes + k2q_layout(s, off);
 }
 
 // The entries the per-row kernels attend: slot sidx below min(K, rb + 1)
@@ -159,19 +168,19 @@ __device__ __forceinline__ void scan_threads(uint32_t& e, uint32_t& c, uint32_t*
   c = bc + xc - c;
 }
 
-// (sequence, group, slice of rows): LDS histogram per block, one global
-// atomic per block to reserve the slice's places, then each entry's place.
+// (sequence, group, slice of rows): LDS histogram per block, each entry's
+// place among its slice's entries of that block, the histogram stored whole
+// (no atomics outside LDS, nothing to clear first).
 __global__ __launch_bounds__(kCountThreads) void k2q_count_kernel(AttendArgs a, K2qBufs w) {
   extern __shared__ int32_t hist[];  // [MB]
   const int tid = threadIdx.x;
   const int bg = blockIdx.x / w.slices, slice = blockIdx.x % w.slices;
   const int b = bg / a.G, g = bg % a.G;
-  const int rows_per = (a.R + w.slices - 1) / w.slices;
-  const int r0 = slice * rows_per, r1 = min(a.R, r0 + rows_per);
+  const int r0 = slice * w.rows_per, r1 = min(a.R, r0 + w.rows_per);
   const int n = max(0, r1 - r0) * a.K;  // <= kCountThreads * kCountPairs
   for (int x = tid; x < a.MB; x += kCountThreads) hist[x] = 0;
   __syncthreads();
-  int jj[kCountPairs], lp[kCountPairs];
+  int jj[kCountPairs];
 #pragma unroll
   for (int k = 0; k < kCountPairs; ++k) {
     const int i = tid + k * kCountThreads;
@@ -182,41 +191,51 @@ __global__ __launch_bounds__(kCountThreads) void k2q_count_kernel(AttendArgs a, 
     }
   }
 #pragma unroll
-  for (int k = 0; k < kCountPairs; ++k) lp[k] = jj[k] >= 0 ? atomicAdd(&hist[jj[k]], 1) : -1;
-  __syncthreads();
-  for (int x = tid; x < a.MB; x += kCountThreads) {
-    const int c = hist[x];
-    if (c > 0) hist[x] = atomicAdd(&w.counts[(size_t)bg * a.MB + x], c);
-  }
-  __syncthreads();
-#pragma unroll
   for (int k = 0; k < kCountPairs; ++k) {
     const int i = tid + k * kCountThreads;
+    const int lp = jj[k] >= 0 ? atomicAdd(&hist[jj[k]], 1) : -1;
     if (i < n) {
       const int row = b * a.R + r0 + i / a.K;
-      w.place[((size_t)row * a.G + g) * a.K + i % a.K] = jj[k] >= 0 ? hist[jj[k]] + lp[k] : -1;
+      w.place[((size_t)row * a.G + g) * a.K + i % a.K] = lp;
     }
   }
+  __syncthreads();
+  int32_t* cnt = w.counts + ((size_t)bg * w.slices + slice) * a.MB;
+  for (int x = tid; x < a.MB; x += kCountThreads) cnt[x] = hist[x];
 }
 
 // (sequence, group): bucket starts and the table of work chunks.
 __global__ __launch_bounds__(kScanThreads) void k2q_scan_kernel(AttendArgs a, K2qBufs w) {
   __shared__ uint32_t sm[32];
   const int tid = threadIdx.x, bg = blockIdx.x;
-  const int* cnt = w.counts + (size_t)bg * a.MB;
+  int* cnt = w.counts + (size_t)bg * w.slices * a.MB;  // [slices][MB]
   const int per = (a.MB + kScanThreads - 1) / kScanThreads;
   const int x0 = min(a.MB, tid * per), x1 = min(a.MB, x0 + per);
+  // each block's total over the slices; each slice's count becomes its
+  // offset inside the block's bucket
   uint32_t se = 0, sc = 0;
   for (int x = x0; x < x1; ++x) {
-    se += (uint32_t)cnt[x];
-    sc += ((uint32_t)cnt[x] + kChunkRows - 1) / kChunkRows;
+    int n = 0;
+    for (int s0 = 0; s0 < w.slices; s0 += 16) {  // 16 slices' loads in flight at once
+      int c[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) c[k] = s0 + k < w.slices ? cnt[(size_t)(s0 + k) * a.MB + x] : 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (s0 + k < w.slices) cnt[(size_t)(s0 + k) * a.MB + x] = n;
+        n += c[k];
+      }
+    }
+    w.starts[(size_t)bg * a.MB + x] = n;  // the total, for the pass below
+    se += (uint32_t)n;
+    sc += ((uint32_t)n + kChunkRows - 1) / kChunkRows;
   }
   scan_threads(se, sc, sm);
   const size_t ebase = (size_t)bg * a.R * a.K;
   const int b = bg / a.G;
   int4* chunks = w.chunks + (size_t)bg * w.max_chunks;
   for (int x = x0; x < x1; ++x) {
-    const int n = cnt[x];
+    const int n = w.starts[(size_t)bg * a.MB + x];
     const int start = (int)(ebase + se);
     w.starts[(size_t)bg * a.MB + x] = start;
     const int nch = (n + kChunkRows - 1) / kChunkRows;
@@ -236,7 +255,9 @@ __global__ __launch_bounds__(256) void k2q_scatter_kernel(AttendArgs a, K2qBufs 
   const int place = w.place[i];
   if (place < 0) return;
   const int u = i / a.K, row = u / a.G, g = u % a.G, b = row / a.R;
-  w.entries[w.starts[((size_t)b * a.G + g) * a.MB + a.topk[i]] + place] = i;
+  const int bg = b * a.G + g, slice = (row % a.R) / w.rows_per, j = a.topk[i];
+  const int off = w.counts[((size_t)bg * w.slices + slice) * a.MB + j];
+  w.entries[w.starts[(size_t)bg * a.MB + j] + off + place] = i;
 }
 
 // ---- 2. attend ------------------------------------------------------------------
@@ -616,18 +637,17 @@ __global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w)
 
 // ---- launch ----------------------------------------------------------------------
 
-// workspace: the status header, then this path's buffers.  The header and
-// the counts are cleared first (one fill: they are adjacent); after the
-// merge the split zone is cleared again (lists and the first records live
-// there), so that a later call of any shape finds it zero.
+// workspace: the status header and the split zone, both left alone (this
+// path needs neither and keeps a workspace's merge-failure mark as it is),
+// then this path's buffers, which need no clearing.
 hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
                              const void* kv_data, const void* kv_scales, void* workspace,
                              hipStream_t st) {
   size_t off[8];
-  const size_t region_bytes = k2q_layout(s, off);
+  k2q_layout(s, off);
   const K2qSizes z = k2q_sizes(s);
   if (z.pairs == 0) return hipSuccess;
-  char* base = static_cast<char*>(workspace) + kStatusBytes;
+  char* base = static_cast<char*>(workspace) + kStatusBytes + kSplitZoneBytes;
   K2qBufs w;
   w.counts = reinterpret_cast<int32_t*>(base + off[0]);
   w.starts = reinterpret_cast<int32_t*>(base + off[1]);
@@ -638,10 +658,8 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
   w.ml = reinterpret_cast<float*>(base + off[6]);
   w.o = reinterpret_cast<uint4*>(base + off[7]);
   w.max_chunks = (int)z.max_chunks;
-  const int rows_per = std::max(1, kCountThreads * kCountPairs / s.K);
-  w.slices = (s.R + rows_per - 1) / rows_per;
-  hipError_t e = launch_zero_fill(workspace, kStatusBytes + off[1], st);  // header + counts
-  if (e != hipSuccess) return e;
+  w.rows_per = k2q_rows_per(s);
+  w.slices = k2q_slices(s);
   hipLaunchKernelGGL(k2q_count_kernel, dim3((unsigned)(z.bg * w.slices)), dim3(kCountThreads),
                      sizeof(int32_t) * (size_t)s.MB, st, a, w);
   hipLaunchKernelGGL(k2q_scan_kernel, dim3((unsigned)z.bg), dim3(kScanThreads), 0, st, a, w);
@@ -658,9 +676,7 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
   else
     hipLaunchKernelGGL((k2q_attend_kernel<kNVFP4, E>), agrid, ablock, 0, st, qp, kd, ks, a, w);
   hipLaunchKernelGGL(k2q_merge_kernel, dim3((unsigned)(s.rows * s.G)), dim3(256), 0, st, a, w);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_zero_fill(base, std::min(region_bytes, kSplitZoneBytes), st);
+  return hipGetLastError();
 }
 
 }  // namespace msa

@@ -85,8 +85,8 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 hipStream_t st);
 // Chunks of many rows per sequence (chunked prefill): the attention grouped
 // by key block (k2q_attend.hip).  launch_sparse_attend takes this path when
-// k2q_eligible; its workspace after the status header is the path's own
-// (cleared in the header and the split zone, not beyond).
+// k2q_eligible; its workspace is the status header and the split zone, both
+// left untouched, then the path's own buffers.
 struct AttendArgs;
 bool k2q_eligible(const Shape& s);
 size_t k2q_workspace_bytes(const Shape& s);

@@ -6,6 +6,7 @@
 // MSA_STATIC_SCRATCH_BYTES, one copy per GPU, held until the process ends.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -69,9 +70,11 @@ extern "C" msa_status msa_decode_static(const msa_problem* p, const void* index_
   if (st != MSA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   // the array keeps the last call's contents (possibly a call that gave up
-  // waiting): the part this call's kernels need zero is cleared first, with
-  // a fill kernel rather than a memset node
-  st = hip_status(msa::launch_zero_fill(ws, w.total, hs), "scratch clear launch");
+  // waiting): the part this call's kernels need zero -- the status header
+  // and the split zone -- is cleared first, with a fill kernel rather than a
+  // memset node
+  const size_t zero_bytes = std::min(w.total, msa::kStatusBytes + msa::kSplitZoneBytes);
+  st = hip_status(msa::launch_zero_fill(ws, zero_bytes, hs), "scratch clear launch");
   if (st != MSA_OK) return st;
   return decode_impl(p, index_q, ik_data, ik_scales, q, kv_data, kv_scales, block_table,
                      seq_lens, q_pos, block_scores, topk_idx, out, lse, ws, w, hs);

@@ -156,8 +156,9 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  *   - msa_sparse_attend: room for the split-K partial states when a (row,
  *     group) is split over several workgroups (0 when it is not); for a
  *     chunk of 384 or more rows per sequence over an FP8 or NVFP4 cache, the
- *     key-block path's buffers instead (see msa_sparse_attend): about 4.3 KB
- *     per (row, group, top-k slot), 1.1 GB for 4,096 rows at G = 4, top-16;
+ *     zone described below (which that path leaves alone) followed by the
+ *     key-block path's buffers (see msa_sparse_attend): about 4.3 KB per
+ *     (row, group, top-k slot), 1.1 GB for 4,096 rows at G = 4, top-16;
  *   - msa_decode: B*R*G*MB words for the pooled scores, then that;
  *   - the other calls: 0.
  * Every region is rounded up to 256 bytes, and a workspace that holds
@@ -171,9 +172,10 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * Every msa_decode and msa_sparse_attend call leaves that part zero-filled
  * again, so one zero fill serves any sequence of calls and problem shapes;
  * past it a call may leave its scratch (the key-block path's lists and
- * partials).  msa_sparse_attend itself needs no initialisation (it clears
- * what it uses).  Calls that share a workspace must not overlap.  A call
- * whose size is 0 accepts a NULL workspace.
+ * partials, pooled scores that reach past the zone).  msa_sparse_attend
+ * itself needs no initialisation (it clears what it uses).  Calls that
+ * share a workspace must not overlap.  A call whose size is 0 accepts a
+ * NULL workspace.
  *
  * Failure mode: the workgroup that merges a (row, group)'s partial states
  * waits for them with a bounded poll (about a second).  Should it ever give
@@ -183,10 +185,11 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * msa_workspace_status reads the mark; later msa_decode calls on a marked
  * workspace give NaN for every split (row, group) until the caller
  * zero-fills it again.  msa_sparse_attend, and msa_decode calls that run the
- * three calls' kernels (block tables over 8064 blocks per row, chunks of 384
- * or more rows per sequence), clear the header and the zone at the start of
- * any call that uses them (split-K partials or the key-block path), like a
- * caller's zero fill.
+ * three calls' kernels (block tables over 8064 blocks per row), clear the
+ * header and the zone at the start of any call that splits a (row, group)
+ * over workgroups, like a caller's zero fill.  The key-block path (chunks of
+ * 384 or more rows per sequence) uses neither and leaves both as they are,
+ * a mark included.
  */
 msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
 

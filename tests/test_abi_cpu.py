@@ -124,9 +124,10 @@ def test_workspace_sizes():
 
 def test_workspace_sizes_of_the_key_block_path():
     """A chunk of 384+ rows per sequence over an FP8 or NVFP4 cache takes
-    the key-block attention, whose workspace holds per (row, group, slot) a
-    4 KB f16 partial, a 128-byte (max, sum) record and two list words, plus
-    small per-block arrays and the chunk table; 383 rows take the per-row
+    the key-block attention, whose workspace holds, after the status header
+    and the split-K zone, per (row, group, slot) a 4 KB f16 partial, a
+    128-byte (max, sum) record and two list words, plus per-slice and
+    per-block arrays and the chunk table; 383 rows take the per-row
     kernel, which needs none at 512+ (row, group) units."""
     def sizes(R, kv=2):
         p = good(num_seqs=1, rows_per_seq=R, max_blocks_per_seq=544, num_phys_blocks=544,
@@ -137,7 +138,8 @@ def test_workspace_sizes_of_the_key_block_path():
         a, d = sizes(4096, kv)
         slots = 4096 * 4 * 16
         per_slot = 4096 + 128 + 8
-        assert slots * per_slot < a - 256 < slots * per_slot * 1.001
+        zone = 512 * 16 * 130 * 4  # the split-K zone, which the path leaves alone
+        assert slots * per_slot < a - 256 - zone < slots * per_slot * 1.002
         # decode adds the pooled scores
         assert d - a == -(-(4096 * 4 * 544 * 4) // 256) * 256
     a384, _ = sizes(384)

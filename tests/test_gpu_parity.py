@@ -798,12 +798,18 @@ def test_rows_that_see_no_key(kv):
     parity.check_attention(w, o, o_ref)
 
 
-def test_decode_long_block_table_unfused_path():
+@pytest.mark.parametrize("lens", [[5000, 20000, 130], [130 + 977 * i for i in range(32)]])
+def test_decode_long_block_table_unfused_path(lens):
     """A block-table stride past the fused selection's LDS limit makes
-    msa_decode take the three-kernel path; results follow the same rules."""
-    w = synth.make("wide", seed=91, seq_lens=[5000, 20000, 130], q_dtype=synth.BF16,
+    msa_decode take the three-kernel path; results follow the same rules.
+    The status header and split zone are zero again afterwards: the pooled
+    scores kept in the workspace lie inside the zone for 3 sequences and
+    reach past it for 32, whose part past the zone may stay."""
+    w = synth.make(f"wide-{len(lens)}", seed=91, seq_lens=lens, q_dtype=synth.BF16,
                    kv_dtype=synth.FP8, max_blocks=9000, plant_per_seq=3)
-    _run_and_check(w, fused=True, name="wide-table")
+    dw, _ = _run_and_check(w, fused=True, name=f"wide-table-{len(lens)}")
+    assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0
+    assert (dw.ws_decode.numel() > SPLIT_ZONE_BYTES) == (len(lens) == 32)
 
 
 # ---------------------------------------------------------------------------
