@@ -16,8 +16,9 @@
  *   msa_decode         the three in one call
  * msa_decode's scores, selection, outputs and lse are bitwise those of the
  * three-call chain (both attend the selected blocks in ascending order with
- * the same launch shape, or both take the key-block path below).  A fifth call writes new tokens into the caches
- * the others read:
+ * the same launch shape, or both take the key-block path of
+ * msa_sparse_attend).  A fifth call writes new tokens into the caches the
+ * others read:
  *   msa_cache_write    quantise new K / V / index keys into their slots
  *
  * ---------------------------------------------------------------------------
