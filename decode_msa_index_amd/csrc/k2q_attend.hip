@@ -27,19 +27,21 @@
 //               time -- the entry's (up to 16) heads over that block: S^T =
 //               K Q^T and O = P V on MFMA, the block's softmax in fp32 --
 //               with the next entry's queries already in flight.  It stores
-//               a partial per entry: the normalised output O / l in f16 and
-//               (max, sum) in fp32, the sum l being that of the f16 weights
-//               the P V product uses (a ninth MFMA tile against ones);
+//               a partial per entry: the output O / l in f16 (O itself for
+//               e4m3 V, see kUnnormalised) and (max, sum) in fp32, the sum l
+//               being that of the f16 weights the P V product uses (a ninth
+//               MFMA tile against ones);
 //   3. merge:   one workgroup per (row, group) takes the row's largest
 //               partial maximum M, then sums the partials weighted by
-//               l 2^(max - M) in selection order (fp32), scales by v_scale
+//               l 2^(max - M) (2^(max - M) for O) in selection order (fp32),
+//               divides by the sum of l 2^(max - M), scales by v_scale
 //               and stores the output and lse; each wave a quarter of the
 //               dims, with all of its loads in flight at once.
 // Which wave takes which entry depends on the order of atomics; the
 // arithmetic of an entry and the merge order do not, so the results are
 // deterministic.  They differ from a per-row gather by the f16 rounding of
-// each block's normalised output (relative 2^-11), which the merge weights
-// by at most 1.
+// each block's output (relative 2^-11), which the merge weights by at most 1
+// once normalised.
 #include "attend_task.hpp"
 #include "device.hpp"
 #include "launch.hpp"
@@ -64,6 +66,13 @@ constexpr size_t kPartialMlBytes = (size_t)kHeadsPad * 2 * 4;     // f32 [16 hea
 // 256 rows and fewer the fixed cost of the extra launches dominates.
 constexpr int kK2qMinRows = 384;
 constexpr int kK2qMaxBlocks = 8192;  // the count's LDS histogram of MB words
+// The partial output a block leaves: O / l in f16 in general; O itself for
+// e4m3 V, where |O| <= (sum of the block's f16 weights, <= 128) * 448 =
+// 57,344 fits f16 (65,504) and the same relative rounding is had without a
+// multiply per value (the attend kernel's arithmetic adds to its time).
+// NVFP4 V reaches 6 * 448 per value, so there O is normalised first.
+template <int KV>
+constexpr bool kUnnormalised = KV == kFP8;
 
 // Buffers inside the workspace (after its status header and the split zone).  Per (sequence,
 // group) bg: entries [bg * R * K, +R * K), chunks [bg * max_chunks, +max_chunks).
@@ -510,21 +519,27 @@ __attribute__((amdgpu_waves_per_eu(K2qShape<E>::waves_per_simd))) void k2q_atten
         for (int e = 0; e < E; ++e) oacc[e][dt] = mfma_f16(pop[e][cc], vv, oacc[e][dt]);
       }
     }
-    // ---- the partials: O / l of heads 4qd+i, dims 16 dt + n, lane-major ----
+    // ---- the partials: O / l of heads 4qd+i, dims 16 dt + n, lane-major;
+    // O itself for e4m3 V (see kUnnormalised) ----
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (e > 0 && it0 + e >= cnt) break;
       float inv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) inv[i] = __builtin_amdgcn_rcpf(lacc[e][i]);
+      for (int i = 0; i < 4; ++i) inv[i] = kUnnormalised<KV> ? 1.0f : __builtin_amdgcn_rcpf(lacc[e][i]);
       uint4* po = w.o + (size_t)pair[e] * 256;
 #pragma unroll
       for (int p2 = 0; p2 < 4; ++p2) {
         f16x8 h;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          h[i] = (_Float16)(oacc[e][2 * p2][i] * inv[i]);
-          h[4 + i] = (_Float16)(oacc[e][2 * p2 + 1][i] * inv[i]);
+          if constexpr (kUnnormalised<KV>) {
+            h[i] = (_Float16)oacc[e][2 * p2][i];
+            h[4 + i] = (_Float16)oacc[e][2 * p2 + 1][i];
+          } else {
+            h[i] = (_Float16)(oacc[e][2 * p2][i] * inv[i]);
+            h[4 + i] = (_Float16)(oacc[e][2 * p2 + 1][i] * inv[i]);
+          }
         }
         // streaming stores: the partials are read once, by the merge, and
         // should not push the queries out of the caches
@@ -552,6 +567,7 @@ __attribute__((amdgpu_waves_per_eu(K2qShape<E>::waves_per_simd))) void k2q_atten
 // 16 heads from every partial (one 16-byte load per lane and partial, all
 // issued at once), weighted by l 2^(max - M) and summed in ascending slot
 // order, then stores those dims.
+template <bool UNNORM>
 __global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w) {
   __shared__ f32x4 mls[32 * 8];            // the unit's records: [slot][8 x 4 floats]
   __shared__ float ob[4][kHeadsPad][36];   // each wave's 16 heads x 32 dims
@@ -588,10 +604,11 @@ __global__ __launch_bounds__(256) void k2q_merge_kernel(AttendArgs a, K2qBufs w)
     const f16x8 h = __builtin_bit_cast(f16x8, piece);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float wt = l[i] * exp2f(m[i] - M[i]);
+      // the partial's weight: 2^(max - M) on O, l 2^(max - M) on O / l
+      const float f = exp2f(m[i] - M[i]), wt = l[i] * f, wo = UNNORM ? f : wt;
       L[i] += wt;
-      c0[i] = fmaf((float)h[i], wt, c0[i]);
-      c1[i] = fmaf((float)h[4 + i], wt, c1[i]);
+      c0[i] = fmaf((float)h[i], wo, c0[i]);
+      c1[i] = fmaf((float)h[4 + i], wo, c1[i]);
     }
   };
 #pragma unroll
@@ -675,7 +692,12 @@ hipError_t launch_k2q_attend(const Shape& s, const AttendArgs& a, const void* q,
     hipLaunchKernelGGL((k2q_attend_kernel<kFP8, E>), agrid, ablock, 0, st, qp, kd, ks, a, w);
   else
     hipLaunchKernelGGL((k2q_attend_kernel<kNVFP4, E>), agrid, ablock, 0, st, qp, kd, ks, a, w);
-  hipLaunchKernelGGL(k2q_merge_kernel, dim3((unsigned)(s.rows * s.G)), dim3(256), 0, st, a, w);
+  if (s.kv_dtype == kFP8)
+    hipLaunchKernelGGL(k2q_merge_kernel<kUnnormalised<kFP8>>, dim3((unsigned)(s.rows * s.G)),
+                       dim3(256), 0, st, a, w);
+  else
+    hipLaunchKernelGGL(k2q_merge_kernel<kUnnormalised<kNVFP4>>, dim3((unsigned)(s.rows * s.G)),
+                       dim3(256), 0, st, a, w);
   return hipGetLastError();
 }
 

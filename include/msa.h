@@ -239,9 +239,9 @@ msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
  * block instead (API reference, MiniMaxM3Model: the top-k buffer inverted by
  * build_k2q_csr): each selected block is read and dequantised once per up to
  * 64 rows that selected it, each (row, group, block) leaves a partial whose
- * normalised output is rounded to f16, and each row's partials are merged in
- * selection order with fp32 weights; out and lse then differ from a per-row
- * gather by that rounding (relative 2^-11 of each partial).  topk_idx: the first
+ * output is rounded to f16, and each row's partials are merged in selection
+ * order with fp32 weights; out and lse then differ from a per-row gather by
+ * that rounding (relative 2^-11 of each partial).  topk_idx: the first
  * min(top_k, last visible block + 1) entries of a row are read; an entry
  * outside [0, last visible block] contributes nothing (msa_block_topk never
  * writes one).  kv_scales is required for NVFP4 and ignored otherwise.  lse
