@@ -195,10 +195,10 @@ __global__ __launch_bounds__(64) void block_topk_wave_kernel(
   const int u = blockIdx.x, row = u / G, b = row / R;
   const float* s = scores + (size_t)u * MB;
   // the first round of score loads does not wait for the row length
-  load_keys(s, min(MB, 32 * 64), lds + 256, 64);
+  load_keys<16>(s, min(MB, 16 * 64), lds + 256, 64);
   const int pos = row_last_key(lens, qpos, row, b, MB);
   const int rb = pos < 0 ? -1 : pos / kBlock;
-  if (rb > 32 * 64) load_keys(s + 32 * 64, rb - 32 * 64, lds + 256 + 32 * 64, 64);
+  if (rb > 16 * 64) load_keys<16>(s + 16 * 64, rb - 16 * 64, lds + 256 + 16 * 64, 64);
   wave_lds_sync();
   wave_select_keys(lds + 256, rb, K, init, local, lds, topk + (size_t)u * K);
 }

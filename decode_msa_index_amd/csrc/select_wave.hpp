@@ -433,17 +433,18 @@ __device__ __forceinline__ int sort_selection(int entry, int K) {
 }
 
 // Loads the row's scores s[0..n) into LDS as order keys.  All loads of a
-// round (32 per thread) are in flight together; the row has MB entries, so
+// round (PT per thread) are in flight together; the row has MB entries, so
 // reading up to n = MB needs no row length.  Called by threads 0..nthreads-1.
+template <int PT = 32>
 __device__ __forceinline__ void load_keys(const float* __restrict__ s, int n, uint32_t* keys,
                                           int nthreads) {
   const int t = threadIdx.x;
-  for (int base = 0; base < n; base += 32 * nthreads) {
-    float v[32];
+  for (int base = 0; base < n; base += PT * nthreads) {
+    float v[PT];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) v[r] = s[min(base + r * nthreads + t, n - 1)];
+    for (int r = 0; r < PT; ++r) v[r] = s[min(base + r * nthreads + t, n - 1)];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < PT; ++r) {
       const int jj = base + r * nthreads + t;
       if (jj < n) keys[jj] = order_key(v[r]);
     }
