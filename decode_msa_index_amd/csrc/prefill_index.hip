@@ -203,7 +203,7 @@ __device__ __forceinline__ void make_b(const uint4 (&raw)[4], f16x8 (&b)[4], flo
 }
 
 template <int IK>
-__global__ __launch_bounds__(256, 2) void prefill_index_kernel(PrefillArgs x) {
+__global__ __launch_bounds__(256, 3) void prefill_index_kernel(PrefillArgs x) {
   // two staged key blocks, swizzled; two arrays rather than one [2][...] so
   // that the compiler sees the reads of one and the LDS-direct loads into the
   // other as disjoint and does not wait for those loads before the reads
