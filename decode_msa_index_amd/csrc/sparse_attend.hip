@@ -21,8 +21,11 @@
 
 namespace msa {
 
+// At most 256 registers per lane (VGPRs and AGPRs together), so that every
+// form keeps 2 waves per SIMD: the one-wave form, used for grids of many
+// units, came out a few registers past that (1 wave per SIMD) on its own.
 template <int KV, int NW, bool SELECT>
-__global__ __launch_bounds__(64 * NW) void attend_mfma_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attend_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kvd,
     const uint8_t* __restrict__ kvs, AttendArgs a, Partials part) {
   extern __shared__ uint32_t sel_lds[];
