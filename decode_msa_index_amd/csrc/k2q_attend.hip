@@ -61,10 +61,11 @@ constexpr int kCountPairs = 16;  // entries per thread of a count workgroup
 constexpr size_t kPartialOBytes = (size_t)kHeadsPad * kDim * 2;   // f16 [4][64 lanes][8]
 constexpr size_t kPartialMlBytes = (size_t)kHeadsPad * 2 * 4;     // f32 [16 heads][max, sum]
 // Rows per sequence from which the grouping pays: measured on a 65,536-token
-// context (G = 4, top-16) against the per-(row, group) kernel, 0.177 against
-// 0.191 ms per step at 384 rows and 1.05 against 1.36 ms at 4,096 rows; at
-// 256 rows and fewer the fixed cost of the extra launches dominates.
-constexpr int kK2qMinRows = 384;
+// context (G = 4, top-16, FP8) against the per-(row, group) kernel, msa_decode
+// per step: 182 against 171 us at 512 rows, 230 against 247 us at 768,
+// 0.81 against 1.11 ms at 4,096; below the crossover the fixed cost of the
+// list build and the merge dominates.
+constexpr int kK2qMinRows = 640;
 constexpr int kK2qMaxBlocks = 8192;  // the count's LDS histogram of MB words
 // The partial output a block leaves: O / l in f16 in general; O itself for
 // e4m3 V, where |O| <= (sum of the block's f16 weights, <= 128) * 448 =

@@ -156,7 +156,7 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * Workspace bytes a call needs for problem p (op as for msa_check_problem):
  *   - msa_sparse_attend: room for the split-K partial states when a (row,
  *     group) is split over several workgroups (0 when it is not); for a
- *     chunk of 384 or more rows per sequence over an FP8 or NVFP4 cache, the
+ *     chunk of 640 or more rows per sequence over an FP8 or NVFP4 cache, the
  *     zone described below (which that path leaves alone) followed by the
  *     key-block path's buffers (see msa_sparse_attend): about 4.3 KB per
  *     (row, group, top-k slot), 1.1 GB for 4,096 rows at G = 4, top-16;
@@ -189,7 +189,7 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * three calls' kernels (block tables over 8064 blocks per row), clear the
  * header and the zone at the start of any call that splits a (row, group)
  * over workgroups, like a caller's zero fill.  The key-block path (chunks of
- * 384 or more rows per sequence) uses neither and leaves both as they are,
+ * 640 or more rows per sequence) uses neither and leaves both as they are,
  * a mark included.
  */
 msa_status msa_workspace_bytes(const msa_problem* p, int32_t op, size_t* bytes);
@@ -234,7 +234,7 @@ msa_status msa_block_topk(const msa_problem* p, const float* block_scores,
  * blocks: out = sum_t softmax_t(sm_scale * k_scale * q.k_t) * v_scale * v_t,
  * with fp32 softmax state, split over the selected blocks (across the waves
  * of a workgroup and, for small batches, across workgroups, one of which
- * merges the others' partial states).  A chunk of 384 or more rows per
+ * merges the others' partial states).  A chunk of 640 or more rows per
  * sequence over an FP8 or NVFP4 cache (chunked prefill) is grouped by key
  * block instead (API reference, MiniMaxM3Model: the top-k buffer inverted by
  * build_k2q_csr): each selected block is read and dequantised once per up to
@@ -259,7 +259,7 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
  * msa_block_topk -> msa_sparse_attend; scores, selection, out and lse are
  * bitwise the three calls'.  For FP8 or NVFP4 caches and block tables of up
  * to 8064 blocks per row (about a million tokens) it is two kernels, the
- * scan and then selection + attention in one; chunks of 384 or more rows
+ * scan and then selection + attention in one; chunks of 640 or more rows
  * per sequence, longer tables and fp32 caches run the three calls' kernels
  * in turn.
  * topk_idx receives the selection; block_scores (nullable) receives the

@@ -123,17 +123,17 @@ def test_workspace_sizes():
 
 
 def test_workspace_sizes_of_the_key_block_path():
-    """A chunk of 384+ rows per sequence over an FP8 or NVFP4 cache takes
+    """A chunk of 640+ rows per sequence over an FP8 or NVFP4 cache takes
     the key-block attention, whose workspace holds, after the status header
     and the split-K zone, per (row, group, slot) a 4 KB f16 partial, a
     128-byte (max, sum) record and two list words, plus per-slice and
-    per-block arrays and the chunk table; 383 rows take the per-row
+    per-block arrays and the chunk table; 639 rows take the per-row
     kernel, which needs none at 512+ (row, group) units."""
     def sizes(R, kv=2):
         p = good(num_seqs=1, rows_per_seq=R, max_blocks_per_seq=544, num_phys_blocks=544,
                  kv_dtype=kv)
         return msa.workspace_bytes(p, msa.OP_ATTEND), msa.workspace_bytes(p, msa.OP_DECODE)
-    assert sizes(383)[0] == 0
+    assert sizes(639)[0] == 0
     for kv in (2, 3):
         a, d = sizes(4096, kv)
         slots = 4096 * 4 * 16
@@ -142,8 +142,8 @@ def test_workspace_sizes_of_the_key_block_path():
         assert slots * per_slot < a - 256 - zone < slots * per_slot * 1.002
         # decode adds the pooled scores
         assert d - a == -(-(4096 * 4 * 544 * 4) // 256) * 256
-    a384, _ = sizes(384)
-    assert a384 > 384 * 4 * 16 * (4096 + 128 + 8)
+    a640, _ = sizes(640)
+    assert a640 > 640 * 4 * 16 * (4096 + 128 + 8)
 
 
 def test_status_strings():

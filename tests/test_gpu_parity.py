@@ -726,10 +726,10 @@ SPLIT_ZONE_BYTES = 256 + 512 * 16 * 130 * 4
 def test_one_workspace_across_shapes():
     """msa_decode leaves the status header and the split-K zone of its
     workspace zero-filled, so one workspace (zeroed once) serves calls of
-    different shapes in any order: two split-K decode shapes and a 384-row
-    prefill chunk whose key-block attention writes lists and partials over
-    the zone and beyond (and clears the zone after use)."""
-    R = 384
+    different shapes in any order: two split-K decode shapes and a 640-row
+    prefill chunk whose key-block attention keeps its lists and partials
+    past the zone and leaves the header and the zone as they are."""
+    R = 640
     qp = np.arange(5000 - R, 5000).astype(np.int32)
     ws_ = [synth.make("shapeA", seed=61, seq_lens=[9000, 40000, 128, 1], q_dtype=synth.BF16,
                       kv_dtype=synth.FP8, plant_per_seq=3),
@@ -884,7 +884,7 @@ def test_prefill_scattered_positions(kv):
 
 
 # ---------------------------------------------------------------------------
-# chunked prefill (384+ rows per sequence): the attention grouped by key block
+# chunked prefill (640+ rows per sequence): the attention grouped by key block
 # ---------------------------------------------------------------------------
 
 SCATTER_QP = [-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 2900,
@@ -893,26 +893,28 @@ SCATTER_QP = [-1, 0, 1, 126, 127, 128, 129, 255, 256, 1000, 2047, 2048, 2049, 29
 
 @pytest.mark.parametrize("kv", [synth.FP8, synth.NVFP4])
 def test_key_block_attention_edge_cases(kv):
-    """Two sequences of 384 rows: one at scattered positions (rows that see no
+    """Two sequences of 640 rows: one at scattered positions (rows that see no
     key or one key, block edges, positions past the end), one causal at its
     end; an out-of-pool table entry in each sequence, one of them the recent
     block of some rows.  Through msa_decode and the chain, then
     msa_sparse_attend on a given selection with malformed entries (-1, past
     the row's recent block, a duplicate, attended twice as by the oracle):
     outputs and lse against the oracle."""
-    R = 384
+    R = 640
     lens = np.array([3000, 4100])
-    qp = np.concatenate([np.array((SCATTER_QP * 16)[:R]),
+    qp = np.concatenate([np.array((SCATTER_QP * 27)[:R]),
                          np.arange(lens[1] - R, lens[1])]).astype(np.int32)
     base = synth.make(f"k2q-edge-{kv}", seed=211 + kv, seq_lens=lens, rows_per_seq=R, q_pos=qp,
-                      q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2)
+                      num_q_heads=16, q_dtype=synth.BF16, kv_dtype=kv, plant_per_seq=2)
     bt = base.block_table.copy()
     bt[0, 5] = -1
     bt[1, 31] = base.num_phys_blocks  # the recent block of sequence 1's rows 3968 .. 4095
     w = dataclasses.replace(base, block_table=bt)
     tag = synth.DTYPE_NAMES[kv]
-    _run_and_check(w, fused=True, name=f"k2q-edge-{tag}")
-    dw, _ = _run_and_check(w, fused=False, name=f"k2q-edge-{tag}-chain")
+    say(f"[parity] k2q-edge-{tag}: oracle on {w.rows} rows")
+    ref = _oracle_all(w)
+    _run_and_check(w, fused=True, name=f"k2q-edge-{tag}", ref=ref)
+    dw, _ = _run_and_check(w, fused=False, name=f"k2q-edge-{tag}-chain", ref=ref)
     # a given selection with malformed entries, inside each row's first
     # min(K, rb + 1) slots (the entries the kernels read)
     k_given = dw.topk.cpu().numpy().copy()
@@ -938,46 +940,50 @@ def test_key_block_attention_edge_cases(kv):
 
 
 def test_key_block_attention_many_chunks_per_block():
-    """400 causal rows with the first block forced for every row: bucket 0
-    of each group holds 400 entries, seven work chunks; local_blocks = 2.
+    """700 causal rows with the first block forced for every row: bucket 0
+    of each group holds 700 entries, eleven work chunks; local_blocks = 2.
     Through msa_decode and the chain."""
-    R = 400
+    R = 700
     lens = np.array([20000])
     qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
     base = synth.make("k2q-chunks", seed=233, seq_lens=lens, rows_per_seq=R, q_pos=qp,
-                      q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3)
+                      num_q_heads=16, q_dtype=synth.BF16, kv_dtype=synth.FP8, plant_per_seq=3)
     w = dataclasses.replace(base, init_blocks=1, local_blocks=2)
-    dw, _ = _run_and_check(w, fused=True, name="k2q-chunks")
+    say(f"[parity] k2q-chunks: oracle on {w.rows} rows")
+    ref = _oracle_all(w)
+    dw, _ = _run_and_check(w, fused=True, name="k2q-chunks", ref=ref)
     assert np.all(dw.topk.cpu().numpy()[:, :, 0] == 0)
-    _run_and_check(w, fused=False, name="k2q-chunks-chain")
+    _run_and_check(w, fused=False, name="k2q-chunks-chain", ref=ref)
 
 
 @pytest.mark.parametrize("G,H,kv", [(8, 64, synth.NVFP4), (1, 16, synth.FP8)])
 def test_key_block_attention_groups(G, H, kv):
-    """384 causal rows with G = 8 (8 heads per group: half of each MFMA
+    """640 causal rows with G = 8 (8 heads per group: half of each MFMA
     column tile is padding) over NVFP4, and G = 1 over FP8; through
     msa_decode and the chain."""
-    R = 384
+    R = 640
     lens = np.array([6000])
     qp = np.arange(lens[0] - R, lens[0]).astype(np.int32)
     w = synth.make(f"k2q-g{G}", seed=251 + G, seq_lens=lens, rows_per_seq=R, q_pos=qp,
                    num_q_heads=H, num_groups=G, q_dtype=synth.BF16, kv_dtype=kv,
                    plant_per_seq=3)
     tag = synth.DTYPE_NAMES[kv]
-    _run_and_check(w, fused=True, name=f"k2q-g{G}-{tag}")
-    _run_and_check(w, fused=False, name=f"k2q-g{G}-{tag}-chain")
+    say(f"[parity] k2q-g{G}-{tag}: oracle on {w.rows} rows")
+    ref = _oracle_all(w)
+    _run_and_check(w, fused=True, name=f"k2q-g{G}-{tag}", ref=ref)
+    _run_and_check(w, fused=False, name=f"k2q-g{G}-{tag}-chain", ref=ref)
 
 
 @pytest.mark.parametrize("K,init,local,kv", [(32, 2, 3, synth.FP8), (32, 0, 0, synth.NVFP4),
                                            (4, 0, 0, synth.FP8), (1, 0, 0, synth.FP8)])
 def test_key_block_attention_top_k(K, init, local, kv):
-    """384 causal rows per sequence with top-k other than 16: 32 (the merge
+    """640 causal rows per sequence with top-k other than 16: 32 (the merge
     takes its partials in two batches of 16; count slices of 128 rows), with
     and without forced blocks, 4, and 1 (only each row's recent block, always
     the masked case).  Two sequences (G = 2, 4 heads per group), one of them
     shorter than 32 blocks (rows whose whole past is selected).  Through msa_decode and the chain,
     against one oracle run."""
-    R = 384
+    R = 640
     lens = np.array([5500, 3000])
     qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
     base = synth.make(f"k2q-k{K}", seed=263 + K + kv, seq_lens=lens, rows_per_seq=R, q_pos=qp,
@@ -1002,15 +1008,17 @@ def test_key_block_attention_1024_rows():
     w = synth.make("k2q-1024", seed=239, seq_lens=lens, rows_per_seq=R, q_pos=qp,
                    num_q_heads=8, num_groups=2, q_dtype=synth.BF16, kv_dtype=synth.FP8,
                    plant_per_seq=3)
-    _run_and_check(w, fused=True, name="k2q-1024")
-    _run_and_check(w, fused=False, name="k2q-1024-chain")
+    say(f"[parity] k2q-1024: oracle on {w.rows} rows")
+    ref = _oracle_all(w)
+    _run_and_check(w, fused=True, name="k2q-1024", ref=ref)
+    _run_and_check(w, fused=False, name="k2q-1024-chain", ref=ref)
 
 
 def test_key_block_attention_is_deterministic_and_equals_the_chain():
     """Which wave attends which entry follows the order of atomics; the
     results do not: repeated msa_decode calls and the three-call chain give
     bit-identical outputs and lse."""
-    R = 384
+    R = 640
     lens = np.array([9000, 6100])
     qp = np.concatenate([np.arange(L - R, L) for L in lens]).astype(np.int32)
     w = synth.make("k2q-det", seed=47, seq_lens=lens, rows_per_seq=R, q_pos=qp,
@@ -1031,13 +1039,13 @@ def test_key_block_attention_is_deterministic_and_equals_the_chain():
 
 
 def test_key_block_attention_8000_blocks():
-    """A 384-row chunk over a 1,040,000-token context (8,125 blocks, near the
+    """A 640-row chunk over a 1,040,000-token context (8,125 blocks, near the
     key-block path's 8,192-block limit): each thread of the list scan takes 8
     blocks and the count's histogram spans 32 KB of LDS.  Rows at the end of
     the context plus a few far back.  The oracle on sampled rows; every row's
     selection against its own pooled scores; msa_decode equal to the chain
     bit for bit."""
-    R, L = 384, 1_040_000
+    R, L = 640, 1_040_000
     qp = np.arange(L - R, L).astype(np.int32)
     qp[[5, 77, 200, 311]] = [0, 127, 128, 500_000]
     w = synth.make("k2q-8000", seed=271, seq_lens=[L], rows_per_seq=R, q_pos=qp,

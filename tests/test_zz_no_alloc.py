@@ -52,13 +52,13 @@ def test_static_scratch_decode_equals_workspace_decode(kv):
 
 
 def test_static_scratch_key_block_chunk():
-    """A 384-row prefill chunk small enough for the static scratch (G = 1,
-    top-4: its key-block lists and partials take about 6.5 MB after the
+    """A 640-row prefill chunk small enough for the static scratch (G = 1,
+    top-4: its key-block lists and partials take about 10.8 MB after the
     4.3 MB split zone), then a small decode batch on the same scratch: each
     bit for bit equal to msa_decode."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    R = 384
+    R = 640
     qp = np.arange(3000 - R, 3000).astype(np.int32)
     chunk = synth.make("static-k2q", seed=311, seq_lens=[3000], rows_per_seq=R, q_pos=qp,
                        num_q_heads=16, num_groups=1, q_dtype=synth.BF16, kv_dtype=synth.FP8,
