@@ -57,7 +57,8 @@ constexpr int kChunkRows = 64;  // entries (rows) per work chunk
 constexpr int kK2qEntries = 1;
 constexpr int kScanThreads = 1024;
 constexpr int kCountThreads = 256;
-constexpr int kCountPairs = 16;  // entries per thread of a count workgroup
+constexpr int kCountPairs = 4;  // entries per thread of a count workgroup
+constexpr int kScanBatch = 16;  // slice counts a scan thread loads at once
 constexpr size_t kPartialOBytes = (size_t)kHeadsPad * kDim * 2;   // f16 [4][64 lanes][8]
 constexpr size_t kPartialMlBytes = (size_t)kHeadsPad * 2 * 4;     // f32 [16 heads][max, sum]
 // Rows per sequence from which the grouping pays: measured on a 65,536-token
@@ -226,12 +227,13 @@ __global__ __launch_bounds__(kScanThreads) void k2q_scan_kernel(AttendArgs a, K2
   uint32_t se = 0, sc = 0;
   for (int x = x0; x < x1; ++x) {
     int n = 0;
-    for (int s0 = 0; s0 < w.slices; s0 += 16) {  // 16 slices' loads in flight at once
-      int c[16];
+    for (int s0 = 0; s0 < w.slices; s0 += kScanBatch) {  // the slices' loads in flight at once
+      int c[kScanBatch];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) c[k] = s0 + k < w.slices ? cnt[(size_t)(s0 + k) * a.MB + x] : 0;
+      for (int k = 0; k < kScanBatch; ++k)
+        c[k] = s0 + k < w.slices ? cnt[(size_t)(s0 + k) * a.MB + x] : 0;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < kScanBatch; ++k) {
         if (s0 + k < w.slices) cnt[(size_t)(s0 + k) * a.MB + x] = n;
         n += c[k];
       }
