@@ -261,6 +261,8 @@ __global__ __launch_bounds__(kScanThreads) void k2q_scan_kernel(AttendArgs a, K2
   if (tid == kScanThreads - 1) w.nchunks[bg] = (int)sc;  // past every chunk
 }
 
+// (32-bit entry indices: the host allows at most 65,535 (row, group) units
+// of at most 32 slots.)
 __global__ __launch_bounds__(256) void k2q_scatter_kernel(AttendArgs a, K2qBufs w, int pairs) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= pairs) return;
