@@ -1142,3 +1142,25 @@ def test_full_size(name):
     w = getattr(synth, name)()
     dw, same = _run_and_check(w, fused=True, name=name)
     assert same.mean() > 0.9
+
+
+@pytest.mark.parametrize("name", ["fp8_share64", "nvfp4_share64"])
+def test_full_size_shared_prefix(name):
+    """The shared-prefix batches (64 requests on one 131,072-token prefix,
+    one share group of 64): msa_decode with the share hint against the
+    oracle on every output, then bit for bit against the same call without
+    the hint (scores, selection, output, lse)."""
+    say(f"[parity] generating {name}")
+    w = getattr(synth, name)()
+    assert w.share_seqs == 64
+    dw, same = _run_and_check(w, fused=True, name=name)
+    assert same.mean() > 0.9
+    hinted = (dw.scores.clone(), dw.topk.clone(), dw.out.view(torch.uint8).clone(), dw.lse.clone())
+    say(f"[parity] {name}: the same call without the share hint")
+    dw0 = parity.DeviceWorkload(dataclasses.replace(w, share_seqs=0))
+    dw0.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(dw0.scores, hinted[0])
+    assert torch.equal(dw0.topk, hinted[1])
+    assert torch.equal(dw0.out.view(torch.uint8), hinted[2])
+    assert torch.equal(dw0.lse, hinted[3])
