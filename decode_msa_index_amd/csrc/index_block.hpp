@@ -200,19 +200,29 @@ struct HalfRaw<kFP8> {
   }
   __device__ __forceinline__ void pool(int j, int h2, int pos, int lane, const QueryB<kFP8>& q,
                                        TileMax& tm, uint4* stage) const {
-    // token t (0..63) row at 8t chunks; chunk c at slot c ^ (t % 8).  The
-    // syncs order the lanes' LDS accesses: reads of the previous half, these
-    // writes, then reads of other lanes' writes.
+    // The syncs order the lanes' LDS accesses: reads of the previous half,
+    // these writes, then reads of other lanes' writes.
     wave_lds_sync();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) stage[(8 * i + (lane >> 3)) * 8 + ((lane & 7) ^ (lane >> 3))] = r[i];
+    for (int i = 0; i < 8; ++i) stage[stage_slot(i, lane)] = r[i];
     wave_lds_sync();
+    fold_staged(j, h2, pos, lane, q, tm, stage);
+  }
+  // LDS slot of the half's 16-byte chunk lane % 8 of token 8i + lane / 8:
+  // token t's row is at 8t chunks, chunk c at slot c ^ (t % 8)
+  __device__ static __forceinline__ int stage_slot(int i, int lane) {
+    return (8 * i + (lane >> 3)) * 8 + ((lane & 7) ^ (lane >> 3));
+  }
+  // Folds half h2 of logical block j, staged at st, into tm (keys t <= pos).
+  __device__ static __forceinline__ void fold_staged(int j, int h2, int pos, int lane,
+                                                     const QueryB<kFP8>& q, TileMax& tm,
+                                                     const uint4* st) {
     const int n = lane & 15, rg = lane >> 4;
     const int tok = j * kBlock + 64 * h2 + 4 * rg;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint4 v0 = stage[(16 * t + n) * 8 + (rg ^ (n & 7))];
-      const uint4 v1 = stage[(16 * t + n) * 8 + ((rg + 4) ^ (n & 7))];
+      const uint4 v0 = st[(16 * t + n) * 8 + (rg ^ (n & 7))];
+      const uint4 v1 = st[(16 * t + n) * 8 + ((rg + 4) ^ (n & 7))];
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       acc = mfma_bf16(fp8x8_bf16(v0.x, v0.y), q.b[0], acc);
       acc = mfma_bf16(fp8x8_bf16(v0.z, v0.w), q.b[1], acc);
