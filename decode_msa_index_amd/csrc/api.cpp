@@ -75,7 +75,12 @@ WsLayout ws_layout(const msa_problem* p, int op) {
   w.attend = msa::kStatusBytes;
   w.scores = w.attend + attend;
   w.total = w.scores;
-  if (op == kOpDecode) w.total += round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
+  if (op == kOpDecode) {
+    // the pooled scores lie past the split zone, which every call leaves
+    // zero: they need no clearing after use
+    w.scores = std::max(w.scores, msa::kStatusBytes + msa::kSplitZoneBytes);
+    w.total = w.scores + round_up(sizeof(float) * (size_t)s.rows * s.G * s.MB);
+  }
   return w;
 }
 
@@ -289,7 +294,6 @@ msa_status decode_impl(const msa_problem* p, const void* index_q, const void* ik
   void* aws = ws + w.attend;
   uint32_t* status = reinterpret_cast<uint32_t*>(ws + w.status);
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
-  float* ws_scores = block_scores ? nullptr : scores;  // cleared again after use
   msa_status st;
   if (msa::select_fusable(s)) {
     // two launches: the index scan, then selection + attention in one kernel
@@ -299,10 +303,10 @@ msa_status decode_impl(const msa_problem* p, const void* index_q, const void* ik
     if (st != MSA_OK) return st;
     return hip_status(msa::launch_select_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
                                                 q_pos, scores, topk_idx, out, lse, aws, status,
-                                                ws_scores, hs),
+                                                hs),
                       "select + attend launch");
   }
-  // three kernels; pooled scores kept in the workspace are cleared again
+  // three kernels
   st = hip_status(msa::launch_index_scores(s, index_q, ik_data, ik_scales, block_table,
                                            seq_lens, q_pos, scores, hs),
                   "index scores launch");
@@ -310,17 +314,9 @@ msa_status decode_impl(const msa_problem* p, const void* index_q, const void* ik
   st = hip_status(msa::launch_block_topk(s, scores, seq_lens, q_pos, topk_idx, hs),
                   "block top-k launch");
   if (st != MSA_OK) return st;
-  st = hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
-                                            q_pos, topk_idx, out, lse, ws + w.status, hs),
-                  "sparse attend launch");
-  if (st != MSA_OK || block_scores) return st;
-  // the scores that lie inside the part of the workspace every call leaves
-  // zero (the status header and the split zone) are cleared again; past it
-  // (a large attention scratch before them) they may stay
-  const size_t zero_end = std::min(w.total, msa::kStatusBytes + msa::kSplitZoneBytes);
-  if (zero_end <= w.scores) return MSA_OK;
-  return hip_status(msa::launch_zero_fill(ws + w.scores, zero_end - w.scores, hs),
-                    "workspace clear launch");
+  return hip_status(msa::launch_sparse_attend(s, q, kv_data, kv_scales, block_table, seq_lens,
+                                              q_pos, topk_idx, out, lse, ws + w.status, hs),
+                    "sparse attend launch");
 }
 
 msa_status check_decode_args(const msa_problem* p, const void* index_q,

@@ -54,7 +54,6 @@ struct AttendArgs {
   const int32_t* qpos;
   const int32_t* topk;    // selection input (attend only)
   const float* scores;    // pooled scores (select + attend, written by an earlier kernel)
-  uint32_t* clear;        // select + attend: [units][MB] words the last reader zeroes (nullable)
   int32_t* topk_out;      // selection output (select + attend), may be null
   void* out;
   float* lse;
@@ -147,7 +146,6 @@ inline AttendArgs make_attend_args(const Shape& s, const int32_t* block_table,
   a.qpos = q_pos;
   a.topk = topk;
   a.scores = scores;
-  a.clear = nullptr;
   a.topk_out = topk_out;
   a.out = out;
   a.lse = lse;
@@ -231,20 +229,6 @@ constexpr int kSpinLimit = 1 << 20;
 // the kernels that attend a unit (given selection, selection made in-kernel)
 // must round it alike.
 
-// Returns the unit's row of the scores to 0 once every reader is done with
-// it, so that the workspace is left as the call found it.
-__device__ __forceinline__ void clear_row(const AttendArgs& a, int u, int nw) {
-  uint32_t* row = a.clear + (size_t)u * a.MB;
-  const int nt = 64 * nw;
-  // words up to the first 16-byte boundary, 16-byte stores, then the tail
-  const int head = min(a.MB, (int)(((16 - (reinterpret_cast<uintptr_t>(row) & 15)) & 15) >> 2));
-  if ((int)threadIdx.x < head) row[threadIdx.x] = 0u;
-  uint4* v = reinterpret_cast<uint4*>(row + head);
-  const int nv = (a.MB - head) >> 2;
-  for (int i = threadIdx.x; i < nv; i += nt) v[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int jj = head + 4 * nv + (int)threadIdx.x; jj < a.MB; jj += nt) row[jj] = 0u;
-}
-
 // Where a task's selection comes from.
 enum SelMode {
   kSelGiven = 0,  // topk_idx, an input
@@ -324,7 +308,6 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
       }
     }
     group_select<NW>(keys, rb, a.K, a.init, a.local, tmax, gsl, sel_lds, sel_w[wave]);
-    if (a.clear && part.S == 1) clear_row(a, u, NW);
     // the selection in ascending order, as msa_block_topk stores it: the
     // blocks are then attended in the same order as from a given selection
     sorted_sel = sort_selection(lane < a.K ? sel_w[wave][lane] : -1, a.K);
@@ -701,8 +684,6 @@ __device__ __forceinline__ void attend_task(const uint16_t* __restrict__ q,
         zm[2 * qd + 1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
-    // every split has finished its selection: the scores row is free
-    if (SELECT && a.clear) clear_row(a, u, NW);
   }
 }
 

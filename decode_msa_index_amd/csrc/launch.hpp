@@ -73,16 +73,13 @@ hipError_t launch_sparse_attend(const Shape& s, const void* q, const void* kv_da
                                 hipStream_t st);
 // Selection fused into the attention kernel (msa_decode): needs the row's
 // block keys in LDS, so only for block tables short enough.  The split-K
-// partials in workspace must be zero (they are left zero).  clear_scores
-// (nullable): the scores array (the workspace's), zeroed again by each
-// unit's last reader.
+// partials in workspace must be zero (they are left zero).
 bool select_fusable(const Shape& s);
 hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_data,
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, uint32_t* status, float* clear_scores,
-                                hipStream_t st);
+                                void* workspace, uint32_t* status, hipStream_t st);
 // Chunks of many rows per sequence (chunked prefill): the attention grouped
 // by key block (k2q_attend.hip).  launch_sparse_attend takes this path when
 // k2q_eligible; its workspace is the status header and the split zone, both

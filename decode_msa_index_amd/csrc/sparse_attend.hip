@@ -302,11 +302,9 @@ hipError_t launch_select_attend(const Shape& s, const void* q, const void* kv_da
                                 const void* kv_scales, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* q_pos,
                                 const float* scores, int32_t* topk_out, void* out, float* lse,
-                                void* workspace, uint32_t* status, float* clear_scores,
-                                hipStream_t st) {
+                                void* workspace, uint32_t* status, hipStream_t st) {
   AttendArgs a =
       make_attend_args(s, block_table, seq_lens, q_pos, nullptr, scores, topk_out, out, lse);
-  a.clear = reinterpret_cast<uint32_t*>(clear_scores);
   return launch_mfma<true>(s, attend_config(s), a, q, kv_data, kv_scales, workspace, status,
                            false, st);
 }

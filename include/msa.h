@@ -160,7 +160,10 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  *     zone described below (which that path leaves alone) followed by the
  *     key-block path's buffers (see msa_sparse_attend): about 4.3 KB per
  *     (row, group, top-k slot), 1.1 GB for 4,096 rows at G = 4, top-16;
- *   - msa_decode: B*R*G*MB words for the pooled scores, then that;
+ *   - msa_decode: msa_sparse_attend's part, or at least the status header
+ *     and the whole zone described below (256 + 4,259,840 bytes), then
+ *     B*R*G*MB words for the pooled scores: they lie past the zone, every
+ *     call writes all of them before reading them, and they are not cleared;
  *   - the other calls: 0.
  * Every region is rounded up to 256 bytes, and a workspace that holds
  * partial states starts with a 256-byte status header.  The workspace is
@@ -172,8 +175,8 @@ msa_status msa_check_problem(const msa_problem* p, int32_t op);
  * each other through it, and a word still zero means "not yet written".
  * Every msa_decode and msa_sparse_attend call leaves that part zero-filled
  * again, so one zero fill serves any sequence of calls and problem shapes;
- * past it a call may leave its scratch (the key-block path's lists and
- * partials, pooled scores that reach past the zone).  msa_sparse_attend
+ * past it a call may leave its scratch (msa_decode's pooled scores, the
+ * key-block path's lists and partials).  msa_sparse_attend
  * itself needs no initialisation (it clears what it uses).  Calls that
  * share a workspace must not overlap.  A call whose size is 0 accepts a
  * NULL workspace.
@@ -263,8 +266,9 @@ msa_status msa_sparse_attend(const msa_problem* p, const void* q, const void* kv
  * per sequence, longer tables and fp32 caches run the three calls' kernels
  * in turn.
  * topk_idx receives the selection; block_scores (nullable) receives the
- * pooled scores.  workspace: msa_workspace_bytes(p, 3) bytes, zero-filled
- * before its first use (see msa_workspace_bytes) and left zero-filled.
+ * pooled scores.  workspace: msa_workspace_bytes(p, 3) bytes, its first
+ * 256 + 4,259,840 bytes zero-filled before its first use and left
+ * zero-filled (see msa_workspace_bytes).
  */
 msa_status msa_decode(const msa_problem* p, const void* index_q, const void* ik_data,
                       const void* ik_scales, const void* q, const void* kv_data,

@@ -108,10 +108,11 @@ def test_workspace_sizes():
     a = msa.workspace_bytes(p, msa.OP_ATTEND)
     d = msa.workspace_bytes(p, msa.OP_DECODE)
     scores = 8 * 4 * 2049 * 4
+    zone_end = 256 + 512 * 16 * 130 * 4  # the status header and the split-K zone
     assert d % 256 == 0 and a % 256 == 0
-    # decode: the attention's part (status header + partials), then the
-    # pooled scores rounded up to 256
-    assert d - a == -(-scores // 256) * 256
+    # decode: the pooled scores (rounded up to 256) after the status header
+    # and the whole split zone, which every call leaves zero
+    assert a < zone_end and d == zone_end + -(-scores // 256) * 256
     # a 256-byte status header, then the split partials: 16 heads x (128
     # outputs + max + denominator) per split
     units = 8 * 4
@@ -119,7 +120,7 @@ def test_workspace_sizes():
     assert S >= 2 and a == 256 + -(-(units * S * 16 * 130 * 4) // 256) * 256
     big = good(num_seqs=512, max_blocks_per_seq=16)
     assert msa.workspace_bytes(big, msa.OP_ATTEND) == 0  # enough (row, group)s: no split
-    assert msa.workspace_bytes(big, msa.OP_DECODE) == 256 + 512 * 4 * 16 * 4
+    assert msa.workspace_bytes(big, msa.OP_DECODE) == zone_end + 512 * 4 * 16 * 4
 
 
 def test_workspace_sizes_of_the_key_block_path():

@@ -397,7 +397,7 @@ def test_decode_equals_chain_and_is_deterministic():
                 first = now
             else:
                 assert all(torch.equal(x, y) for x, y in zip(first, now)), "decode not deterministic"
-            assert int(torch.count_nonzero(dw.ws_decode)) == 0, "workspace not left zero-filled"
+            assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0, "workspace not left zero-filled"
 
 
 def test_decode_in_graph_replays_match_eager():
@@ -431,7 +431,7 @@ def test_decode_in_graph_replays_match_eager():
         for x, y in zip(ref, (dw.scores, dw.topk, dw.out, dw.lse)):
             assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                                y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
-        assert int(torch.count_nonzero(dw.ws_decode)) == 0
+        assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0
 
 
 def test_repeated_decode_never_stalls():
@@ -455,7 +455,7 @@ def test_repeated_decode_never_stalls():
     assert elapsed < 0.5, f"40 decodes took {elapsed:.3f} s: a merge waited for its spin limit"
     assert torch.isfinite(dw.out.float()).all()
     assert torch.equal(dw.out.view(torch.uint8), ref)
-    assert int(torch.count_nonzero(dw.ws_decode)) == 0
+    assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0
 
 
 def test_nan_in_cache_reaches_the_output_without_stalling_the_merge():
@@ -488,7 +488,7 @@ def test_nan_in_cache_reaches_the_output_without_stalling_the_merge():
     mask = torch.ones_like(out, dtype=torch.bool)
     mask[b, heads, d] = False
     assert torch.equal(out[mask], ref[mask])
-    assert int(torch.count_nonzero(dw.ws_decode)) == 0
+    assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0
 
 
 def _cache_write_inputs(kv, ik, q_dtype, iq_dtype, seed, spikes=True, G=4, H=64):
@@ -711,7 +711,7 @@ def test_merge_timeout_is_reported():
     dw.decode(with_scores=False)
     assert msa.workspace_status(dw.ws_decode) == 0
     assert torch.equal(dw.out.float(), ref)
-    assert int(torch.count_nonzero(dw.ws_decode)) == 0
+    assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0
     dw.sparse_attend()  # clears its workspace first
     assert msa.workspace_status(dw.ws_attend) == 0
     assert torch.isfinite(dw.out.float()).all()
@@ -803,13 +803,12 @@ def test_decode_long_block_table_unfused_path(lens):
     """A block-table stride past the fused selection's LDS limit makes
     msa_decode take the three-kernel path; results follow the same rules.
     The status header and split zone are zero again afterwards: the pooled
-    scores kept in the workspace lie inside the zone for 3 sequences and
-    reach past it for 32, whose part past the zone may stay."""
+    scores kept in the workspace lie past the zone, where they may stay."""
     w = synth.make(f"wide-{len(lens)}", seed=91, seq_lens=lens, q_dtype=synth.BF16,
                    kv_dtype=synth.FP8, max_blocks=9000, plant_per_seq=3)
     dw, _ = _run_and_check(w, fused=True, name=f"wide-table-{len(lens)}")
     assert int(torch.count_nonzero(dw.ws_decode[:SPLIT_ZONE_BYTES])) == 0
-    assert (dw.ws_decode.numel() > SPLIT_ZONE_BYTES) == (len(lens) == 32)
+    assert dw.ws_decode.numel() > SPLIT_ZONE_BYTES
 
 
 # ---------------------------------------------------------------------------
